@@ -1,0 +1,84 @@
+"""Brute-force Sketch Attention at 50 significant digits (test infrastructure only).
+
+An independent second implementation used to pin the C oracle on tiny inputs.
+It materialises every score and every assignment weight as an ``mpmath``
+number with pure-Python loops, following the definitions of the SequenceO1
+paper, section 3.1 (scores P W_Q (X W_K)^T / sqrt(d), prototype-normalised
+assignment, sketch A X) and appendix A.4, with the history-axis reading as the
+default.  It never calls the C oracle and shares no code with it.
+"""
+from __future__ import annotations
+
+import mpmath
+
+mpmath.mp.dps = 50
+
+
+def _user_rows(b, cu, lengths, L_max, mask):
+    if cu is not None:
+        rows = list(range(int(cu[b]), int(cu[b + 1])))
+    else:
+        n = L_max if lengths is None else max(0, min(int(lengths[b]), L_max))
+        rows = [b * L_max + i for i in range(n)]
+    if mask is not None:
+        rows = [r for r in rows if int(mask[r]) != 0]
+    return rows
+
+
+def sketch_packed(P, K, V, cu, mask=None, norm="history", scale=None):
+    """Packed layout: K, V [rows][H][dh]; cu [B+1].  See :func:`_sketch`."""
+    return _sketch(P, K, V, len(cu) - 1, lambda b: _user_rows(b, cu, None, 0, mask), norm, scale)
+
+
+def sketch_dense(P, K, V, B, L_max, lengths=None, mask=None, norm="history", scale=None):
+    """Dense layout flattened to rows: K, V [B*L_max][H][dh]."""
+    return _sketch(P, K, V, B, lambda b: _user_rows(b, None, lengths, L_max, mask), norm, scale)
+
+
+def _sketch(P, K, V, B, rows_of, norm, scale):
+    """P [H][m][dh]; K, V [rows][H][dh] (any nested indexable of floats).
+
+    Returns (S [B][H][m][dh], A, lse) as mpf: A[b][h] is the materialised
+    [m][n_valid] assignment matrix; lse[b][h] is per prototype (history axis)
+    or per valid token (prototype axis), natural log, scale included.
+    """
+    H, m, dh = len(P), len(P[0]), len(P[0][0])
+    sc = mpmath.mpf(1) / mpmath.sqrt(dh) if scale is None else mpmath.mpf(scale)
+    S, W, LSE = [], [], []
+    for b in range(B):
+        rows = rows_of(b)
+        Sb, Wb, Lb = [], [], []
+        for h in range(H):
+            # scores s[j][t] = scale * <P[h][j], K[row_t][h]>
+            s = [[sc * mpmath.fsum(mpmath.mpf(float(P[h][j][e])) * mpmath.mpf(float(K[r][h][e]))
+                                   for e in range(dh)) for r in rows] for j in range(m)]
+            n = len(rows)
+            if norm == "history":
+                A, lse = [], []
+                for j in range(m):
+                    if n == 0:
+                        A.append([])
+                        lse.append(mpmath.mpf("-inf"))
+                        continue
+                    e_ = [mpmath.exp(x) for x in s[j]]
+                    Z = mpmath.fsum(e_)
+                    A.append([x / Z for x in e_])
+                    lse.append(mpmath.log(Z))
+            else:
+                A = [[mpmath.mpf(0)] * n for _ in range(m)]
+                lse = []
+                for t in range(n):
+                    e_ = [mpmath.exp(s[j][t]) for j in range(m)]
+                    Z = mpmath.fsum(e_)
+                    for j in range(m):
+                        A[j][t] = e_[j] / Z
+                    lse.append(mpmath.log(Z))
+            Sbh = [[mpmath.fsum(A[j][t] * mpmath.mpf(float(V[rows[t]][h][e])) for t in range(n))
+                    for e in range(dh)] for j in range(m)]
+            Sb.append(Sbh)
+            Wb.append(A)
+            Lb.append(lse)
+        S.append(Sb)
+        W.append(Wb)
+        LSE.append(Lb)
+    return S, W, LSE

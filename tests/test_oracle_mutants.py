@@ -1,0 +1,58 @@
+"""Plant plausible mistakes in copies of the oracle's C source (CPU only) and
+check that at least one pin rejects each copy.  This is what shows the pins
+are strong enough to trust the oracle: a dropped term, a wrong sign, a wrong
+index or a transposed operand anywhere in it must fail some pin."""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+from pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "sa_oracle.c")
+
+# (name, text in sa_oracle.c, replacement)
+MUTANTS = [
+    ("scale_dropped", "return acc * scale_of(pb);", "return acc;"),
+    ("scale_squared", "1.0 / sqrt((double)pb->dh)", "1.0 / (double)pb->dh"),
+    ("max_not_subtracted", "const double w = exp(s[t] - M);", "const double w = exp(s[t]);"),
+    ("sign_flipped", "const double w = exp(s[t] - M);", "const double w = exp(M - s[t]);"),
+    ("prototype_index_transposed", "((int64_t)h * pb->m + j) * pb->dh", "((int64_t)j * pb->H + h) * pb->dh"),
+    ("value_head_offset_dropped", "const int64_t vbase = rows[t] * vstride(pb) + (int64_t)h * pb->dh;",
+     "const int64_t vbase = rows[t] * vstride(pb);"),
+    ("key_head_offset_dropped", "const int64_t kbase = row * kstride(pb) + (int64_t)h * pb->dh;",
+     "const int64_t kbase = row * kstride(pb);"),
+    ("normaliser_skips_first_row", "        Z += w;\n", "        if (t > 0) Z += w;\n"),
+    ("not_normalised", "for (int e = 0; e < pb->dh; ++e) out[e] /= Z;", "(void)Z;"),
+    ("user_rows_off_by_one", "*count = (int64_t)cu[b + 1] - cu[b];", "*count = (int64_t)cu[b + 1] - cu[b] - 1;"),
+    ("mask_ignored", "if (mask && mask[row] == 0) continue;", "(void)mask;"),
+    ("dense_lengths_ignored", "int64_t len = lengths ? lengths[b] : pb->L_max;", "int64_t len = pb->L_max;"),
+    ("lse_missing_max", "*lse = M + log(Z);", "*lse = log(Z);"),
+    ("bf16_widening_wrong", "<< 16;", "<< 15;"),
+    ("prototype_axis_unnormalised", "const double a = exp(s[j] - M) / Z;", "const double a = exp(s[j] - M);"),
+    ("prototype_axis_wrong_max", "            if (s[j] > M) M = s[j];\n        }\n        double Z = 0.0;\n        for (int j = 0; j < m; ++j) Z += exp(s[j] - M);",
+     "        }\n        double Z = 0.0;\n        for (int j = 0; j < m; ++j) Z += exp(s[j] - M);"),
+    ("value_used_as_key", "acc += widen(P, pb->in_dtype, pbase + e) * widen(K, pb->in_dtype, kbase + e);",
+     "acc += widen(P, pb->in_dtype, pbase + e) * widen(K, pb->in_dtype, kbase + (pb->dh - 1 - e));"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    mutated = src.replace(old, new, 1)
+    with tempfile.TemporaryDirectory() as td:
+        path = os.path.join(td, "mutant.c")
+        with open(path, "w") as f:
+            f.write(mutated)
+        lib = oracle.build(extra_flags=("-w",), out=os.path.join(td, "libmutant.so"), src=path)
+        failed = []
+        with oracle.using(lib):
+            for pin in ALL_PINS:
+                try:
+                    pin()
+                except Exception as e:  # AssertionError, or a crash-free error path
+                    failed.append((pin.__name__, type(e).__name__))
+        assert failed, f"no pin rejects the mutant '{name}'"
