@@ -1,0 +1,201 @@
+/*
+ * sketchattn.h -- C ABI of libsketchattn, Sketch Attention (SA) on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * SA (SequenceO1 paper, section 3.1 "Sketch Attention (SA)" and appendix A.4)
+ * compresses one user's history of n behaviour rows into a fixed-size sketch
+ * of m rows ("prototypes", the paper's k):
+ *
+ *     score   s[j,i]     = scale * < P[h,j,:], K[i,h,:] >
+ *     weight  A[j,i]     = softmax of s over one axis (see sa_norm)
+ *     sketch  S[b,h,j,:] = sum_i A[j,i] * V[i,h,:]
+ *
+ * for every user b and head h.  The library computes it the way section 4.4
+ * (FlashSA) describes: score blocks, running softmax statistics (maximum and
+ * log-sum-exp) and the weighted aggregation are fused and streamed, so the
+ * m x n score matrix never reaches device memory, and a whole ragged batch of
+ * users is served by one pass.
+ *
+ * Conventions for every entry point below
+ *   - All data pointers are DEVICE memory owned by the caller; the library
+ *     never allocates, frees or retains them.  Inputs are read-only; outputs
+ *     are fully overwritten.
+ *   - Work is enqueued asynchronously on `stream`; no call synchronises with
+ *     the device or reads device memory from the host (offsets, lengths and
+ *     masks stay on the device).
+ *   - Results are deterministic: the same call on the same device gives
+ *     bitwise-identical outputs (fixed reduction order, no float atomics).
+ *   - Errors that the host can detect (null or misaligned pointers, bad
+ *     sizes, unsupported shapes, a short workspace) return a non-zero status
+ *     before anything is enqueued; sa_last_error() then describes it.  No C++
+ *     exception crosses this interface.  Offsets and lengths are NOT checked
+ *     on the device: they must satisfy the stated rules or results are
+ *     undefined.
+ *   - Thread safety: calls may be made from several host threads; the only
+ *     per-thread state is the error text and the timing events below.
+ */
+#ifndef SKETCHATTN_H
+#define SKETCHATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SA_VERSION_MAJOR 0
+#define SA_VERSION_MINOR 1
+#define SA_VERSION_PATCH 0
+
+typedef enum sa_status {
+    SA_OK = 0,
+    SA_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, negative or inconsistent size */
+    SA_ERR_UNSUPPORTED = 2,  /* valid request outside the compiled shapes (see sa_forward) */
+    SA_ERR_WORKSPACE = 3,    /* workspace pointer null or smaller than the query says */
+    SA_ERR_HIP = 4           /* the HIP runtime reported an error when launching */
+} sa_status;
+
+/* Element type of P, K, V (and X, Wk, Wv). */
+typedef enum sa_dtype {
+    SA_DTYPE_F32 = 0,  /* IEEE binary32; no rounding to a narrower type anywhere */
+    SA_DTYPE_BF16 = 1  /* bfloat16 storage; products accumulate in fp32 */
+} sa_dtype;
+
+/*
+ * Which axis the softmax normalises.
+ *   SA_NORM_HISTORY   (default) one distribution per prototype over the
+ *                     user's valid rows: sum_i A[j,i] = 1.  With P = 0 the
+ *                     sketch is the mean of V.  This is the prototype-query
+ *                     attention S = softmax_L(P_h K_b^T * scale) V_b.
+ *   SA_NORM_PROTOTYPE one distribution per row over the m prototypes:
+ *                     sum_j A[j,i] = 1 -- the normalisation display of the
+ *                     paper's section 3.1 -- with the sketch X~ = A V taken
+ *                     as written (no renormalisation over rows).
+ */
+typedef enum sa_norm {
+    SA_NORM_HISTORY = 0,
+    SA_NORM_PROTOTYPE = 1
+} sa_norm;
+
+typedef struct sa_problem {
+    int32_t B;              /* users (>= 0) */
+    int32_t H;              /* heads (>= 1) */
+    int32_t m;              /* prototypes per head (>= 1) */
+    int32_t dh;             /* width of one head (>= 1) */
+    int64_t total_rows;     /* rows of the K/V (or X) buffers; packed: >= cu_offsets[B];
+                               dense: 0 or >= B * L_max */
+    int32_t L_max;          /* dense layout: row slots per user; must be 0 for packed */
+    int32_t dtype;          /* sa_dtype */
+    int32_t norm;           /* sa_norm */
+    float scale;            /* score scale; 0 means 1/sqrt(dh) */
+    int64_t k_row_stride;   /* elements between consecutive rows of K; 0 means H*dh */
+    int64_t v_row_stride;   /* elements between consecutive rows of V; 0 means H*dh */
+    int64_t q_batch_stride; /* elements between users' prototype sets in P; 0 means one
+                               shared set P[H, m, dh] (the paper shares prototypes
+                               across users, section 3.1) */
+    int32_t chunk_rows;     /* 0: automatic work split over the device; > 0: every work
+                               segment covers this many rows (multiple of 32) */
+    int32_t flags;          /* reserved, must be 0 */
+} sa_problem;
+
+/*
+ * Sketch Attention forward over a ragged batch of user histories.
+ *
+ * Operation: SequenceO1 paper, section 3.1 (scores, normalisation, sketch
+ * construction) and appendix A.4; fused and streamed as in section 4.4.
+ *
+ * P           [H, m, dh] (or [B, ...] via q_batch_stride), dtype.  Head h uses
+ *             P[h]; head h of a row is its channels [h*dh, (h+1)*dh).
+ * K, V        packed: [total_rows, H, dh] rows, user b owning rows
+ *             [cu_offsets[b], cu_offsets[b+1]);
+ *             dense (cu_offsets == NULL): [B, L_max, H, dh], user b owning
+ *             rows b*L_max + [0, len_b), len_b = min(lengths[b], L_max), or
+ *             L_max when lengths == NULL.  dh is contiguous and the H heads
+ *             of a row are contiguous; rows are k_row_stride / v_row_stride
+ *             elements apart.  bf16 rows must start on 16-byte boundaries.
+ * cu_offsets  int32 [B+1], non-decreasing, cu_offsets[0] >= 0,
+ *             cu_offsets[B] <= total_rows; rows outside every user are never
+ *             read.  NULL selects the dense layout.
+ * lengths     int32 [B] (dense only, optional); negative counts as 0.
+ * mask        uint8, one byte per row of the K/V buffers (dense: [B, L_max]),
+ *             optional; 0 excludes the row (it is never read as a number, so
+ *             NaN or Inf there cannot leak).  A user with no valid row is
+ *             empty.
+ * S_out       float32 [B, H, m, dh].  Empty users get 0.
+ * lse_out     optional float32.  HISTORY: [B, H, m], natural-log
+ *             log-sum-exp of the scaled scores over the user's valid rows
+ *             (-inf for empty users).  PROTOTYPE: [total_rows, H], the
+ *             log-sum-exp over the m prototypes of each row (-inf for rows
+ *             that are masked or belong to no user).
+ * workspace   device scratch of at least sa_forward_workspace_size(pb)
+ *             bytes, 256-byte aligned; contents need no initialisation and
+ *             are clobbered.  May be NULL when the query returns 0.
+ * stream      HIP stream the work is enqueued on.
+ *
+ * Compiled shapes: bf16: dh in {32, 64, 128}, m a multiple of 16.
+ * f32: dh in {16, 32, 64, 128}, any m.  Others return SA_ERR_UNSUPPORTED.
+ */
+sa_status sa_forward(const sa_problem* pb, const void* P, const void* K, const void* V,
+                     const int32_t* cu_offsets, const int32_t* lengths, const uint8_t* mask,
+                     float* S_out, float* lse_out, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* Bytes of workspace sa_forward needs for this problem on the current device
+ * (0 if the problem itself is invalid; sa_last_error() then says why). */
+size_t sa_forward_workspace_size(const sa_problem* pb);
+
+/*
+ * Fused key/value projection + Sketch Attention forward (packed layout only).
+ *
+ * Operation: the key projection K = X W_K of the paper's section 3.1 scores
+ * (costed in appendix G.3), and V = X W_V, computed on chip tile by tile and
+ * consumed at once by the sa_forward computation above, so K and V never
+ * reach device memory.  K and V are rounded to bf16 before the score and
+ * aggregation products (fp32 accumulation throughout).
+ *
+ * X        [total_rows, d_model], dtype (bf16 only), rows 16-byte aligned.
+ * Wk, Wv   [d_model, H*dh] row-major: K[i, h*dh + e] = sum_c X[i,c] Wk[c, h*dh + e].
+ *          Wv == NULL means V = X (the paper's sketch aggregates X itself,
+ *          section 3.1); that requires H*dh == d_model.
+ * P, cu_offsets, mask, S_out, lse_out, workspace, stream: as for sa_forward
+ *          (pb->L_max must be 0, pb->k_row_stride and v_row_stride are ignored).
+ *
+ * Compiled shapes: bf16, d_model in {128, 256}, dh == 32, m a multiple of 16,
+ * H*dh a multiple of 64.
+ */
+sa_status sa_forward_fused_proj(const sa_problem* pb, const void* X, int32_t d_model,
+                                const void* Wk, const void* Wv, const void* P,
+                                const int32_t* cu_offsets, const uint8_t* mask,
+                                float* S_out, float* lse_out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace sa_forward_fused_proj needs on the current device. */
+size_t sa_forward_fused_proj_workspace_size(const sa_problem* pb, int32_t d_model);
+
+/*
+ * Timing hook for benchmarks and profilers (not part of the computation).
+ * When both events are non-NULL, the next sa_forward or sa_forward_fused_proj
+ * call made on this host thread records `start` on its stream immediately
+ * before the streaming kernel (the pass over K/V or X) and `stop` immediately
+ * after it, then forgets both.  NULL, NULL clears a pending request.  The
+ * events belong to the caller (hipEventCreate); the library never creates,
+ * waits on or destroys them.  Returns SA_ERR_INVALID_ARG if exactly one is NULL.
+ */
+sa_status sa_set_timing_events(hipEvent_t start, hipEvent_t stop);
+
+/* Static text for a status code. */
+const char* sa_status_string(sa_status status);
+
+/* Detail of the last failing call on this host thread ("" if none). */
+const char* sa_last_error(void);
+
+/* SA_VERSION_MAJOR * 10000 + SA_VERSION_MINOR * 100 + SA_VERSION_PATCH. */
+int sa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKETCHATTN_H */

@@ -1,0 +1,243 @@
+"""Python binding of libsketchattn (Sketch Attention on MI355X / gfx950).
+
+A thin ctypes layer over the C ABI declared in ``include/sketchattn.h``: it
+checks torch tensors, allocates outputs and the workspace with torch, and
+passes raw device pointers and the current HIP stream.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.  If the
+library is not built this module raises on import of the compute functions.
+
+Names follow the C ABI: :func:`sa_forward`, :func:`sa_forward_fused_proj`,
+:func:`sa_forward_workspace_size`, :func:`sa_status_string`,
+:func:`sa_last_error`, :func:`sa_version`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsketchattn.so")
+
+SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
+SA_DTYPE_F32, SA_DTYPE_BF16 = 0, 1
+SA_NORM_HISTORY, SA_NORM_PROTOTYPE = 0, 1
+_NORMS = {"history": SA_NORM_HISTORY, "prototype": SA_NORM_PROTOTYPE}
+
+EXPORTED = ("sa_forward", "sa_forward_workspace_size", "sa_forward_fused_proj",
+            "sa_forward_fused_proj_workspace_size", "sa_set_timing_events", "sa_status_string", "sa_last_error",
+            "sa_version")
+
+
+class SaProblem(ctypes.Structure):
+    """Mirror of ``sa_problem`` in include/sketchattn.h."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("m", ctypes.c_int32), ("dh", ctypes.c_int32),
+        ("total_rows", ctypes.c_int64),
+        ("L_max", ctypes.c_int32), ("dtype", ctypes.c_int32), ("norm", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("k_row_stride", ctypes.c_int64), ("v_row_stride", ctypes.c_int64),
+        ("q_batch_stride", ctypes.c_int64),
+        ("chunk_rows", ctypes.c_int32), ("flags", ctypes.c_int32),
+    ]
+
+
+class SketchAttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{sa_status_string(status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str | None = None):
+    """Load libsketchattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"libsketchattn.so not found at {p}; run `python -m sketch_attention_flashsa_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, pp = ctypes.c_void_p, ctypes.POINTER(SaProblem)
+    lib.sa_forward.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.sa_forward.restype = ctypes.c_int
+    lib.sa_forward_workspace_size.argtypes = [pp]
+    lib.sa_forward_workspace_size.restype = ctypes.c_size_t
+    lib.sa_forward_fused_proj.argtypes = [pp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.sa_forward_fused_proj.restype = ctypes.c_int
+    lib.sa_forward_fused_proj_workspace_size.argtypes = [pp, ctypes.c_int32]
+    lib.sa_forward_fused_proj_workspace_size.restype = ctypes.c_size_t
+    lib.sa_status_string.argtypes = [ctypes.c_int]
+    lib.sa_status_string.restype = ctypes.c_char_p
+    lib.sa_last_error.argtypes = []
+    lib.sa_last_error.restype = ctypes.c_char_p
+    lib.sa_version.argtypes = []
+    lib.sa_version.restype = ctypes.c_int
+    lib.sa_set_timing_events.argtypes = [vp, vp]
+    lib.sa_set_timing_events.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def sa_set_timing_events(start, stop) -> None:
+    """Record HIP events ``start``/``stop`` (raw hipEvent_t handles, or None)
+    around the streaming kernel of the next forward call on this thread."""
+    _check(load_library().sa_set_timing_events(start, stop))
+
+
+def sa_status_string(status: int) -> str:
+    return load_library().sa_status_string(int(status)).decode()
+
+
+def sa_last_error() -> str:
+    return load_library().sa_last_error().decode()
+
+
+def sa_version() -> int:
+    return int(load_library().sa_version())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def make_problem(B, H, m, dh, total_rows, L_max=0, dtype="bf16", norm="history", scale=0.0,
+                 k_row_stride=0, v_row_stride=0, q_batch_stride=0, chunk_rows=0) -> SaProblem:
+    return SaProblem(B=B, H=H, m=m, dh=dh, total_rows=total_rows, L_max=L_max,
+                     dtype=SA_DTYPE_BF16 if dtype == "bf16" else SA_DTYPE_F32,
+                     norm=_NORMS[norm], scale=float(scale or 0.0), k_row_stride=k_row_stride,
+                     v_row_stride=v_row_stride, q_batch_stride=q_batch_stride, chunk_rows=chunk_rows, flags=0)
+
+
+def sa_forward_workspace_size(pb: SaProblem) -> int:
+    return int(load_library().sa_forward_workspace_size(ctypes.byref(pb)))
+
+
+def _check(status):
+    if status != SA_OK:
+        raise SketchAttnError(status, sa_last_error())
+
+
+def _dtype_name(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return "bf16"
+    if t.dtype == torch.float32:
+        return "f32"
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def sa_forward(P, K, V, cu_offsets=None, lengths=None, mask=None, norm: str = "history",
+               return_lse: bool = False, scale: float | None = None, chunk_rows: int = 0,
+               workspace=None, out=None):
+    """Sketch Attention forward on the GPU.
+
+    P: [H, m, dh] (or [B, H, m, dh] per-user prototypes), bf16 or fp32.
+    K, V: packed [rows, H, dh] with ``cu_offsets`` int32 [B+1], or dense
+    [B, L_max, H, dh] (``cu_offsets`` None) with optional ``lengths`` int32 [B].
+    ``mask``: uint8/bool per buffer row ([rows] or [B, L_max]), 0 = excluded.
+    Returns S [B, H, m, dh] float32, and lse when ``return_lse``
+    ([B, H, m] history axis; [rows, H] prototype axis).
+    """
+    import torch
+    lib = load_library()
+    dt = _dtype_name(K)
+    if P.dtype != K.dtype or V.dtype != K.dtype:
+        raise TypeError("P, K and V must share one dtype")
+    dev = K.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    for name, t in (("P", P), ("K", K), ("V", V)):
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    per_user = P.dim() == 4
+    H, m, dh = P.shape[-3:]
+    if cu_offsets is not None:
+        if K.dim() != 3 or K.shape[1:] != (H, dh) or V.shape != K.shape:
+            raise ValueError(f"packed K/V must be [rows, {H}, {dh}]; got {tuple(K.shape)}, {tuple(V.shape)}")
+        if cu_offsets.dtype != torch.int32 or cu_offsets.device != dev or cu_offsets.dim() != 1:
+            raise ValueError("cu_offsets must be a 1-D int32 tensor on the same device")
+        if lengths is not None:
+            raise ValueError("lengths is only valid for the dense layout")
+        B = cu_offsets.numel() - 1
+        rows, L_max = K.shape[0], 0
+    else:
+        if K.dim() != 4 or K.shape[2:] != (H, dh) or V.shape != K.shape:
+            raise ValueError(f"dense K/V must be [B, L_max, {H}, {dh}]; got {tuple(K.shape)}")
+        B, L_max = K.shape[0], K.shape[1]
+        rows = B * L_max
+        if lengths is not None and (lengths.dtype != torch.int32 or lengths.numel() != B or lengths.device != dev):
+            raise ValueError("lengths must be an int32 tensor [B] on the same device")
+    if per_user and P.shape[0] != B:
+        raise ValueError("per-user P must be [B, H, m, dh]")
+    # rows must be contiguous in dh and heads; the row stride may be larger
+    ks = K.stride(-3) if cu_offsets is not None else K.stride(1)
+    vs = V.stride(-3) if cu_offsets is not None else V.stride(1)
+    for t in (K, V):
+        if t.stride(-1) != 1 or t.stride(-2) != dh:
+            raise ValueError("K/V rows must be contiguous [H, dh]")
+    if cu_offsets is None and (K.stride(0) != L_max * ks or V.stride(0) != L_max * vs):
+        raise ValueError("dense K/V must have uniform row strides")
+    P = P.contiguous()
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.to(torch.uint8)
+        if mask.dtype != torch.uint8 or mask.numel() != rows or mask.device != dev:
+            raise ValueError(f"mask must be uint8/bool with {rows} elements on the same device")
+        mask = mask.contiguous()
+    pb = make_problem(B, H, m, dh, rows, L_max=L_max, dtype=dt, norm=norm, scale=scale or 0.0,
+                      k_row_stride=ks, v_row_stride=vs, q_batch_stride=(H * m * dh if per_user else 0),
+                      chunk_rows=chunk_rows)
+    nws = sa_forward_workspace_size(pb)
+    if nws == 0:
+        _check(lib.sa_forward(ctypes.byref(pb), None, None, None, None, None, None, None, None, None, 0, None))
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    S = out if out is not None else torch.empty((B, H, m, dh), dtype=torch.float32, device=dev)
+    lse = None
+    if return_lse:
+        lse = torch.empty((B, H, m) if norm == "history" else (rows, H), dtype=torch.float32, device=dev)
+    st = lib.sa_forward(ctypes.byref(pb), _ptr(P), _ptr(K), _ptr(V), _ptr(cu_offsets), _ptr(lengths), _ptr(mask),
+                        _ptr(S), _ptr(lse), _ptr(workspace), nws, _stream_handle(dev))
+    _check(st)
+    return (S, lse) if return_lse else S
+
+
+def sa_forward_fused_proj(X, Wk, Wv, P, cu_offsets, mask=None, norm: str = "history", return_lse: bool = False,
+                          scale: float | None = None, chunk_rows: int = 0, workspace=None, out=None):
+    """Fused K/V projection + Sketch Attention: K = X Wk, V = X Wv (V = X when
+    ``Wv`` is None) computed on chip.  X [rows, d_model] bf16, Wk/Wv
+    [d_model, H*dh], P [H, m, dh], cu_offsets int32 [B+1]."""
+    import torch
+    lib = load_library()
+    dev = X.device
+    H, m, dh = P.shape
+    rows, d_model = X.shape
+    B = cu_offsets.numel() - 1
+    for t in (X, Wk, P) + ((Wv,) if Wv is not None else ()):
+        if t.device != dev or t.dtype != X.dtype:
+            raise ValueError("X, Wk, Wv and P must share one device and dtype")
+    X, Wk, P = X.contiguous(), Wk.contiguous(), P.contiguous()
+    Wv = Wv.contiguous() if Wv is not None else None
+    if mask is not None:
+        mask = (mask.to(torch.uint8) if mask.dtype == torch.bool else mask).contiguous()
+    pb = make_problem(B, H, m, dh, rows, dtype=_dtype_name(X), norm=norm, scale=scale or 0.0, chunk_rows=chunk_rows)
+    nws = int(lib.sa_forward_fused_proj_workspace_size(ctypes.byref(pb), int(d_model)))
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    S = out if out is not None else torch.empty((B, H, m, dh), dtype=torch.float32, device=dev)
+    lse = None
+    if return_lse:
+        lse = torch.empty((B, H, m) if norm == "history" else (rows, H), dtype=torch.float32, device=dev)
+    st = lib.sa_forward_fused_proj(ctypes.byref(pb), _ptr(X), int(d_model), _ptr(Wk), _ptr(Wv), _ptr(P),
+                                   _ptr(cu_offsets), _ptr(mask), _ptr(S), _ptr(lse), _ptr(workspace), nws,
+                                   _stream_handle(dev))
+    _check(st)
+    return (S, lse) if return_lse else S

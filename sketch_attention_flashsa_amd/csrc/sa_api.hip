@@ -1,0 +1,318 @@
+// sa_api.hip -- host side of the libsketchattn C ABI (include/sketchattn.h):
+// argument validation, work split, workspace layout and kernel dispatch.
+// Nothing here reads device memory or synchronises; every launch goes to the
+// caller's stream.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "sa_internal.h"
+#include "sketchattn.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+
+sa_status fail(sa_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+struct DeviceInfo {
+    int cus = 256;
+    size_t lds = 65536;
+};
+
+DeviceInfo device_info() {
+    static std::mutex mu;
+    static DeviceInfo cache[64];
+    static bool known[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DeviceInfo{};
+    std::lock_guard<std::mutex> lock(mu);
+    if (!known[dev]) {
+        int cus = 0, lds = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+            cache[dev].cus = cus;
+        if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && lds > 0)
+            cache[dev].lds = (size_t)lds;
+        known[dev] = true;
+    }
+    return cache[dev];
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+constexpr int kRowMinBf16 = 512;   // smallest automatic segment (rows)
+constexpr int kRowMinF32 = 128;
+
+// Everything the dispatcher derives from the problem.
+struct Plan {
+    bool f32 = false;
+    bool packed = true;
+    int64_t buf_rows = 0;     // rows of the K/V buffers the kernels may address
+    int G = 1;                // row-range blocks
+    int R_fixed = 0, R_min = kRowMinBf16;
+    sa::Bf16Config cfg{};
+    int groups = 1;           // bf16: unit groups per row range
+    // workspace layout (byte offsets)
+    size_t off_vcu = 0, off_M = 0, off_Z = 0, off_acc = 0, off_tok = 0, total = 0;
+};
+
+// Validation and work split shared by every entry point.  The workspace size
+// depends only on the problem description, never on which optional pointers
+// a call passes, so the size query and the call always agree.
+sa_status make_plan(const sa_problem* pb, bool packed, Plan* pl) {
+    if (!pb) return fail(SA_ERR_INVALID_ARG, "problem is NULL");
+    if (pb->B < 0 || pb->H < 1 || pb->m < 1 || pb->dh < 1)
+        return fail(SA_ERR_INVALID_ARG, "need B >= 0, H >= 1, m >= 1, dh >= 1 (got B=%d H=%d m=%d dh=%d)", pb->B,
+                    pb->H, pb->m, pb->dh);
+    if (pb->dtype != SA_DTYPE_F32 && pb->dtype != SA_DTYPE_BF16)
+        return fail(SA_ERR_INVALID_ARG, "unknown dtype %d", pb->dtype);
+    if (pb->norm != SA_NORM_HISTORY && pb->norm != SA_NORM_PROTOTYPE)
+        return fail(SA_ERR_INVALID_ARG, "unknown norm %d", pb->norm);
+    if (pb->flags != 0) return fail(SA_ERR_INVALID_ARG, "flags must be 0");
+    if (pb->total_rows < 0 || pb->total_rows > INT32_MAX)
+        return fail(SA_ERR_INVALID_ARG, "total_rows must be in [0, 2^31)");
+    if (pb->chunk_rows < 0 || pb->chunk_rows % sa::kRowAlign != 0)
+        return fail(SA_ERR_INVALID_ARG, "chunk_rows must be 0 or a positive multiple of %d", sa::kRowAlign);
+    if (!(pb->scale >= 0.f) || isinf(pb->scale)) return fail(SA_ERR_INVALID_ARG, "scale must be finite and >= 0");
+    const int64_t hd = (int64_t)pb->H * pb->dh;
+    if ((pb->k_row_stride != 0 && pb->k_row_stride < hd) || (pb->v_row_stride != 0 && pb->v_row_stride < hd))
+        return fail(SA_ERR_INVALID_ARG, "row strides must be 0 or >= H*dh");
+    if (pb->q_batch_stride < 0) return fail(SA_ERR_INVALID_ARG, "q_batch_stride must be >= 0");
+    if (pb->q_batch_stride != 0 && pb->q_batch_stride < (int64_t)pb->H * pb->m * pb->dh)
+        return fail(SA_ERR_INVALID_ARG, "q_batch_stride must be 0 or >= H*m*dh");
+    if ((int64_t)pb->H * pb->m * pb->dh > INT32_MAX) return fail(SA_ERR_INVALID_ARG, "H*m*dh too large");
+
+    pl->f32 = pb->dtype == SA_DTYPE_F32;
+    pl->packed = packed;
+    if (pb->L_max < 0) return fail(SA_ERR_INVALID_ARG, "L_max must be >= 0");
+    if (packed && pb->L_max != 0) return fail(SA_ERR_INVALID_ARG, "L_max must be 0 with cu_offsets");
+    const int64_t need = (int64_t)pb->B * pb->L_max;
+    if (need > INT32_MAX) return fail(SA_ERR_INVALID_ARG, "B*L_max must be < 2^31");
+    if (pb->L_max > 0 && pb->total_rows != 0 && pb->total_rows < need)
+        return fail(SA_ERR_INVALID_ARG, "dense layout: total_rows (%lld) < B*L_max (%lld)",
+                    (long long)pb->total_rows, (long long)need);
+    pl->buf_rows = pb->total_rows > need ? pb->total_rows : need;
+    if (pl->f32) {
+        if (!(pb->dh == 16 || pb->dh == 32 || pb->dh == 64 || pb->dh == 128))
+            return fail(SA_ERR_UNSUPPORTED, "f32: dh must be 16, 32, 64 or 128 (got %d)", pb->dh);
+    } else {
+        if (!(pb->dh == 32 || pb->dh == 64 || pb->dh == 128) || pb->m % 16 != 0)
+            return fail(SA_ERR_UNSUPPORTED, "bf16: dh must be 32, 64 or 128 and m a multiple of 16 (got dh=%d m=%d)",
+                        pb->dh, pb->m);
+        if (!sa::bf16_config(pb->dh, pb->m, pb->H, device_info().lds, &pl->cfg))
+            return fail(SA_ERR_UNSUPPORTED, "bf16: tile needs %zu bytes of LDS, device allows %zu",
+                        pl->cfg.lds_bytes, device_info().lds);
+        const int64_t ks = pb->k_row_stride ? pb->k_row_stride : hd;
+        const int64_t vs = pb->v_row_stride ? pb->v_row_stride : hd;
+        if (ks % 8 != 0 || vs % 8 != 0 || pb->q_batch_stride % 8 != 0)
+            return fail(SA_ERR_UNSUPPORTED, "bf16: row strides and q_batch_stride must be multiples of 8 elements");
+    }
+
+    const DeviceInfo dev = device_info();
+    int per_row_range, blocks_per_cu;
+    if (pl->f32) {
+        per_row_range = pb->H * ((pb->m + 255) / 256);
+        blocks_per_cu = 4;
+        pl->R_min = kRowMinF32;
+    } else {
+        const int units = pb->H * (pb->m / pl->cfg.protos_per_wave);
+        pl->groups = (units + pl->cfg.waves - 1) / pl->cfg.waves;
+        per_row_range = pl->groups;
+        blocks_per_cu = pl->cfg.blocks_per_cu;
+        pl->R_min = kRowMinBf16;
+    }
+    const int64_t rows_upper = pb->L_max > 0 ? need : pb->total_rows;
+    if (pb->chunk_rows > 0) {
+        pl->R_fixed = pb->chunk_rows;
+        const int64_t G = (rows_upper + pb->chunk_rows - 1) / pb->chunk_rows;
+        pl->G = (int)(G > 0 ? G : 1);
+    } else {
+        const int64_t G = (int64_t)dev.cus * blocks_per_cu / per_row_range;
+        pl->G = (int)(G > 0 ? G : 1);
+    }
+
+    // workspace layout
+    const size_t nslot = (size_t)pl->G + (size_t)pb->B;
+    const size_t hm = (size_t)pb->H * pb->m;
+    size_t off = 0;
+    pl->off_vcu = off;
+    off = align_up(off + sizeof(int32_t) * ((size_t)pb->B + 1));
+    pl->off_M = off;
+    off = align_up(off + sizeof(float) * nslot * hm);
+    pl->off_Z = off;
+    off = align_up(off + sizeof(float) * nslot * hm);
+    pl->off_acc = off;
+    off = align_up(off + sizeof(float) * nslot * hm * pb->dh);
+    pl->off_tok = off;
+    if (pb->norm == SA_NORM_PROTOTYPE) off = align_up(off + sizeof(float) * (size_t)pl->buf_rows * pb->H);
+    pl->total = off;
+    return SA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+sa_status hip_fail(hipError_t e, const char* what) {
+    return fail(SA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sa_forward_workspace_size(const sa_problem* pb) {
+    Plan pl;
+    if (!pb || make_plan(pb, pb->L_max == 0, &pl) != SA_OK) return 0;
+    return pl.total;
+}
+
+sa_status sa_forward(const sa_problem* pb, const void* P, const void* K, const void* V, const int32_t* cu_offsets,
+                     const int32_t* lengths, const uint8_t* mask, float* S_out, float* lse_out, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+    g_err[0] = 0;
+    Plan pl;
+    const bool packed = cu_offsets != nullptr;
+    sa_status st = make_plan(pb, packed, &pl);
+    if (st != SA_OK) return st;
+    if (lengths && packed) return fail(SA_ERR_INVALID_ARG, "lengths is only valid for the dense layout");
+    if (pb->B == 0) return SA_OK;
+    if (!P || !K || !V || !S_out) return fail(SA_ERR_INVALID_ARG, "P, K, V and S_out must be non-NULL");
+    const size_t el = pl.f32 ? 4 : 2;
+    if (!pl.f32 && (!aligned(P, 16) || !aligned(K, 16) || !aligned(V, 16)))
+        return fail(SA_ERR_INVALID_ARG, "bf16: P, K and V must be 16-byte aligned");
+    if (!aligned(P, el) || !aligned(K, el) || !aligned(V, el) || !aligned(S_out, 4) || !aligned(lse_out, 4))
+        return fail(SA_ERR_INVALID_ARG, "misaligned pointer");
+    if (pl.total > 0 && (!workspace || workspace_bytes < pl.total))
+        return fail(SA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", pl.total, workspace_bytes);
+    if (workspace && !aligned(workspace, kAlign)) return fail(SA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+    unsigned char* ws = (unsigned char*)workspace;
+    sa::Users users{};
+    users.cu = cu_offsets;
+    users.vcu = nullptr;
+    users.B = pb->B;
+    users.L_max = pb->L_max;
+    const int64_t hd = (int64_t)pb->H * pb->dh;
+    const float scale = pb->scale > 0.f ? pb->scale : 1.0f / sqrtf((float)pb->dh);
+
+    hipError_t e;
+    if (!packed && lengths) {
+        users.vcu = (int32_t*)(ws + pl.off_vcu);
+        e = sa::launch_dense_vcu(lengths, pb->B, pb->L_max, (int32_t*)(ws + pl.off_vcu), stream);
+        if (e != hipSuccess) return hip_fail(e, "dense offsets");
+    }
+    sa::Partials part{(float*)(ws + pl.off_acc), (float*)(ws + pl.off_M), (float*)(ws + pl.off_Z)};
+    float* lse2_tok = (float*)(ws + pl.off_tok);
+
+    if (pb->norm == SA_NORM_PROTOTYPE) {
+        sa::TokLseArgs t{};
+        t.users = users;
+        t.total_rows = pl.buf_rows;
+        t.mask = mask;
+        t.P = P;
+        t.K = K;
+        t.k_stride = pb->k_row_stride ? pb->k_row_stride : hd;
+        t.H = pb->H;
+        t.m = pb->m;
+        t.dh = pb->dh;
+        t.c = scale * sa::kLog2e;
+        t.lse2_tok = lse2_tok;
+        t.lse_out = lse_out;
+        if (pb->q_batch_stride != 0)
+            return fail(SA_ERR_UNSUPPORTED, "prototype axis with per-user prototypes is not supported");
+        e = pl.f32 ? sa::launch_f32_tok_lse(t, stream) : sa::launch_bf16_tok_lse(t, stream);
+        if (e != hipSuccess) return hip_fail(e, "row normaliser");
+    }
+
+    sa::FwdArgs a{};
+    a.users = users;
+    a.mask = mask;
+    a.P = P;
+    a.q_batch_stride = pb->q_batch_stride;
+    a.K = K;
+    a.V = V;
+    a.k_stride = pb->k_row_stride ? pb->k_row_stride : hd;
+    a.v_stride = pb->v_row_stride ? pb->v_row_stride : hd;
+    a.H = pb->H;
+    a.m = pb->m;
+    a.dh = pb->dh;
+    a.c = scale * sa::kLog2e;
+    a.G = pl.G;
+    a.R_fixed = pl.R_fixed;
+    a.R_min = pl.R_min;
+    a.part = part;
+    a.lse2_tok = lse2_tok;
+    a.norm = pb->norm;
+    const hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
+    g_ev_start = g_ev_stop = nullptr;
+    if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return hip_fail(e, "timing event");
+    e = pl.f32 ? sa::launch_f32_forward(a, stream) : sa::launch_bf16_forward(a, pl.cfg, stream);
+    if (e != hipSuccess) return hip_fail(e, "forward");
+    if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return hip_fail(e, "timing event");
+
+    sa::MergeArgs mg{};
+    mg.users = users;
+    mg.H = pb->H;
+    mg.m = pb->m;
+    mg.dh = pb->dh;
+    mg.G = pl.G;
+    mg.R_fixed = pl.R_fixed;
+    mg.R_min = pl.R_min;
+    mg.part = part;
+    mg.S = S_out;
+    mg.lse = pb->norm == SA_NORM_HISTORY ? lse_out : nullptr;
+    mg.norm = pb->norm;
+    e = sa::launch_merge(mg, stream);
+    if (e != hipSuccess) return hip_fail(e, "merge");
+    return SA_OK;
+}
+
+sa_status sa_forward_fused_proj(const sa_problem* pb, const void* X, int32_t d_model, const void* Wk, const void* Wv,
+                                const void* P, const int32_t* cu_offsets, const uint8_t* mask, float* S_out,
+                                float* lse_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    g_err[0] = 0;
+    (void)pb; (void)X; (void)d_model; (void)Wk; (void)Wv; (void)P; (void)cu_offsets; (void)mask;
+    (void)S_out; (void)lse_out; (void)workspace; (void)workspace_bytes; (void)stream;
+    return fail(SA_ERR_UNSUPPORTED, "fused projection is not built yet");
+}
+
+size_t sa_forward_fused_proj_workspace_size(const sa_problem* pb, int32_t d_model) {
+    (void)d_model;
+    Plan pl;
+    if (!pb || make_plan(pb, true, &pl) != SA_OK) return 0;
+    return pl.total;
+}
+
+sa_status sa_set_timing_events(hipEvent_t start, hipEvent_t stop) {
+    if ((start == nullptr) != (stop == nullptr)) return fail(SA_ERR_INVALID_ARG, "give both timing events or neither");
+    g_ev_start = start;
+    g_ev_stop = stop;
+    return SA_OK;
+}
+
+const char* sa_status_string(sa_status status) {
+    switch (status) {
+        case SA_OK: return "ok";
+        case SA_ERR_INVALID_ARG: return "invalid argument";
+        case SA_ERR_UNSUPPORTED: return "unsupported problem";
+        case SA_ERR_WORKSPACE: return "workspace too small";
+        case SA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* sa_last_error(void) { return g_err; }
+
+int sa_version(void) { return SA_VERSION_MAJOR * 10000 + SA_VERSION_MINOR * 100 + SA_VERSION_PATCH; }
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+// sa_internal.h -- shared definitions of libsketchattn's kernels and host code.
+//
+// Work decomposition used by every forward kernel (one launch per ragged
+// batch, section 4.4 of the SequenceO1 paper):
+//   * The valid-length rows of all users, concatenated in user order, form a
+//     "virtual row" axis of sigma_L = sum_b L_b positions.  User b occupies
+//     [vstart(b), vstart(b+1)).
+//   * Row-range block w covers virtual rows [w*R, (w+1)*R), R = chunk rows.
+//     Its intersection with user b is a "segment"; segment (w, b) stores its
+//     partial statistics at slot w + b (distinct for distinct intersecting
+//     pairs, at most G + B - 1 slots).
+//   * The merge kernel combines the segments of user b in ascending w.
+// Because R and the segments depend only on the valid lengths (not on the
+// buffer layout), packed and dense+lengths inputs give bitwise-equal results.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kTile = 32;        // rows per streaming tile
+constexpr int kRowAlign = 32;    // chunk rows are a multiple of this
+
+// Where user b's rows live and where it sits on the virtual row axis.
+struct Users {
+    const int32_t* cu;       // packed offsets [B+1] or nullptr (dense)
+    const int32_t* vcu;      // dense + lengths: virtual starts [B+1] (workspace)
+    int32_t B;
+    int32_t L_max;           // dense slot size
+    __device__ __forceinline__ int64_t vstart(int b) const {
+        if (cu) return (int64_t)cu[b] - cu[0];
+        if (vcu) return vcu[b];
+        return (int64_t)b * L_max;
+    }
+    __device__ __forceinline__ int64_t row_base(int b) const {
+        return cu ? (int64_t)cu[b] : (int64_t)b * L_max;
+    }
+    __device__ __forceinline__ int64_t total() const { return vstart(B); }
+    // largest b in [0, B) with vstart(b) <= v (v < total())
+    __device__ __forceinline__ int find(int64_t v) const {
+        int lo = 0, hi = B;  // invariant: vstart(lo) <= v < vstart(hi)
+        while (hi - lo > 1) {
+            int mid = (lo + hi) >> 1;
+            if (vstart(mid) <= v) lo = mid; else hi = mid;
+        }
+        return lo;
+    }
+};
+
+// Rows per segment: fixed by the caller, or spread evenly over G blocks.
+__device__ __forceinline__ int64_t chunk_rows(int64_t total, int G, int R_fixed, int R_min) {
+    if (R_fixed > 0) return R_fixed;
+    int64_t R = (total + G - 1) / G;
+    if (R < R_min) R = R_min;
+    return (R + kRowAlign - 1) / kRowAlign * kRowAlign;
+}
+
+// Partial statistics of the segments, laid out [slot][H][m](*dh).
+struct Partials {
+    float* acc;   // [nslot][H][m][dh]   unnormalised weighted value sums
+    float* M;     // [nslot][H][m]       running maximum, log2 units, scale folded in
+    float* Z;     // [nslot][H][m]       sum of 2^(x - M)
+};
+
+struct FwdArgs {
+    Users users;
+    const uint8_t* mask;     // per buffer row or nullptr
+    const void* P;
+    int64_t q_batch_stride;  // elements; 0 = shared
+    const void* K;
+    const void* V;
+    int64_t k_stride, v_stride;  // elements between rows
+    int32_t H, m, dh;
+    float c;                 // scale * log2(e)
+    int32_t G;               // row-range blocks
+    int32_t R_fixed, R_min;
+    Partials part;
+    const float* lse2_tok;   // prototype axis: per (row, head) log2 normaliser
+    int32_t norm;            // 0 history, 1 prototype
+};
+
+struct MergeArgs {
+    Users users;
+    int32_t H, m, dh;
+    int32_t G, R_fixed, R_min;
+    Partials part;
+    float* S;                // [B][H][m][dh]
+    float* lse;              // [B][H][m] or nullptr (history axis only)
+    int32_t norm;
+};
+
+struct TokLseArgs {
+    Users users;
+    int64_t total_rows;
+    const uint8_t* mask;
+    const void* P;
+    const void* K;
+    int64_t k_stride;
+    int32_t H, m, dh;
+    float c;
+    float* lse2_tok;         // [total_rows][H], log2 units
+    float* lse_out;          // [total_rows][H], natural log, or nullptr
+};
+
+// ---- launchers (return hipGetLastError() of the launch) ----
+hipError_t launch_dense_vcu(const int32_t* lengths, int32_t B, int32_t L_max, int32_t* vcu, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_f32_forward(const FwdArgs& a, hipStream_t s);
+hipError_t launch_f32_tok_lse(const TokLseArgs& a, hipStream_t s);
+hipError_t launch_bf16_tok_lse(const TokLseArgs& a, hipStream_t s);
+
+// bf16 MFMA forward: the tile configuration chosen by the host.
+struct Bf16Config {
+    int protos_per_wave;     // MB: prototypes one wave owns (multiple of 16)
+    int waves;               // NW: (head, prototype-block) units per block
+    int blocks_per_cu;       // occupancy target used to size G
+    int max_heads;           // most heads one block stages
+    int k_row, v_row;        // LDS row strides (bytes) of the K and V tiles
+    size_t lds_bytes;        // dynamic LDS per block
+};
+bool bf16_config(int dh, int m, int H, size_t lds_limit, Bf16Config* cfg);
+hipError_t launch_bf16_forward(const FwdArgs& a, const Bf16Config& cfg, hipStream_t s);
+
+}  // namespace sa

@@ -1,0 +1,108 @@
+// sa_merge.hip -- second pass of the split-row Sketch Attention forward, and
+// the prefix of dense lengths that places users on the virtual row axis.
+//
+// History axis: every segment (w, b) left (M_w, Z_w, acc_w) with
+//   Z_w = sum_i 2^(x_i - M_w),  acc_w = sum_i 2^(x_i - M_w) V_i,  x = s*scale*log2(e).
+// User b's sketch is the log-sum-exp combination over its segments in
+// ascending w (the max and log-sum-exp statistics of section 4.4 of the
+// SequenceO1 paper, merged across row chunks):
+//   M = max_w M_w,  Z = sum_w Z_w 2^(M_w - M),  S = sum_w acc_w 2^(M_w - M) / Z,
+//   lse = (M + log2 Z) * ln 2.
+// Prototype axis: the weights are already normalised per row, so the merge is
+// the plain ordered sum of the segments' acc.
+#include "sa_internal.h"
+
+namespace sa {
+
+__global__ __launch_bounds__(256) void sa_merge_kernel(MergeArgs a) {
+    const int b = blockIdx.x;
+    const int h = blockIdx.y;
+    const int md = a.m * a.dh;
+    const int64_t total = a.users.total();
+    const int64_t R = chunk_rows(total, a.G, a.R_fixed, a.R_min);
+    const int64_t us = a.users.vstart(b), ue = a.users.vstart(b + 1);
+    const bool empty = ue <= us;
+    const int64_t w_first = empty ? 0 : us / R;
+    const int64_t w_last = empty ? -1 : (ue - 1) / R;
+    float* Sb = a.S + ((int64_t)b * a.H + h) * md;
+
+    for (int e = threadIdx.x; e < md; e += blockDim.x) {
+        const int j = e / a.dh, d = e - j * a.dh;
+        if (a.norm == 1) {
+            float acc = 0.f;
+            for (int64_t w = w_first; w <= w_last; ++w) {
+                const int64_t base = ((w + b) * a.H + h) * a.m + j;
+                acc += a.part.acc[base * a.dh + d];
+            }
+            Sb[e] = acc;
+            continue;
+        }
+        float M = -INFINITY;
+        for (int64_t w = w_first; w <= w_last; ++w)
+            M = fmaxf(M, a.part.M[((w + b) * a.H + h) * a.m + j]);
+        float out = 0.f, lse = -INFINITY;
+        if (M > -INFINITY) {
+            float Z = 0.f, acc = 0.f;
+            for (int64_t w = w_first; w <= w_last; ++w) {
+                const int64_t base = ((w + b) * a.H + h) * a.m + j;
+                const float Mw = a.part.M[base];
+                if (Mw == -INFINITY) continue;       // segment with no valid row
+                const float f = exp2f(Mw - M);
+                Z += a.part.Z[base] * f;
+                acc += a.part.acc[base * a.dh + d] * f;
+            }
+            out = acc / Z;
+            lse = (M + log2f(Z)) * kLn2;
+        }
+        Sb[e] = out;
+        if (d == 0 && a.lse) a.lse[((int64_t)b * a.H + h) * a.m + j] = lse;
+    }
+}
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
+    if (a.users.B == 0) return hipSuccess;
+    hipLaunchKernelGGL(sa_merge_kernel, dim3(a.users.B, a.H), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// vcu[b] = sum_{b' < b} clamp(lengths[b'], 0, L_max): one block, 1024 threads.
+__global__ __launch_bounds__(1024) void sa_dense_vcu_kernel(const int32_t* lengths, int32_t B, int32_t L_max,
+                                                             int32_t* vcu) {
+    __shared__ int32_t wsum[16];
+    __shared__ int32_t carry;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) {
+        carry = 0;
+        vcu[0] = 0;
+    }
+    __syncthreads();
+    for (int base = 0; base < B; base += 1024) {
+        const int i = base + tid;
+        int x = 0;
+        if (i < B) {
+            x = lengths[i];
+            x = x < 0 ? 0 : (x > L_max ? L_max : x);
+        }
+        // inclusive scan within the wave
+        int v = x;
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(v, off, 64);
+            if (lane >= off) v += y;
+        }
+        if (lane == 63) wsum[wave] = v;
+        __syncthreads();
+        int before = carry;
+        for (int k = 0; k < wave; ++k) before += wsum[k];
+        if (i < B) vcu[i + 1] = before + v;
+        __syncthreads();
+        if (tid == 1023) carry = before + v;
+        __syncthreads();
+    }
+}
+
+hipError_t launch_dense_vcu(const int32_t* lengths, int32_t B, int32_t L_max, int32_t* vcu, hipStream_t s) {
+    hipLaunchKernelGGL(sa_dense_vcu_kernel, dim3(1), dim3(1024), 0, s, lengths, B, L_max, vcu);
+    return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,106 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, the Python mirror of sa_problem matches the header, and
+host-detectable errors return a status before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sketch_attention_flashsa_amd as sa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sketchattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(sa.LIB_PATH), reason="libsketchattn.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(sa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert set(names) == set(sa.EXPORTED), names
+    lib = ctypes.CDLL(sa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_problem_struct_matches_header():
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct sa_problem \{(.*?)\} sa_problem;", text, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"(int32_t|int64_t|float)\s+([\w, ]+);", body)
+    names = [n.strip() for _, group in fields for n in group.split(",")]
+    assert names == [f[0] for f in sa.SaProblem._fields_]
+    ctypes_of = {"int32_t": ctypes.c_int32, "int64_t": ctypes.c_int64, "float": ctypes.c_float}
+    types = [ctypes_of[t] for t, group in fields for _ in group.split(",")]
+    assert types == [f[1] for f in sa.SaProblem._fields_]
+
+
+def test_version_and_status_strings():
+    assert sa.sa_version() == 100
+    assert sa.sa_status_string(0) == "ok"
+    assert "workspace" in sa.sa_status_string(3)
+    assert sa.sa_status_string(99) == "unknown status"
+
+
+def _call(pb, **ptrs):
+    lib = sa.load_library()
+    p = {k: ptrs.get(k) for k in ("P", "K", "V", "cu", "len", "mask", "S", "lse", "ws")}
+    return lib.sa_forward(ctypes.byref(pb), p["P"], p["K"], p["V"], p["cu"], p["len"], p["mask"], p["S"], p["lse"],
+                          p["ws"], ptrs.get("nws", 0), None)
+
+
+FAKE = ctypes.c_void_p(1 << 20)   # never dereferenced: every case below fails validation first
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("B", -1, sa.SA_ERR_INVALID_ARG),
+    ("H", 0, sa.SA_ERR_INVALID_ARG),
+    ("dtype", 7, sa.SA_ERR_INVALID_ARG),
+    ("norm", 5, sa.SA_ERR_INVALID_ARG),
+    ("flags", 1, sa.SA_ERR_INVALID_ARG),
+    ("chunk_rows", 33, sa.SA_ERR_INVALID_ARG),
+    ("dh", 48, sa.SA_ERR_UNSUPPORTED),
+    ("m", 40, sa.SA_ERR_UNSUPPORTED),
+    ("k_row_stride", 7, sa.SA_ERR_INVALID_ARG),
+    ("total_rows", -5, sa.SA_ERR_INVALID_ARG),
+])
+def test_invalid_problem_rejected(field, value, status):
+    pb = sa.make_problem(2, 4, 64, 32, 100, dtype="bf16")
+    setattr(pb, field, value)
+    st = _call(pb, P=FAKE, K=FAKE, V=FAKE, cu=FAKE, S=FAKE)
+    assert st == status, (st, sa.sa_last_error())
+    assert sa.sa_last_error() != ""
+
+
+def test_null_pointers_and_workspace_rejected():
+    pb = sa.make_problem(2, 4, 64, 32, 100, dtype="bf16")
+    assert _call(pb, P=None, K=FAKE, V=FAKE, cu=FAKE, S=FAKE) == sa.SA_ERR_INVALID_ARG
+    nws = sa.sa_forward_workspace_size(pb)
+    assert nws > 0
+    assert _call(pb, P=FAKE, K=FAKE, V=FAKE, cu=FAKE, S=FAKE, ws=None, nws=0) == sa.SA_ERR_WORKSPACE
+    assert _call(pb, P=FAKE, K=FAKE, V=FAKE, cu=FAKE, S=FAKE, ws=FAKE, nws=nws - 1) == sa.SA_ERR_WORKSPACE
+    # packed layout must not carry L_max
+    pb2 = sa.make_problem(2, 4, 64, 32, 100, L_max=10, dtype="bf16")
+    assert _call(pb2, P=FAKE, K=FAKE, V=FAKE, cu=FAKE, S=FAKE) == sa.SA_ERR_INVALID_ARG
+    # misaligned bf16 pointer
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    assert _call(pb, P=FAKE, K=odd, V=FAKE, cu=FAKE, S=FAKE, ws=FAKE, nws=nws) == sa.SA_ERR_INVALID_ARG
+
+
+def test_empty_batch_is_a_no_op():
+    pb = sa.make_problem(0, 4, 64, 32, 0, dtype="bf16")
+    assert _call(pb, cu=FAKE) == sa.SA_OK
+
+
+def test_workspace_size_is_layout_independent_and_monotone():
+    a = sa.sa_forward_workspace_size(sa.make_problem(16, 8, 128, 64, 1_600_000, dtype="bf16"))
+    b = sa.sa_forward_workspace_size(sa.make_problem(16, 8, 128, 64, 1_600_000, dtype="bf16", norm="prototype"))
+    assert 0 < a < b          # the prototype axis adds the per-row normaliser
+    # partials stay a small fraction of the K/V bytes at the 100K workload
+    assert a < 0.05 * (2 * 1_600_000 * 8 * 64 * 2)

@@ -1,0 +1,242 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs, at sizes the oracle finishes in seconds (several tiles,
+ragged tails) and, for the large workloads, at full size on sampled outputs.
+
+Bars: fp32 inputs max|g-o|/max|o| <= 1e-5; bf16 inputs relative L2 <= 1e-2
+(oracle fed the same bf16 tensors).  Offsets and masks are checked
+bit-exactly: NaN-poisoned rows outside users or masked change nothing,
+packed == dense+lengths, an all-ones mask == no mask, two runs are equal."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import assert_lse, assert_parity, run, to_dev, device
+import sketch_attention_flashsa_amd as sa
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(w, norm="history", mask=None, lengths_ok=True):
+    msk = mask if mask is not None else w.get("mask")
+    if w["layout"] == "packed":
+        return oracle.forward(w["P"], w["K"], w["V"], cu_offsets=w["cu_offsets"], mask=msk, norm=norm)
+    return oracle.forward(w["P"], w["K"], w["V"], lengths=w["lengths"] if lengths_ok else None, mask=msk, norm=norm)
+
+
+# ----------------------------------------------------------- named workloads
+def test_tiny_fp32_workload_full():
+    """B=1, L=1000, H=1, m=16, dh=32, fp32 -- the whole workload."""
+    w = W.make(1)
+    S, lse = run(w)
+    So, lo = _oracle(w)
+    assert_parity(S, So, "f32", "tiny fp32")
+    assert_lse(lse, lo, "f32", "tiny fp32")
+
+
+@pytest.mark.parametrize("cfg,B,max_len", [(2, 4, None), (3, 8, 6000), (4, 2, 3000)])
+def test_bf16_workloads_reduced(cfg, B, max_len):
+    """The bf16 workloads with fewer users / capped lengths, full oracle."""
+    w = W.make(cfg, B=B, max_len=max_len)
+    S, lse = run(w)
+    So, lo = _oracle(w)
+    assert_parity(S, So, "bf16", f"workload {cfg}")
+    assert_lse(lse, lo, "bf16", f"workload {cfg}")
+
+
+def _sample_bhj(w, n, rng):
+    B, H, m = w["B"], w["H"], w["m"]
+    L = w["lengths"].numpy()
+    users = list(np.argsort(L)[:2]) + list(np.argsort(L)[-2:]) + list(rng.integers(0, B, size=n))
+    out = []
+    for b in users[:n]:
+        out.append((int(b), int(rng.integers(0, H)), int(rng.integers(0, m))))
+    return out
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_bf16_workloads_full_size_sampled(cfg):
+    """Full-size workloads in the launch configuration the benchmark times;
+    the oracle computes sampled (user, head, prototype) rows one by one."""
+    w = W.make(cfg)
+    S, lse = run(w)
+    rng = np.random.default_rng(cfg)
+    bhj = _sample_bhj(w, 24, rng)
+    if w["layout"] == "packed":
+        o, lo = oracle.forward_sample(w["P"], w["K"], w["V"], bhj, cu_offsets=w["cu_offsets"])
+    else:
+        o, lo = oracle.forward_sample(w["P"], w["K"], w["V"], bhj, lengths=w["lengths"])
+    g = np.stack([S[b, h, j] for b, h, j in bhj])
+    gl = np.array([lse[b, h, j] for b, h, j in bhj])
+    assert_parity(g, o, "bf16", f"workload {cfg} sampled")
+    assert_lse(gl, lo, "bf16", f"workload {cfg} sampled")
+    assert np.all(np.isfinite(S))
+    # users of length 1 (workload 3) reproduce their single value row exactly
+    cu = w.get("cu_offsets")
+    if cu is not None:
+        for b in np.nonzero(w["lengths"].numpy() == 1)[0]:
+            row = w["V"][int(cu[b])].double().numpy()              # [H, dh]
+            assert np.array_equal(S[b], np.broadcast_to(row[:, None, :], S[b].shape)), "L=1 user must be exact"
+
+
+# ------------------------------------------------------------- edge cases
+RAGGED = [0, 1, 2, 31, 32, 33, 65, 700]
+
+
+@pytest.mark.parametrize("dtype,H,m,dh", [("bf16", 4, 64, 32), ("bf16", 2, 128, 64), ("bf16", 3, 48, 32),
+                                          ("bf16", 1, 32, 128), ("f32", 2, 16, 32), ("f32", 1, 300, 64),
+                                          ("f32", 2, 8, 16)])
+@pytest.mark.parametrize("norm", ["history", "prototype"])
+def test_ragged_edges(dtype, H, m, dh, norm):
+    """Empty users, L = 1, 2, tile-boundary lengths and a long tail."""
+    w = W.random_case(101, B=len(RAGGED), H=H, m=m, dh=dh, lengths=RAGGED, dtype=dtype)
+    S, lse = run(w, norm=norm)
+    So, lo = _oracle(w, norm=norm)
+    assert_parity(S, So, dtype, f"ragged {dtype} {norm}")
+    assert_lse(lse, lo, dtype, f"ragged {dtype} {norm}")
+    assert np.all(S[0] == 0), "empty user must give zeros"
+    if norm == "history":
+        assert np.all(np.isneginf(lse[0])), "empty user must give lse = -inf"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_small_chunks_many_segments(dtype):
+    """A fixed small chunk size splits users over many segments; the merge
+    must still agree with the oracle."""
+    w = W.random_case(102, B=3, H=2, m=32, dh=32, lengths=[1000, 37, 2049], dtype=dtype)
+    S, lse = run(w, chunk_rows=64)
+    So, lo = _oracle(w)
+    assert_parity(S, So, dtype, "chunk_rows=64")
+    assert_lse(lse, lo, dtype, "chunk_rows=64")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mask_poisoned_rows_bit_exact(dtype):
+    """Masked rows and rows outside every user, filled with NaN/Inf, change
+    nothing bitwise; an all-ones mask equals no mask bitwise; masked results
+    match the oracle."""
+    w = W.random_case(103, B=4, H=2, m=32, dh=32, lengths=[300, 0, 77, 129], dtype=dtype, mask_p=0.3)
+    S_ref, l_ref = run(w)
+    So, lo = _oracle(w)
+    assert_parity(S_ref, So, dtype, "masked")
+    assert_lse(l_ref, lo, dtype, "masked")
+    # poison masked rows
+    w2 = dict(w)
+    K, V = w["K"].clone(), w["V"].clone()
+    bad = ~w["mask"].bool()
+    K[bad] = float("nan")
+    V[bad] = float("inf")
+    w2["K"], w2["V"] = K, V
+    S2, l2 = run(w2)
+    assert np.array_equal(S2, S_ref) and np.array_equal(l2, l_ref), "masked rows must not leak"
+    # rows outside every user: pad the buffer front and back with NaN
+    pad = 40
+    K3 = torch.full((pad + K.shape[0] + pad, 2, 32), float("nan"), dtype=K.dtype)
+    V3 = K3.clone()
+    K3[pad:pad + K.shape[0]] = w["K"]
+    V3[pad:pad + V.shape[0]] = w["V"]
+    mk3 = torch.zeros(K3.shape[0], dtype=torch.uint8)
+    mk3[pad:pad + K.shape[0]] = w["mask"]
+    w3 = dict(w, K=K3, V=V3, cu_offsets=w["cu_offsets"] + pad)
+    S3, l3 = run(w3, mask=mk3)
+    assert np.array_equal(S3, S_ref) and np.array_equal(l3, l_ref), "rows outside users must not leak"
+    # all-ones mask == no mask
+    w4 = dict(w)
+    w4.pop("mask")
+    S4, _ = run(w4)
+    S5, _ = run(w4, mask=torch.ones(w["K"].shape[0], dtype=torch.uint8))
+    assert np.array_equal(S4, S5), "all-ones mask must equal no mask"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_packed_equals_dense_bitwise(dtype):
+    lengths = [500, 3, 0, 1200, 64]
+    wp = W.random_case(104, B=5, H=4, m=64, dh=32, lengths=lengths, dtype=dtype, layout="packed")
+    wd = W.random_case(104, B=5, H=4, m=64, dh=32, lengths=lengths, dtype=dtype, layout="dense")
+    Sp, lp = run(wp)
+    Sd, ld = run(wd)
+    assert np.array_equal(Sp, Sd) and np.array_equal(lp, ld), "packed and dense+lengths must agree bitwise"
+    # dense padding filled with NaN changes nothing
+    K, V = wd["K"].clone(), wd["V"].clone()
+    for b, n in enumerate(lengths):
+        K[b, n:] = float("nan")
+        V[b, n:] = float("nan")
+    Sn, _ = run(dict(wd, K=K, V=V))
+    assert np.array_equal(Sn, Sd), "dense padding must not leak"
+
+
+def test_deterministic_and_isolated():
+    w = W.random_case(105, B=3, H=2, m=64, dh=64, lengths=[3000, 1500, 2500], dtype="bf16")
+    S1, l1 = run(w)
+    S2, l2 = run(w)
+    assert np.array_equal(S1, S2) and np.array_equal(l1, l2), "two runs must be bitwise equal"
+    K = w["K"].clone()
+    cu = w["cu_offsets"].tolist()
+    K[cu[2]:cu[3]] = -K[cu[2]:cu[3]]
+    S3, _ = run(dict(w, K=K))
+    assert np.array_equal(S3[:2], S1[:2]) and not np.array_equal(S3[2], S1[2]), "users must not interact"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_p_zero_gives_mean(dtype):
+    w = W.random_case(106, B=2, H=2, m=16, dh=32, lengths=[999, 45], dtype=dtype)
+    w["P"] = torch.zeros_like(w["P"])
+    S, _ = run(w)
+    cu = w["cu_offsets"].tolist()
+    for b in range(2):
+        mean = w["V"][cu[b]:cu[b + 1]].double().mean(dim=0).numpy()     # [H, dh]
+        assert_parity(S[b], np.broadcast_to(mean[:, None, :], S[b].shape), dtype, "P=0 mean")
+
+
+@pytest.mark.parametrize("scale_p,offset", [(4.0, 0.0), (1.0, 80.0), (1.0, -200.0), (8.0, 120.0)])
+def test_peaked_and_shifted_scores(scale_p, offset):
+    """Peaked rows (P scaled up) and large constant score offsets neither
+    overflow nor lose accuracy.  The offset is exact: channel 0 of every
+    prototype is set to 4 and channel 0 of every key row is shifted by
+    offset*sqrt(dh)/4, so every score moves by about `offset` (past the fp32
+    exp range for |offset| >= 89)."""
+    dh = 32
+    w = W.random_case(107, B=2, H=2, m=32, dh=dh, lengths=[4000, 777], dtype="bf16")
+    P = w["P"].float() * scale_p
+    K = w["K"].float()
+    if offset:
+        P[:, :, 0] = 4.0
+        K[:, :, 0] += offset * np.sqrt(dh) / 4.0
+    w = dict(w, P=P.to(torch.bfloat16), K=K.to(torch.bfloat16))
+    S, lse = run(w)
+    So, lo = _oracle(w)
+    assert np.all(np.isfinite(S))
+    assert_parity(S, So, "bf16", f"peaked x{scale_p} offset {offset}")
+    assert_lse(lse, lo, "bf16", f"peaked x{scale_p} offset {offset}")
+
+
+def test_per_user_prototypes():
+    """P [B, H, m, dh] (stacked refinement feeds per-user queries): each user
+    equals a shared-P call with that user's prototypes."""
+    w = W.random_case(108, B=3, H=2, m=32, dh=32, lengths=[700, 1, 300], dtype="bf16")
+    Pu = torch.stack([w["P"], -w["P"], w["P"].flip(-1)])
+    S, _ = run(dict(w, P=Pu))
+    for b in range(3):
+        Sb, _ = run(dict(w, P=Pu[b]))
+        assert np.array_equal(S[b], Sb[b]), "per-user prototypes must match the shared call"
+
+
+# --------------------------------------------------------- prototype axis
+@pytest.mark.parametrize("cfg,B,max_len", [(1, None, None), (2, 2, 4000), (3, 6, 3000), (4, 2, 2000)])
+def test_prototype_axis_workloads(cfg, B, max_len):
+    w = W.make(cfg, B=B, max_len=max_len)
+    S, lse = run(w, norm="prototype")
+    So, lo = _oracle(w, norm="prototype")
+    dt = w["dtype"]
+    assert_parity(S, So, dt, f"prototype axis, workload {cfg}")
+    rows = lo.shape[0]
+    assert_lse(lse.reshape(rows, -1), lo, dt, f"prototype axis lse, workload {cfg}")
+
+
+def test_prototype_axis_masked_and_dense():
+    w = W.random_case(109, B=3, H=2, m=64, dh=64, lengths=[600, 0, 130], dtype="bf16", layout="dense", mask_p=0.2)
+    S, lse = run(w, norm="prototype")
+    So, lo = _oracle(w, norm="prototype")
+    assert_parity(S, So, "bf16", "prototype masked dense")
+    assert_lse(lse, lo, "bf16", "prototype masked dense")
