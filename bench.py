@@ -1,0 +1,212 @@
+"""Benchmark of the Sketch Attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
+
+A step is one full forward (the streaming kernel and the merge) over one
+batch of synthetic histories already resident in HBM: by default the full
+100K workload (B=16 users x L=100,000 rows, H=8 heads, m=128 prototypes,
+dh=64, bf16, packed with int32 offsets).  Prints ONE JSON line with the
+whole-job throughput in history tokens per second, the roofline of the
+streaming kernel (algorithmic bytes / its HIP-event-timed duration against
+the 8 TB/s HBM peak) and the CPU oracle timed on a bounded sample on this
+host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "history tokens/sec compressed by SA (bf16, 100K varlen) + % HBM peak"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+KERNEL_SRC = os.path.join(ROOT, "sketch_attention_flashsa_amd", "csrc", "sa_bf16_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_full100k_bf16.json")
+
+
+class _Hip:
+    """Just enough of the HIP runtime (via ctypes) for timing events."""
+
+    def __init__(self):
+        for name in ("libamdhip64.so", "/opt/rocm/lib/libamdhip64.so"):
+            try:
+                self.lib = ctypes.CDLL(name)
+                break
+            except OSError:
+                continue
+        else:
+            raise RuntimeError("libamdhip64.so not found")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
+
+
+def _kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.dirname(KERNEL_SRC))):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(os.path.dirname(KERNEL_SRC), f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(per_launch_alg_bytes: float):
+    """HBM bytes per launch of the streaming kernel from the committed
+    rocprofv3 counter summary, or None if absent or taken on other sources."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sources_sha256_16") != _kernel_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, n_users: int):
+    """The oracle as it stands, on the first n_users users of the workload."""
+    import oracle
+    n = min(n_users, w["B"])
+    if w["layout"] == "packed":
+        cu = w["cu_offsets"][: n + 1].clone()
+        rows = int(cu[-1])
+        t0 = time.perf_counter()
+        oracle.forward(w["P"], w["K"][:rows], w["V"][:rows], cu_offsets=cu)
+    else:
+        rows = int(w["lengths"][:n].sum())
+        t0 = time.perf_counter()
+        oracle.forward(w["P"], w["K"][:n], w["V"][:n], lengths=w["lengths"][:n])
+    dt = time.perf_counter() - t0
+    pairs = n * w["H"]
+    return {
+        "value": rows / dt,
+        "unit": "tokens/s",
+        "cores": int(min(oracle.threads(), pairs)),
+        "kind": "oracle",
+        "sample": f"first {n} users of the workload ({rows} history rows, all {w['H']} heads and {w['m']} "
+                  f"prototypes), double precision, {dt:.1f} s wall",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=4, help="workload number (default 4: full 100K bf16)")
+    ap.add_argument("--cpu-users", type=int, default=4, help="users in the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the forward has no multi-GPU path in this build "
+              "(users shard across GPUs with no exchange; run one process per GPU).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import sketch_attention_flashsa_amd as sa
+    from sketch_attention_flashsa_amd import flops
+
+    dev = torch.device("cuda:0")
+    w = W.make(args.workload)
+    spec = w["spec"]
+    B, H, m, dh = w["B"], w["H"], w["m"], w["dh"]
+    tokens = int(w["lengths"].sum())
+    if "X" in w:
+        raise SystemExit("the fused-projection workload is benchmarked by its own entry point")
+    P, K, V = w["P"].to(dev), w["K"].to(dev), w["V"].to(dev)
+    cu = w["cu_offsets"].to(dev) if w["layout"] == "packed" else None
+    lengths = w["lengths"].to(dev) if w["layout"] == "dense" else None
+    S = torch.empty((B, H, m, dh), dtype=torch.float32, device=dev)
+    pb_kw = {}
+    # one workspace for all steps (no allocation inside the timed region)
+    rows = K.shape[0] if cu is not None else B * K.shape[1]
+    pb = sa.make_problem(B, H, m, dh, rows, L_max=0 if cu is not None else K.shape[1], dtype=w["dtype"])
+    ws = torch.empty(sa.sa_forward_workspace_size(pb), dtype=torch.uint8, device=dev)
+
+    def step():
+        sa.sa_forward(P, K, V, cu_offsets=cu, lengths=lengths, out=S, workspace=ws, **pb_kw)
+
+    hip = _Hip()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        sa.sa_set_timing_events(evs[i][0], evs[i][1])
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern_ms = [hip.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = tokens / (ms_per_step / 1e3)
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+    el = 2 if w["dtype"] == "bf16" else 4
+    # algorithmic bytes of the streaming kernel: every K and V element once, plus P and offsets
+    alg_bytes = 2 * tokens * H * dh * el + H * m * dh * el + 4 * (B + 1)
+    achieved = alg_bytes / (kern_avg_ms / 1e3) / 1e9
+    step_bytes = W.algorithmic_bytes(w)
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["dtype"],
+        "data": "synthetic (seeded normal draws shaped like the paper's histories)",
+        "config": {"workload": spec.name, "B": B, "sum_L": tokens, "L_max": int(w["lengths"].max()), "H": H,
+                   "m": m, "dh": dh, "layout": w["layout"], "parallelism": "single GPU"},
+        "hbm_frac_step": step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "sa_bf16_fwd_kernel" if w["dtype"] == "bf16" else "sa_f32_fwd_kernel",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": _traffic(alg_bytes),
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "kernel_ms_avg": kern_avg_ms,
+            "kernel_ms_min": min(kern_ms),
+            "mfma_tflops": flops.sa_forward_flops(tokens, H, m, dh) / (kern_avg_ms / 1e3) / 1e12,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_users)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

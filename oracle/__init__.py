@@ -99,7 +99,14 @@ def _bind(lib):
     lib.sao_project.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                 ctypes.c_int64, vp, ctypes.c_int64, ctypes.c_int64, vp]
     lib.sao_project.restype = ctypes.c_int
+    lib.sao_threads.argtypes = []
+    lib.sao_threads.restype = ctypes.c_int
     return lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops may use."""
+    return int(load().sao_threads())
 
 
 # ---------------------------------------------------------------- marshalling

@@ -285,3 +285,11 @@ int sao_project(const void* X, const void* W, int32_t in_dtype, int32_t d_model,
     }
     return 0;
 }
+
+/* Number of OpenMP threads the parallel loops above may use (1 without OpenMP). */
+#ifdef _OPENMP
+#include <omp.h>
+int sao_threads(void) { return omp_get_max_threads(); }
+#else
+int sao_threads(void) { return 1; }
+#endif

@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -62,6 +63,8 @@ struct Plan {
     int G = 1;                // row-range blocks
     int R_fixed = 0, R_min = kRowMinBf16;
     sa::Bf16Config cfg{};
+    bool stream = false;      // bf16: the direct-to-LDS streaming kernel serves this shape
+    sa::StreamConfig scfg{};
     int groups = 1;           // bf16: unit groups per row range
     // workspace layout (byte offsets)
     size_t off_vcu = 0, off_M = 0, off_Z = 0, off_acc = 0, off_tok = 0, total = 0;
@@ -126,10 +129,17 @@ sa_status make_plan(const sa_problem* pb, bool packed, Plan* pl) {
         blocks_per_cu = 4;
         pl->R_min = kRowMinF32;
     } else {
-        const int units = pb->H * (pb->m / pl->cfg.protos_per_wave);
-        pl->groups = (units + pl->cfg.waves - 1) / pl->cfg.waves;
+        const char* kern = getenv("SA_KERNEL");
+        pl->stream = !(kern && strcmp(kern, "v1") == 0) && sa::stream_config(pb->dh, pb->m, pb->H, &pl->scfg);
+        if (pl->stream) {
+            pl->groups = pl->scfg.groups;
+            blocks_per_cu = pl->scfg.blocks_per_cu;
+        } else {
+            const int units = pb->H * (pb->m / pl->cfg.protos_per_wave);
+            pl->groups = (units + pl->cfg.waves - 1) / pl->cfg.waves;
+            blocks_per_cu = pl->cfg.blocks_per_cu;
+        }
         per_row_range = pl->groups;
-        blocks_per_cu = pl->cfg.blocks_per_cu;
         pl->R_min = kRowMinBf16;
     }
     const int64_t rows_upper = pb->L_max > 0 ? need : pb->total_rows;
@@ -138,6 +148,7 @@ sa_status make_plan(const sa_problem* pb, bool packed, Plan* pl) {
         const int64_t G = (rows_upper + pb->chunk_rows - 1) / pb->chunk_rows;
         pl->G = (int)(G > 0 ? G : 1);
     } else {
+        if (const char* e = getenv("SA_BLOCKS_PER_CU")) blocks_per_cu = atoi(e) > 0 ? atoi(e) : blocks_per_cu;
         const int64_t G = (int64_t)dev.cus * blocks_per_cu / per_row_range;
         pl->G = (int)(G > 0 ? G : 1);
     }
@@ -256,7 +267,9 @@ sa_status sa_forward(const sa_problem* pb, const void* P, const void* K, const v
     const hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
     g_ev_start = g_ev_stop = nullptr;
     if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return hip_fail(e, "timing event");
-    e = pl.f32 ? sa::launch_f32_forward(a, stream) : sa::launch_bf16_forward(a, pl.cfg, stream);
+    if (pl.f32) e = sa::launch_f32_forward(a, stream);
+    else if (pl.stream) e = sa::launch_bf16_stream(a, pl.scfg, stream);
+    else e = sa::launch_bf16_forward(a, pl.cfg, stream);
     if (e != hipSuccess) return hip_fail(e, "forward");
     if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return hip_fail(e, "timing event");
 

@@ -132,4 +132,16 @@ struct Bf16Config {
 bool bf16_config(int dh, int m, int H, size_t lds_limit, Bf16Config* cfg);
 hipError_t launch_bf16_forward(const FwdArgs& a, const Bf16Config& cfg, hipStream_t s);
 
+// bf16 streaming kernel with the direct-to-LDS ring (sa_bf16_stream.hip):
+// 8 waves of 32 prototypes per block.
+struct StreamConfig {
+    int PB;                  // 32-prototype blocks per head
+    int NH;                  // heads per block
+    int NW;                  // waves per block
+    int groups;              // blocks per row range
+    int blocks_per_cu;
+};
+bool stream_config(int dh, int m, int H, StreamConfig* cfg);
+hipError_t launch_bf16_stream(const FwdArgs& a, const StreamConfig& cfg, hipStream_t s);
+
 }  // namespace sa

@@ -14,10 +14,15 @@
 
 namespace sa {
 
+// One thread per output element (b, h, j, e): the per-segment loads of one
+// element are independent, so a block covers 256 consecutive (j, e).
 __global__ __launch_bounds__(256) void sa_merge_kernel(MergeArgs a) {
-    const int b = blockIdx.x;
+    const int b = blockIdx.z;
     const int h = blockIdx.y;
     const int md = a.m * a.dh;
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= md) return;
+    const int j = e / a.dh, d = e - j * a.dh;
     const int64_t total = a.users.total();
     const int64_t R = chunk_rows(total, a.G, a.R_fixed, a.R_min);
     const int64_t us = a.users.vstart(b), ue = a.users.vstart(b + 1);
@@ -26,42 +31,39 @@ __global__ __launch_bounds__(256) void sa_merge_kernel(MergeArgs a) {
     const int64_t w_last = empty ? -1 : (ue - 1) / R;
     float* Sb = a.S + ((int64_t)b * a.H + h) * md;
 
-    for (int e = threadIdx.x; e < md; e += blockDim.x) {
-        const int j = e / a.dh, d = e - j * a.dh;
-        if (a.norm == 1) {
-            float acc = 0.f;
-            for (int64_t w = w_first; w <= w_last; ++w) {
-                const int64_t base = ((w + b) * a.H + h) * a.m + j;
-                acc += a.part.acc[base * a.dh + d];
-            }
-            Sb[e] = acc;
-            continue;
+    if (a.norm == 1) {
+        float acc = 0.f;
+        for (int64_t w = w_first; w <= w_last; ++w) {
+            const int64_t base = ((w + b) * a.H + h) * a.m + j;
+            acc += a.part.acc[base * a.dh + d];
         }
-        float M = -INFINITY;
-        for (int64_t w = w_first; w <= w_last; ++w)
-            M = fmaxf(M, a.part.M[((w + b) * a.H + h) * a.m + j]);
-        float out = 0.f, lse = -INFINITY;
-        if (M > -INFINITY) {
-            float Z = 0.f, acc = 0.f;
-            for (int64_t w = w_first; w <= w_last; ++w) {
-                const int64_t base = ((w + b) * a.H + h) * a.m + j;
-                const float Mw = a.part.M[base];
-                if (Mw == -INFINITY) continue;       // segment with no valid row
-                const float f = exp2f(Mw - M);
-                Z += a.part.Z[base] * f;
-                acc += a.part.acc[base * a.dh + d] * f;
-            }
-            out = acc / Z;
-            lse = (M + log2f(Z)) * kLn2;
-        }
-        Sb[e] = out;
-        if (d == 0 && a.lse) a.lse[((int64_t)b * a.H + h) * a.m + j] = lse;
+        Sb[e] = acc;
+        return;
     }
+    float M = -INFINITY;
+    for (int64_t w = w_first; w <= w_last; ++w) M = fmaxf(M, a.part.M[((w + b) * a.H + h) * a.m + j]);
+    float out = 0.f, lse = -INFINITY;
+    if (M > -INFINITY) {
+        float Z = 0.f, acc = 0.f;
+        for (int64_t w = w_first; w <= w_last; ++w) {
+            const int64_t base = ((w + b) * a.H + h) * a.m + j;
+            const float Mw = a.part.M[base];
+            if (Mw == -INFINITY) continue;       // segment with no valid row
+            const float f = exp2f(Mw - M);
+            Z += a.part.Z[base] * f;
+            acc += a.part.acc[base * a.dh + d] * f;
+        }
+        out = acc / Z;
+        lse = (M + log2f(Z)) * kLn2;
+    }
+    Sb[e] = out;
+    if (d == 0 && a.lse) a.lse[((int64_t)b * a.H + h) * a.m + j] = lse;
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
     if (a.users.B == 0) return hipSuccess;
-    hipLaunchKernelGGL(sa_merge_kernel, dim3(a.users.B, a.H), dim3(256), 0, s, a);
+    const int md = a.m * a.dh;
+    hipLaunchKernelGGL(sa_merge_kernel, dim3((md + 255) / 256, a.H, a.users.B), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
