@@ -36,7 +36,7 @@ namespace sa {
 
 namespace {
 
-constexpr int kStages = 5;   // ring slots: 3 stages in flight, 1 computed, 1 still read for V
+constexpr int kStages = 4;   // ring slots: 2 stages in flight, 1 computed, 1 still read for V
 constexpr float kLazyBound = 65536.0f;   // fast path while a lane's tile sum <= 2^16
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -147,6 +147,35 @@ __device__ __forceinline__ void read_k(const uint32_t (&addr)[KC], bf16x8 (&lo)[
     }
 }
 
+// One direct-to-LDS load of 16 bytes per lane: lane i's 16 bytes from `src`
+// land at LDS address lds + 16*i (lds is wave-uniform; it goes through M0).
+// Written as asm so the compiler does not know that the ring is a DMA target
+// and therefore never inserts its own (whole-ring) waits before LDS reads;
+// the kernel's counted vmcnt waits are what orders the ring.  The asm has no
+// output register, so nothing of it is left in flight in a register.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(src), "s"(lds)
+        : "memory");
+}
+
+// acc *= f in place.  A tied-operand ALU asm statement keeps the accumulator
+// in the same registers on the (rare) rescale path, so the common path does
+// not pay register copies to merge two versions of it.
+__device__ __forceinline__ void scale_in_place(f32x4& acc, float f) {
+    asm volatile(
+        "v_mul_f32 %0, %4, %0\n\t"
+        "v_mul_f32 %1, %4, %1\n\t"
+        "v_mul_f32 %2, %4, %2\n\t"
+        "v_mul_f32 %3, %4, %3"
+        : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
+        : "v"(f));
+}
+
 // Bits j = 0..7 of a lane: validity of the rows of its PV k-slots.
 __device__ __forceinline__ uint32_t lane_slots(uint32_t valid, int g) {
     return ((valid >> (4 * g)) & 0xFu) | (((valid >> (16 + 4 * g)) & 0xFu) << 4);
@@ -164,11 +193,12 @@ __device__ __forceinline__ void block_barrier() {
 
 }  // namespace
 
-template <int DH, int MB, int NW, int NH, bool MASKED, bool PROTO, int S = kStages, int WPE = 2, int PADKB = 0>
+template <int DH, int MB, int NW, int NH, bool MASKED, bool PROTO, int S = kStages, int WPE = 2, int PADKB = 0,
+          int DMUL = 1>  // PADKB: unused extra LDS (kept 0)
 __global__ __launch_bounds__(NW * 64, WPE) void sa_bf16_stream_kernel(FwdArgs a, int PB) {
     constexpr int CPR = NH * DH / 8;                      // 16-byte chunks per row per tensor
     constexpr int ROWB = CPR * 16;                        // bytes per row per tensor
-    constexpr int D = (32 * CPR + NW * 64 - 1) / (NW * 64);  // DMA ops per wave per tensor per stage
+    constexpr int D = DMUL * ((32 * CPR + NW * 64 - 1) / (NW * 64));  // DMA ops per wave per tensor per stage
     constexpr int TR = NW * D * 64 / CPR;                 // rows per stage
     constexpr int NSUB = TR / 32;                         // 32-row units per stage
     constexpr int STAGE = TR * ROWB;                      // bytes per tensor per stage
@@ -185,10 +215,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void sa_bf16_stream_kernel(FwdArgs a,
     static_assert(S >= 3 && S <= 8 && (AHEAD - 1) * VMS < 64, "ring depth");
 
     __shared__ __attribute__((aligned(1024))) unsigned char ring[S][2][STAGE];
-    if constexpr (PADKB > 0) {   // tuning experiments only: extra, unused LDS
-        __shared__ unsigned char pad[PADKB * 1024];
-        if (threadIdx.x == 1023) pad[blockIdx.x % (PADKB * 1024)] = 0;
-    }
+    static_assert(PADKB == 0, "no padding");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -298,15 +325,13 @@ __global__ __launch_bounds__(NW * 64, WPE) void sa_bf16_stream_kernel(FwdArgs a,
         // ---- issue stage t into ring slot t % S (every lane of every wave, always);
         // stages are issued in order, so t == (number issued so far)
         auto issue = [&](int t) {
-            const int slot = t % S;
+            const uint32_t slot_lds = ring_lds + (uint32_t)((t % S) * 2 * STAGE) + (uint32_t)(wave * D * 1024);
             const int r0 = t * TR;
 #pragma unroll
             for (int d = 0; d < D; ++d) {
                 const bool in = r0 + dma_row[d] < nrows32;
-                const unsigned char* ks = in ? kp[d] : klast[d];
-                const unsigned char* vs = in ? vp[d] : vlast[d];
-                __builtin_amdgcn_global_load_lds((const void*)ks, (lds_void*)(ring[slot][0] + (wave * D + d) * 1024), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((const void*)vs, (lds_void*)(ring[slot][1] + (wave * D + d) * 1024), 16, 0, 0);
+                dma16(in ? kp[d] : klast[d], __builtin_amdgcn_readfirstlane(slot_lds + d * 1024));
+                dma16(in ? vp[d] : vlast[d], __builtin_amdgcn_readfirstlane(slot_lds + STAGE + d * 1024));
                 kp[d] += kstep;
                 vp[d] += vstep;
             }
@@ -326,7 +351,13 @@ __global__ __launch_bounds__(NW * 64, WPE) void sa_bf16_stream_kernel(FwdArgs a,
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) addr[kc] = klane[kc] + kb;
             bf16x8 ka[2][KC];
-            read_k<KC, 16 * ROWB>(addr, ka[0], ka[1]);
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const __attribute__((address_space(3))) bf16x8* pk0 =
+                    (const __attribute__((address_space(3))) bf16x8*)(uintptr_t)addr[kc];
+                ka[0][kc] = pk0[0];
+                ka[1][kc] = pk0[16 * ROWB / 16];
+            }
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
 #pragma unroll
@@ -393,7 +424,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void sa_bf16_stream_kernel(FwdArgs a,
                 Zs[sb] = Zs[sb] * f + dot2sum(q3, dot2sum(q2, dot2sum(q1, dot2sum(q0, 0.f))));
                 Mc[sb] = Mnew;
 #pragma unroll
-                for (int db = 0; db < DB; ++db) acc[sb][db] *= f;
+                for (int db = 0; db < DB; ++db) scale_in_place(acc[sb][db], f);
             }
         };
         // prototype axis: weights 2^(s*c - lse2[row]) with the per-row normaliser
@@ -419,7 +450,11 @@ __global__ __launch_bounds__(NW * 64, WPE) void sa_bf16_stream_kernel(FwdArgs a,
 #pragma unroll
             for (int db = 0; db < DB; ++db) addr[db] = vlane[db] + vb;
             i16x4 lo[DB], hi[DB];
-            read_vt<DB, 16 * ROWB>(addr, lo, hi);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                lo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr[db]);
+                hi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(addr[db] + 16 * ROWB));
+            }
             if (valid != 0xffffffffu) {
                 // rows outside the segment or masked: zero their values (NaN must not leak)
                 const uint32_t vj = lane_slots(valid, g);
@@ -542,6 +577,13 @@ __global__ __launch_bounds__(NW * 64, WPE) void sa_bf16_stream_kernel(FwdArgs a,
 
 namespace {
 
+// Ring shape: kStages slots of 32*kStageMul rows (history axis, no mask).
+// SA_STREAM_RING="S,MUL" selects another of the compiled shapes (tuning).
+template <int DH, int MB, int NW, int NH, int S, int MUL>
+void launch_hist(dim3 grid, dim3 block, const FwdArgs& a, int PB, hipStream_t s) {
+    hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, MB, NW, NH, false, false, S, 2, 0, MUL>), grid, block, 0, s, a, PB);
+}
+
 template <int DH, int MB, int NW, int NH>
 hipError_t launch_stream(const FwdArgs& a, bool masked, int PB, hipStream_t s) {
     int groups;
@@ -549,29 +591,29 @@ hipError_t launch_stream(const FwdArgs& a, bool masked, int PB, hipStream_t s) {
     else groups = (a.H + NH - 1) / NH;
     dim3 grid(a.G, groups), block(NW * 64);
     const bool proto = a.norm == 1;
-    if constexpr (DH == 64 && NH == 2) {
-        // tuning variants (ring depth, waves-per-SIMD hint) for sweeps: SA_STREAM_VARIANT
-        if (const char* v = getenv("SA_STREAM_VARIANT")) {
-            if (!masked && !proto) {
-                if (!strcmp(v, "s3")) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, MB, NW, NH, false, false, 3, 2>), grid, block, 0, s, a, PB);
-                else if (!strcmp(v, "s6")) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, MB, NW, NH, false, false, 6, 2>), grid, block, 0, s, a, PB);
-                else if (!strcmp(v, "s4")) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, MB, NW, NH, false, false, 4, 2>), grid, block, 0, s, a, PB);
-                else if (!strcmp(v, "s3p16")) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, MB, NW, NH, false, false, 3, 2, 16>), grid, block, 0, s, a, PB);
-                else if (!strcmp(v, "s3p32")) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, MB, NW, NH, false, false, 3, 2, 32>), grid, block, 0, s, a, PB);
-                else if (!strcmp(v, "s3p64")) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, MB, NW, NH, false, false, 3, 2, 64>), grid, block, 0, s, a, PB);
-                else if (!strcmp(v, "s3p8")) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, MB, NW, NH, false, false, 3, 2, 8>), grid, block, 0, s, a, PB);
-                else if (!strcmp(v, "s3p15")) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, MB, NW, NH, false, false, 3, 2, 15>), grid, block, 0, s, a, PB);
-                else if (!strcmp(v, "s3p17")) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, MB, NW, NH, false, false, 3, 2, 17>), grid, block, 0, s, a, PB);
-                else if (!strcmp(v, "s3dyn16")) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, MB, NW, NH, false, false, 3, 2>), grid, block, 16384, s, a, PB);
-                else if (!strcmp(v, "s4dyn1")) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, MB, NW, NH, false, false, 4, 2>), grid, block, 1024, s, a, PB);
-                else if (!strcmp(v, "s4w4")) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, MB, NW, NH, false, false, 4, 4>), grid, block, 0, s, a, PB);
-                else if (!strcmp(v, "s3w4")) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, MB, NW, NH, false, false, 3, 4>), grid, block, 0, s, a, PB);
-                else hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, MB, NW, NH, false, false>), grid, block, 0, s, a, PB);
-                return hipGetLastError();
+    if (!masked && !proto) {
+        // 64-row stages when a stage of 32 rows is a single DMA op per wave and
+        // the ring still fits the LDS; else 32-row stages
+        constexpr int CPR = NH * DH / 8;
+        constexpr int D1 = (32 * CPR + NW * 64 - 1) / (NW * 64);
+        constexpr int TR1 = NW * D1 * 64 / CPR;              // stage rows at MUL = 1
+        constexpr int SLOT = 2 * NW * D1 * 1024;             // bytes per slot at MUL = 1
+        constexpr bool wide = D1 == 1 && TR1 == 32 && 4 * 2 * SLOT <= 160 * 1024;
+        int S = 4, mul = wide ? 2 : 1;
+        if (const char* e = getenv("SA_STREAM_RING")) {
+            int es = 0, em = 0;
+            if (sscanf(e, "%d,%d", &es, &em) == 2) {
+                S = es;
+                mul = em;
             }
         }
+        if (S == 3 && mul == 1) launch_hist<DH, MB, NW, NH, 3, 1>(grid, block, a, PB, s);
+        else if (S == 5 && mul == 1 && 5 * SLOT <= 160 * 1024) launch_hist<DH, MB, NW, NH, 5, 1>(grid, block, a, PB, s);
+        else if (mul == 2 && wide && S == 3) launch_hist<DH, MB, NW, NH, 3, (wide ? 2 : 1)>(grid, block, a, PB, s);
+        else if (mul == 2 && wide) launch_hist<DH, MB, NW, NH, 4, (wide ? 2 : 1)>(grid, block, a, PB, s);
+        else launch_hist<DH, MB, NW, NH, 4, 1>(grid, block, a, PB, s);
+        return hipGetLastError();
     }
-    if (!masked && !proto) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, MB, NW, NH, false, false>), grid, block, 0, s, a, PB);
     if (masked && !proto) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, MB, NW, NH, true, false>), grid, block, 0, s, a, PB);
     if (!masked && proto) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, MB, NW, NH, false, true>), grid, block, 0, s, a, PB);
     if (masked && proto) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, MB, NW, NH, true, true>), grid, block, 0, s, a, PB);
