@@ -15,7 +15,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import sys
@@ -27,7 +26,6 @@ sys.path.insert(0, ROOT)
 METRIC = "history tokens/sec compressed by SA (bf16, 100K varlen) + % HBM peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-KERNEL_SRC = os.path.join(ROOT, "sketch_attention_flashsa_amd", "csrc", "sa_bf16_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_full100k_bf16.json")
 
 
@@ -64,23 +62,39 @@ class _Hip:
 
 
 def _kernel_hash() -> str:
-    h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.dirname(KERNEL_SRC))):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(os.path.dirname(KERNEL_SRC), f), "rb").read())
-    return h.hexdigest()[:16]
+    from sketch_attention_flashsa_amd.build import sources_hash
+    return sources_hash()
 
 
-def _traffic(per_launch_alg_bytes: float):
+def _traffic(kernel: str):
     """HBM bytes per launch of the streaming kernel from the committed
-    rocprofv3 counter summary, or None if absent or taken on other sources."""
+    rocprofv3 counter summary, or None if absent, taken on another kernel or
+    on other sources."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sources_sha256_16") != _kernel_hash():
+    if t.get("kernel_sources_sha256_16") != _kernel_hash() or t.get("kernel") != kernel:
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(mib: int, steps: int) -> None:
+    """A plain elementwise copy (torch.neg, bf16) that reads and writes
+    mib MiB per launch: the reference for scaling the HBM byte counters."""
+    import torch
+    n = mib * (1 << 20) // 2
+    x = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"calibration": "copy", "kernel": "neg (elementwise)", "bytes_read": 2 * n,
+                      "bytes_written": 2 * n, "launches": steps, "ms_per_launch": dt * 1e3,
+                      "GBps": 4 * n / dt / 1e9}))
 
 
 def cpu_baseline(w, n_users: int):
@@ -116,11 +130,17 @@ def main():
     ap.add_argument("--workload", type=int, default=4, help="workload number (default 4: full 100K bf16)")
     ap.add_argument("--cpu-users", type=int, default=4, help="users in the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of the forward, time a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the forward has no multi-GPU path in this build "
               "(users shard across GPUs with no exchange; run one process per GPU).", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_mib:
+        copy_calibration(args.copy_mib, args.steps)
+        return
 
     import torch
     import workloads as W
@@ -143,6 +163,7 @@ def main():
     rows = K.shape[0] if cu is not None else B * K.shape[1]
     pb = sa.make_problem(B, H, m, dh, rows, L_max=0 if cu is not None else K.shape[1], dtype=w["dtype"])
     ws = torch.empty(sa.sa_forward_workspace_size(pb), dtype=torch.uint8, device=dev)
+    kernel = sa.sa_forward_kernel_name(pb)
 
     def step():
         sa.sa_forward(P, K, V, cu_offsets=cu, lengths=lengths, out=S, workspace=ws, **pb_kw)
@@ -190,12 +211,12 @@ def main():
         "hbm_frac_step": step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
         "roofline": {
             "bound": "hbm",
-            "kernel": "sa_bf16_fwd_kernel" if w["dtype"] == "bf16" else "sa_f32_fwd_kernel",
+            "kernel": kernel,
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": _traffic(alg_bytes),
+            "traffic": _traffic(kernel) if spec.name == "full100k_bf16" else None,
             "algorithmic_bytes_per_launch": alg_bytes,
             "kernel_ms_avg": kern_avg_ms,
             "kernel_ms_min": min(kern_ms),

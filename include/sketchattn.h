@@ -146,6 +146,12 @@ sa_status sa_forward(const sa_problem* pb, const void* P, const void* K, const v
  * (0 if the problem itself is invalid; sa_last_error() then says why). */
 size_t sa_forward_workspace_size(const sa_problem* pb);
 
+/* Name of the kernel that performs the pass over K/V for this problem on the
+ * current device (the one the timing events below bracket): a static string,
+ * or NULL if the problem is invalid or unsupported (sa_last_error() says why).
+ * Profilers use it to find that kernel in a trace. */
+const char* sa_forward_kernel_name(const sa_problem* pb);
+
 /*
  * Fused key/value projection + Sketch Attention forward (packed layout only).
  *

@@ -23,7 +23,7 @@ SA_DTYPE_F32, SA_DTYPE_BF16 = 0, 1
 SA_NORM_HISTORY, SA_NORM_PROTOTYPE = 0, 1
 _NORMS = {"history": SA_NORM_HISTORY, "prototype": SA_NORM_PROTOTYPE}
 
-EXPORTED = ("sa_forward", "sa_forward_workspace_size", "sa_forward_fused_proj",
+EXPORTED = ("sa_forward", "sa_forward_workspace_size", "sa_forward_kernel_name", "sa_forward_fused_proj",
             "sa_forward_fused_proj_workspace_size", "sa_set_timing_events", "sa_status_string", "sa_last_error",
             "sa_version")
 
@@ -64,6 +64,8 @@ def load_library(path: str | None = None):
     lib.sa_forward.restype = ctypes.c_int
     lib.sa_forward_workspace_size.argtypes = [pp]
     lib.sa_forward_workspace_size.restype = ctypes.c_size_t
+    lib.sa_forward_kernel_name.argtypes = [pp]
+    lib.sa_forward_kernel_name.restype = ctypes.c_char_p
     lib.sa_forward_fused_proj.argtypes = [pp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.sa_forward_fused_proj.restype = ctypes.c_int
     lib.sa_forward_fused_proj_workspace_size.argtypes = [pp, ctypes.c_int32]
@@ -118,6 +120,14 @@ def make_problem(B, H, m, dh, total_rows, L_max=0, dtype="bf16", norm="history",
 
 def sa_forward_workspace_size(pb: SaProblem) -> int:
     return int(load_library().sa_forward_workspace_size(ctypes.byref(pb)))
+
+
+def sa_forward_kernel_name(pb: SaProblem) -> str:
+    """Name of the kernel that makes the pass over K/V for this problem."""
+    name = load_library().sa_forward_kernel_name(ctypes.byref(pb))
+    if name is None:
+        raise SketchAttnError(SA_ERR_INVALID_ARG, sa_last_error())
+    return name.decode()
 
 
 def _check(status):

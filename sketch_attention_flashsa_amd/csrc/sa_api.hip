@@ -187,6 +187,13 @@ size_t sa_forward_workspace_size(const sa_problem* pb) {
     return pl.total;
 }
 
+const char* sa_forward_kernel_name(const sa_problem* pb) {
+    Plan pl;
+    if (!pb || make_plan(pb, pb->L_max == 0, &pl) != SA_OK) return nullptr;
+    if (pl.f32) return "sa_f32_fwd_kernel";
+    return pl.stream ? "sa_bf16_stream_kernel" : "sa_bf16_fwd_kernel";
+}
+
 sa_status sa_forward(const sa_problem* pb, const void* P, const void* K, const void* V, const int32_t* cu_offsets,
                      const int32_t* lengths, const uint8_t* mask, float* S_out, float* lse_out, void* workspace,
                      size_t workspace_bytes, hipStream_t stream) {

@@ -104,3 +104,14 @@ def test_workspace_size_is_layout_independent_and_monotone():
     assert 0 < a < b          # the prototype axis adds the per-row normaliser
     # partials stay a small fraction of the K/V bytes at the 100K workload
     assert a < 0.05 * (2 * 1_600_000 * 8 * 64 * 2)
+
+
+def test_kernel_name_query():
+    # the streaming kernel serves the 64- and 32-wide heads; f32 has its own kernel
+    assert sa.sa_forward_kernel_name(sa.make_problem(16, 8, 128, 64, 1_600_000, dtype="bf16")) == "sa_bf16_stream_kernel"
+    assert sa.sa_forward_kernel_name(sa.make_problem(8, 4, 64, 32, 4096, dtype="bf16")) == "sa_bf16_stream_kernel"
+    assert sa.sa_forward_kernel_name(sa.make_problem(8, 2, 16, 16, 4096, dtype="f32")) == "sa_f32_fwd_kernel"
+    # dh = 128 is outside the streaming kernel's shapes and uses the tiled kernel
+    assert sa.sa_forward_kernel_name(sa.make_problem(8, 2, 64, 128, 4096, dtype="bf16")) == "sa_bf16_fwd_kernel"
+    with pytest.raises(sa.SketchAttnError):
+        sa.sa_forward_kernel_name(sa.make_problem(8, 0, 64, 32, 4096, dtype="bf16"))
