@@ -224,13 +224,17 @@ def sa_forward_fused_proj(X, Wk, Wv, P, cu_offsets, mask=None, norm: str = "hist
                           scale: float | None = None, chunk_rows: int = 0, workspace=None, out=None):
     """Fused K/V projection + Sketch Attention: K = X Wk, V = X Wv (V = X when
     ``Wv`` is None) computed on chip.  X [rows, d_model] bf16, Wk/Wv
-    [d_model, H*dh], P [H, m, dh], cu_offsets int32 [B+1]."""
+    [d_model, H*dh], P [H, m, dh] (or [B, H, m, dh], per user), cu_offsets
+    int32 [B+1]."""
     import torch
     lib = load_library()
     dev = X.device
-    H, m, dh = P.shape
-    rows, d_model = X.shape
     B = cu_offsets.numel() - 1
+    per_user = P.dim() == 4
+    if per_user and P.shape[0] != B:
+        raise ValueError("per-user P must be [B, H, m, dh]")
+    H, m, dh = P.shape[-3:]
+    rows, d_model = X.shape
     for t in (X, Wk, P) + ((Wv,) if Wv is not None else ()):
         if t.device != dev or t.dtype != X.dtype:
             raise ValueError("X, Wk, Wv and P must share one device and dtype")
@@ -238,8 +242,12 @@ def sa_forward_fused_proj(X, Wk, Wv, P, cu_offsets, mask=None, norm: str = "hist
     Wv = Wv.contiguous() if Wv is not None else None
     if mask is not None:
         mask = (mask.to(torch.uint8) if mask.dtype == torch.bool else mask).contiguous()
-    pb = make_problem(B, H, m, dh, rows, dtype=_dtype_name(X), norm=norm, scale=scale or 0.0, chunk_rows=chunk_rows)
+    pb = make_problem(B, H, m, dh, rows, dtype=_dtype_name(X), norm=norm, scale=scale or 0.0, chunk_rows=chunk_rows,
+                      q_batch_stride=(H * m * dh if per_user else 0))
     nws = int(lib.sa_forward_fused_proj_workspace_size(ctypes.byref(pb), int(d_model)))
+    if nws == 0:
+        _check(lib.sa_forward_fused_proj(ctypes.byref(pb), None, int(d_model), None, None, None, None, None, None,
+                                         None, None, 0, None))
     if workspace is None or workspace.numel() < nws:
         workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
     S = out if out is not None else torch.empty((B, H, m, dh), dtype=torch.float32, device=dev)

@@ -70,6 +70,8 @@ struct Plan {
     size_t off_vcu = 0, off_M = 0, off_Z = 0, off_acc = 0, off_tok = 0, total = 0;
 };
 
+void set_layout(const sa_problem* pb, Plan* pl);
+
 // Validation and work split shared by every entry point.  The workspace size
 // depends only on the problem description, never on which optional pointers
 // a call passes, so the size query and the call always agree.
@@ -153,7 +155,12 @@ sa_status make_plan(const sa_problem* pb, bool packed, Plan* pl) {
         pl->G = (int)(G > 0 ? G : 1);
     }
 
-    // workspace layout
+    set_layout(pb, pl);
+    return SA_OK;
+}
+
+// Workspace layout for the plan's G (byte offsets, 256-byte aligned sections).
+void set_layout(const sa_problem* pb, Plan* pl) {
     const size_t nslot = (size_t)pl->G + (size_t)pb->B;
     const size_t hm = (size_t)pb->H * pb->m;
     size_t off = 0;
@@ -168,6 +175,30 @@ sa_status make_plan(const sa_problem* pb, bool packed, Plan* pl) {
     pl->off_tok = off;
     if (pb->norm == SA_NORM_PROTOTYPE) off = align_up(off + sizeof(float) * (size_t)pl->buf_rows * pb->H);
     pl->total = off;
+}
+
+// Plan of the fused projection entry: the general validation (packed layout),
+// the fused kernel's shape limits, and its own work split.
+sa_status make_fused_plan(const sa_problem* pb, int32_t d_model, Plan* pl) {
+    sa_status st = make_plan(pb, true, pl);
+    if (st != SA_OK) return st;
+    if (pb->dtype != SA_DTYPE_BF16) return fail(SA_ERR_UNSUPPORTED, "fused projection: bf16 inputs only");
+    if (pb->norm != SA_NORM_HISTORY) return fail(SA_ERR_UNSUPPORTED, "fused projection: history axis only");
+    if (d_model < 1) return fail(SA_ERR_INVALID_ARG, "d_model must be >= 1 (got %d)", d_model);
+    if (!sa::fused_supported(d_model, pb->m, pb->dh))
+        return fail(SA_ERR_UNSUPPORTED, "fused projection: needs dh == 32, d_model in {128, 256}, m in {64, 128, 256} "
+                                        "(got dh=%d d_model=%d m=%d)", pb->dh, d_model, pb->m);
+    if (pb->chunk_rows > 0) {
+        pl->R_fixed = pb->chunk_rows;
+        const int64_t G = (pb->total_rows + pb->chunk_rows - 1) / pb->chunk_rows;
+        pl->G = (int)(G > 0 ? G : 1);
+    } else {
+        pl->R_fixed = 0;
+        const int64_t G = (int64_t)device_info().cus / sa::fused_groups(pb->H);
+        pl->G = (int)(G > 0 ? G : 1);
+    }
+    pl->R_min = kRowMinBf16;
+    set_layout(pb, pl);
     return SA_OK;
 }
 
@@ -301,15 +332,73 @@ sa_status sa_forward_fused_proj(const sa_problem* pb, const void* X, int32_t d_m
                                 const void* P, const int32_t* cu_offsets, const uint8_t* mask, float* S_out,
                                 float* lse_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     g_err[0] = 0;
-    (void)pb; (void)X; (void)d_model; (void)Wk; (void)Wv; (void)P; (void)cu_offsets; (void)mask;
-    (void)S_out; (void)lse_out; (void)workspace; (void)workspace_bytes; (void)stream;
-    return fail(SA_ERR_UNSUPPORTED, "fused projection is not built yet");
+    Plan pl;
+    sa_status st = make_fused_plan(pb, d_model, &pl);
+    if (st != SA_OK) return st;
+    if (!cu_offsets) return fail(SA_ERR_INVALID_ARG, "the fused entry takes packed rows: cu_offsets must be non-NULL");
+    if (pb->B == 0) return SA_OK;
+    if (!X || !Wk || !P || !S_out) return fail(SA_ERR_INVALID_ARG, "X, Wk, P and S_out must be non-NULL");
+    if (!Wv && (int64_t)pb->H * pb->dh != d_model)
+        return fail(SA_ERR_INVALID_ARG, "Wv == NULL (V = X) needs H*dh == d_model (got %d*%d vs %d)", pb->H, pb->dh,
+                    d_model);
+    if (!aligned(X, 16) || !aligned(Wk, 16) || (Wv && !aligned(Wv, 16)) || !aligned(P, 16))
+        return fail(SA_ERR_INVALID_ARG, "X, Wk, Wv and P must be 16-byte aligned");
+    if (!aligned(S_out, 4) || !aligned(lse_out, 4)) return fail(SA_ERR_INVALID_ARG, "misaligned pointer");
+    if (pl.total > 0 && (!workspace || workspace_bytes < pl.total))
+        return fail(SA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", pl.total, workspace_bytes);
+    if (workspace && !aligned(workspace, kAlign)) return fail(SA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+    unsigned char* ws = (unsigned char*)workspace;
+    sa::Users users{};
+    users.cu = cu_offsets;
+    users.B = pb->B;
+    const float scale = pb->scale > 0.f ? pb->scale : 1.0f / sqrtf((float)pb->dh);
+    sa::Partials part{(float*)(ws + pl.off_acc), (float*)(ws + pl.off_M), (float*)(ws + pl.off_Z)};
+
+    sa::FusedArgs a{};
+    a.users = users;
+    a.mask = mask;
+    a.X = X;
+    a.Wk = Wk;
+    a.Wv = Wv;
+    a.P = P;
+    a.q_batch_stride = pb->q_batch_stride;
+    a.H = pb->H;
+    a.m = pb->m;
+    a.d_model = d_model;
+    a.c = scale * sa::kLog2e;
+    a.G = pl.G;
+    a.R_fixed = pl.R_fixed;
+    a.R_min = pl.R_min;
+    a.part = part;
+    hipError_t e;
+    const hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
+    g_ev_start = g_ev_stop = nullptr;
+    if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return hip_fail(e, "timing event");
+    e = sa::launch_fused(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "fused forward");
+    if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return hip_fail(e, "timing event");
+
+    sa::MergeArgs mg{};
+    mg.users = users;
+    mg.H = pb->H;
+    mg.m = pb->m;
+    mg.dh = pb->dh;
+    mg.G = pl.G;
+    mg.R_fixed = pl.R_fixed;
+    mg.R_min = pl.R_min;
+    mg.part = part;
+    mg.S = S_out;
+    mg.lse = lse_out;
+    mg.norm = SA_NORM_HISTORY;
+    e = sa::launch_merge(mg, stream);
+    if (e != hipSuccess) return hip_fail(e, "merge");
+    return SA_OK;
 }
 
 size_t sa_forward_fused_proj_workspace_size(const sa_problem* pb, int32_t d_model) {
-    (void)d_model;
     Plan pl;
-    if (!pb || make_plan(pb, true, &pl) != SA_OK) return 0;
+    if (!pb || make_fused_plan(pb, d_model, &pl) != SA_OK) return 0;
     return pl.total;
 }
 

@@ -30,171 +30,19 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include "sa_internal.h"
+#include "sa_device.h"
 
 namespace sa {
+
+using namespace dev;
 
 namespace {
 
 constexpr int kStages = 4;   // ring slots: 2 stages in flight, 1 computed, 1 still read for V
-constexpr float kLazyBound = 65536.0f;   // fast path while a lane's tile sum <= 2^16
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ bf16x2 pack2(float a, float b) {
-    f32x2 v = {a, b};
-    return __builtin_convertvector(v, bf16x2);
-}
-__device__ __forceinline__ bf16x8 cat8(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
-    bf16x4 lo = __builtin_shufflevector(a, b, 0, 1, 2, 3);
-    bf16x4 hi = __builtin_shufflevector(c, d, 0, 1, 2, 3);
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-__device__ __forceinline__ float dot2sum(bf16x2 a, float acc) {
-    const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(a, one, acc, false);
-}
-// k-slot j (0..7) of lane group g <-> row of the 32-row sub-tile
-__device__ __forceinline__ int tok_of(int g, int j) { return (j < 4) ? 4 * g + j : 16 + 4 * g + (j - 4); }
-
-// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt[3:0],
-// expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14]); the others are left at max.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
-
-// wait_vm<n * VMS> for a runtime n in [0, NMAX] (the counter operand is an immediate)
-template <int NMAX, int VMS>
-__device__ __forceinline__ void wait_after(int n) {
-    if constexpr (NMAX == 0) {
-        wait_vm<0>();
-    } else {
-        if (n >= NMAX) wait_vm<NMAX * VMS>();
-        else wait_after<NMAX - 1, VMS>(n);
-    }
-}
-
-// The V^T operands of one 32-row unit: for each 16-wide dh block db, two
-// ds_read_b64_tr_b16 (rows 4g..4g+3 and, OFFB bytes further, 16+4g..16+4g+3 of
-// the lane group).  Issued from one asm block that waits for its own results
-// (lgkmcnt(0)) before returning, so no load is in flight when the outputs are
-// used.  The builtin form would make the compiler drain every in-flight DMA
-// of the ring first (it cannot tell this read from the DMA targets).
-template <int DB, int OFFB>
-__device__ __forceinline__ void read_vt(const uint32_t (&addr)[DB], i16x4 (&lo)[DB], i16x4 (&hi)[DB]) {
-    static_assert(DB == 2 || DB == 4, "dh blocks");
-    if constexpr (DB == 2) {
-        asm volatile(
-            "ds_read_b64_tr_b16 %0, %4\n\t"
-            "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
-            "ds_read_b64_tr_b16 %2, %5\n\t"
-            "ds_read_b64_tr_b16 %3, %5 offset:%6\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1])
-            : "v"(addr[0]), "v"(addr[1]), "i"(OFFB)
-            : "memory");
-    } else {
-        asm volatile(
-            "ds_read_b64_tr_b16 %0, %8\n\t"
-            "ds_read_b64_tr_b16 %1, %8 offset:%12\n\t"
-            "ds_read_b64_tr_b16 %2, %9\n\t"
-            "ds_read_b64_tr_b16 %3, %9 offset:%12\n\t"
-            "ds_read_b64_tr_b16 %4, %10\n\t"
-            "ds_read_b64_tr_b16 %5, %10 offset:%12\n\t"
-            "ds_read_b64_tr_b16 %6, %11\n\t"
-            "ds_read_b64_tr_b16 %7, %11 offset:%12\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1]), "=&v"(lo[2]), "=&v"(hi[2]), "=&v"(lo[3]),
-              "=&v"(hi[3])
-            : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "i"(OFFB)
-            : "memory");
-    }
-}
-
-// The K operands of one 32-row unit: for each k-chunk kc a 16-byte read of the
-// lane's row in each 16-row half (the second OFFB bytes further).  Same asm
-// discipline as read_vt: the block waits for its own results; as a compiler
-// builtin the read would be preceded by a wait for the whole DMA ring.
-template <int KC, int OFFB>
-__device__ __forceinline__ void read_k(const uint32_t (&addr)[KC], bf16x8 (&lo)[KC], bf16x8 (&hi)[KC]) {
-    static_assert(KC == 1 || KC == 2, "k chunks");
-    if constexpr (KC == 1) {
-        asm volatile(
-            "ds_read_b128 %0, %2\n\t"
-            "ds_read_b128 %1, %2 offset:%3\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(lo[0]), "=&v"(hi[0])
-            : "v"(addr[0]), "i"(OFFB)
-            : "memory");
-    } else {
-        asm volatile(
-            "ds_read_b128 %0, %4\n\t"
-            "ds_read_b128 %1, %4 offset:%6\n\t"
-            "ds_read_b128 %2, %5\n\t"
-            "ds_read_b128 %3, %5 offset:%6\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(lo[0]), "=&v"(hi[0]), "=&v"(lo[1]), "=&v"(hi[1])
-            : "v"(addr[0]), "v"(addr[1]), "i"(OFFB)
-            : "memory");
-    }
-}
-
-// One direct-to-LDS load of 16 bytes per lane: lane i's 16 bytes from `src`
-// land at LDS address lds + 16*i (lds is wave-uniform; it goes through M0).
-// Written as asm so the compiler does not know that the ring is a DMA target
-// and therefore never inserts its own (whole-ring) waits before LDS reads;
-// the kernel's counted vmcnt waits are what orders the ring.  The asm has no
-// output register, so nothing of it is left in flight in a register.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-    asm volatile(
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %0, off"
-        :
-        : "v"(src), "s"(lds)
-        : "memory");
-}
-
-// acc *= f in place.  A tied-operand ALU asm statement keeps the accumulator
-// in the same registers on the (rare) rescale path, so the common path does
-// not pay register copies to merge two versions of it.
-__device__ __forceinline__ void scale_in_place(f32x4& acc, float f) {
-    asm volatile(
-        "v_mul_f32 %0, %4, %0\n\t"
-        "v_mul_f32 %1, %4, %1\n\t"
-        "v_mul_f32 %2, %4, %2\n\t"
-        "v_mul_f32 %3, %4, %3"
-        : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
-        : "v"(f));
-}
-
-// Bits j = 0..7 of a lane: validity of the rows of its PV k-slots.
-__device__ __forceinline__ uint32_t lane_slots(uint32_t valid, int g) {
-    return ((valid >> (4 * g)) & 0xFu) | (((valid >> (16 + 4 * g)) & 0xFu) << 4);
-}
-
-// Block barrier without the memory fence of __syncthreads (which would also
-// wait for every DMA still in flight).  The empty asm statements only stop the
-// compiler from moving memory accesses across the barrier; the counted waits
-// before it make the stage's LDS contents complete.
-__device__ __forceinline__ void block_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 
 }  // namespace
 
-template <int DH, int MB, int NW, int NH, bool MASKED, bool PROTO, int S = kStages, int WPE = 2, int PADKB = 0,
-          int DMUL = 1>  // PADKB: unused extra LDS (kept 0)
+template <int DH, int MB, int NW, int NH, bool MASKED, bool PROTO, int S = kStages, int WPE = 2, int DMUL = 1>
 __global__ __launch_bounds__(NW * 64, WPE) void sa_bf16_stream_kernel(FwdArgs a, int PB) {
     constexpr int CPR = NH * DH / 8;                      // 16-byte chunks per row per tensor
     constexpr int ROWB = CPR * 16;                        // bytes per row per tensor
@@ -215,7 +63,6 @@ __global__ __launch_bounds__(NW * 64, WPE) void sa_bf16_stream_kernel(FwdArgs a,
     static_assert(S >= 3 && S <= 8 && (AHEAD - 1) * VMS < 64, "ring depth");
 
     __shared__ __attribute__((aligned(1024))) unsigned char ring[S][2][STAGE];
-    static_assert(PADKB == 0, "no padding");
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -581,7 +428,7 @@ namespace {
 // SA_STREAM_RING="S,MUL" selects another of the compiled shapes (tuning).
 template <int DH, int MB, int NW, int NH, int S, int MUL>
 void launch_hist(dim3 grid, dim3 block, const FwdArgs& a, int PB, hipStream_t s) {
-    hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, MB, NW, NH, false, false, S, 2, 0, MUL>), grid, block, 0, s, a, PB);
+    hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, MB, NW, NH, false, false, S, 2, MUL>), grid, block, 0, s, a, PB);
 }
 
 template <int DH, int MB, int NW, int NH>

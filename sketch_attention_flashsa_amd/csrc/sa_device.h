@@ -1,0 +1,123 @@
+// sa_device.h -- device helpers shared by the MFMA streaming kernels
+// (sa_bf16_stream.hip, sa_fused_proj.hip): MFMA and bf16 packing wrappers,
+// counted memory waits, the direct-to-LDS load and the bare block barrier.
+#pragma once
+
+#include "sa_internal.h"
+
+namespace sa {
+namespace dev {
+
+// Fast path of the online softmax while a lane's tile sum stays <= 2^16
+// (relative to the running maximum); a larger sum takes the exact path.
+constexpr float kLazyBound = 65536.0f;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x2 pack2(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_convertvector(v, bf16x2);
+}
+__device__ __forceinline__ bf16x8 cat8(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
+    bf16x4 lo = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+    bf16x4 hi = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ float dot2sum(bf16x2 a, float acc) {
+    const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(a, one, acc, false);
+}
+// k-slot j (0..7) of lane group g <-> row of the 32-row sub-tile
+__device__ __forceinline__ int tok_of(int g, int j) { return (j < 4) ? 4 * g + j : 16 + 4 * g + (j - 4); }
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt[3:0],
+// expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14]); the others are left at max.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+// wait_vm<n * VMS> for a runtime n in [0, NMAX] (the counter operand is an immediate)
+template <int NMAX, int VMS>
+__device__ __forceinline__ void wait_after(int n) {
+    if constexpr (NMAX == 0) {
+        wait_vm<0>();
+    } else {
+        if (n >= NMAX) wait_vm<NMAX * VMS>();
+        else wait_after<NMAX - 1, VMS>(n);
+    }
+}
+
+// One direct-to-LDS load of 16 bytes per lane: lane i's 16 bytes from `src`
+// land at LDS address lds + 16*i (lds is wave-uniform; it goes through M0).
+// Written as asm so the compiler does not know that the ring is a DMA target
+// and therefore never inserts its own (whole-ring) waits before LDS reads;
+// the kernel's counted vmcnt waits are what orders the ring.  The asm has no
+// output register, so nothing of it is left in flight in a register.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(src), "s"(lds)
+        : "memory");
+}
+
+// The same load with a wave-uniform 64-bit base and a per-lane 32-bit byte
+// offset (lane i's 16 bytes come from base + voff).
+__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t lds) {
+    // uniform: pin it to SGPRs.  readfirstlane returns int: each half goes
+    // through uint32_t so that the low half is zero-extended, not sign-extended.
+    const uint64_t bb = (uint64_t)(uintptr_t)base;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(bb >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bb);
+    const uint64_t ub = ((uint64_t)hi << 32) | (uint64_t)lo;
+    base = (const void*)(uintptr_t)ub;
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(base), "s"(lds)
+        : "memory");
+}
+
+// acc *= f in place.  A tied-operand ALU asm statement keeps the accumulator
+// in the same registers on the (rare) rescale path, so the common path does
+// not pay register copies to merge two versions of it.
+__device__ __forceinline__ void scale_in_place(f32x4& acc, float f) {
+    asm volatile(
+        "v_mul_f32 %0, %4, %0\n\t"
+        "v_mul_f32 %1, %4, %1\n\t"
+        "v_mul_f32 %2, %4, %2\n\t"
+        "v_mul_f32 %3, %4, %3"
+        : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
+        : "v"(f));
+}
+
+// Bits j = 0..7 of a lane: validity of the rows of its PV k-slots.
+__device__ __forceinline__ uint32_t lane_slots(uint32_t valid, int g) {
+    return ((valid >> (4 * g)) & 0xFu) | (((valid >> (16 + 4 * g)) & 0xFu) << 4);
+}
+
+// Block barrier without the memory fence of __syncthreads (which would also
+// wait for every DMA still in flight).  The empty asm statements only stop the
+// compiler from moving memory accesses across the barrier; the counted waits
+// before it make the stage's LDS contents complete.
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+
+}  // namespace dev
+}  // namespace sa

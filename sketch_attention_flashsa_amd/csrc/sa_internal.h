@@ -144,4 +144,23 @@ struct StreamConfig {
 bool stream_config(int dh, int m, int H, StreamConfig* cfg);
 hipError_t launch_bf16_stream(const FwdArgs& a, const StreamConfig& cfg, hipStream_t s);
 
+// Fused key/value projection + forward (sa_fused_proj.hip): X [rows, d_model]
+// bf16, W_K / W_V [d_model, H*dh] (W_V == nullptr: V = X), history axis.
+struct FusedArgs {
+    Users users;             // packed offsets only
+    const uint8_t* mask;     // per row or nullptr
+    const void* X;
+    const void* Wk;
+    const void* Wv;          // nullptr: V = X (needs H*dh == d_model)
+    const void* P;
+    int64_t q_batch_stride;  // elements; 0 = shared
+    int32_t H, m, d_model;
+    float c;                 // scale * log2(e)
+    int32_t G, R_fixed, R_min;
+    Partials part;
+};
+bool fused_supported(int d_model, int m, int dh);
+int fused_groups(int H);     // blocks per row range
+hipError_t launch_fused(const FusedArgs& a, hipStream_t s);
+
 }  // namespace sa

@@ -115,3 +115,28 @@ def test_kernel_name_query():
     assert sa.sa_forward_kernel_name(sa.make_problem(8, 2, 64, 128, 4096, dtype="bf16")) == "sa_bf16_fwd_kernel"
     with pytest.raises(sa.SketchAttnError):
         sa.sa_forward_kernel_name(sa.make_problem(8, 0, 64, 32, 4096, dtype="bf16"))
+
+
+def test_fused_entry_validation():
+    lib = sa.load_library()
+    pb = sa.make_problem(128, 8, 256, 32, 4_240_293, dtype="bf16")
+    n = lib.sa_forward_fused_proj_workspace_size(ctypes.byref(pb), 256)
+    assert n > 0
+    # unsupported: d_model outside {128, 256}, dh != 32, fp32 inputs, prototype axis
+    for bad, dm in ((sa.make_problem(4, 8, 256, 32, 1000, dtype="bf16"), 192),
+                    (sa.make_problem(4, 8, 128, 64, 1000, dtype="bf16"), 256),
+                    (sa.make_problem(4, 8, 128, 32, 1000, dtype="f32"), 256),
+                    (sa.make_problem(4, 8, 128, 32, 1000, dtype="bf16", norm="prototype"), 256)):
+        assert lib.sa_forward_fused_proj_workspace_size(ctypes.byref(bad), dm) == 0
+        st = lib.sa_forward_fused_proj(ctypes.byref(bad), None, dm, None, None, None, None, None, None, None, None,
+                                       0, None)
+        assert st == sa.SA_ERR_UNSUPPORTED, sa.sa_last_error()
+    # packed only, and V = X needs H*dh == d_model: rejected before any GPU work
+    st = lib.sa_forward_fused_proj(ctypes.byref(pb), FAKE, 256, FAKE, None, FAKE, None, None, FAKE, None, FAKE,
+                                   n, None)
+    assert st == sa.SA_ERR_INVALID_ARG and "cu_offsets" in sa.sa_last_error()
+    pb5 = sa.make_problem(4, 5, 64, 32, 1000, dtype="bf16")
+    n5 = lib.sa_forward_fused_proj_workspace_size(ctypes.byref(pb5), 256)
+    st = lib.sa_forward_fused_proj(ctypes.byref(pb5), FAKE, 256, FAKE, None, FAKE, FAKE, None, FAKE, None, FAKE,
+                                   n5, None)
+    assert st == sa.SA_ERR_INVALID_ARG and "H*dh == d_model" in sa.sa_last_error()

@@ -228,6 +228,39 @@ def random_case(seed: int, *, B: int, H: int, m: int, dh: int, lengths, dtype: s
     return out
 
 
+def random_fused_case(seed: int, *, B: int, H: int, m: int, dh: int, d_model: int, lengths,
+                      w_var: float = 1.0 / 256, mask_p: float = 0.0, per_user_p: bool = False):
+    """A small free-form case of the fused-projection recipe (bf16): X rows
+    ~ N(0, 1) [rows, d_model], Wk, Wv ~ N(0, w_var) [d_model, H*dh], P ~ N(0, 1)
+    [H, m, dh] (or [B, H, m, dh] with ``per_user_p``), packed by ``lengths``;
+    ``mask_p`` > 0 adds a per-row mask with that drop probability."""
+    import torch
+    ss = np.random.SeedSequence(seed)
+    kids = ss.spawn(3 + B)
+    g_p, g_w, g_mask = (np.random.Generator(np.random.PCG64(k)) for k in kids[:3])
+    lengths = np.asarray(lengths, dtype=np.int64)
+    pshape = (B, H, m, dh) if per_user_p else (H, m, dh)
+    P = g_p.standard_normal(pshape, dtype=np.float32)
+    std = np.float32(math.sqrt(w_var))
+    Wk = g_w.standard_normal((d_model, H * dh), dtype=np.float32) * std
+    Wv = g_w.standard_normal((d_model, H * dh), dtype=np.float32) * std
+    cu = np.zeros(B + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(lengths)
+    X = torch.empty((int(cu[-1]), d_model), dtype=torch.bfloat16)
+    for b in range(B):
+        g = np.random.Generator(np.random.PCG64(kids[3 + b]))
+        X[cu[b]:cu[b + 1]] = _to_torch(g.standard_normal((int(lengths[b]), d_model), dtype=np.float32), "bf16")
+    spec = Spec("fused_case", B=B, H=H, m=m, dh=dh, dtype="bf16", layout="packed", lengths="fixed", seed=seed,
+                d_model=d_model)
+    out = {"spec": spec, "B": B, "H": H, "m": m, "dh": dh, "dtype": "bf16", "layout": "packed",
+           "lengths": torch.from_numpy(lengths.astype(np.int32)), "P": _to_torch(P, "bf16"),
+           "Wk": _to_torch(Wk, "bf16"), "Wv": _to_torch(Wv, "bf16"), "X": X,
+           "cu_offsets": torch.from_numpy(cu.astype(np.int32)), "d_model": d_model}
+    if mask_p > 0:
+        out["mask"] = torch.from_numpy((g_mask.uniform(size=int(cu[-1])) >= mask_p).astype(np.uint8))
+    return out
+
+
 def algorithmic_bytes(w: dict) -> int:
     """HBM bytes one forward must move at minimum: K and V (or X and the two
     projection matrices), the prototypes, the fp32 sketch and the offsets."""
