@@ -245,8 +245,11 @@ __global__ __launch_bounds__(NW * 64, WPE) void sa_bf16_stream_kernel(FwdArgs a,
             }
             return fits;
         };
-        // exact weights: validity, running-maximum update and rescale
-        auto weights_exact = [&](const f32x4 (&s)[2][NSB], uint32_t valid, bf16x8 (&pk)[NSB]) {
+        // exact weights: validity, running-maximum update and rescale.  It
+        // overwrites the fast path's pk and zt (the tile sums) and sets the
+        // rescale factors f; the caller applies Z = Z f + zt.
+        auto weights_exact = [&](const f32x4 (&s)[2][NSB], uint32_t valid, bf16x8 (&pk)[NSB], float (&zt)[NSB],
+                                 float (&f)[NSB]) {
             const uint32_t vj = lane_slots(valid, g);
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
@@ -261,17 +264,17 @@ __global__ __launch_bounds__(NW * 64, WPE) void sa_bf16_stream_kernel(FwdArgs a,
                 tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
                 const float Mold = Mc[sb];
                 const float Mnew = fmaxf(Mold, tm);
-                const float f = (Mnew == Mold) ? 1.f : __builtin_amdgcn_exp2f(Mold - Mnew);
+                f[sb] = (Mnew == Mold) ? 1.f : __builtin_amdgcn_exp2f(Mold - Mnew);
                 float p[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) p[j] = ((vj >> j) & 1) ? __builtin_amdgcn_exp2f(x[j] - Mnew) : 0.f;
                 const bf16x2 q0 = pack2(p[0], p[1]), q1 = pack2(p[2], p[3]);
                 const bf16x2 q2 = pack2(p[4], p[5]), q3 = pack2(p[6], p[7]);
                 pk[sb] = cat8(q0, q1, q2, q3);
-                Zs[sb] = Zs[sb] * f + dot2sum(q3, dot2sum(q2, dot2sum(q1, dot2sum(q0, 0.f))));
+                zt[sb] = dot2sum(q3, dot2sum(q2, dot2sum(q1, dot2sum(q0, 0.f))));
                 Mc[sb] = Mnew;
 #pragma unroll
-                for (int db = 0; db < DB; ++db) scale_in_place(acc[sb][db], f);
+                for (int db = 0; db < DB; ++db) acc[sb][db] *= f[sb];
             }
         };
         // prototype axis: weights 2^(s*c - lse2[row]) with the per-row normaliser
@@ -326,18 +329,20 @@ __global__ __launch_bounds__(NW * 64, WPE) void sa_bf16_stream_kernel(FwdArgs a,
                 for (int sb = 0; sb < NSB; ++sb) acc[sb][db] = mfma(vt.v, pk[sb], acc[sb][db]);
             }
         };
-        // weights of unit u (held in s, validity in valid), then its aggregation
+        // weights of unit u (held in s, validity in valid), then its aggregation.
+        // The exact path is a then-only branch that overwrites the fast path's
+        // values in place, so the common path carries no register copies.
         auto finish_unit = [&](int u, const f32x4 (&s)[2][NSB], uint32_t valid, bf16x8 (&pk)[NSB], float (&zt)[NSB],
                                bool fits) {
             if constexpr (PROTO) {
                 weights_proto(s, u, valid, pk);
             } else {
-                if (__builtin_expect(__all(fits) && valid == 0xffffffffu, 1)) {
+                float f[NSB];
 #pragma unroll
-                    for (int sb = 0; sb < NSB; ++sb) Zs[sb] += zt[sb];
-                } else {
-                    weights_exact(s, valid, pk);
-                }
+                for (int sb = 0; sb < NSB; ++sb) f[sb] = 1.f;
+                if (__builtin_expect(!(__all(fits) && valid == 0xffffffffu), 0)) weights_exact(s, valid, pk, zt, f);
+#pragma unroll
+                for (int sb = 0; sb < NSB; ++sb) Zs[sb] = fmaf(Zs[sb], f[sb], zt[sb]);
             }
             aggregate(u, valid, pk);
         };

@@ -252,12 +252,13 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
                 const bf16x2 q0 = pack2(p[0], p[1]), q1 = pack2(p[2], p[3]);
                 const bf16x2 q2 = pack2(p[4], p[5]), q3 = pack2(p[6], p[7]);
                 bf16x8 pk = cat8(q0, q1, q2, q3);
-                const float zt = dot2sum(q3, dot2sum(q2, dot2sum(q1, dot2sum(q0, 0.f))));
-                const bool fits = zt <= kLazyBound;   // false for NaN and Inf too
-                if (__builtin_expect(__all(fits) && valid == 0xffffffffu, 1)) {
-                    Zs[sb] += zt;
-                } else {
-                    // exact path: validity, running-maximum update, rescale
+                // fast path: the running maximum stays; Z += the tile's sum
+                float zadd = dot2sum(q3, dot2sum(q2, dot2sum(q1, dot2sum(q0, 0.f))));
+                float f = 1.f;
+                const bool fits = zadd <= kLazyBound;   // false for NaN and Inf too
+                // rare exact path (then-only, so the common path keeps its
+                // values in place): validity, running-maximum update, rescale
+                if (__builtin_expect(!(__all(fits) && valid == 0xffffffffu), 0)) {
                     float x[8];
                     float tm = -INFINITY;
 #pragma unroll
@@ -270,17 +271,18 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
                     tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
                     const float Mold = Mc[sb];
                     const float Mnew = fmaxf(Mold, tm);
-                    const float f = (Mnew == Mold) ? 1.f : __builtin_amdgcn_exp2f(Mold - Mnew);
+                    f = (Mnew == Mold) ? 1.f : __builtin_amdgcn_exp2f(Mold - Mnew);
 #pragma unroll
                     for (int j = 0; j < 8; ++j) p[j] = ((vj >> j) & 1) ? __builtin_amdgcn_exp2f(x[j] - Mnew) : 0.f;
                     const bf16x2 e0 = pack2(p[0], p[1]), e1 = pack2(p[2], p[3]);
                     const bf16x2 e2 = pack2(p[4], p[5]), e3 = pack2(p[6], p[7]);
                     pk = cat8(e0, e1, e2, e3);
-                    Zs[sb] = Zs[sb] * f + dot2sum(e3, dot2sum(e2, dot2sum(e1, dot2sum(e0, 0.f))));
+                    zadd = dot2sum(e3, dot2sum(e2, dot2sum(e1, dot2sum(e0, 0.f))));
                     Mc[sb] = Mnew;
                     acc[sb][0] *= f;
                     acc[sb][1] *= f;
                 }
+                Zs[sb] = fmaf(Zs[sb], f, zadd);
                 acc[sb][0] = mfma(vt[0], pk, acc[sb][0]);
                 acc[sb][1] = mfma(vt[1], pk, acc[sb][1]);
             }
