@@ -135,7 +135,8 @@ hipError_t launch_bf16_forward(const FwdArgs& a, const Bf16Config& cfg, hipStrea
 // bf16 streaming kernel with the direct-to-LDS ring (sa_bf16_stream.hip):
 // 8 waves of 32 prototypes per block.
 struct StreamConfig {
-    int PB;                  // 32-prototype blocks per head
+    int PB;                  // MB-prototype blocks per head
+    int MB;                  // prototypes per wave
     int NH;                  // heads per block
     int NW;                  // waves per block
     int groups;              // blocks per row range
