@@ -123,7 +123,7 @@ typedef struct sa_problem {
  *             optional; 0 excludes the row (it is never read as a number, so
  *             NaN or Inf there cannot leak).  A user with no valid row is
  *             empty.
- * S_out       float32 [B, H, m, dh].  Empty users get 0.
+ * S_out       float32 [B, H, m, dh], 16-byte aligned.  Empty users get 0.
  * lse_out     optional float32.  HISTORY: [B, H, m], natural-log
  *             log-sum-exp of the scaled scores over the user's valid rows
  *             (-inf for empty users).  PROTOTYPE: [total_rows, H], the

@@ -239,7 +239,7 @@ sa_status sa_forward(const sa_problem* pb, const void* P, const void* K, const v
     const size_t el = pl.f32 ? 4 : 2;
     if (!pl.f32 && (!aligned(P, 16) || !aligned(K, 16) || !aligned(V, 16)))
         return fail(SA_ERR_INVALID_ARG, "bf16: P, K and V must be 16-byte aligned");
-    if (!aligned(P, el) || !aligned(K, el) || !aligned(V, el) || !aligned(S_out, 4) || !aligned(lse_out, 4))
+    if (!aligned(P, el) || !aligned(K, el) || !aligned(V, el) || !aligned(S_out, 16) || !aligned(lse_out, 4))
         return fail(SA_ERR_INVALID_ARG, "misaligned pointer");
     if (pl.total > 0 && (!workspace || workspace_bytes < pl.total))
         return fail(SA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", pl.total, workspace_bytes);
@@ -343,7 +343,7 @@ sa_status sa_forward_fused_proj(const sa_problem* pb, const void* X, int32_t d_m
                     d_model);
     if (!aligned(X, 16) || !aligned(Wk, 16) || (Wv && !aligned(Wv, 16)) || !aligned(P, 16))
         return fail(SA_ERR_INVALID_ARG, "X, Wk, Wv and P must be 16-byte aligned");
-    if (!aligned(S_out, 4) || !aligned(lse_out, 4)) return fail(SA_ERR_INVALID_ARG, "misaligned pointer");
+    if (!aligned(S_out, 16) || !aligned(lse_out, 4)) return fail(SA_ERR_INVALID_ARG, "misaligned pointer");
     if (pl.total > 0 && (!workspace || workspace_bytes < pl.total))
         return fail(SA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", pl.total, workspace_bytes);
     if (workspace && !aligned(workspace, kAlign)) return fail(SA_ERR_WORKSPACE, "workspace must be 256-byte aligned");

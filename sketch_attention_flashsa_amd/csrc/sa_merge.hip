@@ -14,56 +14,69 @@
 
 namespace sa {
 
-// One thread per output element (b, h, j, e): the per-segment loads of one
-// element are independent, so a block covers 256 consecutive (j, e).
+// One thread per four consecutive output elements (b, h, j, e..e+3), so the
+// partial sums are read as 16-byte vectors; dh is a multiple of 4.  The
+// segments of user b are combined in ascending w with a running maximum
+// (the same order for every layout, so packed and dense inputs agree
+// bitwise); segments without a valid row (M_w = -inf) are skipped.
 __global__ __launch_bounds__(256) void sa_merge_kernel(MergeArgs a) {
     const int b = blockIdx.z;
     const int h = blockIdx.y;
-    const int md = a.m * a.dh;
-    const int e = blockIdx.x * 256 + threadIdx.x;
-    if (e >= md) return;
-    const int j = e / a.dh, d = e - j * a.dh;
+    const int q = blockIdx.x * 256 + threadIdx.x;      // quad index within (b, h)
+    const int mq = a.m * (a.dh / 4);
+    if (q >= mq) return;
+    const int j = q / (a.dh / 4), e = (q - j * (a.dh / 4)) * 4;
     const int64_t total = a.users.total();
     const int64_t R = chunk_rows(total, a.G, a.R_fixed, a.R_min);
     const int64_t us = a.users.vstart(b), ue = a.users.vstart(b + 1);
     const bool empty = ue <= us;
     const int64_t w_first = empty ? 0 : us / R;
     const int64_t w_last = empty ? -1 : (ue - 1) / R;
-    float* Sb = a.S + ((int64_t)b * a.H + h) * md;
+    float* Sb = a.S + (((int64_t)b * a.H + h) * a.m + j) * a.dh + e;
 
     if (a.norm == 1) {
-        float acc = 0.f;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
         for (int64_t w = w_first; w <= w_last; ++w) {
             const int64_t base = ((w + b) * a.H + h) * a.m + j;
-            acc += a.part.acc[base * a.dh + d];
+            acc += *(const f32x4*)(a.part.acc + base * a.dh + e);
         }
-        Sb[e] = acc;
+        *(f32x4*)Sb = acc;
         return;
     }
-    float M = -INFINITY;
-    for (int64_t w = w_first; w <= w_last; ++w) M = fmaxf(M, a.part.M[((w + b) * a.H + h) * a.m + j]);
-    float out = 0.f, lse = -INFINITY;
-    if (M > -INFINITY) {
-        float Z = 0.f, acc = 0.f;
-        for (int64_t w = w_first; w <= w_last; ++w) {
-            const int64_t base = ((w + b) * a.H + h) * a.m + j;
-            const float Mw = a.part.M[base];
-            if (Mw == -INFINITY) continue;       // segment with no valid row
-            const float f = exp2f(Mw - M);
-            Z += a.part.Z[base] * f;
-            acc += a.part.acc[base * a.dh + d] * f;
+    float M = -INFINITY, Z = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int64_t w = w_first; w <= w_last; ++w) {
+        const int64_t base = ((w + b) * a.H + h) * a.m + j;
+        const float Mw = a.part.M[base];
+        const float Zw = a.part.Z[base];
+        const f32x4 aw = *(const f32x4*)(a.part.acc + base * a.dh + e);
+        if (Mw == -INFINITY) continue;           // segment with no valid row
+        if (Mw > M) {
+            const float r = exp2f(M - Mw);       // 0 while M is -inf
+            Z *= r;
+            acc *= r;
+            M = Mw;
         }
+        const float f = exp2f(Mw - M);
+        Z += Zw * f;
+        acc += aw * f;
+    }
+    f32x4 out = {0.f, 0.f, 0.f, 0.f};
+    float lse = -INFINITY;
+    if (M > -INFINITY) {
         out = acc / Z;
         lse = (M + log2f(Z)) * kLn2;
     }
-    Sb[e] = out;
-    if (d == 0 && a.lse) a.lse[((int64_t)b * a.H + h) * a.m + j] = lse;
+    *(f32x4*)Sb = out;
+    if (e == 0 && a.lse) a.lse[((int64_t)b * a.H + h) * a.m + j] = lse;
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
     if (a.users.B == 0) return hipSuccess;
-    const int md = a.m * a.dh;
-    hipLaunchKernelGGL(sa_merge_kernel, dim3((md + 255) / 256, a.H, a.users.B), dim3(256), 0, s, a);
+    const int mq = a.m * (a.dh / 4);
+    hipLaunchKernelGGL(sa_merge_kernel, dim3((mq + 255) / 256, a.H, a.users.B), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
