@@ -323,6 +323,7 @@ sa_status sa_forward(const sa_problem* pb, const void* P, const void* K, const v
     mg.S = S_out;
     mg.lse = pb->norm == SA_NORM_HISTORY ? lse_out : nullptr;
     mg.norm = pb->norm;
+    mg.lane_major = !pl.f32;   // the MFMA kernels store their accumulators lane-major
     e = sa::launch_merge(mg, stream);
     if (e != hipSuccess) return hip_fail(e, "merge");
     return SA_OK;
@@ -391,6 +392,7 @@ sa_status sa_forward_fused_proj(const sa_problem* pb, const void* X, int32_t d_m
     mg.S = S_out;
     mg.lse = lse_out;
     mg.norm = SA_NORM_HISTORY;
+    mg.lane_major = 1;
     e = sa::launch_merge(mg, stream);
     if (e != hipSuccess) return hip_fail(e, "merge");
     return SA_OK;

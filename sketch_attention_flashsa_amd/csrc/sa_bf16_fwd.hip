@@ -327,7 +327,8 @@ __global__ __launch_bounds__(NW * 64) void sa_bf16_fwd_kernel(FwdArgs a, int PB,
                 }
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
-                    *(f32x4*)(a.part.acc + base * DH + 16 * db + 4 * g) = acc[sb][db];
+                    __builtin_nontemporal_store(
+                        acc[sb][db], (f32x4*)lane_major_acc(a.part, slot, a.H, head, a.m, DH, (pb * MB) / 16 + sb, db, lane));
             }
         }
     }

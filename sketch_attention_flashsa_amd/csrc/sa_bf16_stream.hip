@@ -43,20 +43,21 @@ using namespace dev;
 namespace {
 
 constexpr int kStages = 4;   // ring slots: 3 stages in flight, 1 computed
-constexpr int kMB = 32;      // prototypes per wave
 
 // Ring bytes of a block, and the blocks per CU the 160 KB of LDS allow (at
 // most the two that give four waves per SIMD with 8-wave blocks).
 constexpr int ring_bytes(int DH, int NH) { return kStages * 2 * 32 * NH * DH * 2; }
-constexpr int blocks_per_cu(int DH, int NW, int NH) {
-    return (16 / NW) < (160 * 1024 / ring_bytes(DH, NH)) ? (16 / NW) : (160 * 1024 / ring_bytes(DH, NH));
+constexpr int blocks_per_cu(int DH, int NW, int NH, int MB) {
+    // four waves per SIMD with 32-prototype waves, two with 64
+    return ((MB == 32 ? 16 : 8) / NW) < (160 * 1024 / ring_bytes(DH, NH)) ? ((MB == 32 ? 16 : 8) / NW)
+                                                                          : (160 * 1024 / ring_bytes(DH, NH));
 }
 
 }  // namespace
 
-template <int DH, int NW, int NH, bool MASKED, bool PROTO>
-__global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void sa_bf16_stream_kernel(FwdArgs a,
-                                                                                                    int PB) {
+template <int DH, int NW, int NH, int MB, bool MASKED, bool PROTO>
+__global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH, MB)) void sa_bf16_stream_kernel(FwdArgs a,
+                                                                                                        int PB) {
     constexpr int S = kStages;
     constexpr int CPR = NH * DH / 8;                      // 16-byte chunks per row per tensor
     constexpr int ROWB = CPR * 16;                        // bytes per row per tensor
@@ -66,7 +67,8 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
     constexpr int AHEAD = S - 1;                          // stages issued ahead of the one computed
     constexpr int FK = CPR < 16 ? CPR : 16;               // K swizzle period (rows)
     constexpr int FV = (CPR < 16 ? CPR : 16) / 2;         // V swizzle period (rows), chunk pairs
-    constexpr int NSB = kMB / 16;
+    constexpr int NSB = MB / 16;
+    static_assert(MB == 32 || MB == 64, "prototypes per wave");
     constexpr int KC = DH / 32;
     constexpr int DB = DH / 16;
     static_assert(D >= 1 && D * NW * 64 == 32 * CPR, "a stage is whole DMA ops per wave");
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
     bf16x8 pf[NSB][KC];
     auto load_p = [&](int b) {
         const int hh = active ? head : hc;
-        const bf16* base = Pg + (int64_t)b * a.q_batch_stride + ((int64_t)hh * a.m + (active ? pb : 0) * kMB) * DH;
+        const bf16* base = Pg + (int64_t)b * a.q_batch_stride + ((int64_t)hh * a.m + (active ? pb : 0) * MB) * DH;
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
@@ -325,12 +327,14 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
             wait_lgkm0();
         }
 
-        // ---- segment epilogue: partial statistics at slot w + b
+        // ---- segment epilogue: partial statistics at slot w + b (the sums in
+        // lane order, 1 KB per store, non-temporal: every block ends at about
+        // the same time, and these writes are the kernel's tail)
         if (active) {
             const int64_t slot = (int64_t)w + b;
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
-                const int j = pb * kMB + 16 * sb + l16;
+                const int j = pb * MB + 16 * sb + l16;
                 const int64_t base = (slot * a.H + head) * a.m + j;
                 if constexpr (!PROTO) {
                     float z = Zs[sb];
@@ -342,7 +346,9 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
                     }
                 }
 #pragma unroll
-                for (int db = 0; db < DB; ++db) *(f32x4*)(a.part.acc + base * DH + 16 * db + 4 * g) = acc[sb][db];
+                for (int db = 0; db < DB; ++db)
+                    __builtin_nontemporal_store(
+                        acc[sb][db], (f32x4*)lane_major_acc(a.part, slot, a.H, head, a.m, DH, (pb * MB) / 16 + sb, db, lane));
             }
         }
         // drain this segment's memory traffic and let every wave finish reading
@@ -355,26 +361,27 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
 
 namespace {
 
-template <int DH, int NW, int NH>
+template <int DH, int NW, int NH, int MB>
 hipError_t launch_stream(const FwdArgs& a, bool masked, int PB, hipStream_t s) {
     int groups;
     if (PB > NW) groups = a.H * (PB / NW);
     else groups = (a.H + NH - 1) / NH;
     dim3 grid(a.G, groups), block(NW * 64);
     const bool proto = a.norm == 1;
-    if (!masked && !proto) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, NW, NH, false, false>), grid, block, 0, s, a, PB);
-    if (masked && !proto) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, NW, NH, true, false>), grid, block, 0, s, a, PB);
-    if (!masked && proto) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, NW, NH, false, true>), grid, block, 0, s, a, PB);
-    if (masked && proto) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, NW, NH, true, true>), grid, block, 0, s, a, PB);
+    if (!masked && !proto) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, NW, NH, MB, false, false>), grid, block, 0, s, a, PB);
+    if (masked && !proto) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, NW, NH, MB, true, false>), grid, block, 0, s, a, PB);
+    if (!masked && proto) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, NW, NH, MB, false, true>), grid, block, 0, s, a, PB);
+    if (masked && proto) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, NW, NH, MB, true, true>), grid, block, 0, s, a, PB);
     return hipGetLastError();
 }
 
 // Compiled block shapes (dh, waves, heads per block): each stage of 32 rows x
 // NH*dh*2 bytes is whole 1 KB DMA ops per wave, rows are at most 512 bytes.
 struct Shape {
-    int dh, NW, NH;
+    int dh, NW, NH, MB;
 };
-constexpr Shape kShapes[] = {{64, 16, 4}, {64, 8, 2}, {64, 8, 4}, {32, 16, 8}, {32, 8, 4}, {32, 8, 8}};
+constexpr Shape kShapes[] = {{64, 16, 4, 32}, {64, 8, 2, 32}, {64, 8, 4, 32}, {32, 16, 8, 32},
+                             {32, 8, 4, 32},  {32, 8, 8, 32}, {64, 8, 4, 64}};
 
 }  // namespace
 
@@ -384,20 +391,24 @@ constexpr Shape kShapes[] = {{64, 16, 4}, {64, 8, 2}, {64, 8, 4}, {32, 16, 8}, {
 // SIMD, independent barriers), then 16 waves (one block per CU);
 // SA_STREAM_NW=16 reverses the order.
 bool stream_config(int dh, int m, int H, StreamConfig* cfg) {
-    if (!(dh == 32 || dh == 64) || m % kMB != 0) return false;
-    const int PB = m / kMB;
+    if (!(dh == 32 || dh == 64) || m % 32 != 0) return false;
     int prefer = 8;
     if (const char* e = getenv("SA_STREAM_NW")) prefer = atoi(e) == 16 ? 16 : 8;
-    for (int pass = 0; pass < 2; ++pass) {
-        const int NW = pass == 0 ? prefer : 24 - prefer;
+    int prefer_mb = 32;
+    if (const char* e = getenv("SA_STREAM_MB")) prefer_mb = atoi(e) == 64 ? 64 : 32;
+    for (int pass = 0; pass < 4; ++pass) {
+        const int MB = (pass < 2) ? prefer_mb : 96 - prefer_mb;
+        const int NW = (pass % 2 == 0) ? prefer : 24 - prefer;
+        if (m % MB != 0) continue;
+        const int PB = m / MB;
         for (const Shape& sh : kShapes) {
-            if (sh.dh != dh || sh.NW != NW || sh.NH * PB != NW || H % sh.NH != 0) continue;
+            if (sh.dh != dh || sh.NW != NW || sh.MB != MB || sh.NH * PB != NW || H % sh.NH != 0) continue;
             cfg->PB = PB;
-            cfg->MB = kMB;
+            cfg->MB = MB;
             cfg->NH = sh.NH;
             cfg->NW = NW;
             cfg->groups = H / sh.NH;
-            cfg->blocks_per_cu = blocks_per_cu(dh, NW, sh.NH);
+            cfg->blocks_per_cu = blocks_per_cu(dh, NW, sh.NH, MB);
             return true;
         }
     }
@@ -406,11 +417,11 @@ bool stream_config(int dh, int m, int H, StreamConfig* cfg) {
 
 hipError_t launch_bf16_stream(const FwdArgs& a, const StreamConfig& cfg, hipStream_t s) {
     const bool masked = a.mask != nullptr;
-    const int dh = a.dh, NH = cfg.NH, PB = cfg.PB, NW = cfg.NW;
-#define SA_STREAM(D_, W_, N_) \
-    if (dh == D_ && NW == W_ && NH == N_) return launch_stream<D_, W_, N_>(a, masked, PB, s);
-    SA_STREAM(64, 16, 4) SA_STREAM(64, 8, 2) SA_STREAM(64, 8, 4) SA_STREAM(32, 16, 8) SA_STREAM(32, 8, 4)
-    SA_STREAM(32, 8, 8)
+    const int dh = a.dh, NH = cfg.NH, PB = cfg.PB, NW = cfg.NW, MB = cfg.MB;
+#define SA_STREAM(D_, W_, N_, M_) \
+    if (dh == D_ && NW == W_ && NH == N_ && MB == M_) return launch_stream<D_, W_, N_, M_>(a, masked, PB, s);
+    SA_STREAM(64, 16, 4, 32) SA_STREAM(64, 8, 2, 32) SA_STREAM(64, 8, 4, 32) SA_STREAM(32, 16, 8, 32)
+    SA_STREAM(32, 8, 4, 32) SA_STREAM(32, 8, 8, 32) SA_STREAM(64, 8, 4, 64)
 #undef SA_STREAM
     return hipErrorInvalidValue;
 }

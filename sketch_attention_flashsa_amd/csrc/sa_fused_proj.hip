@@ -330,7 +330,9 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
                     a.part.Z[base] = z;
                 }
 #pragma unroll
-                for (int db = 0; db < 2; ++db) *(f32x4*)(a.part.acc + base * DH + 16 * db + 4 * g) = acc[sb][db];
+                for (int db = 0; db < 2; ++db)
+                    __builtin_nontemporal_store(
+                        acc[sb][db], (f32x4*)lane_major_acc(a.part, slot, a.H, head, a.m, DH, pbase / 16 + sb, db, lane));
             }
         }
         wait_vm<0>();

@@ -66,12 +66,26 @@ __device__ __forceinline__ int64_t chunk_rows(int64_t total, int G, int R_fixed,
     return (R + kRowAlign - 1) / kRowAlign * kRowAlign;
 }
 
-// Partial statistics of the segments, laid out [slot][H][m](*dh).
+// Partial statistics of the segments.  M and Z are [nslot][H][m].  acc (the
+// unnormalised weighted value sums, nslot*H*m*dh floats) has one of two
+// layouts, chosen by the kernel that writes it:
+//   row-major:  acc[((slot*H + h)*m + j)*dh + e];
+//   lane-major: the MFMA accumulator layout, for 16-prototype block j16 and
+//     16-wide dh block db, lane l = 16*g + c holds (j = 16*j16 + c,
+//     e = 16*db + 4*g + i), i = 0..3, at
+//     acc[((((slot*H + h)*(m/16) + j16)*(dh/16) + db)*64 + l)*4 + i],
+//     so that each wave stores 1 KB contiguous per accumulator register set.
 struct Partials {
-    float* acc;   // [nslot][H][m][dh]   unnormalised weighted value sums
-    float* M;     // [nslot][H][m]       running maximum, log2 units, scale folded in
-    float* Z;     // [nslot][H][m]       sum of 2^(x - M)
+    float* acc;
+    float* M;     // running maximum, log2 units, scale folded in
+    float* Z;     // sum of 2^(x - M)
 };
+
+// Address of lane `lane`'s four partial sums of (slot, h, j16, db), lane-major.
+__device__ __forceinline__ float* lane_major_acc(const Partials& p, int64_t slot, int H, int h, int m, int dh,
+                                                 int j16, int db, int lane) {
+    return p.acc + (((((slot * H + h) * (m / 16) + j16) * (dh / 16) + db) * 64 + lane) * 4);
+}
 
 struct FwdArgs {
     Users users;
@@ -98,6 +112,7 @@ struct MergeArgs {
     float* S;                // [B][H][m][dh]
     float* lse;              // [B][H][m] or nullptr (history axis only)
     int32_t norm;
+    int32_t lane_major;      // acc layout written by the forward kernel
 };
 
 struct TokLseArgs {

@@ -25,7 +25,21 @@ __global__ __launch_bounds__(256) void sa_merge_kernel(MergeArgs a) {
     const int q = blockIdx.x * 256 + threadIdx.x;      // quad index within (b, h)
     const int mq = a.m * (a.dh / 4);
     if (q >= mq) return;
-    const int j = q / (a.dh / 4), e = (q - j * (a.dh / 4)) * 4;
+    // the quad's (j, e) and the offset of its partial sums within a (slot, h)
+    // block of m*dh floats; consecutive threads read consecutive 16 bytes
+    int j, e;
+    int64_t qoff;
+    if (a.lane_major) {
+        const int lane = q & 63, blk = q >> 6;         // blk = j16 * (dh/16) + db
+        const int db = blk % (a.dh / 16), j16 = blk / (a.dh / 16);
+        j = 16 * j16 + (lane & 15);
+        e = 16 * db + 4 * (lane >> 4);
+        qoff = (int64_t)q * 4;
+    } else {
+        j = q / (a.dh / 4);
+        e = (q - j * (a.dh / 4)) * 4;
+        qoff = (int64_t)j * a.dh + e;
+    }
     const int64_t total = a.users.total();
     const int64_t R = chunk_rows(total, a.G, a.R_fixed, a.R_min);
     const int64_t us = a.users.vstart(b), ue = a.users.vstart(b + 1);
@@ -33,14 +47,13 @@ __global__ __launch_bounds__(256) void sa_merge_kernel(MergeArgs a) {
     const int64_t w_first = empty ? 0 : us / R;
     const int64_t w_last = empty ? -1 : (ue - 1) / R;
     float* Sb = a.S + (((int64_t)b * a.H + h) * a.m + j) * a.dh + e;
+    const int64_t md = (int64_t)a.m * a.dh;
 
     if (a.norm == 1) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-        for (int64_t w = w_first; w <= w_last; ++w) {
-            const int64_t base = ((w + b) * a.H + h) * a.m + j;
-            acc += *(const f32x4*)(a.part.acc + base * a.dh + e);
-        }
+        for (int64_t w = w_first; w <= w_last; ++w)
+            acc += *(const f32x4*)(a.part.acc + ((w + b) * a.H + h) * md + qoff);
         *(f32x4*)Sb = acc;
         return;
     }
@@ -48,10 +61,10 @@ __global__ __launch_bounds__(256) void sa_merge_kernel(MergeArgs a) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
     for (int64_t w = w_first; w <= w_last; ++w) {
-        const int64_t base = ((w + b) * a.H + h) * a.m + j;
-        const float Mw = a.part.M[base];
-        const float Zw = a.part.Z[base];
-        const f32x4 aw = *(const f32x4*)(a.part.acc + base * a.dh + e);
+        const int64_t sh = (w + b) * a.H + h;
+        const float Mw = a.part.M[sh * a.m + j];
+        const float Zw = a.part.Z[sh * a.m + j];
+        const f32x4 aw = *(const f32x4*)(a.part.acc + sh * md + qoff);
         if (Mw == -INFINITY) continue;           // segment with no valid row
         if (Mw > M) {
             const float r = exp2f(M - Mw);       // 0 while M is -inf
