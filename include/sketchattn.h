@@ -135,7 +135,8 @@ typedef struct sa_problem {
  * stream      HIP stream the work is enqueued on.
  *
  * Compiled shapes: bf16: dh in {32, 64, 128}, m a multiple of 16.
- * f32: dh in {16, 32, 64, 128}, any m.  Others return SA_ERR_UNSUPPORTED.
+ * f32: dh in {16, 32, 64, 128}, any m.  The prototype axis takes shared
+ * prototypes only (q_batch_stride == 0).  Others return SA_ERR_UNSUPPORTED.
  */
 sa_status sa_forward(const sa_problem* pb, const void* P, const void* K, const void* V,
                      const int32_t* cu_offsets, const int32_t* lengths, const uint8_t* mask,
@@ -168,8 +169,10 @@ const char* sa_forward_kernel_name(const sa_problem* pb);
  * P, cu_offsets, mask, S_out, lse_out, workspace, stream: as for sa_forward
  *          (pb->L_max must be 0, pb->k_row_stride and v_row_stride are ignored).
  *
- * Compiled shapes: bf16, d_model in {128, 256}, dh == 32, m a multiple of 16,
- * H*dh a multiple of 64.
+ * Compiled shapes: bf16, history axis (SA_NORM_HISTORY), dh == 32,
+ * d_model in {128, 256}, m in {64, 128, 256}; P shared or per user
+ * (q_batch_stride); any H.  Others return SA_ERR_UNSUPPORTED.  S_out is
+ * 16-byte aligned; X, Wk, Wv and P are 16-byte aligned.
  */
 sa_status sa_forward_fused_proj(const sa_problem* pb, const void* X, int32_t d_model,
                                 const void* Wk, const void* Wv, const void* P,

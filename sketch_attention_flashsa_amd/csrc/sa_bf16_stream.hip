@@ -47,16 +47,14 @@ constexpr int kStages = 4;   // ring slots: 3 stages in flight, 1 computed
 // Ring bytes of a block, and the blocks per CU the 160 KB of LDS allow (at
 // most the two that give four waves per SIMD with 8-wave blocks).
 constexpr int ring_bytes(int DH, int NH) { return kStages * 2 * 32 * NH * DH * 2; }
-constexpr int blocks_per_cu(int DH, int NW, int NH, int MB) {
-    // four waves per SIMD with 32-prototype waves, two with 64
-    return ((MB == 32 ? 16 : 8) / NW) < (160 * 1024 / ring_bytes(DH, NH)) ? ((MB == 32 ? 16 : 8) / NW)
-                                                                          : (160 * 1024 / ring_bytes(DH, NH));
+constexpr int blocks_per_cu(int DH, int NW, int NH) {
+    return (16 / NW) < (160 * 1024 / ring_bytes(DH, NH)) ? (16 / NW) : (160 * 1024 / ring_bytes(DH, NH));
 }
 
 }  // namespace
 
 template <int DH, int NW, int NH, int MB, bool MASKED, bool PROTO>
-__global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH, MB)) void sa_bf16_stream_kernel(FwdArgs a,
+__global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void sa_bf16_stream_kernel(FwdArgs a,
                                                                                                         int PB) {
     constexpr int S = kStages;
     constexpr int CPR = NH * DH / 8;                      // 16-byte chunks per row per tensor
@@ -68,7 +66,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH, MB)) vo
     constexpr int FK = CPR < 16 ? CPR : 16;               // K swizzle period (rows)
     constexpr int FV = (CPR < 16 ? CPR : 16) / 2;         // V swizzle period (rows), chunk pairs
     constexpr int NSB = MB / 16;
-    static_assert(MB == 32 || MB == 64, "prototypes per wave");
+    static_assert(MB == 32, "prototypes per wave");
     constexpr int KC = DH / 32;
     constexpr int DB = DH / 16;
     static_assert(D >= 1 && D * NW * 64 == 32 * CPR, "a stage is whole DMA ops per wave");
@@ -82,13 +80,11 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH, MB)) vo
     const int g = lane >> 4, l16 = lane & 15;
     const int w = blockIdx.x;
 
-    // block heads and this wave's unit
-    const int blocks_per_head = PB > NW ? PB / NW : 1;
-    const int h0 = (PB > NW) ? blockIdx.y / blocks_per_head : blockIdx.y * NH;
-    const int pb0 = (PB > NW) ? (blockIdx.y % blocks_per_head) * NW : 0;
-    const int hl = (PB > NW) ? 0 : wave / PB;
+    // block heads and this wave's unit (NH heads x PB prototype blocks = NW)
+    const int h0 = blockIdx.y * NH;
+    const int hl = wave / PB;
     const int head = h0 + hl;
-    const int pb = (PB > NW) ? pb0 + wave : wave % PB;
+    const int pb = wave % PB;
     const bool active = head < a.H;
 
     const int64_t total = a.users.total();
@@ -363,10 +359,7 @@ namespace {
 
 template <int DH, int NW, int NH, int MB>
 hipError_t launch_stream(const FwdArgs& a, bool masked, int PB, hipStream_t s) {
-    int groups;
-    if (PB > NW) groups = a.H * (PB / NW);
-    else groups = (a.H + NH - 1) / NH;
-    dim3 grid(a.G, groups), block(NW * 64);
+    dim3 grid(a.G, a.H / NH), block(NW * 64);
     const bool proto = a.norm == 1;
     if (!masked && !proto) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, NW, NH, MB, false, false>), grid, block, 0, s, a, PB);
     if (masked && !proto) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, NW, NH, MB, true, false>), grid, block, 0, s, a, PB);
@@ -380,8 +373,8 @@ hipError_t launch_stream(const FwdArgs& a, bool masked, int PB, hipStream_t s) {
 struct Shape {
     int dh, NW, NH, MB;
 };
-constexpr Shape kShapes[] = {{64, 16, 4, 32}, {64, 8, 2, 32}, {64, 8, 4, 32}, {32, 16, 8, 32},
-                             {32, 8, 4, 32},  {32, 8, 8, 32}, {64, 8, 4, 64}};
+constexpr Shape kShapes[] = {{64, 16, 4, 32}, {64, 8, 2, 32}, {64, 8, 4, 32},
+                             {32, 16, 8, 32}, {32, 8, 4, 32}, {32, 8, 8, 32}};
 
 }  // namespace
 
@@ -394,13 +387,9 @@ bool stream_config(int dh, int m, int H, StreamConfig* cfg) {
     if (!(dh == 32 || dh == 64) || m % 32 != 0) return false;
     int prefer = 8;
     if (const char* e = getenv("SA_STREAM_NW")) prefer = atoi(e) == 16 ? 16 : 8;
-    int prefer_mb = 32;
-    if (const char* e = getenv("SA_STREAM_MB")) prefer_mb = atoi(e) == 64 ? 64 : 32;
-    for (int pass = 0; pass < 4; ++pass) {
-        const int MB = (pass < 2) ? prefer_mb : 96 - prefer_mb;
-        const int NW = (pass % 2 == 0) ? prefer : 24 - prefer;
-        if (m % MB != 0) continue;
-        const int PB = m / MB;
+    const int MB = 32, PB = m / MB;
+    for (int pass = 0; pass < 2; ++pass) {
+        const int NW = pass == 0 ? prefer : 24 - prefer;
         for (const Shape& sh : kShapes) {
             if (sh.dh != dh || sh.NW != NW || sh.MB != MB || sh.NH * PB != NW || H % sh.NH != 0) continue;
             cfg->PB = PB;
@@ -408,7 +397,7 @@ bool stream_config(int dh, int m, int H, StreamConfig* cfg) {
             cfg->NH = sh.NH;
             cfg->NW = NW;
             cfg->groups = H / sh.NH;
-            cfg->blocks_per_cu = blocks_per_cu(dh, NW, sh.NH, MB);
+            cfg->blocks_per_cu = blocks_per_cu(dh, NW, sh.NH);
             return true;
         }
     }
@@ -421,7 +410,7 @@ hipError_t launch_bf16_stream(const FwdArgs& a, const StreamConfig& cfg, hipStre
 #define SA_STREAM(D_, W_, N_, M_) \
     if (dh == D_ && NW == W_ && NH == N_ && MB == M_) return launch_stream<D_, W_, N_, M_>(a, masked, PB, s);
     SA_STREAM(64, 16, 4, 32) SA_STREAM(64, 8, 2, 32) SA_STREAM(64, 8, 4, 32) SA_STREAM(32, 16, 8, 32)
-    SA_STREAM(32, 8, 4, 32) SA_STREAM(32, 8, 8, 32) SA_STREAM(64, 8, 4, 64)
+    SA_STREAM(32, 8, 4, 32) SA_STREAM(32, 8, 8, 32)
 #undef SA_STREAM
     return hipErrorInvalidValue;
 }
