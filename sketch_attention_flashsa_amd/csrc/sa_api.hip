@@ -54,6 +54,9 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 constexpr int kRowMinBf16 = 512;   // smallest automatic segment (rows)
 constexpr int kRowMinF32 = 128;
+// Share (percent) of the rows that the first half of the streaming kernel's
+// row ranges takes when two of its blocks share a CU (measured on MI355X).
+constexpr int kStreamSplit = 64;
 
 // Everything the dispatcher derives from the problem.
 struct Plan {
@@ -62,6 +65,7 @@ struct Plan {
     int64_t buf_rows = 0;     // rows of the K/V buffers the kernels may address
     int G = 1;                // row-range blocks
     int R_fixed = 0, R_min = kRowMinBf16;
+    int split = 50;           // RowSplit share of the first half of the ranges
     sa::Bf16Config cfg{};
     bool stream = false;      // bf16: the direct-to-LDS streaming kernel serves this shape
     sa::StreamConfig scfg{};
@@ -153,6 +157,12 @@ sa_status make_plan(const sa_problem* pb, bool packed, Plan* pl) {
         if (const char* e = getenv("SA_BLOCKS_PER_CU")) blocks_per_cu = atoi(e) > 0 ? atoi(e) : blocks_per_cu;
         const int64_t G = (int64_t)dev.cus * blocks_per_cu / per_row_range;
         pl->G = (int)(G > 0 ? G : 1);
+        // two streaming blocks per CU: the older one (first half of the
+        // ranges in dispatch order) gets the larger share of the rows
+        if (pl->stream && blocks_per_cu == 2) {
+            pl->split = kStreamSplit;
+            if (const char* e = getenv("SA_RANGE_SPLIT")) pl->split = atoi(e);
+        }
     }
 
     set_layout(pb, pl);
@@ -198,6 +208,7 @@ sa_status make_fused_plan(const sa_problem* pb, int32_t d_model, Plan* pl) {
         pl->G = (int)(G > 0 ? G : 1);
     }
     pl->R_min = kRowMinBf16;
+    pl->split = 50;
     set_layout(pb, pl);
     return SA_OK;
 }
@@ -299,6 +310,7 @@ sa_status sa_forward(const sa_problem* pb, const void* P, const void* K, const v
     a.G = pl.G;
     a.R_fixed = pl.R_fixed;
     a.R_min = pl.R_min;
+    a.split = pl.split;
     a.part = part;
     a.lse2_tok = lse2_tok;
     a.norm = pb->norm;
@@ -319,6 +331,7 @@ sa_status sa_forward(const sa_problem* pb, const void* P, const void* K, const v
     mg.G = pl.G;
     mg.R_fixed = pl.R_fixed;
     mg.R_min = pl.R_min;
+    mg.split = pl.split;
     mg.part = part;
     mg.S = S_out;
     mg.lse = pb->norm == SA_NORM_HISTORY ? lse_out : nullptr;
@@ -388,6 +401,7 @@ sa_status sa_forward_fused_proj(const sa_problem* pb, const void* X, int32_t d_m
     mg.G = pl.G;
     mg.R_fixed = pl.R_fixed;
     mg.R_min = pl.R_min;
+    mg.split = pl.split;
     mg.part = part;
     mg.S = S_out;
     mg.lse = lse_out;

@@ -100,10 +100,10 @@ __global__ __launch_bounds__(NW * 64) void sa_bf16_fwd_kernel(FwdArgs a, int PB,
 
     // ---- row range of this block
     const int64_t total = a.users.total();
-    const int64_t R = chunk_rows(total, a.G, a.R_fixed, a.R_min);
-    const int64_t v_lo = (int64_t)w * R;
+    const RowSplit rs = row_split(total, a.G, a.R_fixed, a.R_min, a.split);
+    const int64_t v_lo = rs.lo(w);
     if (v_lo >= total) return;
-    const int64_t v_hi = min(v_lo + R, total);
+    const int64_t v_hi = min(rs.lo(w + 1), total);
 
     const bf16* Pg = (const bf16*)a.P;
     const bf16* Kg = (const bf16*)a.K;

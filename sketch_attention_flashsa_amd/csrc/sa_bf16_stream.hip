@@ -78,20 +78,34 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, l16 = lane & 15;
-    const int w = blockIdx.x;
+
+    // (row range w, head group gy) of this block.  Blocks are dispatched in
+    // linear order and round-robin over the 8 XCDs; with G a multiple of 8
+    // the ranges w < G/2 (all head groups) come first, and every head group
+    // of range w sits on XCD w % 8 as with the plain (x, y) order.
+    int w, gy;
+    if (gridDim.x % 8 == 0) {
+        const int L = blockIdx.y * gridDim.x + blockIdx.x;
+        const int q = L / (8 * gridDim.y), r = L % (8 * gridDim.y);
+        w = 8 * q + r % 8;
+        gy = r / 8;
+    } else {
+        w = blockIdx.x;
+        gy = blockIdx.y;
+    }
 
     // block heads and this wave's unit (NH heads x PB prototype blocks = NW)
-    const int h0 = blockIdx.y * NH;
+    const int h0 = gy * NH;
     const int hl = wave / PB;
     const int head = h0 + hl;
     const int pb = wave % PB;
     const bool active = head < a.H;
 
     const int64_t total = a.users.total();
-    const int64_t R = chunk_rows(total, a.G, a.R_fixed, a.R_min);
-    const int64_t v_lo = (int64_t)w * R;
+    const RowSplit rs = row_split(total, a.G, a.R_fixed, a.R_min, a.split);
+    const int64_t v_lo = rs.lo(w);
     if (v_lo >= total) return;
-    const int64_t v_hi = min(v_lo + R, total);
+    const int64_t v_hi = min(rs.lo(w + 1), total);
 
     const bf16* Pg = (const bf16*)a.P;
     const unsigned char* Kg = (const unsigned char*)a.K;

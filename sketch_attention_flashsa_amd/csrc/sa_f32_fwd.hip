@@ -23,10 +23,10 @@ __global__ __launch_bounds__(256) void sa_f32_fwd_kernel(FwdArgs a) {
     const int j = blockIdx.z * 256 + threadIdx.x;
     const bool active = j < a.m;
     const int64_t total = a.users.total();
-    const int64_t R = chunk_rows(total, a.G, a.R_fixed, a.R_min);
-    const int64_t v_lo = (int64_t)w * R;
+    const RowSplit rs = row_split(total, a.G, a.R_fixed, a.R_min, a.split);
+    const int64_t v_lo = rs.lo(w);
     if (v_lo >= total) return;
-    const int64_t v_hi = min(v_lo + R, total);
+    const int64_t v_hi = min(rs.lo(w + 1), total);
     const float* Pg = (const float*)a.P;
     const float* Kg = (const float*)a.K;
     const float* Vg = (const float*)a.V;

@@ -5,13 +5,16 @@
 //   * The valid-length rows of all users, concatenated in user order, form a
 //     "virtual row" axis of sigma_L = sum_b L_b positions.  User b occupies
 //     [vstart(b), vstart(b+1)).
-//   * Row-range block w covers virtual rows [w*R, (w+1)*R), R = chunk rows.
-//     Its intersection with user b is a "segment"; segment (w, b) stores its
+//   * Row-range block w covers virtual rows [lo(w), lo(w+1)) (RowSplit):
+//     R rows each, or -- for the streaming kernel's two blocks per CU --
+//     R1 rows for the first G/2 ranges and R2 for the rest.  Its
+//     intersection with user b is a "segment"; segment (w, b) stores its
 //     partial statistics at slot w + b (distinct for distinct intersecting
 //     pairs, at most G + B - 1 slots).
 //   * The merge kernel combines the segments of user b in ascending w.
-// Because R and the segments depend only on the valid lengths (not on the
-// buffer layout), packed and dense+lengths inputs give bitwise-equal results.
+// Because the ranges and the segments depend only on the valid lengths (not
+// on the buffer layout), packed and dense+lengths inputs give bitwise-equal
+// results.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -59,11 +62,42 @@ struct Users {
 };
 
 // Rows per segment: fixed by the caller, or spread evenly over G blocks.
+// Row counts are below 2^31 (the entry points check), so the divisions by
+// run-time values are 32-bit.
 __device__ __forceinline__ int64_t chunk_rows(int64_t total, int G, int R_fixed, int R_min) {
     if (R_fixed > 0) return R_fixed;
-    int64_t R = (total + G - 1) / G;
+    int64_t R = (uint32_t)(total + G - 1) / (uint32_t)G;
     if (R < R_min) R = R_min;
     return (R + kRowAlign - 1) / kRowAlign * kRowAlign;
+}
+
+// Row ranges: the first G1 ranges have R1 rows, the others R2 (R1 = R2 = R
+// and G1 = G when uniform).  `split` is the share, in percent, of the rows
+// that the first half of the ranges takes (50 = uniform).  The streaming
+// kernel dispatches the first half of its ranges first; on a CU that holds
+// two of its blocks the older one is issued first and runs faster, so a
+// split above 50 lets both finish together.  Small inputs, fixed chunk rows
+// and splits that would leave a range under R_min rows stay uniform.
+struct RowSplit {
+    int64_t R1, R2, G1;
+    __device__ __forceinline__ int64_t lo(int64_t w) const { return w < G1 ? w * R1 : G1 * R1 + (w - G1) * R2; }
+    // the range holding virtual row v (0 <= v < total < 2^31)
+    __device__ __forceinline__ int64_t range_of(int64_t v) const {
+        return v < G1 * R1 ? (int64_t)((uint32_t)v / (uint32_t)R1)
+                           : G1 + (int64_t)((uint32_t)(v - G1 * R1) / (uint32_t)R2);
+    }
+};
+__device__ __forceinline__ RowSplit row_split(int64_t total, int G, int R_fixed, int R_min, int split) {
+    const int64_t R = chunk_rows(total, G, R_fixed, R_min);
+    const RowSplit uniform = {R, R, (int64_t)G};
+    if (R_fixed > 0 || split == 50 || split < 1 || split > 99 || G < 2 || (G & 1)) return uniform;
+    const int64_t G1 = G / 2, G2 = G - G1;
+    const int64_t even = (uint32_t)(total + G - 1) / (uint32_t)G;     // rows per range if uniform
+    const int64_t R1 = (even * split / 50 + kRowAlign - 1) / kRowAlign * kRowAlign;
+    if (R1 * G1 >= total) return uniform;
+    const int64_t R2 = ((uint32_t)(total - G1 * R1 + G2 - 1) / (uint32_t)G2 + kRowAlign - 1) / kRowAlign * kRowAlign;
+    if (R1 < R_min || R2 < R_min) return uniform;
+    return {R1, R2, G1};
 }
 
 // Partial statistics of the segments.  M and Z are [nslot][H][m].  acc (the
@@ -99,6 +133,7 @@ struct FwdArgs {
     float c;                 // scale * log2(e)
     int32_t G;               // row-range blocks
     int32_t R_fixed, R_min;
+    int32_t split;           // RowSplit share of the first G/2 ranges (50 = uniform)
     Partials part;
     const float* lse2_tok;   // prototype axis: per (row, head) log2 normaliser
     int32_t norm;            // 0 history, 1 prototype
@@ -107,7 +142,7 @@ struct FwdArgs {
 struct MergeArgs {
     Users users;
     int32_t H, m, dh;
-    int32_t G, R_fixed, R_min;
+    int32_t G, R_fixed, R_min, split;
     Partials part;
     float* S;                // [B][H][m][dh]
     float* lse;              // [B][H][m] or nullptr (history axis only)

@@ -16,9 +16,9 @@ namespace sa {
 
 // One thread per four consecutive output elements (b, h, j, e..e+3), so the
 // partial sums are read as 16-byte vectors; dh is a multiple of 4.  The
-// segments of user b are combined in ascending w with a running maximum
-// (the same order for every layout, so packed and dense inputs agree
-// bitwise); segments without a valid row (M_w = -inf) are skipped.
+// segments of user b are combined in ascending w (the same order for every
+// layout, so packed and dense inputs agree bitwise); segments without a
+// valid row (M_w = -inf) are skipped.
 __global__ __launch_bounds__(256) void sa_merge_kernel(MergeArgs a) {
     const int b = blockIdx.z;
     const int h = blockIdx.y;
@@ -41,11 +41,11 @@ __global__ __launch_bounds__(256) void sa_merge_kernel(MergeArgs a) {
         qoff = (int64_t)j * a.dh + e;
     }
     const int64_t total = a.users.total();
-    const int64_t R = chunk_rows(total, a.G, a.R_fixed, a.R_min);
+    const RowSplit rs = row_split(total, a.G, a.R_fixed, a.R_min, a.split);
     const int64_t us = a.users.vstart(b), ue = a.users.vstart(b + 1);
     const bool empty = ue <= us;
-    const int64_t w_first = empty ? 0 : us / R;
-    const int64_t w_last = empty ? -1 : (ue - 1) / R;
+    const int64_t w_first = empty ? 0 : rs.range_of(us);
+    const int64_t w_last = empty ? -1 : rs.range_of(ue - 1);
     float* Sb = a.S + (((int64_t)b * a.H + h) * a.m + j) * a.dh + e;
     const int64_t md = (int64_t)a.m * a.dh;
 
@@ -57,24 +57,46 @@ __global__ __launch_bounds__(256) void sa_merge_kernel(MergeArgs a) {
         *(f32x4*)Sb = acc;
         return;
     }
+    // batches of 8 segments: all loads of a batch are issued together (slots
+    // past the last segment re-read the last one and are masked), then the
+    // running maximum moves once per batch and each segment is scaled once
+    const float* Mb = a.part.M + ((int64_t)b * a.H + h) * a.m + j;     // slot w + b = Mb[w * H * m]
+    const float* Zb = a.part.Z + ((int64_t)b * a.H + h) * a.m + j;
+    const float* Ab = a.part.acc + ((int64_t)b * a.H + h) * md + qoff;
+    const int64_t hm = (int64_t)a.H * a.m, hmd = (int64_t)a.H * md;
     float M = -INFINITY, Z = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int64_t w = w_first; w <= w_last; ++w) {
-        const int64_t sh = (w + b) * a.H + h;
-        const float Mw = a.part.M[sh * a.m + j];
-        const float Zw = a.part.Z[sh * a.m + j];
-        const f32x4 aw = *(const f32x4*)(a.part.acc + sh * md + qoff);
-        if (Mw == -INFINITY) continue;           // segment with no valid row
-        if (Mw > M) {
-            const float r = exp2f(M - Mw);       // 0 while M is -inf
-            Z *= r;
-            acc *= r;
-            M = Mw;
+    for (int64_t w0 = w_first; w0 <= w_last; w0 += 8) {
+        float Mw[8], Zw[8];
+        f32x4 aw[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int64_t w = min(w0 + k, w_last);
+            Mw[k] = Mb[w * hm];
+            Zw[k] = Zb[w * hm];
+            aw[k] = *(const f32x4*)(Ab + w * hmd);
         }
-        const float f = exp2f(Mw - M);
-        Z += Zw * f;
-        acc += aw * f;
+        float bm = M;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (w0 + k <= w_last) bm = fmaxf(bm, Mw[k]);
+        // selects, not branches, so that no load is deferred behind the
+        // maximum; segments with no valid row add nothing
+        const float r = bm > -INFINITY ? exp2f(M - bm) : 1.f;   // 0 while M is -inf
+        Z *= r;
+        acc *= r;
+        M = bm;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const bool live = w0 + k <= w_last && Mw[k] > -INFINITY;
+            const float f = exp2f(Mw[k] - M);
+            Z += live ? Zw[k] * f : 0.f;
+            const f32x4 t = aw[k] * f;
+            acc.x += live ? t.x : 0.f;
+            acc.y += live ? t.y : 0.f;
+            acc.z += live ? t.z : 0.f;
+            acc.w += live ? t.w : 0.f;
+        }
     }
     f32x4 out = {0.f, 0.f, 0.f, 0.f};
     float lse = -INFINITY;

@@ -166,6 +166,28 @@ def test_packed_equals_dense_bitwise(dtype):
     assert np.array_equal(Sn, Sd), "dense padding must not leak"
 
 
+def test_uneven_row_split(monkeypatch):
+    """About 118K rows (H=8, m=128, dh=64, bf16): enough rows that the
+    streaming kernel gives the first half of its row ranges a larger share
+    (R1 > R2), so ranges straddle user boundaries at uneven places.  Checked
+    against the oracle, against the uniform split (same values to tolerance,
+    different segments), and packed against dense+lengths bitwise."""
+    lengths = [30011, 1, 0, 20000, 17, 19968, 12345, 511, 9000, 20000, 6992]
+    wp = W.random_case(106, B=len(lengths), H=8, m=128, dh=64, lengths=lengths, dtype="bf16", layout="packed")
+    S, lse = run(wp)
+    So, lo = _oracle(wp)
+    assert_parity(S, So, "bf16", "uneven row split")
+    assert_lse(lse, lo, "bf16", "uneven row split")
+    monkeypatch.setenv("SA_RANGE_SPLIT", "50")
+    Su, lu = run(wp)
+    monkeypatch.delenv("SA_RANGE_SPLIT")
+    assert_parity(Su, So, "bf16", "uniform row split")
+    assert not np.array_equal(S, Su), "the default split should segment these users differently"
+    wd = W.random_case(106, B=len(lengths), H=8, m=128, dh=64, lengths=lengths, dtype="bf16", layout="dense")
+    Sd, ld = run(wd)
+    assert np.array_equal(S, Sd) and np.array_equal(lse, ld), "packed and dense+lengths must agree bitwise"
+
+
 def test_deterministic_and_isolated():
     w = W.random_case(105, B=3, H=2, m=64, dh=64, lengths=[3000, 1500, 2500], dtype="bf16")
     S1, l1 = run(w)
