@@ -25,6 +25,10 @@
  *     masks stay on the device).
  *   - Results are deterministic: the same call on the same device gives
  *     bitwise-identical outputs (fixed reduction order, no float atomics).
+ *     The row segmentation depends on the device's CU count and on the
+ *     tuning variables SA_KERNEL, SA_STREAM_NW, SA_BLOCKS_PER_CU,
+ *     SA_BF16_TILE and SA_RANGE_SPLIT (read when a call is planned); other
+ *     settings round differently, within the stated tolerances.
  *   - Errors that the host can detect (null or misaligned pointers, bad
  *     sizes, unsupported shapes, a short workspace) return a non-zero status
  *     before anything is enqueued; sa_last_error() then describes it.  No C++
