@@ -82,3 +82,66 @@ def _sketch(P, K, V, B, rows_of, norm, scale):
         W.append(Wb)
         LSE.append(Lb)
     return S, W, LSE
+
+
+# ------------------------------------------------- stacked refinement (tiny)
+def _mat(A):
+    return [[mpmath.mpf(float(v)) for v in row] for row in A]
+
+
+def _matmul(A, B):
+    n, k, m = len(A), len(B), len(B[0])
+    return [[mpmath.fsum(A[i][t] * B[t][j] for t in range(k)) for j in range(m)] for i in range(n)]
+
+
+def _layer_norm_row(x, g, bta, eps):
+    n = len(x)
+    mu = mpmath.fsum(x) / n
+    var = mpmath.fsum((v - mu) ** 2 for v in x) / n
+    inv = 1 / mpmath.sqrt(var + eps)
+    return [(x[i] - mu) * inv * g[i] + bta[i] for i in range(n)]
+
+
+def refine(X, P0, layers, cu, H, eps=1e-5):
+    """Section 3.3 of the SequenceO1 paper, one user at a time, every score
+    and weight an mpf: Q = Xt Wq, K = X Wk, per head h (channels
+    [h dh, (h+1) dh)) weights softmax over the user's rows of
+    Q_h K_h^T / sqrt(dh), Xhat_h = weights X_h, then
+    Xbar = LN(Xt + Xhat), Xt' = LN(Xbar + (silu(Xbar W1) * Xbar W3) W2).
+    X [rows][d], P0 [k][d]; ``layers`` as in ``oracle.refine.refine`` (nested
+    lists or arrays of floats).  Returns [B][k][d] mpf."""
+    B = len(cu) - 1
+    d = len(P0[0])
+    dh = d // H
+    sc = 1 / mpmath.sqrt(dh)
+    out = []
+    for b in range(B):
+        rows = [_mat([X[r]])[0] for r in range(int(cu[b]), int(cu[b + 1]))]
+        Xt = _mat(P0)
+        for L in layers:
+            Wq, Wk = _mat(L["Wq"]), _mat(L["Wk"])
+            Q = _matmul(Xt, Wq)
+            K = _matmul(rows, Wk) if rows else []
+            k = len(Q)
+            Xhat = [[mpmath.mpf(0)] * d for _ in range(k)]
+            for h in range(H):
+                c = range(h * dh, (h + 1) * dh)
+                for j in range(k):
+                    if not rows:
+                        continue
+                    s = [mpmath.fsum(Q[j][e] * K[i][e] for e in c) * sc for i in range(len(rows))]
+                    M = max(s)
+                    w = [mpmath.exp(v - M) for v in s]
+                    Z = mpmath.fsum(w)
+                    for e in c:
+                        Xhat[j][e] = mpmath.fsum(w[i] * rows[i][e] for i in range(len(rows))) / Z
+            g1, b1 = [mpmath.mpf(float(v)) for v in L["ln1_g"]], [mpmath.mpf(float(v)) for v in L["ln1_b"]]
+            g2, b2 = [mpmath.mpf(float(v)) for v in L["ln2_g"]], [mpmath.mpf(float(v)) for v in L["ln2_b"]]
+            Xbar = [_layer_norm_row([Xt[j][e] + Xhat[j][e] for e in range(d)], g1, b1, eps) for j in range(k)]
+            A1 = _matmul(Xbar, _mat(L["W1"]))
+            A3 = _matmul(Xbar, _mat(L["W3"]))
+            Hid = [[A1[j][t] / (1 + mpmath.exp(-A1[j][t])) * A3[j][t] for t in range(len(A1[0]))] for j in range(k)]
+            F = _matmul(Hid, _mat(L["W2"]))
+            Xt = [_layer_norm_row([Xbar[j][e] + F[j][e] for e in range(d)], g2, b2, eps) for j in range(k)]
+        out.append(Xt)
+    return out
