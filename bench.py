@@ -207,6 +207,69 @@ def bench_fused(args, w):
     print(json.dumps(out))
 
 
+REFINE_METRIC = "history tokens/sec through stacked SA refinement (bf16, 2 layers, fused-workload shape)"
+
+
+def bench_refine(args):
+    """Stacked refinement (two layers, the paper's N_sa = 2) over the fused
+    workload's users: each layer's attention pass streams X with the keys
+    projected on chip, then the sketch update (layer norms, SwiGLU FFN, next
+    queries) runs on MFMA.  Timed end to end (every launch of the call)."""
+    import torch
+    import workloads as W
+    import sketch_attention_flashsa_amd as sa
+    from sketch_attention_flashsa_amd import flops
+    dev = torch.device("cuda:0")
+    w = W.make(5)
+    B, H, m, dh, dm = w["B"], w["H"], w["m"], w["dh"], w["d_model"]
+    n_layers = 2
+    tokens = int(w["lengths"].sum())
+    X, cu = w["X"].to(dev), w["cu_offsets"].to(dev)
+    P0 = W.random_refine_case(6, B=1, H=H, m=m, dh=dh, lengths=[1])["P0"].to(dev)
+    layers = [{k: v.to(dev) for k, v in L.items()} for L in W.refine_layers(6, dm, n_layers)]
+    out = torch.empty((B, m, dm), dtype=torch.float32, device=dev)
+    pb = sa.make_problem(B, H, m, dh, X.shape[0], dtype="bf16")
+    ws = torch.empty(sa.sa_refine_workspace_size(pb, dm, n_layers), dtype=torch.uint8, device=dev)
+
+    def step():
+        sa.sa_refine_forward(X, P0, layers, cu, H, out=out, workspace=ws)
+
+    ms_per_step, call_ms = _timed(step, args.steps, args.warmup)
+    call_avg = sum(call_ms) / len(call_ms)
+    fl = flops.refine_flops(tokens, B, m, dm, n_layers)
+    tflops = fl / (call_avg / 1e3) / 1e12
+    print(json.dumps({
+        "metric": REFINE_METRIC,
+        "value": tokens / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal draws shaped like the paper's histories; random-init layers)",
+        "config": {"workload": "refine2_fusedproj_bf16", "B": B, "sum_L": tokens, "L_max": int(w["lengths"].max()),
+                   "H": H, "m": m, "dh": dh, "d_model": dm, "n_layers": n_layers, "layout": "packed",
+                   "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "sa_refine_forward (all launches of one call)",
+            "achieved": tflops,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": None,
+            "algorithmic_flops_per_launch": fl,
+            "kernel_ms_avg": call_avg,
+            "kernel_ms_min": min(call_ms),
+        },
+        "cpu_baseline": None,
+    }))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,7 +277,8 @@ def main():
     # The device lowers its clocks for a few tens of back-to-back launches
     # before it settles; 50 untimed steps (~40 ms) keep that out of the timing.
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", type=int, default=4, help="workload number (default 4: full 100K bf16)")
+    ap.add_argument("--workload", type=int, default=4,
+                    help="workload number (default 4: full 100K bf16; 5: fused projection; 6: two refinement layers)")
     ap.add_argument("--cpu-users", type=int, default=4, help="users in the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -234,6 +298,8 @@ def main():
     import sketch_attention_flashsa_amd as sa
     from sketch_attention_flashsa_amd import flops
 
+    if args.workload == 6:
+        return bench_refine(args)
     dev = torch.device("cuda:0")
     w = W.make(args.workload)
     spec = w["spec"]

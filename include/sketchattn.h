@@ -188,11 +188,67 @@ sa_status sa_forward_fused_proj(const sa_problem* pb, const void* X, int32_t d_m
 size_t sa_forward_fused_proj_workspace_size(const sa_problem* pb, int32_t d_model);
 
 /*
+ * Stacked Sketch Attention refinement (section 3.3 of the SequenceO1 paper),
+ * n_layers layers over a packed ragged batch.  The sketch starts as the
+ * prototypes, Xt_0 = P0 [m, d]; layer l computes, for every user b,
+ *     Q    = Xt_l Wq_l                      (queries from the current sketch)
+ *     Xhat = softmax_L(Q (X_b Wk_l)^T / sqrt(dh)) X_b   per head (values = X)
+ *     Xbar = LN(Xt_l + Xhat; ln1_g, ln1_b)
+ *     Xt_{l+1} = LN(Xbar + (silu(Xbar W1) * (Xbar W3)) W2; ln2_g, ln2_b)
+ * where head h uses channels [h*dh, (h+1)*dh) of Q, K and X, LN is a per-row
+ * layer norm over the d channels with eps inside the square root, and the
+ * FFN is SwiGLU with inner width 2d (appendix G of the paper) and no biases.
+ * The attention pass of each layer is sa_forward_fused_proj's (keys
+ * projected on chip, never written to memory); the sketch update runs on
+ * MFMA with fp32 layer norms.  Queries, keys and the FFN's inputs and hidden
+ * units are rounded to bf16 before their products (fp32 accumulation).
+ *
+ * pb       B, H, m, dh (d = H*dh = d_model), total_rows, dtype BF16, norm
+ *          SA_NORM_HISTORY, scale (0: 1/sqrt(dh)); q_batch_stride, L_max and
+ *          the row strides must be 0.
+ * X        [total_rows, d_model] bf16 history rows (the values), packed by
+ *          cu_offsets [B+1] as in sa_forward; mask optional per row.
+ * P0       [m, d_model] fp32 prototypes.
+ * layers   host array of n_layers (1..8) descriptors; every pointer in them is
+ *          device memory: Wq, Wk [d, d] and W1, W3 [d, 2d] and W2 [2d, d],
+ *          bf16, row-major [in, out] (y = x W); ln*_g, ln*_b [d] fp32.
+ * eps      layer-norm epsilon (> 0 recommended; 1e-5 is the usual value).
+ * out      [B, m, d_model] fp32: the final sketch Xt_{n_layers}.
+ * workspace, workspace_bytes: at least sa_refine_workspace_size(pb, d_model,
+ *          n_layers) bytes, 256-byte aligned, owned by the caller.
+ *
+ * Compiled shapes: dh == 32, d_model in {128, 256}, m in {64, 128, 256}.
+ * Others return SA_ERR_UNSUPPORTED.  X, P0, out and every matrix are 16-byte
+ * aligned.  Users with no valid row get Xhat = 0.
+ */
+typedef struct sa_refine_layer {
+    const void* Wq;
+    const void* Wk;
+    const float* ln1_g;
+    const float* ln1_b;
+    const void* W1;
+    const void* W3;
+    const void* W2;
+    const float* ln2_g;
+    const float* ln2_b;
+} sa_refine_layer;
+
+sa_status sa_refine_forward(const sa_problem* pb, const void* X, int32_t d_model, const float* P0,
+                            int32_t n_layers, const sa_refine_layer* layers, float eps,
+                            const int32_t* cu_offsets, const uint8_t* mask, float* out,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace sa_refine_forward needs on the current device (0 if the
+ * problem is invalid; sa_last_error() says why). */
+size_t sa_refine_workspace_size(const sa_problem* pb, int32_t d_model, int32_t n_layers);
+
+/*
  * Timing hook for benchmarks and profilers (not part of the computation).
  * When both events are non-NULL, the next sa_forward or sa_forward_fused_proj
  * call made on this host thread records `start` on its stream immediately
  * before the streaming kernel (the pass over K/V or X) and `stop` immediately
- * after it, then forgets both.  NULL, NULL clears a pending request.  The
+ * after it, then forgets both; the next sa_refine_forward call records them
+ * before its first and after its last launch.  NULL, NULL clears a pending request.  The
  * events belong to the caller (hipEventCreate); the library never creates,
  * waits on or destroys them.  Returns SA_ERR_INVALID_ARG if exactly one is NULL.
  */

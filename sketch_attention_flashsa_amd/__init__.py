@@ -24,8 +24,13 @@ SA_NORM_HISTORY, SA_NORM_PROTOTYPE = 0, 1
 _NORMS = {"history": SA_NORM_HISTORY, "prototype": SA_NORM_PROTOTYPE}
 
 EXPORTED = ("sa_forward", "sa_forward_workspace_size", "sa_forward_kernel_name", "sa_forward_fused_proj",
-            "sa_forward_fused_proj_workspace_size", "sa_set_timing_events", "sa_status_string", "sa_last_error",
-            "sa_version")
+            "sa_forward_fused_proj_workspace_size", "sa_refine_forward", "sa_refine_workspace_size",
+            "sa_set_timing_events", "sa_status_string", "sa_last_error", "sa_version")
+
+
+class SaRefineLayer(ctypes.Structure):
+    """Mirror of ``sa_refine_layer`` in include/sketchattn.h."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ("Wq", "Wk", "ln1_g", "ln1_b", "W1", "W3", "W2", "ln2_g", "ln2_b")]
 
 
 class SaProblem(ctypes.Structure):
@@ -70,6 +75,11 @@ def load_library(path: str | None = None):
     lib.sa_forward_fused_proj.restype = ctypes.c_int
     lib.sa_forward_fused_proj_workspace_size.argtypes = [pp, ctypes.c_int32]
     lib.sa_forward_fused_proj_workspace_size.restype = ctypes.c_size_t
+    lib.sa_refine_forward.argtypes = [pp, vp, ctypes.c_int32, vp, ctypes.c_int32, ctypes.POINTER(SaRefineLayer),
+                                      ctypes.c_float, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.sa_refine_forward.restype = ctypes.c_int
+    lib.sa_refine_workspace_size.argtypes = [pp, ctypes.c_int32, ctypes.c_int32]
+    lib.sa_refine_workspace_size.restype = ctypes.c_size_t
     lib.sa_status_string.argtypes = [ctypes.c_int]
     lib.sa_status_string.restype = ctypes.c_char_p
     lib.sa_last_error.argtypes = []
@@ -259,3 +269,57 @@ def sa_forward_fused_proj(X, Wk, Wv, P, cu_offsets, mask=None, norm: str = "hist
                                    _stream_handle(dev))
     _check(st)
     return (S, lse) if return_lse else S
+
+
+REFINE_KEYS = ("Wq", "Wk", "ln1_g", "ln1_b", "W1", "W3", "W2", "ln2_g", "ln2_b")
+
+
+def sa_refine_forward(X, P0, layers, cu_offsets, H: int, mask=None, eps: float = 1e-5, scale: float | None = None,
+                      workspace=None, out=None):
+    """Stacked Sketch Attention refinement: ``len(layers)`` layers starting from
+    the prototypes P0 [m, d] (fp32).  X [rows, d] bf16 (the history, also the
+    values), cu_offsets int32 [B+1], H heads of d/H channels.  Each layer is a
+    dict of device tensors: Wq, Wk [d, d], W1, W3 [d, 2d], W2 [2d, d] (bf16,
+    [in, out]) and ln1_g, ln1_b, ln2_g, ln2_b [d] (fp32).  Returns the final
+    sketch [B, m, d] fp32."""
+    import torch
+    lib = load_library()
+    dev = X.device
+    B = cu_offsets.numel() - 1
+    rows, d = X.shape
+    m = P0.shape[0]
+    if P0.shape[1] != d or d % H:
+        raise ValueError("P0 must be [m, d] with d a multiple of H")
+    if X.dtype != torch.bfloat16 or P0.dtype != torch.float32:
+        raise ValueError("X must be bf16 and P0 fp32")
+    X, P0 = X.contiguous(), P0.contiguous()
+    keep = []
+    arr = (SaRefineLayer * len(layers))()
+    for i, L in enumerate(layers):
+        for k in REFINE_KEYS:
+            t = L[k]
+            want = torch.float32 if k.startswith("ln") else torch.bfloat16
+            if t.device != dev or t.dtype != want:
+                raise ValueError(f"layer {i}: {k} must be a {want} tensor on {dev}")
+            t = t.contiguous()
+            keep.append(t)
+            setattr(arr[i], k, t.data_ptr())
+    if mask is not None:
+        mask = (mask.to(torch.uint8) if mask.dtype == torch.bool else mask).contiguous()
+    pb = make_problem(B, H, m, d // H, rows, dtype="bf16", norm="history", scale=scale or 0.0)
+    nl = len(layers)
+    nws = int(lib.sa_refine_workspace_size(ctypes.byref(pb), int(d), nl))
+    if nws == 0:
+        _check(lib.sa_refine_forward(ctypes.byref(pb), None, int(d), None, nl, None, float(eps), None, None, None, None,
+                                     0, None))
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    out = out if out is not None else torch.empty((B, m, d), dtype=torch.float32, device=dev)
+    st = lib.sa_refine_forward(ctypes.byref(pb), _ptr(X), int(d), _ptr(P0), nl, arr, float(eps), _ptr(cu_offsets),
+                               _ptr(mask), _ptr(out), _ptr(workspace), nws, _stream_handle(dev))
+    _check(st)
+    return out
+
+
+def sa_refine_workspace_size(pb, d_model: int, n_layers: int) -> int:
+    return int(load_library().sa_refine_workspace_size(ctypes.byref(pb), int(d_model), int(n_layers)))

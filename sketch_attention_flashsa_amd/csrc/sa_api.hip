@@ -418,6 +418,153 @@ size_t sa_forward_fused_proj_workspace_size(const sa_problem* pb, int32_t d_mode
     return pl.total;
 }
 
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxRefineLayers = 8;
+
+// Workspace of the refinement: the attention pass's own workspace, then the
+// attention output, the per-user and first-layer queries, and the weights
+// transposed to [out][in] (Wq, W1, W3, W2 per layer).
+struct RefinePlan {
+    Plan att;
+    size_t off_xhat = 0, off_q = 0, off_q0 = 0, off_w = 0, total = 0;
+};
+
+sa_status make_refine_plan(const sa_problem* pb, int32_t d_model, int32_t n_layers, RefinePlan* rp) {
+    if (!pb) return fail(SA_ERR_INVALID_ARG, "problem is NULL");
+    if (pb->q_batch_stride != 0 || pb->L_max != 0 || pb->k_row_stride != 0 || pb->v_row_stride != 0)
+        return fail(SA_ERR_INVALID_ARG, "refinement: q_batch_stride, L_max and the row strides must be 0");
+    if (n_layers < 1 || n_layers > kMaxRefineLayers)
+        return fail(SA_ERR_INVALID_ARG, "n_layers must be in 1..%d (got %d)", kMaxRefineLayers, n_layers);
+    if ((int64_t)pb->H * pb->dh != d_model)
+        return fail(SA_ERR_INVALID_ARG, "refinement aggregates X itself: needs H*dh == d_model (got %d*%d vs %d)",
+                    pb->H, pb->dh, d_model);
+    sa_status st = make_fused_plan(pb, d_model, &rp->att);
+    if (st != SA_OK) return st;
+    if (!sa::sketch_supported(d_model))
+        return fail(SA_ERR_UNSUPPORTED, "refinement: d_model must be 128 or 256 (got %d)", d_model);
+    const size_t bhmd = (size_t)pb->B * pb->H * pb->m * pb->dh, d = (size_t)d_model;
+    size_t off = align_up(rp->att.total);
+    rp->off_xhat = off;
+    off = align_up(off + sizeof(float) * bhmd);
+    rp->off_q = off;
+    off = align_up(off + 2 * bhmd);
+    rp->off_q0 = off;
+    off = align_up(off + 2 * (size_t)pb->H * pb->m * pb->dh);
+    rp->off_w = off;
+    off = align_up(off + 2 * 7 * d * d * (size_t)n_layers);
+    rp->total = off;
+    return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sa_status sa_refine_forward(const sa_problem* pb, const void* X, int32_t d_model, const float* P0, int32_t n_layers,
+                            const sa_refine_layer* layers, float eps, const int32_t* cu_offsets, const uint8_t* mask,
+                            float* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    g_err[0] = 0;
+    RefinePlan rp;
+    sa_status st = make_refine_plan(pb, d_model, n_layers, &rp);
+    if (st != SA_OK) return st;
+    if (!cu_offsets) return fail(SA_ERR_INVALID_ARG, "refinement takes packed rows: cu_offsets must be non-NULL");
+    if (!layers) return fail(SA_ERR_INVALID_ARG, "layers is NULL");
+    if (!(eps >= 0.f) || !isfinite(eps)) return fail(SA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    for (int l = 0; l < n_layers; ++l) {
+        const sa_refine_layer& L = layers[l];
+        const void* ptrs[] = {L.Wq, L.Wk, L.ln1_g, L.ln1_b, L.W1, L.W3, L.W2, L.ln2_g, L.ln2_b};
+        for (const void* q : ptrs)
+            if (!q) return fail(SA_ERR_INVALID_ARG, "layer %d: every weight pointer must be non-NULL", l);
+        if (!aligned(L.Wq, 16) || !aligned(L.Wk, 16) || !aligned(L.W1, 16) || !aligned(L.W3, 16) ||
+            !aligned(L.W2, 16) || !aligned(L.ln1_g, 4) || !aligned(L.ln1_b, 4) || !aligned(L.ln2_g, 4) ||
+            !aligned(L.ln2_b, 4))
+            return fail(SA_ERR_INVALID_ARG, "layer %d: matrices must be 16-byte aligned", l);
+    }
+    if (pb->B == 0) return SA_OK;
+    if (!X || !P0 || !out) return fail(SA_ERR_INVALID_ARG, "X, P0 and out must be non-NULL");
+    if (!aligned(X, 16) || !aligned(P0, 16) || !aligned(out, 16))
+        return fail(SA_ERR_INVALID_ARG, "X, P0 and out must be 16-byte aligned");
+    if (!workspace || workspace_bytes < rp.total)
+        return fail(SA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", rp.total, workspace_bytes);
+    if (!aligned(workspace, kAlign)) return fail(SA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+    unsigned char* ws = (unsigned char*)workspace;
+    float* xhat = (float*)(ws + rp.off_xhat);
+    sa::bf16* q = (sa::bf16*)(ws + rp.off_q);
+    sa::bf16* q0 = (sa::bf16*)(ws + rp.off_q0);
+    sa::bf16* wt = (sa::bf16*)(ws + rp.off_w);
+    const int D = d_model;
+    const size_t dd = (size_t)D * D;
+    auto wq_t = [&](int l) { return wt + 7 * dd * l; };
+    auto w1_t = [&](int l) { return wt + 7 * dd * l + dd; };
+    auto w3_t = [&](int l) { return wt + 7 * dd * l + 3 * dd; };
+    auto w2_t = [&](int l) { return wt + 7 * dd * l + 5 * dd; };
+
+    const hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
+    g_ev_start = g_ev_stop = nullptr;
+    hipError_t e;
+    if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return hip_fail(e, "timing event");
+
+    // weights to [out][in]
+    sa::TransposeArgs ta{};
+    for (int l = 0; l < n_layers; ++l) {
+        ta.mat[ta.n++] = {(const sa::bf16*)layers[l].Wq, wq_t(l), D, D};
+        ta.mat[ta.n++] = {(const sa::bf16*)layers[l].W1, w1_t(l), D, 2 * D};
+        ta.mat[ta.n++] = {(const sa::bf16*)layers[l].W3, w3_t(l), D, 2 * D};
+        ta.mat[ta.n++] = {(const sa::bf16*)layers[l].W2, w2_t(l), 2 * D, D};
+    }
+    if ((e = sa::launch_transpose(ta, stream)) != hipSuccess) return hip_fail(e, "weight transpose");
+
+    // first-layer queries P0 Wq_0 (shared by every user)
+    sa::SketchArgs sk{};
+    sk.m = pb->m;
+    sk.H = pb->H;
+    sk.dh = pb->dh;
+    sk.eps = eps;
+    sk.mode = 1;
+    sk.rows = pb->m;
+    sk.base = P0;
+    sk.wqt = wq_t(0);
+    sk.q = q0;
+    if ((e = sa::launch_sketch(sk, D, stream)) != hipSuccess) return hip_fail(e, "query projection");
+
+    for (int l = 0; l < n_layers; ++l) {
+        sa_problem pl = *pb;
+        pl.q_batch_stride = l == 0 ? 0 : (int64_t)pb->H * pb->m * pb->dh;
+        st = sa_forward_fused_proj(&pl, X, d_model, layers[l].Wk, nullptr, l == 0 ? (const void*)q0 : (const void*)q,
+                                   cu_offsets, mask, xhat, nullptr, workspace, rp.att.total, stream);
+        if (st != SA_OK) return st;
+        sa::SketchArgs u = sk;
+        u.mode = 0;
+        u.rows = pb->B * pb->m;
+        u.base = l == 0 ? P0 : out;
+        u.base_shared = l == 0;
+        u.xhat = xhat;
+        u.ln1_g = layers[l].ln1_g;
+        u.ln1_b = layers[l].ln1_b;
+        u.ln2_g = layers[l].ln2_g;
+        u.ln2_b = layers[l].ln2_b;
+        u.w1t = w1_t(l);
+        u.w3t = w3_t(l);
+        u.w2t = w2_t(l);
+        u.wqt = l + 1 < n_layers ? wq_t(l + 1) : nullptr;
+        u.q = q;
+        u.out = out;
+        if ((e = sa::launch_sketch(u, D, stream)) != hipSuccess) return hip_fail(e, "sketch update");
+    }
+    if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return hip_fail(e, "timing event");
+    return SA_OK;
+}
+
+size_t sa_refine_workspace_size(const sa_problem* pb, int32_t d_model, int32_t n_layers) {
+    RefinePlan rp;
+    if (make_refine_plan(pb, d_model, n_layers, &rp) != SA_OK) return 0;
+    return rp.total;
+}
+
 sa_status sa_set_timing_events(hipEvent_t start, hipEvent_t stop) {
     if ((start == nullptr) != (stop == nullptr)) return fail(SA_ERR_INVALID_ARG, "give both timing events or neither");
     g_ev_start = start;

@@ -210,6 +210,39 @@ struct FusedArgs {
     int32_t G, R_fixed, R_min;
     Partials part;
 };
+// One sketch-update launch of stacked refinement (sa_refine.hip).
+struct SketchArgs {
+    int32_t rows;            // sketch rows: B*m (layer) or m (projection only)
+    int32_t m, H, dh;        // D = H*dh features per row
+    int32_t mode;            // 0: LN1 + FFN + LN2 [+ queries]; 1: queries only
+    const float* base;       // residual input [rows][D], or [m][D] shared (base_shared)
+    int32_t base_shared;
+    const float* xhat;       // attention output [B][H][m][dh]
+    const float* ln1_g;
+    const float* ln1_b;
+    const float* ln2_g;
+    const float* ln2_b;
+    const bf16* w1t;         // [2D][D] (W1 transposed)
+    const bf16* w3t;         // [2D][D]
+    const bf16* w2t;         // [D][2D]
+    const bf16* wqt;         // [D][D] next queries' weight transposed, or nullptr
+    float eps;
+    float* out;              // [rows][D] fp32 (mode 0); may equal base
+    bf16* q;                 // [B][H][m][dh] bf16 queries (when wqt)
+};
+constexpr int kMaxTranspose = 64;
+struct TransposeArgs {
+    struct Mat {
+        const bf16* src;     // [rows][cols]
+        bf16* dst;           // [cols][rows]
+        int32_t rows, cols;
+    } mat[kMaxTranspose];
+    int32_t n;
+};
+bool sketch_supported(int D);
+hipError_t launch_sketch(const SketchArgs& a, int D, hipStream_t s);
+hipError_t launch_transpose(const TransposeArgs& a, hipStream_t s);
+
 bool fused_supported(int d_model, int m, int dh);
 int fused_groups(int H);     // blocks per row range
 hipError_t launch_fused(const FusedArgs& a, hipStream_t s);

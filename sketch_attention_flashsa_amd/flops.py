@@ -96,3 +96,10 @@ def sa_forward_flops(total_tokens: int, H: int, m: int, dh: int) -> float:
 def projection_flops(total_tokens: int, d_model: int, n_cols: int, n_mats: int = 2) -> float:
     """Key (and value) projection FLOPs: 2 * L * d_model * n_cols per matrix."""
     return 2.0 * total_tokens * d_model * n_cols * n_mats
+
+
+def refine_flops(total_tokens: int, B: int, m: int, d: int, n_layers: int) -> float:
+    """Stacked refinement over a batch (G.3's SA layer summed over users, with
+    L the user's rows and L_s = m): n_sa * (2 L d^2 + 14 L_s d^2 + 4 L_s L d)
+    per user.  Linear in L, so the batch total uses the row total."""
+    return n_layers * (2.0 * total_tokens * d * d + 14.0 * B * m * d * d + 4.0 * m * total_tokens * d)

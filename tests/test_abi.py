@@ -140,3 +140,36 @@ def test_fused_entry_validation():
     st = lib.sa_forward_fused_proj(ctypes.byref(pb5), FAKE, 256, FAKE, None, FAKE, FAKE, None, FAKE, None, FAKE,
                                    n5, None)
     assert st == sa.SA_ERR_INVALID_ARG and "H*dh == d_model" in sa.sa_last_error()
+
+
+def test_refine_entry_validation():
+    lib = sa.load_library()
+    pb = sa.make_problem(128, 8, 256, 32, 4_240_293, dtype="bf16")
+    n = lib.sa_refine_workspace_size(ctypes.byref(pb), 256, 2)
+    n1 = lib.sa_refine_workspace_size(ctypes.byref(pb), 256, 1)
+    # the attention workspace plus xhat, queries and 7 d^2 bf16 weights per layer
+    assert n > n1 > lib.sa_forward_fused_proj_workspace_size(ctypes.byref(pb), 256)
+    assert n - n1 == 7 * 256 * 256 * 2
+    # H*dh != d_model, n_layers out of range, fp32 inputs, dh != 32, d_model 192
+    bad = [(sa.make_problem(4, 4, 256, 32, 1000, dtype="bf16"), 256, 2, sa.SA_ERR_INVALID_ARG),
+           (pb, 256, 0, sa.SA_ERR_INVALID_ARG), (pb, 256, 9, sa.SA_ERR_INVALID_ARG),
+           (sa.make_problem(4, 8, 128, 32, 1000, dtype="f32"), 256, 2, sa.SA_ERR_UNSUPPORTED),
+           (sa.make_problem(4, 4, 128, 64, 1000, dtype="bf16"), 256, 2, sa.SA_ERR_UNSUPPORTED),
+           (sa.make_problem(4, 6, 128, 32, 1000, dtype="bf16"), 192, 2, sa.SA_ERR_UNSUPPORTED)]
+    for p, dm, nl, code in bad:
+        assert lib.sa_refine_workspace_size(ctypes.byref(p), dm, nl) == 0
+        st = lib.sa_refine_forward(ctypes.byref(p), None, dm, None, nl, None, 1e-5, None, None, None, None, 0, None)
+        assert st == code, (st, sa.sa_last_error())
+    # packed only, layers required, eps checked: all before any GPU work
+    layers = (sa.SaRefineLayer * 2)()
+    st = lib.sa_refine_forward(ctypes.byref(pb), FAKE, 256, FAKE, 2, layers, 1e-5, None, None, FAKE, FAKE, n, None)
+    assert st == sa.SA_ERR_INVALID_ARG and "cu_offsets" in sa.sa_last_error()
+    st = lib.sa_refine_forward(ctypes.byref(pb), FAKE, 256, FAKE, 2, None, 1e-5, FAKE, None, FAKE, FAKE, n, None)
+    assert st == sa.SA_ERR_INVALID_ARG and "layers" in sa.sa_last_error()
+    st = lib.sa_refine_forward(ctypes.byref(pb), FAKE, 256, FAKE, 2, layers, float("nan"), FAKE, None, FAKE, FAKE, n,
+                               None)
+    assert st == sa.SA_ERR_INVALID_ARG and "eps" in sa.sa_last_error()
+    st = lib.sa_refine_forward(ctypes.byref(pb), FAKE, 256, FAKE, 2, layers, 1e-5, FAKE, None, FAKE, FAKE, n, None)
+    assert st == sa.SA_ERR_INVALID_ARG and "non-NULL" in sa.sa_last_error()
+    pq = sa.make_problem(4, 8, 256, 32, 1000, dtype="bf16", q_batch_stride=8 * 256 * 32)
+    assert lib.sa_refine_workspace_size(ctypes.byref(pq), 256, 2) == 0

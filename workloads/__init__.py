@@ -261,6 +261,42 @@ def random_fused_case(seed: int, *, B: int, H: int, m: int, dh: int, d_model: in
     return out
 
 
+def refine_layers(seed: int, d: int, n_layers: int):
+    """Seeded weights of stacked refinement layers (random init, no training):
+    Wq, Wk, W1, W3 ~ N(0, 1/d) and W2 ~ N(0, 1/(2d)) in bf16 ([in, out]),
+    layer-norm gains 1 + N(0, 0.01) and biases N(0, 0.01) in fp32.  The
+    1/fan-in variances keep queries, keys and FFN outputs at unit scale."""
+    import torch
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7919])))
+    out = []
+    for _ in range(n_layers):
+        L = {}
+        for k, shape, var in (("Wq", (d, d), 1.0 / d), ("Wk", (d, d), 1.0 / d), ("W1", (d, 2 * d), 1.0 / d),
+                              ("W3", (d, 2 * d), 1.0 / d), ("W2", (2 * d, d), 0.5 / d)):
+            L[k] = _to_torch(g.standard_normal(shape, dtype=np.float32) * np.float32(math.sqrt(var)), "bf16")
+        for k in ("ln1", "ln2"):
+            L[k + "_g"] = torch.from_numpy(1 + 0.1 * g.standard_normal(d, dtype=np.float32))
+            L[k + "_b"] = torch.from_numpy(0.1 * g.standard_normal(d, dtype=np.float32))
+        out.append(L)
+    return out
+
+
+def random_refine_case(seed: int, *, B: int, H: int, m: int, dh: int, lengths, n_layers: int = 2,
+                       mask_p: float = 0.0):
+    """Stacked-refinement inputs: the fused-projection recipe's X (N(0, 1)
+    bf16 rows, d = H*dh, packed by ``lengths``), prototypes P0 ~ N(0, 1)
+    [m, d] fp32 and ``n_layers`` seeded layers (:func:`refine_layers`)."""
+    import torch
+    d = H * dh
+    w = random_fused_case(seed, B=B, H=H, m=m, dh=dh, d_model=d, lengths=lengths, mask_p=mask_p)
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 104729])))
+    w["P0"] = torch.from_numpy(g.standard_normal((m, d), dtype=np.float32))
+    w["layers"] = refine_layers(seed, d, n_layers)
+    for k in ("P", "Wk", "Wv"):
+        del w[k]
+    return w
+
+
 def algorithmic_bytes(w: dict) -> int:
     """HBM bytes one forward must move at minimum: K and V (or X and the two
     projection matrices), the prototypes, the fp32 sketch and the offsets."""
