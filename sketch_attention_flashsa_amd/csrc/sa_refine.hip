@@ -12,8 +12,9 @@
 //   A  LN1 per row (lanes across the D features, fp32), Xbar kept in fp32 in
 //      the output rows (overwritten in D) and in bf16 in LDS;
 //   B  [a | g] = Xbar [W1 | W3] on v_mfma_f32_16x16x32_bf16, 64 hidden units
-//      at a time, h = silu(a) * g to LDS in bf16;
-//   C  f = h W2 on MFMA;
+//      at a time, h = silu(a) * g through a small per-wave LDS chunk (bf16)
+//   C  into f += h W2 for those 64 units, so the hidden layer never exists
+//      whole and three blocks fit on a CU;
 //   D  z = Xbar + f, LN2 per row (lane-group reductions), fp32 out;
 //   E  optional Q' = Xt' Wq' on MFMA, bf16 out.
 // The projection-only mode runs E alone on fp32 input rows (the first
@@ -45,17 +46,19 @@ __device__ __forceinline__ float silu(float a) {
     return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a * kLog2e));
 }
 
-// acc[cb] (16 rows x 16 columns each) += A (rows of `a_lds`, k = 0..K-1) x
-// Wt^T, columns n0 + 16 cb of the transposed weight Wt [N][K].
-template <int K, int NCB>
-__device__ __forceinline__ void gemm_rows16(f32x4 (&acc)[NCB], const bf16* a_lds_row, const bf16* __restrict__ wt,
-                                            int n0, int l16, int g) {
+// acc[cb] (16 rows x 16 columns each) += A x B over KS k-steps of 32: A row
+// l16 of this lane group starts at `a_row` (LDS, k contiguous); B column
+// 16 cb + l16 is row 16 cb + l16 of the transposed weight `wt` (k
+// contiguous, `ldw` elements between rows).
+template <int KS, int NCB>
+__device__ __forceinline__ void gemm_rows16(f32x4 (&acc)[NCB], const bf16* a_row, const bf16* __restrict__ wt,
+                                            int ldw, int l16, int g) {
 #pragma unroll 2
-    for (int ks = 0; ks < K / 32; ++ks) {
-        const bf16x8 a = *(const bf16x8*)(a_lds_row + 32 * ks + 8 * g);
+    for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = *(const bf16x8*)(a_row + 32 * ks + 8 * g);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-            const bf16x8 bw = *(const bf16x8*)(wt + (size_t)(n0 + 16 * cb + l16) * K + 32 * ks + 8 * g);
+            const bf16x8 bw = *(const bf16x8*)(wt + (size_t)(16 * cb + l16) * ldw + 32 * ks + 8 * g);
             acc[cb] = mfma(a, bw, acc[cb]);
         }
     }
@@ -64,14 +67,14 @@ __device__ __forceinline__ void gemm_rows16(f32x4 (&acc)[NCB], const bf16* a_lds
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void sa_sketch_kernel(SketchArgs a) {
+__global__ __launch_bounds__(256, 3) void sa_sketch_kernel(SketchArgs a) {
     constexpr int F = 2 * D;
     constexpr int XS = D + 8;          // bf16 row strides in LDS (16-byte aligned rows, shifted banks)
-    constexpr int HS = F + 8;
+    constexpr int HC = 64 + 8;         // one 64-unit chunk of the hidden layer
     constexpr int VEC = D / 64;        // features per lane in the row-wise phases
     constexpr int NCB = D / 16;        // 16-column blocks of a D-wide output
     __shared__ __attribute__((aligned(16))) bf16 xb[kRows * XS];
-    __shared__ __attribute__((aligned(16))) bf16 hid[kRows * HS];
+    __shared__ __attribute__((aligned(16))) bf16 hch[4 * 16 * HC];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, l16 = lane & 15;
@@ -122,26 +125,27 @@ __global__ __launch_bounds__(256, 1) void sa_sketch_kernel(SketchArgs a) {
         // the fp32 Xbar rows are read back in another lane order in D
         __syncthreads();
 
-        // ---- B: h = silu(Xbar W1) * (Xbar W3), 64 hidden units at a time
+        // ---- B, C: per chunk of 64 hidden units, a = Xbar W1 and g = Xbar W3
+        // (16 rows x 64 each), h = silu(a) * g through this wave's LDS chunk
+        // into the A operand, f += h W2[chunk rows]
         const bf16* arow = xb + (wrow0 + l16) * XS;
+        bf16* hw = hch + wave * 16 * HC;
+        f32x4 acc[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
         for (int n0 = 0; n0 < F; n0 += 64) {
             f32x4 acc_a[4], acc_g[4];
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) acc_a[cb] = acc_g[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            gemm_rows16<D, 4>(acc_a, arow, a.w1t, n0, l16, g);
-            gemm_rows16<D, 4>(acc_g, arow, a.w3t, n0, l16, g);
+            gemm_rows16<D / 32, 4>(acc_a, arow, a.w1t + (size_t)n0 * D, D, l16, g);
+            gemm_rows16<D / 32, 4>(acc_g, arow, a.w3t + (size_t)n0 * D, D, l16, g);
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    hid[(wrow0 + 4 * g + i) * HS + n0 + 16 * cb + l16] = (bf16)(silu(acc_a[cb][i]) * acc_g[cb][i]);
+                    hw[(4 * g + i) * HC + 16 * cb + l16] = (bf16)(silu(acc_a[cb][i]) * acc_g[cb][i]);
+            gemm_rows16<2, NCB>(acc, hw + l16 * HC, a.w2t + n0, F, l16, g);
         }
-
-        // ---- C: f = h W2
-        f32x4 acc[NCB];
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) acc[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        gemm_rows16<F, NCB>(acc, hid + (wrow0 + l16) * HS, a.w2t, 0, l16, g);
 
         // ---- D: Xt' = LN2(Xbar + f); row 4g + i of the wave lives in the 16
         // lanes of group g, 16 features per lane (one per column block)
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(256, 1) void sa_sketch_kernel(SketchArgs a) {
         f32x4 acc[NCB];
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) acc[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        gemm_rows16<D, NCB>(acc, xb + (wrow0 + l16) * XS, a.wqt, 0, l16, g);
+        gemm_rows16<D / 32, NCB>(acc, xb + (wrow0 + l16) * XS, a.wqt, D, l16, g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = tile0 + wrow0 + 4 * g + i;
