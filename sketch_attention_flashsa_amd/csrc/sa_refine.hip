@@ -14,7 +14,7 @@
 //   B  [a | g] = Xbar [W1 | W3] on v_mfma_f32_16x16x32_bf16, 64 hidden units
 //      at a time, h = silu(a) * g through a small per-wave LDS chunk (bf16)
 //   C  into f += h W2 for those 64 units, so the hidden layer never exists
-//      whole and three blocks fit on a CU;
+//      whole (43 KB of LDS per block);
 //   D  z = Xbar + f, LN2 per row (lane-group reductions), fp32 out;
 //   E  optional Q' = Xt' Wq' on MFMA, bf16 out.
 // The projection-only mode runs E alone on fp32 input rows (the first
@@ -67,7 +67,7 @@ __device__ __forceinline__ void gemm_rows16(f32x4 (&acc)[NCB], const bf16* a_row
 }  // namespace
 
 template <int D>
-__global__ __launch_bounds__(256, 3) void sa_sketch_kernel(SketchArgs a) {
+__global__ __launch_bounds__(256, 2) void sa_sketch_kernel(SketchArgs a) {
     constexpr int F = 2 * D;
     constexpr int XS = D + 8;          // bf16 row strides in LDS (16-byte aligned rows, shifted banks)
     constexpr int HC = 64 + 8;         // one 64-unit chunk of the hidden layer
