@@ -188,6 +188,44 @@ sa_status sa_forward_fused_proj(const sa_problem* pb, const void* X, int32_t d_m
 size_t sa_forward_fused_proj_workspace_size(const sa_problem* pb, int32_t d_model);
 
 /*
+ * Backward pass of sa_forward, history axis (the paper trains SA end to end;
+ * the gradient is the chain rule through section 3.1's weighted sum and the
+ * softmax over each user's rows).  With A_ji = exp(c P_j.K_i - lse_j) over
+ * user b's valid rows i, and dS the gradient arriving at S:
+ *     dV_i = sum_j A_ji dS_j
+ *     ds_ji = A_ji (dS_j.V_i - dS_j.S_j)
+ *     dK_i = c sum_j ds_ji P_j,      dP_j = c sum_i ds_ji K_i
+ * (dP summed over users when P is shared).  The weights are recomputed from
+ * the forward's saved lse; P, K, V and dS enter the MFMA products in bf16,
+ * everything accumulates in fp32.
+ *
+ * pb, P, K, V, cu_offsets, lengths, mask: exactly as given to sa_forward.
+ * S, lse   the forward's outputs [B, H, m, dh] and [B, H, m] (lse is required).
+ * dS       [B, H, m, dh] fp32 upstream gradient.
+ * dP       fp32, shaped like P ([H, m, dh], or [B, H, m, dh] with per-user P).
+ * dK, dV   fp32 [rows, H, dh] (packed) or [B, L_max, H, dh] (dense), dh
+ *          contiguous, heads contiguous in a row.  Rows of users (valid,
+ *          masked or past a dense length) are written; masked rows get 0.
+ *          Rows outside every user and dense padding past L_b are left as
+ *          they are.
+ * workspace, workspace_bytes: at least sa_backward_workspace_size(pb).
+ *
+ * Compiled shapes: bf16, history axis, dh in {32, 64}, m in {32, 64, 128,
+ * 256}; any H; P shared or per user.  Others return SA_ERR_UNSUPPORTED.
+ * P, K, V, S, dS and dP are 16-byte aligned.  Deterministic: dP's partial
+ * sums are added in a fixed order, no float atomics.
+ */
+sa_status sa_backward(const sa_problem* pb, const void* P, const void* K, const void* V,
+                      const int32_t* cu_offsets, const int32_t* lengths, const uint8_t* mask,
+                      const float* S, const float* lse, const float* dS, float* dP, float* dK,
+                      float* dV, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace sa_backward needs on the current device (0 if the
+ * problem is invalid or unsupported; sa_last_error() says why).  pb->L_max
+ * > 0 means the dense layout, else packed. */
+size_t sa_backward_workspace_size(const sa_problem* pb);
+
+/*
  * Stacked Sketch Attention refinement (section 3.3 of the SequenceO1 paper),
  * n_layers layers over a packed ragged batch.  The sketch starts as the
  * prototypes, Xt_0 = P0 [m, d]; layer l computes, for every user b,
@@ -247,8 +285,8 @@ size_t sa_refine_workspace_size(const sa_problem* pb, int32_t d_model, int32_t n
  * When both events are non-NULL, the next sa_forward or sa_forward_fused_proj
  * call made on this host thread records `start` on its stream immediately
  * before the streaming kernel (the pass over K/V or X) and `stop` immediately
- * after it, then forgets both; the next sa_refine_forward call records them
- * before its first and after its last launch.  NULL, NULL clears a pending request.  The
+ * after it, then forgets both; the next sa_refine_forward or sa_backward call
+ * records them before its first and after its last launch.  NULL, NULL clears a pending request.  The
  * events belong to the caller (hipEventCreate); the library never creates,
  * waits on or destroys them.  Returns SA_ERR_INVALID_ARG if exactly one is NULL.
  */

@@ -25,6 +25,7 @@ _NORMS = {"history": SA_NORM_HISTORY, "prototype": SA_NORM_PROTOTYPE}
 
 EXPORTED = ("sa_forward", "sa_forward_workspace_size", "sa_forward_kernel_name", "sa_forward_fused_proj",
             "sa_forward_fused_proj_workspace_size", "sa_refine_forward", "sa_refine_workspace_size",
+            "sa_backward", "sa_backward_workspace_size",
             "sa_set_timing_events", "sa_status_string", "sa_last_error", "sa_version")
 
 
@@ -78,6 +79,10 @@ def load_library(path: str | None = None):
     lib.sa_refine_forward.argtypes = [pp, vp, ctypes.c_int32, vp, ctypes.c_int32, ctypes.POINTER(SaRefineLayer),
                                       ctypes.c_float, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.sa_refine_forward.restype = ctypes.c_int
+    lib.sa_backward.argtypes = [pp] + [vp] * 13 + [ctypes.c_size_t, vp]
+    lib.sa_backward.restype = ctypes.c_int
+    lib.sa_backward_workspace_size.argtypes = [pp]
+    lib.sa_backward_workspace_size.restype = ctypes.c_size_t
     lib.sa_refine_workspace_size.argtypes = [pp, ctypes.c_int32, ctypes.c_int32]
     lib.sa_refine_workspace_size.restype = ctypes.c_size_t
     lib.sa_status_string.argtypes = [ctypes.c_int]
@@ -323,3 +328,49 @@ def sa_refine_forward(X, P0, layers, cu_offsets, H: int, mask=None, eps: float =
 
 def sa_refine_workspace_size(pb, d_model: int, n_layers: int) -> int:
     return int(load_library().sa_refine_workspace_size(ctypes.byref(pb), int(d_model), int(n_layers)))
+
+
+def sa_backward(P, K, V, S, lse, dS, cu_offsets=None, lengths=None, mask=None, scale: float | None = None,
+                workspace=None, out=None):
+    """Gradients of the history-axis forward: returns (dP, dK, dV) in fp32.
+    P, K, V, cu_offsets, lengths, mask as given to :func:`sa_forward`; S and
+    lse its outputs; dS [B, H, m, dh] fp32.  dK and dV are zero-initialised
+    here, so rows outside every user come back as 0."""
+    import torch
+    lib = load_library()
+    dev = K.device
+    packed = cu_offsets is not None
+    H, m, dh = P.shape[-3:]
+    if packed:
+        B = cu_offsets.numel() - 1
+        rows, L_max = K.shape[0], 0
+    else:
+        B, L_max = K.shape[0], K.shape[1]
+        rows = B * L_max
+    per_user = P.dim() == 4
+    P, K, V = P.contiguous(), K.contiguous(), V.contiguous()
+    S, lse, dS = S.contiguous(), lse.contiguous(), dS.to(torch.float32).contiguous()
+    if mask is not None:
+        mask = (mask.to(torch.uint8) if mask.dtype == torch.bool else mask).contiguous()
+    pb = make_problem(B, H, m, dh, rows, L_max=L_max, dtype=_dtype_name(K), scale=scale or 0.0,
+                      q_batch_stride=(H * m * dh if per_user else 0))
+    nws = int(lib.sa_backward_workspace_size(ctypes.byref(pb)))
+    if nws == 0:
+        _check(lib.sa_backward(ctypes.byref(pb), *([None] * 13), 0, None))
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    if out is None:
+        dP = torch.empty(P.shape, dtype=torch.float32, device=dev)
+        dK = torch.zeros(K.shape, dtype=torch.float32, device=dev)
+        dV = torch.zeros(V.shape, dtype=torch.float32, device=dev)
+    else:
+        dP, dK, dV = out
+    st = lib.sa_backward(ctypes.byref(pb), _ptr(P), _ptr(K), _ptr(V), _ptr(cu_offsets), _ptr(lengths), _ptr(mask),
+                         _ptr(S), _ptr(lse), _ptr(dS), _ptr(dP), _ptr(dK), _ptr(dV), _ptr(workspace), nws,
+                         _stream_handle(dev))
+    _check(st)
+    return dP, dK, dV
+
+
+def sa_backward_workspace_size(pb) -> int:
+    return int(load_library().sa_backward_workspace_size(ctypes.byref(pb)))

@@ -559,6 +559,133 @@ sa_status sa_refine_forward(const sa_problem* pb, const void* X, int32_t d_model
     return SA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Backward plan: the forward's validation, the kernels' own limits and work
+// split, and the workspace (dense prefix, D, lse2, dS in bf16, dP partials).
+struct BwdPlan {
+    Plan fw;
+    int G = 1, G1 = 1;
+    size_t off_vcu = 0, off_D = 0, off_L2 = 0, off_dsb = 0, off_part = 0, total = 0;
+};
+
+sa_status make_bwd_plan(const sa_problem* pb, bool packed, BwdPlan* bp) {
+    sa_status st = make_plan(pb, packed, &bp->fw);
+    if (st != SA_OK) return st;
+    if (pb->dtype != SA_DTYPE_BF16) return fail(SA_ERR_UNSUPPORTED, "backward: bf16 inputs only");
+    if (pb->norm != SA_NORM_HISTORY) return fail(SA_ERR_UNSUPPORTED, "backward: history axis only");
+    if (!sa::bwd_supported(pb->dh, pb->m))
+        return fail(SA_ERR_UNSUPPORTED, "backward: dh in {32, 64} and m in {32, 64, 128, 256} (got dh=%d m=%d)", pb->dh,
+                    pb->m);
+    const int cus = device_info().cus;
+    int NH, PB;
+    sa::bwd_dp_shape(pb->m, pb->H, &NH, &PB);
+    const int groups = (pb->H + NH - 1) / NH;
+    const int64_t rows_upper = pb->L_max > 0 ? (int64_t)pb->B * pb->L_max : pb->total_rows;
+    if (pb->chunk_rows > 0) {
+        const int64_t G = (rows_upper + pb->chunk_rows - 1) / pb->chunk_rows;
+        bp->G = bp->G1 = (int)(G > 0 ? G : 1);
+    } else {
+        bp->G = cus * 2 / groups > 0 ? cus * 2 / groups : 1;
+        bp->G1 = cus * 2 / pb->H > 0 ? cus * 2 / pb->H : 1;
+    }
+    const size_t bhm = (size_t)pb->B * pb->H * pb->m;
+    size_t off = 0;
+    bp->off_vcu = off;
+    off = align_up(off + sizeof(int32_t) * ((size_t)pb->B + 1));
+    bp->off_D = off;
+    off = align_up(off + sizeof(float) * bhm);
+    bp->off_L2 = off;
+    off = align_up(off + sizeof(float) * bhm);
+    bp->off_dsb = off;
+    off = align_up(off + 2 * bhm * pb->dh);
+    bp->off_part = off;
+    off = align_up(off + sizeof(float) * ((size_t)bp->G + pb->B) * pb->H * pb->m * pb->dh);
+    bp->total = off;
+    return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sa_status sa_backward(const sa_problem* pb, const void* P, const void* K, const void* V, const int32_t* cu_offsets,
+                      const int32_t* lengths, const uint8_t* mask, const float* S, const float* lse, const float* dS,
+                      float* dP, float* dK, float* dV, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    g_err[0] = 0;
+    BwdPlan bp;
+    const bool packed = cu_offsets != nullptr;
+    sa_status st = make_bwd_plan(pb, packed, &bp);
+    if (st != SA_OK) return st;
+    if (lengths && packed) return fail(SA_ERR_INVALID_ARG, "lengths is only valid for the dense layout");
+    if (pb->B == 0) return SA_OK;
+    if (!P || !K || !V || !S || !lse || !dS || !dP || !dK || !dV)
+        return fail(SA_ERR_INVALID_ARG, "P, K, V, S, lse, dS, dP, dK and dV must be non-NULL");
+    if (!aligned(P, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(S, 16) || !aligned(dS, 16) ||
+        !aligned(dP, 16) || !aligned(dK, 4) || !aligned(dV, 4) || !aligned(lse, 4))
+        return fail(SA_ERR_INVALID_ARG, "P, K, V, S, dS and dP must be 16-byte aligned");
+    if (!workspace || workspace_bytes < bp.total)
+        return fail(SA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", bp.total, workspace_bytes);
+    if (!aligned(workspace, kAlign)) return fail(SA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+    unsigned char* ws = (unsigned char*)workspace;
+    sa::Users users{};
+    users.cu = cu_offsets;
+    users.B = pb->B;
+    users.L_max = pb->L_max;
+    hipError_t e;
+    const hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
+    g_ev_start = g_ev_stop = nullptr;
+    if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return hip_fail(e, "timing event");
+    if (!packed && lengths) {
+        users.vcu = (int32_t*)(ws + bp.off_vcu);
+        e = sa::launch_dense_vcu(lengths, pb->B, pb->L_max, (int32_t*)(ws + bp.off_vcu), stream);
+        if (e != hipSuccess) return hip_fail(e, "dense offsets");
+    }
+    const int64_t hd = (int64_t)pb->H * pb->dh;
+    const float scale = pb->scale > 0.f ? pb->scale : 1.0f / sqrtf((float)pb->dh);
+    sa::BwdArgs a{};
+    a.users = users;
+    a.mask = mask;
+    a.P = P;
+    a.q_batch_stride = pb->q_batch_stride;
+    a.K = K;
+    a.V = V;
+    a.k_stride = pb->k_row_stride ? pb->k_row_stride : hd;
+    a.v_stride = pb->v_row_stride ? pb->v_row_stride : hd;
+    a.H = pb->H;
+    a.m = pb->m;
+    a.dh = pb->dh;
+    a.c = scale;
+    a.c2 = scale * sa::kLog2e;
+    a.G = bp.G;
+    a.G1 = bp.G1;
+    a.R_fixed = pb->chunk_rows;
+    a.R_min = sa::kRowAlign;
+    a.S = S;
+    a.lse = lse;
+    a.dS = dS;
+    a.Dv = (float*)(ws + bp.off_D);
+    a.L2v = (float*)(ws + bp.off_L2);
+    a.dSb = (sa::bf16*)(ws + bp.off_dsb);
+    a.dK = dK;
+    a.dV = dV;
+    a.part = sa::Partials{(float*)(ws + bp.off_part), nullptr, nullptr};
+    a.dP = dP;
+    a.per_user = pb->q_batch_stride != 0;
+    if ((e = sa::launch_backward(a, stream)) != hipSuccess) return hip_fail(e, "backward");
+    if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return hip_fail(e, "timing event");
+    return SA_OK;
+}
+
+size_t sa_backward_workspace_size(const sa_problem* pb) {
+    BwdPlan bp;
+    if (!pb || make_bwd_plan(pb, pb->L_max == 0, &bp) != SA_OK) return 0;
+    return bp.total;
+}
+
 size_t sa_refine_workspace_size(const sa_problem* pb, int32_t d_model, int32_t n_layers) {
     RefinePlan rp;
     if (make_refine_plan(pb, d_model, n_layers, &rp) != SA_OK) return 0;

@@ -1,0 +1,379 @@
+// sa_backward.hip -- gradients of the history-axis Sketch Attention forward
+// (section 3.1 of the SequenceO1 paper; the paper trains SA end to end).  Per
+// user b, head h, prototype j and valid row i, with the forward's saved
+// log-sum-exp lse_j:
+//     A_ji  = exp(c P_j.K_i - lse_j)          (recomputed, never stored)
+//     dA_ji = dS_j . V_i,   D_j = dS_j . S_j  (= sum_i A_ji dA_ji)
+//     ds_ji = A_ji (dA_ji - D_j)
+//     dV_i = sum_j A_ji dS_j,  dK_i = c sum_j ds_ji P_j,  dP_j = c sum_i ds_ji K_i.
+//
+// Three passes:
+//   sa_bwd_prep_kernel   D_j, lse_j in log2 units, and dS in bf16 (MFMA operand);
+//   sa_bwd_dkdv_kernel   dK and dV.  A block owns a row range and one head; P_h
+//                        and dS (bf16) of the current user sit in LDS; each wave
+//                        takes 16-row tiles and ALL m prototypes, so the sums
+//                        over j stay inside the wave.  Scores are computed as
+//                        S = P K^T (prototypes in the MFMA output rows), which
+//                        is the layout in which the prototype index can be the
+//                        reduction index of the next two products:
+//                        dV = A^T dS and dK = ds^T P (B operands read with
+//                        ds_read_b64_tr_b16).  K and V fragments come straight
+//                        from memory (16 bytes per lane);
+//   sa_bwd_dp_kernel     dP.  Waves own (head, 32-prototype block) as in the
+//                        forward; scores as S^T = K P^T (rows in the output
+//                        rows), so rows are the reduction index of
+//                        dP^T += K^T ds^T.  32-row K/V tiles are staged in LDS;
+//                        one partial per (segment, head) like the forward's,
+//                        summed in fixed order by sa_bwd_dp_merge_kernel.
+// Rows past a segment's end load a clamped valid row; rows that are invalid
+// (past the end, masked) get weight 0 by select, and their K values are
+// zeroed before the dP product, so NaN in masked rows cannot leak.
+#include "sa_device.h"
+
+namespace sa {
+
+using namespace dev;
+
+// ---------------------------------------------------------------- prep
+__global__ __launch_bounds__(256) void sa_bwd_prep_kernel(BwdArgs a) {
+    const int64_t n = (int64_t)a.users.B * a.H * a.m;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= n) return;
+    const float* s = a.S + t * a.dh;
+    const float* gs = a.dS + t * a.dh;
+    float d = 0.f;
+    for (int e = 0; e < a.dh; e += 4) {
+        const f32x4 x = *(const f32x4*)(s + e), y = *(const f32x4*)(gs + e);
+        d += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+        bf16* o = a.dSb + t * a.dh + e;
+        o[0] = (bf16)y[0];
+        o[1] = (bf16)y[1];
+        o[2] = (bf16)y[2];
+        o[3] = (bf16)y[3];
+    }
+    a.Dv[t] = d;
+    a.L2v[t] = a.lse[t] * kLog2e;
+}
+
+// ---------------------------------------------------------------- dK, dV
+template <int DH, int NKB>
+__global__ __launch_bounds__(256, 2) void sa_bwd_dkdv_kernel(BwdArgs a) {
+    constexpr int M = 32 * NKB;
+    constexpr int KC = DH / 32, DB = DH / 16;
+    constexpr int PS = DH + 8;                       // LDS row stride (elements)
+    __shared__ __attribute__((aligned(16))) bf16 p_l[M * PS];
+    __shared__ __attribute__((aligned(16))) bf16 g_l[M * PS];
+    __shared__ __attribute__((aligned(16))) float l2_l[M];
+    __shared__ __attribute__((aligned(16))) float d_l[M];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, l16 = lane & 15, kq = l16 >> 2, q = l16 & 3;
+    const int w = blockIdx.x, h = blockIdx.y;
+    const int64_t total = a.users.total();
+    const RowSplit rs = row_split(total, a.G1, a.R_fixed, a.R_min, 50);
+    const int64_t v_lo = rs.lo(w);
+    if (v_lo >= total) return;
+    const int64_t v_hi = min(rs.lo(w + 1), total);
+    const uint32_t p_base = (uint32_t)(uintptr_t)(lds_void*)p_l, g_base = (uint32_t)(uintptr_t)(lds_void*)g_l;
+    // transposed reads: lane (g, kq, q) points at row 4g + kq, columns 16 db + 4q..+3
+    const uint32_t tr_off = (uint32_t)(((4 * g + kq) * PS + 4 * q) * 2);
+    const bf16* Pg = (const bf16*)a.P;
+    const bf16* Kg = (const bf16*)a.K;
+    const bf16* Vg = (const bf16*)a.V;
+
+    for (int b = a.users.find(v_lo); b < a.users.B; ++b) {
+        const int64_t us = a.users.vstart(b), ue = a.users.vstart(b + 1);
+        if (us >= v_hi) break;
+        const int64_t s_lo = max(v_lo, us), s_hi = min(v_hi, ue);
+        if (s_hi <= s_lo) continue;
+        __syncthreads();                             // the previous segment's LDS reads are done
+        const bf16* Pb = Pg + (int64_t)b * a.q_batch_stride + (int64_t)h * M * DH;
+        const bf16* Gb = a.dSb + ((int64_t)b * a.H + h) * M * DH;
+        for (int idx = threadIdx.x; idx < M * DH / 8; idx += 256) {
+            const int r = idx / (DH / 8), c8 = idx - r * (DH / 8);
+            *(bf16x8*)&p_l[r * PS + c8 * 8] = *(const bf16x8*)(Pb + r * DH + c8 * 8);
+            *(bf16x8*)&g_l[r * PS + c8 * 8] = *(const bf16x8*)(Gb + r * DH + c8 * 8);
+        }
+        for (int j = threadIdx.x; j < M; j += 256) {
+            l2_l[j] = a.L2v[((int64_t)b * a.H + h) * M + j];
+            d_l[j] = a.Dv[((int64_t)b * a.H + h) * M + j];
+        }
+        __syncthreads();
+
+        const int64_t gbase = a.users.row_base(b) + (s_lo - us);
+        const int n = (int)(s_hi - s_lo);
+        for (int t0 = 16 * wave; t0 < n; t0 += 64) {
+            const int tok = t0 + l16;
+            const int tc = min(tok, n - 1);
+            const int64_t row = gbase + tc;
+            const bool valid = tok < n && (a.mask == nullptr || a.mask[row] != 0);
+            bf16x8 kf[KC], vf[KC];
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                kf[kc] = *(const bf16x8*)(Kg + row * a.k_stride + (int64_t)h * DH + 32 * kc + 8 * g);
+                vf[kc] = *(const bf16x8*)(Vg + row * a.v_stride + (int64_t)h * DH + 32 * kc + 8 * g);
+            }
+            // weights and score gradients for all M prototypes, packed as the
+            // A operands (row = this lane's token, k = 32 prototypes in the
+            // tok_of order) of dV = A^T dS and dK = ds^T P
+            bf16x8 apk[NKB], dpk[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                float av[8], dv[8];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int pb = 2 * kb + half;
+                    f32x4 s = {0.f, 0.f, 0.f, 0.f}, da = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kc = 0; kc < KC; ++kc) {
+                        const bf16x8 pa = *(const bf16x8*)&p_l[(16 * pb + l16) * PS + 32 * kc + 8 * g];
+                        const bf16x8 ga = *(const bf16x8*)&g_l[(16 * pb + l16) * PS + 32 * kc + 8 * g];
+                        s = mfma(pa, kf[kc], s);
+                        da = mfma(ga, vf[kc], da);
+                    }
+                    const f32x4 l2 = *(const f32x4*)&l2_l[16 * pb + 4 * g];
+                    const f32x4 dd = *(const f32x4*)&d_l[16 * pb + 4 * g];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float x = __builtin_amdgcn_exp2f(fmaf(s[i], a.c2, -l2[i]));
+                        av[4 * half + i] = valid ? x : 0.f;
+                        dv[4 * half + i] = valid ? x * (da[i] - dd[i]) : 0.f;
+                    }
+                }
+                apk[kb] = cat8(pack2(av[0], av[1]), pack2(av[2], av[3]), pack2(av[4], av[5]), pack2(av[6], av[7]));
+                dpk[kb] = cat8(pack2(dv[0], dv[1]), pack2(dv[2], dv[3]), pack2(dv[4], dv[5]), pack2(dv[6], dv[7]));
+            }
+            f32x4 dva[DB], dka[DB];
+#pragma unroll
+            for (int db = 0; db < DB; ++db) dva[db] = dka[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const uint32_t o = tr_off + (uint32_t)((32 * kb * PS + 16 * db) * 2);
+                    union {
+                        i16x4 h[2];
+                        bf16x8 v;
+                    } gt, pt;
+                    gt.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(g_base + o));
+                    gt.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(g_base + o + 16 * PS * 2));
+                    pt.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(p_base + o));
+                    pt.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(p_base + o + 16 * PS * 2));
+                    dva[db] = mfma(apk[kb], gt.v, dva[db]);
+                    dka[db] = mfma(dpk[kb], pt.v, dka[db]);
+                }
+            }
+            // rows 4g + i of the tile, columns 16 db + l16
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = t0 + 4 * g + i;
+                if (t >= n) continue;
+                const int64_t r = gbase + t;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const int64_t o = (r * a.H + h) * DH + 16 * db + l16;
+                    a.dV[o] = dva[db][i];
+                    a.dK[o] = dka[db][i] * a.c;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- dP
+template <int DH>
+__global__ __launch_bounds__(512) void sa_bwd_dp_kernel(BwdArgs a, int NH, int PB) {
+    constexpr int KC = DH / 32, DB = DH / 16, NSB = 2;
+    constexpr int TS = kBwdTileCols + 8;            // LDS row stride of the K/V tile (elements)
+    __shared__ __attribute__((aligned(16))) bf16 kt[32 * TS];
+    __shared__ __attribute__((aligned(16))) bf16 vt[32 * TS];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, l16 = lane & 15, kq = l16 >> 2, q = l16 & 3;
+    const int nthreads = NH * PB * 64;
+    const int w = blockIdx.x;
+    const int h0 = blockIdx.y * NH;
+    const int hl = wave / PB, pb = wave - hl * PB;
+    const int head = h0 + hl;
+    const bool active = head < a.H;
+    const int cols = NH * DH;                        // tile columns actually used
+
+    const int64_t total = a.users.total();
+    const RowSplit rs = row_split(total, a.G, a.R_fixed, a.R_min, 50);
+    const int64_t v_lo = rs.lo(w);
+    if (v_lo >= total) return;
+    const int64_t v_hi = min(rs.lo(w + 1), total);
+    const bf16* Pg = (const bf16*)a.P;
+    const bf16* Kg = (const bf16*)a.K;
+    const bf16* Vg = (const bf16*)a.V;
+    const uint32_t k_base = (uint32_t)(uintptr_t)(lds_void*)kt;
+    const uint32_t tr_off = (uint32_t)(((4 * g + kq) * TS + hl * DH + 4 * q) * 2);
+
+    for (int b = a.users.find(v_lo); b < a.users.B; ++b) {
+        const int64_t us = a.users.vstart(b), ue = a.users.vstart(b + 1);
+        if (us >= v_hi) break;
+        const int64_t s_lo = max(v_lo, us), s_hi = min(v_hi, ue);
+        if (s_hi <= s_lo) continue;
+        const int64_t gbase = a.users.row_base(b) + (s_lo - us);
+        const int n = (int)(s_hi - s_lo);
+        const int hh = active ? head : h0;
+        // B operands: column = prototype 32 pb + 16 sb + l16, k = dh
+        bf16x8 pf[NSB][KC], gf[NSB][KC];
+        float l2v[NSB], dv[NSB];
+        const bf16* Pb = Pg + (int64_t)b * a.q_batch_stride + (int64_t)hh * a.m * DH;
+        const bf16* Gb = a.dSb + ((int64_t)b * a.H + hh) * a.m * DH;
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) {
+            const int j = 32 * pb + 16 * sb + l16;
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                pf[sb][kc] = *(const bf16x8*)(Pb + (int64_t)j * DH + 32 * kc + 8 * g);
+                gf[sb][kc] = *(const bf16x8*)(Gb + (int64_t)j * DH + 32 * kc + 8 * g);
+            }
+            l2v[sb] = a.L2v[((int64_t)b * a.H + hh) * a.m + j];
+            dv[sb] = a.Dv[((int64_t)b * a.H + hh) * a.m + j];
+        }
+        f32x4 acc[NSB][DB];
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[sb][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+        for (int t0 = 0; t0 < n; t0 += 32) {
+            __syncthreads();                         // the previous tile's LDS reads are done
+            for (int idx = threadIdx.x; idx < 32 * cols / 8; idx += nthreads) {
+                const int r = idx / (cols / 8), c8 = idx - r * (cols / 8);
+                const int64_t row = gbase + min(t0 + r, n - 1);
+                *(bf16x8*)&kt[r * TS + c8 * 8] = *(const bf16x8*)(Kg + row * a.k_stride + (int64_t)h0 * DH + c8 * 8);
+                *(bf16x8*)&vt[r * TS + c8 * 8] = *(const bf16x8*)(Vg + row * a.v_stride + (int64_t)h0 * DH + c8 * 8);
+            }
+            __syncthreads();
+            if (!active) continue;
+            // validity of the tile's 32 rows (bit r)
+            const int tl = t0 + lane;
+            bool vr = lane < 32 && tl < n;
+            if (a.mask) vr = vr && a.mask[gbase + min(tl, n - 1)] != 0;
+            const uint32_t valid = (uint32_t)__ballot(vr);
+            // S^T = K P^T and dA^T = V dS^T: rows = tokens (two 16-row halves)
+            f32x4 s[2][NSB], da[2][NSB];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+#pragma unroll
+                for (int sb = 0; sb < NSB; ++sb) s[half][sb] = da[half][sb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) {
+                    const bf16x8 kr = *(const bf16x8*)&kt[(16 * half + l16) * TS + hl * DH + 32 * kc + 8 * g];
+                    const bf16x8 vr8 = *(const bf16x8*)&vt[(16 * half + l16) * TS + hl * DH + 32 * kc + 8 * g];
+#pragma unroll
+                    for (int sb = 0; sb < NSB; ++sb) {
+                        s[half][sb] = mfma(kr, pf[sb][kc], s[half][sb]);
+                        da[half][sb] = mfma(vr8, gf[sb][kc], da[half][sb]);
+                    }
+                }
+            }
+            // ds^T packed as the B operand of dP^T += K^T ds^T (k = tokens in the
+            // tok_of order, column = prototype)
+            const uint32_t vj = lane_slots(valid, g);
+            bf16x8 pk[NSB];
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb) {
+                float x[8];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const float sc = s[jj >> 2][sb][jj & 3], dd = da[jj >> 2][sb][jj & 3];
+                    const float p = __builtin_amdgcn_exp2f(fmaf(sc, a.c2, -l2v[sb]));
+                    x[jj] = ((vj >> jj) & 1) ? p * (dd - dv[sb]) : 0.f;
+                }
+                pk[sb] = cat8(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                union {
+                    i16x4 h[2];
+                    bf16x8 v;
+                } kT;
+                const uint32_t o = k_base + tr_off + (uint32_t)(16 * db * 2);
+                kT.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)o);
+                kT.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(o + 16 * TS * 2));
+                if (valid != 0xffffffffu) {
+                    // invalid rows: zero their keys (NaN in masked rows must not leak)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        if (!((vj >> jj) & 1)) kT.h[0][jj] = 0;
+                        if (!((vj >> (4 + jj)) & 1)) kT.h[1][jj] = 0;
+                    }
+                }
+#pragma unroll
+                for (int sb = 0; sb < NSB; ++sb) acc[sb][db] = mfma(kT.v, pk[sb], acc[sb][db]);
+            }
+        }
+        if (active) {
+            const int64_t slot = (int64_t)w + b;
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    *(f32x4*)lane_major_acc(a.part, slot, a.H, head, a.m, DH, 2 * pb + sb, db, lane) =
+                        acc[sb][db] * a.c;
+        }
+    }
+}
+
+// dP = sum of the dP partials of the segments in fixed order: per user (per-user
+// prototypes) or over all users (shared prototypes).  One thread per four
+// outputs (h, j, e..e+3); the partials are lane-major.
+__global__ __launch_bounds__(256) void sa_bwd_dp_merge_kernel(BwdArgs a) {
+    const int h = blockIdx.y, bo = blockIdx.z;        // bo: user (per-user P) or 0
+    const int qd = blockIdx.x * 256 + threadIdx.x;
+    if (qd >= a.m * (a.dh / 4)) return;
+    const int lane = qd & 63, blk = qd >> 6;
+    const int db = blk % (a.dh / 16), j16 = blk / (a.dh / 16);
+    const int j = 16 * j16 + (lane & 15), e = 16 * db + 4 * (lane >> 4);
+    const int64_t total = a.users.total();
+    const RowSplit rs = row_split(total, a.G, a.R_fixed, a.R_min, 50);
+    const int64_t md = (int64_t)a.m * a.dh;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int b0 = a.per_user ? bo : 0, b1 = a.per_user ? bo + 1 : a.users.B;
+    for (int b = b0; b < b1; ++b) {
+        const int64_t us = a.users.vstart(b), ue = a.users.vstart(b + 1);
+        if (ue <= us) continue;
+        const int64_t w0 = rs.range_of(us), w1 = rs.range_of(ue - 1);
+        for (int64_t w = w0; w <= w1; ++w) acc += *(const f32x4*)(a.part.acc + ((w + b) * a.H + h) * md + (int64_t)qd * 4);
+    }
+    float* o = a.dP + (((int64_t)bo * a.H + h) * a.m + j) * a.dh + e;
+    *(f32x4*)o = acc;
+}
+
+bool bwd_supported(int dh, int m) { return (dh == 32 || dh == 64) && (m == 32 || m == 64 || m == 128 || m == 256); }
+
+// waves per head in the dP kernel (one per 32 prototypes) and heads per block
+void bwd_dp_shape(int m, int H, int* NH, int* PB) {
+    *PB = m / 32;
+    int nh = 8 / *PB;
+    if (nh < 1) nh = 1;
+    while (nh > 1 && (H % nh != 0 || nh * 64 > kBwdTileCols)) nh >>= 1;
+    *NH = nh;
+}
+
+hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
+    if (a.users.B == 0) return hipSuccess;
+    const int64_t n = (int64_t)a.users.B * a.H * a.m;
+    hipLaunchKernelGGL(sa_bwd_prep_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    const dim3 g1(a.G1, a.H);
+#define SA_DKDV(D_, K_) \
+    if (a.dh == D_ && a.m == 32 * K_) hipLaunchKernelGGL((sa_bwd_dkdv_kernel<D_, K_>), g1, dim3(256), 0, s, a);
+    SA_DKDV(32, 1) SA_DKDV(32, 2) SA_DKDV(32, 4) SA_DKDV(32, 8) SA_DKDV(64, 1) SA_DKDV(64, 2) SA_DKDV(64, 4)
+    SA_DKDV(64, 8)
+#undef SA_DKDV
+    int NH, PB;
+    bwd_dp_shape(a.m, a.H, &NH, &PB);
+    const dim3 g2(a.G, (a.H + NH - 1) / NH), blk2(NH * PB * 64);
+    if (a.dh == 32) hipLaunchKernelGGL(sa_bwd_dp_kernel<32>, g2, blk2, 0, s, a, NH, PB);
+    else hipLaunchKernelGGL(sa_bwd_dp_kernel<64>, g2, blk2, 0, s, a, NH, PB);
+    const int mq = a.m * (a.dh / 4);
+    hipLaunchKernelGGL(sa_bwd_dp_merge_kernel, dim3((mq + 255) / 256, a.H, a.per_user ? a.users.B : 1), dim3(256), 0,
+                       s, a);
+    return hipGetLastError();
+}
+
+}  // namespace sa

@@ -243,6 +243,38 @@ bool sketch_supported(int D);
 hipError_t launch_sketch(const SketchArgs& a, int D, hipStream_t s);
 hipError_t launch_transpose(const TransposeArgs& a, hipStream_t s);
 
+// History-axis backward pass (sa_backward.hip).
+constexpr int kBwdTileCols = 256;   // widest K/V row slice (heads x dh) the dP kernel stages
+struct BwdArgs {
+    Users users;
+    const uint8_t* mask;
+    const void* P;           // bf16 [H][m][dh] or per user (q_batch_stride)
+    int64_t q_batch_stride;
+    const void* K;           // bf16 rows
+    const void* V;
+    int64_t k_stride, v_stride;
+    int32_t H, m, dh;
+    float c;                 // scale
+    float c2;                // scale * log2(e)
+    int32_t G;               // row ranges of the dP kernel (and of its partials)
+    int32_t G1;              // row ranges of the dK/dV kernel
+    int32_t R_fixed, R_min;
+    const float* S;          // forward output [B][H][m][dh]
+    const float* lse;        // forward lse [B][H][m] (natural log)
+    const float* dS;         // upstream gradient [B][H][m][dh]
+    float* Dv;               // [B][H][m] dS . S
+    float* L2v;              // [B][H][m] lse in log2 units
+    bf16* dSb;               // [B][H][m][dh] dS in bf16
+    float* dK;               // [rows][H][dh]
+    float* dV;
+    Partials part;           // dP partials (acc only, lane-major)
+    float* dP;               // [H][m][dh] or [B][H][m][dh]
+    int32_t per_user;
+};
+bool bwd_supported(int dh, int m);
+void bwd_dp_shape(int m, int H, int* NH, int* PB);
+hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
+
 bool fused_supported(int d_model, int m, int dh);
 int fused_groups(int H);     // blocks per row range
 hipError_t launch_fused(const FusedArgs& a, hipStream_t s);

@@ -173,3 +173,31 @@ def test_refine_entry_validation():
     assert st == sa.SA_ERR_INVALID_ARG and "non-NULL" in sa.sa_last_error()
     pq = sa.make_problem(4, 8, 256, 32, 1000, dtype="bf16", q_batch_stride=8 * 256 * 32)
     assert lib.sa_refine_workspace_size(ctypes.byref(pq), 256, 2) == 0
+
+
+def test_backward_entry_validation():
+    lib = sa.load_library()
+    pb = sa.make_problem(16, 8, 128, 64, 1_600_000, dtype="bf16")
+    n = lib.sa_backward_workspace_size(ctypes.byref(pb))
+    assert n > 0
+    bad = [(sa.make_problem(4, 8, 128, 64, 1000, dtype="f32"), sa.SA_ERR_UNSUPPORTED),
+           (sa.make_problem(4, 8, 128, 64, 1000, dtype="bf16", norm="prototype"), sa.SA_ERR_UNSUPPORTED),
+           (sa.make_problem(4, 8, 128, 128, 1000, dtype="bf16"), sa.SA_ERR_UNSUPPORTED),
+           (sa.make_problem(4, 8, 48, 32, 1000, dtype="bf16"), sa.SA_ERR_UNSUPPORTED),
+           (sa.make_problem(4, 8, 512, 32, 1000, dtype="bf16"), sa.SA_ERR_UNSUPPORTED),
+           (sa.make_problem(-1, 8, 128, 64, 1000, dtype="bf16"), sa.SA_ERR_INVALID_ARG)]
+    for p, code in bad:
+        assert lib.sa_backward_workspace_size(ctypes.byref(p)) == 0
+        st = lib.sa_backward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, 1 << 30, None)
+        assert st == code, (st, sa.sa_last_error())
+    # required pointers, workspace size: rejected before any GPU work
+    st = lib.sa_backward(ctypes.byref(pb), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                         FAKE, n, None)
+    assert st == sa.SA_ERR_INVALID_ARG and "non-NULL" in sa.sa_last_error()
+    st = lib.sa_backward(ctypes.byref(pb), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                         FAKE, n - 1, None)
+    assert st == sa.SA_ERR_WORKSPACE
+    st = lib.sa_backward(ctypes.byref(pb), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                         FAKE, n, None)
+    assert st == sa.SA_ERR_INVALID_ARG and "lengths" in sa.sa_last_error()
