@@ -270,6 +270,70 @@ def bench_refine(args):
     }))
 
 
+BACKWARD_METRIC = "history tokens/sec through the SA backward pass (bf16, 100K varlen) + % HBM peak"
+
+
+def bench_backward(args):
+    """The backward pass on the 100K workload: S, lse from one forward and a
+    seeded upstream gradient dS are resident; a step is one sa_backward call
+    (all of its launches, bracketed by the timing events)."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import sketch_attention_flashsa_amd as sa
+    from sketch_attention_flashsa_amd import flops
+    dev = torch.device("cuda:0")
+    w = W.make(4)
+    B, H, m, dh = w["B"], w["H"], w["m"], w["dh"]
+    tokens = int(w["lengths"].sum())
+    P, K, V, cu = (w[k].to(dev) for k in ("P", "K", "V", "cu_offsets"))
+    S, lse = sa.sa_forward(P, K, V, cu_offsets=cu, return_lse=True)
+    dS = torch.from_numpy(np.random.default_rng(8).standard_normal((B, H, m, dh), dtype=np.float32)).to(dev)
+    pb = sa.make_problem(B, H, m, dh, K.shape[0], dtype="bf16")
+    ws = torch.empty(sa.sa_backward_workspace_size(pb), dtype=torch.uint8, device=dev)
+    out = (torch.empty(P.shape, dtype=torch.float32, device=dev), torch.zeros(K.shape, dtype=torch.float32, device=dev),
+           torch.zeros(V.shape, dtype=torch.float32, device=dev))
+
+    def step():
+        sa.sa_backward(P, K, V, S, lse, dS, cu_offsets=cu, workspace=ws, out=out)
+
+    ms_per_step, call_ms = _timed(step, args.steps, args.warmup)
+    call_avg = sum(call_ms) / len(call_ms)
+    # every K, V element read once, dK, dV written once (fp32), plus P, dP, S, dS, lse and offsets
+    alg_bytes = tokens * H * dh * (2 + 2 + 4 + 4) + H * m * dh * (2 + 4) + B * H * m * (dh * 8 + 4) + 4 * (B + 1)
+    achieved = alg_bytes / (call_avg / 1e3) / 1e9
+    print(json.dumps({
+        "metric": BACKWARD_METRIC,
+        "value": tokens / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal draws shaped like the paper's histories)",
+        "config": {"workload": "backward_full100k_bf16", "B": B, "sum_L": tokens, "L_max": int(w["lengths"].max()),
+                   "H": H, "m": m, "dh": dh, "layout": "packed", "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "sa_backward (all launches of one call)",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "kernel_ms_avg": call_avg,
+            "kernel_ms_min": min(call_ms),
+            "mfma_tflops": 2.5 * flops.sa_forward_flops(tokens, H, m, dh) / (call_avg / 1e3) / 1e12,
+        },
+        "cpu_baseline": None,
+    }))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,7 +342,8 @@ def main():
     # before it settles; 50 untimed steps (~40 ms) keep that out of the timing.
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=4,
-                    help="workload number (default 4: full 100K bf16; 5: fused projection; 6: two refinement layers)")
+                    help="workload number (default 4: full 100K bf16; 5: fused projection; 6: two refinement "
+                         "layers; 7: backward pass on the 100K workload)")
     ap.add_argument("--cpu-users", type=int, default=4, help="users in the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -300,6 +365,8 @@ def main():
 
     if args.workload == 6:
         return bench_refine(args)
+    if args.workload == 7:
+        return bench_backward(args)
     dev = torch.device("cuda:0")
     w = W.make(args.workload)
     spec = w["spec"]

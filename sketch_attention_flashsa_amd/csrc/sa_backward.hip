@@ -56,8 +56,15 @@ __global__ __launch_bounds__(256) void sa_bwd_prep_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- dK, dV
+// Waves per SIMD the dK/dV kernel is compiled for (blocks of four waves, one
+// per SIMD): as many as its registers allow, and no more than LDS allows
+// (P and dS of one head take 4 m (dh + 8) bytes).
+constexpr int dkdv_occupancy(int DH, int NKB) {
+    return DH == 32 ? (NKB == 8 ? 3 : 4) : (NKB == 2 || NKB == 4) ? 4 : 2;
+}
+
 template <int DH, int NKB>
-__global__ __launch_bounds__(256, 2) void sa_bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, dkdv_occupancy(DH, NKB)) void sa_bwd_dkdv_kernel(BwdArgs a) {
     constexpr int M = 32 * NKB;
     constexpr int KC = DH / 32, DB = DH / 16;
     constexpr int PS = DH + 8;                       // LDS row stride (elements)
@@ -102,22 +109,32 @@ __global__ __launch_bounds__(256, 2) void sa_bwd_dkdv_kernel(BwdArgs a) {
 
         const int64_t gbase = a.users.row_base(b) + (s_lo - us);
         const int n = (int)(s_hi - s_lo);
-        for (int t0 = 16 * wave; t0 < n; t0 += 64) {
-            const int tok = t0 + l16;
-            const int tc = min(tok, n - 1);
-            const int64_t row = gbase + tc;
-            const bool valid = tok < n && (a.mask == nullptr || a.mask[row] != 0);
-            bf16x8 kf[KC], vf[KC];
+        // K and V fragments of a 16-row tile: B operands (column = row l16 of
+        // the tile, k = dh); the next tile's are loaded while this one computes
+        bf16x8 kf[KC], vf[KC];
+        auto load_tile = [&](int t0, bf16x8 (&kk)[KC], bf16x8 (&vv)[KC]) {
+            const int64_t row = gbase + min(t0 + l16, n - 1);
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
-                kf[kc] = *(const bf16x8*)(Kg + row * a.k_stride + (int64_t)h * DH + 32 * kc + 8 * g);
-                vf[kc] = *(const bf16x8*)(Vg + row * a.v_stride + (int64_t)h * DH + 32 * kc + 8 * g);
+                kk[kc] = *(const bf16x8*)(Kg + row * a.k_stride + (int64_t)h * DH + 32 * kc + 8 * g);
+                vv[kc] = *(const bf16x8*)(Vg + row * a.v_stride + (int64_t)h * DH + 32 * kc + 8 * g);
             }
-            // weights and score gradients for all M prototypes, packed as the
-            // A operands (row = this lane's token, k = 32 prototypes in the
-            // tok_of order) of dV = A^T dS and dK = ds^T P
-            bf16x8 apk[NKB], dpk[NKB];
+        };
+        if (16 * wave < n) load_tile(16 * wave, kf, vf);
+        for (int t0 = 16 * wave; t0 < n; t0 += 64) {
+            const int tok = t0 + l16;
+            const bool valid = tok < n && (a.mask == nullptr || a.mask[gbase + min(tok, n - 1)] != 0);
+            bf16x8 kn[KC], vn[KC];
+            const bool more = t0 + 64 < n;
+            if (more) load_tile(t0 + 64, kn, vn);
+            f32x4 dva[DB], dka[DB];
 #pragma unroll
+            for (int db = 0; db < DB; ++db) dva[db] = dka[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            // one block of 32 prototypes at a time: weights and score
+            // gradients packed as the A operands (row = this lane's token, k =
+            // the 32 prototypes in the tok_of order) of dV += A^T dS and
+            // dK += ds^T P
+#pragma unroll 1
             for (int kb = 0; kb < NKB; ++kb) {
                 float av[8], dv[8];
 #pragma unroll
@@ -140,14 +157,8 @@ __global__ __launch_bounds__(256, 2) void sa_bwd_dkdv_kernel(BwdArgs a) {
                         dv[4 * half + i] = valid ? x * (da[i] - dd[i]) : 0.f;
                     }
                 }
-                apk[kb] = cat8(pack2(av[0], av[1]), pack2(av[2], av[3]), pack2(av[4], av[5]), pack2(av[6], av[7]));
-                dpk[kb] = cat8(pack2(dv[0], dv[1]), pack2(dv[2], dv[3]), pack2(dv[4], dv[5]), pack2(dv[6], dv[7]));
-            }
-            f32x4 dva[DB], dka[DB];
-#pragma unroll
-            for (int db = 0; db < DB; ++db) dva[db] = dka[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
+                const bf16x8 apk = cat8(pack2(av[0], av[1]), pack2(av[2], av[3]), pack2(av[4], av[5]), pack2(av[6], av[7]));
+                const bf16x8 dpk = cat8(pack2(dv[0], dv[1]), pack2(dv[2], dv[3]), pack2(dv[4], dv[5]), pack2(dv[6], dv[7]));
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     const uint32_t o = tr_off + (uint32_t)((32 * kb * PS + 16 * db) * 2);
@@ -159,8 +170,8 @@ __global__ __launch_bounds__(256, 2) void sa_bwd_dkdv_kernel(BwdArgs a) {
                     gt.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(g_base + o + 16 * PS * 2));
                     pt.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(p_base + o));
                     pt.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(p_base + o + 16 * PS * 2));
-                    dva[db] = mfma(apk[kb], gt.v, dva[db]);
-                    dka[db] = mfma(dpk[kb], pt.v, dka[db]);
+                    dva[db] = mfma(apk, gt.v, dva[db]);
+                    dka[db] = mfma(dpk, pt.v, dka[db]);
                 }
             }
             // rows 4g + i of the tile, columns 16 db + l16
@@ -174,6 +185,13 @@ __global__ __launch_bounds__(256, 2) void sa_bwd_dkdv_kernel(BwdArgs a) {
                     const int64_t o = (r * a.H + h) * DH + 16 * db + l16;
                     a.dV[o] = dva[db][i];
                     a.dK[o] = dka[db][i] * a.c;
+                }
+            }
+            if (more) {
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) {
+                    kf[kc] = kn[kc];
+                    vf[kc] = vn[kc];
                 }
             }
         }
@@ -239,15 +257,39 @@ __global__ __launch_bounds__(512) void sa_bwd_dp_kernel(BwdArgs a, int NH, int P
 #pragma unroll
             for (int db = 0; db < DB; ++db) acc[sb][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
+        // the block stages 32-row K/V tiles in LDS; tile t + 1 is loaded into
+        // registers while tile t is computed, and written after a barrier
+        // 16-byte chunks per tile per tensor: 4 NH dh of them for NH PB waves,
+        // so at most dh / (16 PB) <= 4 per thread
+        const int nchunk = 32 * cols / 8;
+        const int per = (nchunk + nthreads - 1) / nthreads;
+        bf16x8 kreg[4], vreg[4];
+        auto load_tile = [&](int t0) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int idx = threadIdx.x + u * nthreads;
+                if (u < per && idx < nchunk) {
+                    const int r = idx / (cols / 8), c8 = idx - r * (cols / 8);
+                    const int64_t row = gbase + min(t0 + r, n - 1);
+                    kreg[u] = *(const bf16x8*)(Kg + row * a.k_stride + (int64_t)h0 * DH + c8 * 8);
+                    vreg[u] = *(const bf16x8*)(Vg + row * a.v_stride + (int64_t)h0 * DH + c8 * 8);
+                }
+            }
+        };
+        load_tile(0);
         for (int t0 = 0; t0 < n; t0 += 32) {
             __syncthreads();                         // the previous tile's LDS reads are done
-            for (int idx = threadIdx.x; idx < 32 * cols / 8; idx += nthreads) {
-                const int r = idx / (cols / 8), c8 = idx - r * (cols / 8);
-                const int64_t row = gbase + min(t0 + r, n - 1);
-                *(bf16x8*)&kt[r * TS + c8 * 8] = *(const bf16x8*)(Kg + row * a.k_stride + (int64_t)h0 * DH + c8 * 8);
-                *(bf16x8*)&vt[r * TS + c8 * 8] = *(const bf16x8*)(Vg + row * a.v_stride + (int64_t)h0 * DH + c8 * 8);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int idx = threadIdx.x + u * nthreads;
+                if (u < per && idx < nchunk) {
+                    const int r = idx / (cols / 8), c8 = idx - r * (cols / 8);
+                    *(bf16x8*)&kt[r * TS + c8 * 8] = kreg[u];
+                    *(bf16x8*)&vt[r * TS + c8 * 8] = vreg[u];
+                }
             }
             __syncthreads();
+            if (t0 + 32 < n) load_tile(t0 + 32);
             if (!active) continue;
             // validity of the tile's 32 rows (bit r)
             const int tl = t0 + lane;
@@ -338,7 +380,18 @@ __global__ __launch_bounds__(256) void sa_bwd_dp_merge_kernel(BwdArgs a) {
         const int64_t us = a.users.vstart(b), ue = a.users.vstart(b + 1);
         if (ue <= us) continue;
         const int64_t w0 = rs.range_of(us), w1 = rs.range_of(ue - 1);
-        for (int64_t w = w0; w <= w1; ++w) acc += *(const f32x4*)(a.part.acc + ((w + b) * a.H + h) * md + (int64_t)qd * 4);
+        // eight segments per batch, their loads issued together (slots past
+        // the last re-read it and are masked), added in ascending order
+        const float* base = a.part.acc + ((int64_t)b * a.H + h) * md + (int64_t)qd * 4;
+        const int64_t hmd = (int64_t)a.H * md;
+        for (int64_t x0 = w0; x0 <= w1; x0 += 8) {
+            f32x4 v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = *(const f32x4*)(base + min(x0 + k, w1) * hmd);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (x0 + k <= w1) acc += v[k];
+        }
     }
     float* o = a.dP + (((int64_t)bo * a.H + h) * a.m + j) * a.dh + e;
     *(f32x4*)o = acc;
