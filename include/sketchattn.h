@@ -138,7 +138,10 @@ typedef struct sa_problem {
  *             are clobbered.  May be NULL when the query returns 0.
  * stream      HIP stream the work is enqueued on.
  *
- * Compiled shapes: bf16: dh in {32, 64, 128}, m a multiple of 16.
+ * Compiled shapes: bf16: dh in {32, 64, 128}, m a multiple of 16 (the
+ * direct-to-LDS streaming kernel for dh in {32, 64} with m a multiple of 32,
+ * and for dh == 128 with m a multiple of 256; a register-staged kernel for
+ * the rest).
  * f32: dh in {16, 32, 64, 128}, any m.  The prototype axis takes shared
  * prototypes only (q_batch_stride == 0).  Others return SA_ERR_UNSUPPORTED.
  */
@@ -175,8 +178,13 @@ const char* sa_forward_kernel_name(const sa_problem* pb);
  *
  * Compiled shapes: bf16, history axis (SA_NORM_HISTORY), dh == 32,
  * d_model in {128, 256}, m in {64, 128, 256}; P shared or per user
- * (q_batch_stride); any H.  Others return SA_ERR_UNSUPPORTED.  S_out is
- * 16-byte aligned; X, Wk, Wv and P are 16-byte aligned.
+ * (q_batch_stride); any H.  Two-pass shapes: Wv == NULL (V = X) with
+ * H*dh == d_model in {128, 256}, shared P and a (dh, m, H) that sa_forward
+ * streams (for example the paper's single head of width 128 with m = 1024,
+ * appendix G.5): K = X Wk is first projected into the workspace (bf16), then
+ * the sa_forward pass runs on it, so K makes one round trip through memory.
+ * Others return SA_ERR_UNSUPPORTED.  S_out is 16-byte aligned; X, Wk, Wv and
+ * P are 16-byte aligned.
  */
 sa_status sa_forward_fused_proj(const sa_problem* pb, const void* X, int32_t d_model,
                                 const void* Wk, const void* Wv, const void* P,
@@ -284,8 +292,9 @@ size_t sa_refine_workspace_size(const sa_problem* pb, int32_t d_model, int32_t n
  * Timing hook for benchmarks and profilers (not part of the computation).
  * When both events are non-NULL, the next sa_forward or sa_forward_fused_proj
  * call made on this host thread records `start` on its stream immediately
- * before the streaming kernel (the pass over K/V or X) and `stop` immediately
- * after it, then forgets both; the next sa_refine_forward or sa_backward call
+ * before the streaming kernel (the pass over K/V or X; on the fused entry's
+ * two-pass shapes, before the key projection) and `stop` immediately after
+ * it, then forgets both; the next sa_refine_forward or sa_backward call
  * records them before its first and after its last launch.  NULL, NULL clears a pending request.  The
  * events belong to the caller (hipEventCreate); the library never creates,
  * waits on or destroys them.  Returns SA_ERR_INVALID_ARG if exactly one is NULL.

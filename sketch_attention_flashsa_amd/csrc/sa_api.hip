@@ -66,6 +66,10 @@ struct Plan {
     int G = 1;                // row-range blocks
     int R_fixed = 0, R_min = kRowMinBf16;
     int split = 50;           // RowSplit share of the first half of the ranges
+    // fused entry, shapes outside the on-chip kernel: K = X Wk is projected
+    // into the workspace (after the forward's own sections), then sa_forward
+    bool two_pass = false;
+    size_t off_kproj = 0, off_wt = 0, fwd_total = 0;
     sa::Bf16Config cfg{};
     bool stream = false;      // bf16: the direct-to-LDS streaming kernel serves this shape
     sa::StreamConfig scfg{};
@@ -195,9 +199,22 @@ sa_status make_fused_plan(const sa_problem* pb, int32_t d_model, Plan* pl) {
     if (pb->dtype != SA_DTYPE_BF16) return fail(SA_ERR_UNSUPPORTED, "fused projection: bf16 inputs only");
     if (pb->norm != SA_NORM_HISTORY) return fail(SA_ERR_UNSUPPORTED, "fused projection: history axis only");
     if (d_model < 1) return fail(SA_ERR_INVALID_ARG, "d_model must be >= 1 (got %d)", d_model);
-    if (!sa::fused_supported(d_model, pb->m, pb->dh))
-        return fail(SA_ERR_UNSUPPORTED, "fused projection: needs dh == 32, d_model in {128, 256}, m in {64, 128, 256} "
-                                        "(got dh=%d d_model=%d m=%d)", pb->dh, d_model, pb->m);
+    if (!sa::fused_supported(d_model, pb->m, pb->dh)) {
+        // two passes: the projection kernel, then the streaming forward on
+        // K (workspace) and V = X; make_plan above planned that forward
+        const int64_t hd = (int64_t)pb->H * pb->dh;
+        if (!(pl->stream && hd == d_model && sa::project_supported(d_model, (int)hd) && pb->q_batch_stride == 0))
+            return fail(SA_ERR_UNSUPPORTED,
+                        "fused projection: needs dh == 32, d_model in {128, 256}, m in {64, 128, 256}, or (two "
+                        "passes) V = X with H*dh == d_model in {128, 256}, a streaming-kernel shape and shared P "
+                        "(got dh=%d d_model=%d m=%d H=%d)", pb->dh, d_model, pb->m, pb->H);
+        pl->two_pass = true;
+        pl->fwd_total = pl->total;
+        pl->off_kproj = align_up(pl->total);
+        pl->off_wt = align_up(pl->off_kproj + 2 * (size_t)pl->buf_rows * hd);
+        pl->total = align_up(pl->off_wt + 2 * (size_t)hd * d_model);
+        return SA_OK;
+    }
     if (pb->chunk_rows > 0) {
         pl->R_fixed = pb->chunk_rows;
         const int64_t G = (pb->total_rows + pb->chunk_rows - 1) / pb->chunk_rows;
@@ -363,6 +380,32 @@ sa_status sa_forward_fused_proj(const sa_problem* pb, const void* X, int32_t d_m
     if (workspace && !aligned(workspace, kAlign)) return fail(SA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
 
     unsigned char* ws = (unsigned char*)workspace;
+    if (pl.two_pass) {
+        if (Wv) return fail(SA_ERR_UNSUPPORTED, "fused projection, two-pass shapes: V = X only (Wv must be NULL)");
+        const int hd = pb->H * pb->dh;
+        sa::bf16* kbuf = (sa::bf16*)(ws + pl.off_kproj);
+        sa::bf16* wt = (sa::bf16*)(ws + pl.off_wt);
+        const hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
+        g_ev_start = g_ev_stop = nullptr;
+        hipError_t e;
+        if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return hip_fail(e, "timing event");
+        sa::TransposeArgs ta{};
+        ta.mat[ta.n++] = {(const sa::bf16*)Wk, wt, d_model, hd};
+        if ((e = sa::launch_transpose(ta, stream)) != hipSuccess) return hip_fail(e, "weight transpose");
+        sa::ProjectArgs pa{};
+        pa.X = (const sa::bf16*)X;
+        pa.x_stride = d_model;
+        pa.wt = wt;
+        pa.out = kbuf;
+        pa.rows = pl.buf_rows;
+        if ((e = sa::launch_project(pa, d_model, hd, device_info().cus, stream)) != hipSuccess)
+            return hip_fail(e, "key projection");
+        sa_problem fp = *pb;
+        fp.k_row_stride = hd;
+        fp.v_row_stride = d_model;
+        g_ev_stop = ev1;                 // stop after the streaming pass (start is above)
+        return sa_forward(&fp, P, kbuf, X, cu_offsets, nullptr, mask, S_out, lse_out, workspace, pl.fwd_total, stream);
+    }
     sa::Users users{};
     users.cu = cu_offsets;
     users.B = pb->B;
@@ -443,6 +486,9 @@ sa_status make_refine_plan(const sa_problem* pb, int32_t d_model, int32_t n_laye
                     pb->H, pb->dh, d_model);
     sa_status st = make_fused_plan(pb, d_model, &rp->att);
     if (st != SA_OK) return st;
+    if (rp->att.two_pass || !sa::fused_supported(d_model, pb->m, pb->dh))
+        return fail(SA_ERR_UNSUPPORTED, "refinement: dh == 32, d_model in {128, 256}, m in {64, 128, 256} "
+                                        "(got dh=%d d_model=%d m=%d)", pb->dh, d_model, pb->m);
     if (!sa::sketch_supported(d_model))
         return fail(SA_ERR_UNSUPPORTED, "refinement: d_model must be 128 or 256 (got %d)", d_model);
     const size_t bhmd = (size_t)pb->B * pb->H * pb->m * pb->dh, d = (size_t)d_model;

@@ -45,10 +45,13 @@ namespace {
 constexpr int kStages = 4;   // ring slots: 3 stages in flight, 1 computed
 
 // Ring bytes of a block, and the blocks per CU the 160 KB of LDS allow (at
-// most the two that give four waves per SIMD with 8-wave blocks).
+// most the two that give four waves per SIMD with 8-wave blocks).  dh = 128
+// waves need more than 128 registers (their P fragments and sums double), so
+// that shape runs one 8-wave block, two waves per SIMD, per CU.
 constexpr int ring_bytes(int DH, int NH) { return kStages * 2 * 32 * NH * DH * 2; }
 constexpr int blocks_per_cu(int DH, int NW, int NH) {
-    return (16 / NW) < (160 * 1024 / ring_bytes(DH, NH)) ? (16 / NW) : (160 * 1024 / ring_bytes(DH, NH));
+    return DH == 128 ? 1
+                     : (16 / NW) < (160 * 1024 / ring_bytes(DH, NH)) ? (16 / NW) : (160 * 1024 / ring_bytes(DH, NH));
 }
 
 }  // namespace
@@ -94,11 +97,14 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
         gy = blockIdx.y;
     }
 
-    // block heads and this wave's unit (NH heads x PB prototype blocks = NW)
-    const int h0 = gy * NH;
-    const int hl = wave / PB;
+    // block heads and this wave's unit: NH heads x PB prototype blocks = NW,
+    // or, when a head has more prototype blocks than the block has waves
+    // (PB > NW, then NH = 1), PB / NW blocks per head with NW blocks each
+    const int bph = PB > NW ? PB / NW : 1;
+    const int h0 = PB > NW ? gy / bph : gy * NH;
+    const int hl = PB > NW ? 0 : wave / PB;
     const int head = h0 + hl;
-    const int pb = wave % PB;
+    const int pb = PB > NW ? (gy % bph) * NW + wave : wave % PB;
     const bool active = head < a.H;
 
     const int64_t total = a.users.total();
@@ -373,7 +379,7 @@ namespace {
 
 template <int DH, int NW, int NH, int MB>
 hipError_t launch_stream(const FwdArgs& a, bool masked, int PB, hipStream_t s) {
-    dim3 grid(a.G, a.H / NH), block(NW * 64);
+    dim3 grid(a.G, PB > NW ? a.H * (PB / NW) : a.H / NH), block(NW * 64);
     const bool proto = a.norm == 1;
     if (!masked && !proto) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, NW, NH, MB, false, false>), grid, block, 0, s, a, PB);
     if (masked && !proto) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, NW, NH, MB, true, false>), grid, block, 0, s, a, PB);
@@ -387,8 +393,8 @@ hipError_t launch_stream(const FwdArgs& a, bool masked, int PB, hipStream_t s) {
 struct Shape {
     int dh, NW, NH, MB;
 };
-constexpr Shape kShapes[] = {{64, 16, 4, 32}, {64, 8, 2, 32}, {64, 8, 4, 32},
-                             {32, 16, 8, 32}, {32, 8, 4, 32}, {32, 8, 8, 32}};
+constexpr Shape kShapes[] = {{64, 16, 4, 32}, {64, 8, 2, 32}, {64, 8, 4, 32}, {32, 16, 8, 32},
+                             {32, 8, 4, 32},  {32, 8, 8, 32}, {128, 8, 1, 32}};
 
 }  // namespace
 
@@ -398,6 +404,17 @@ constexpr Shape kShapes[] = {{64, 16, 4, 32}, {64, 8, 2, 32}, {64, 8, 4, 32},
 // SIMD, independent barriers), then 16 waves (one block per CU);
 // SA_STREAM_NW=16 reverses the order.
 bool stream_config(int dh, int m, int H, StreamConfig* cfg) {
+    if (dh == 128) {
+        // one head per block, 8 waves = 256 prototypes; m / 256 blocks per head
+        if (m % 256 != 0) return false;
+        cfg->PB = m / 32;
+        cfg->MB = 32;
+        cfg->NH = 1;
+        cfg->NW = 8;
+        cfg->groups = H * (m / 256);
+        cfg->blocks_per_cu = blocks_per_cu(128, 8, 1);
+        return true;
+    }
     if (!(dh == 32 || dh == 64) || m % 32 != 0) return false;
     int prefer = 8;
     if (const char* e = getenv("SA_STREAM_NW")) prefer = atoi(e) == 16 ? 16 : 8;
@@ -424,7 +441,7 @@ hipError_t launch_bf16_stream(const FwdArgs& a, const StreamConfig& cfg, hipStre
 #define SA_STREAM(D_, W_, N_, M_) \
     if (dh == D_ && NW == W_ && NH == N_ && MB == M_) return launch_stream<D_, W_, N_, M_>(a, masked, PB, s);
     SA_STREAM(64, 16, 4, 32) SA_STREAM(64, 8, 2, 32) SA_STREAM(64, 8, 4, 32) SA_STREAM(32, 16, 8, 32)
-    SA_STREAM(32, 8, 4, 32) SA_STREAM(32, 8, 8, 32)
+    SA_STREAM(32, 8, 4, 32) SA_STREAM(32, 8, 8, 32) SA_STREAM(128, 8, 1, 32)
 #undef SA_STREAM
     return hipErrorInvalidValue;
 }

@@ -239,6 +239,17 @@ struct TransposeArgs {
     } mat[kMaxTranspose];
     int32_t n;
 };
+// Row projection of the fused entry's two-pass path (sa_refine.hip).
+struct ProjectArgs {
+    const bf16* X;           // [rows][x_stride]
+    int64_t x_stride;
+    const bf16* wt;          // [NOUT][DIN] transposed weights
+    bf16* out;               // [rows][NOUT]
+    int64_t rows;
+};
+bool project_supported(int din, int nout);
+hipError_t launch_project(const ProjectArgs& a, int din, int nout, int grid, hipStream_t s);
+
 bool sketch_supported(int D);
 hipError_t launch_sketch(const SketchArgs& a, int D, hipStream_t s);
 hipError_t launch_transpose(const TransposeArgs& a, hipStream_t s);

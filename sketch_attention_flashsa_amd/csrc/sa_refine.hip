@@ -237,3 +237,67 @@ hipError_t launch_transpose(const TransposeArgs& a, hipStream_t s) {
 }
 
 }  // namespace sa
+
+namespace sa {
+
+using namespace dev;
+
+// Row projection out = X W for the fused entry's two-pass shapes: X [rows][DIN]
+// bf16 (row stride x_stride), W^T [NOUT][DIN] bf16 (transposed weights, staged
+// in LDS once per block), out [rows][NOUT] bf16.  16 waves, 16 rows each per
+// pass over a 256-row tile; A operands straight from memory (16 bytes per
+// lane), B operands from LDS, v_mfma_f32_16x16x32_bf16.
+template <int DIN, int NOUT>
+__global__ __launch_bounds__(1024) void sa_project_kernel(ProjectArgs a) {
+    constexpr int WS = DIN + 8;
+    constexpr int NCB = 8;                     // 128 output columns per pass
+    __shared__ __attribute__((aligned(16))) bf16 wl[NOUT * WS];
+    for (int i = threadIdx.x; i < NOUT * DIN / 8; i += 1024) {
+        const int r = i / (DIN / 8), c8 = i - r * (DIN / 8);
+        *(bf16x8*)&wl[r * WS + c8 * 8] = *(const bf16x8*)(a.wt + (size_t)r * DIN + c8 * 8);
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, l16 = lane & 15;
+    for (int64_t t0 = (int64_t)blockIdx.x * 256; t0 < a.rows; t0 += (int64_t)gridDim.x * 256) {
+        const int64_t r0 = t0 + 16 * wave;
+        if (r0 >= a.rows) continue;
+        const int64_t ra = min(r0 + l16, a.rows - 1);
+#pragma unroll 1
+        for (int n0 = 0; n0 < NOUT; n0 += 128) {
+            f32x4 acc[NCB];
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) acc[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < DIN / 32; ++ks) {
+                const bf16x8 x = *(const bf16x8*)(a.X + ra * a.x_stride + 32 * ks + 8 * g);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    acc[cb] = mfma(x, *(const bf16x8*)&wl[(n0 + 16 * cb + l16) * WS + 32 * ks + 8 * g], acc[cb]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t r = r0 + 4 * g + i;
+                if (r >= a.rows) continue;
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) a.out[r * NOUT + n0 + 16 * cb + l16] = (bf16)acc[cb][i];
+            }
+        }
+    }
+}
+
+bool project_supported(int din, int nout) { return (din == 128 || din == 256) && (nout == 128 || nout == 256); }
+
+hipError_t launch_project(const ProjectArgs& a, int din, int nout, int grid, hipStream_t s) {
+    if (a.rows <= 0) return hipSuccess;
+    const int64_t tiles = (a.rows + 255) / 256;
+    const dim3 gr((unsigned)(tiles < grid ? tiles : grid)), blk(1024);
+    if (din == 128 && nout == 128) hipLaunchKernelGGL((sa_project_kernel<128, 128>), gr, blk, 0, s, a);
+    else if (din == 128 && nout == 256) hipLaunchKernelGGL((sa_project_kernel<128, 256>), gr, blk, 0, s, a);
+    else if (din == 256 && nout == 128) hipLaunchKernelGGL((sa_project_kernel<256, 128>), gr, blk, 0, s, a);
+    else if (din == 256 && nout == 256) hipLaunchKernelGGL((sa_project_kernel<256, 256>), gr, blk, 0, s, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace sa

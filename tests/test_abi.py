@@ -201,3 +201,22 @@ def test_backward_entry_validation():
     st = lib.sa_backward(ctypes.byref(pb), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                          FAKE, n, None)
     assert st == sa.SA_ERR_INVALID_ARG and "lengths" in sa.sa_last_error()
+
+
+def test_fused_two_pass_shapes():
+    """Single head of width 128 with 1024 prototypes (the paper's production
+    shape) takes the two-pass path: accepted with V = X, rejected with Wv."""
+    lib = sa.load_library()
+    pb = sa.make_problem(16, 1, 1024, 128, 1_600_000, dtype="bf16")
+    n = lib.sa_forward_fused_proj_workspace_size(ctypes.byref(pb), 128)
+    # the streaming forward's workspace plus K (bf16, rows x 128) and W^T
+    assert n >= lib.sa_forward_workspace_size(ctypes.byref(pb)) + 1_600_000 * 128 * 2 + 128 * 128 * 2
+    st = lib.sa_forward_fused_proj(ctypes.byref(pb), FAKE, 128, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, n, None)
+    assert st == sa.SA_ERR_UNSUPPORTED and "V = X only" in sa.sa_last_error()
+    # per-user P, H*dh != d_model, or a shape the streaming kernel does not take: unsupported
+    for p, dm in ((sa.make_problem(4, 1, 1024, 128, 1000, dtype="bf16", q_batch_stride=1024 * 128), 128),
+                  (sa.make_problem(4, 1, 1024, 128, 1000, dtype="bf16"), 256),
+                  (sa.make_problem(4, 1, 1000, 128, 1000, dtype="bf16"), 128)):
+        assert lib.sa_forward_fused_proj_workspace_size(ctypes.byref(p), dm) == 0
+    # refinement keeps to the on-chip shapes
+    assert lib.sa_refine_workspace_size(ctypes.byref(sa.make_problem(4, 1, 1024, 128, 1000, dtype="bf16")), 128, 2) == 0

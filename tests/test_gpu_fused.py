@@ -138,6 +138,26 @@ def test_fused_per_user_prototypes():
         assert np.array_equal(S[b], Sb[b]), "per-user prototypes must match the shared call"
 
 
+@pytest.mark.parametrize("H,dh,d_model,m", [(1, 128, 128, 1024), (2, 128, 256, 256)])
+def test_fused_two_pass_production_shape(H, dh, d_model, m):
+    """The paper's production shape (one head of width 128, 1024 prototypes,
+    values = X, appendix G.5) and a two-head variant: K = X Wk is projected
+    into the workspace, then the streaming forward runs on it."""
+    lengths = [1200, 0, 1, 31, 33, 700, 64]
+    w = W.random_fused_case(316 + m, B=len(lengths), H=H, m=m, dh=dh, d_model=d_model, lengths=lengths,
+                            w_var=1.0 / d_model, mask_p=0.15)
+    S, lse = run_fused(w, use_wv=False)
+    So, lo = oracle_fused(w, use_wv=False)
+    assert np.all(np.isfinite(S))
+    assert_parity(S, So, "bf16", f"two-pass H={H} dh={dh} m={m}")
+    assert_lse(lse, lo, "bf16", f"two-pass H={H} dh={dh} m={m}")
+    # masked rows poisoned with NaN change nothing
+    X2 = w["X"].clone()
+    X2[w["mask"] == 0] = float("nan")
+    S2, lse2 = run_fused(dict(w, X=X2), use_wv=False)
+    assert np.array_equal(S, S2) and np.array_equal(lse, lse2), "masked NaN rows leaked"
+
+
 @pytest.mark.slow
 def test_fused_workload5_full_size_sampled():
     """The full fused workload (128 users, 4.24M rows, X 2.17 GB) in the launch

@@ -188,6 +188,25 @@ def test_uneven_row_split(monkeypatch):
     assert np.array_equal(S, Sd) and np.array_equal(lse, ld), "packed and dense+lengths must agree bitwise"
 
 
+@pytest.mark.parametrize("H,m", [(1, 1024), (2, 256), (3, 512)])
+def test_dh128_streaming(H, m):
+    """dh = 128 with m a multiple of 256 runs the streaming kernel with m / 256
+    blocks per head: ragged users, a mask, packed == dense bitwise."""
+    lengths = [900, 0, 1, 31, 33, 257, 1500]
+    w = W.random_case(107 + m + H, B=len(lengths), H=H, m=m, dh=128, lengths=lengths, dtype="bf16", mask_p=0.2)
+    assert sa.sa_forward_kernel_name(sa.make_problem(len(lengths), H, m, 128, int(sum(lengths)))) == \
+        "sa_bf16_stream_kernel"
+    S, lse = run(w)
+    So, lo = _oracle(w)
+    assert_parity(S, So, "bf16", f"dh=128 H={H} m={m}")
+    assert_lse(lse, lo, "bf16", f"dh=128 H={H} m={m}")
+    wd = W.random_case(107 + m + H, B=len(lengths), H=H, m=m, dh=128, lengths=lengths, dtype="bf16", layout="dense")
+    wp = W.random_case(107 + m + H, B=len(lengths), H=H, m=m, dh=128, lengths=lengths, dtype="bf16")
+    Sp, lp = run(wp)
+    Sd, ld = run(wd)
+    assert np.array_equal(Sp, Sd) and np.array_equal(lp, ld), "packed and dense+lengths must agree bitwise"
+
+
 def test_deterministic_and_isolated():
     w = W.random_case(105, B=3, H=2, m=64, dh=64, lengths=[3000, 1500, 2500], dtype="bf16")
     S1, l1 = run(w)
