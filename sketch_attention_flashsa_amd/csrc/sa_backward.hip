@@ -203,8 +203,8 @@ template <int DH>
 __global__ __launch_bounds__(512) void sa_bwd_dp_kernel(BwdArgs a, int NH, int PB) {
     constexpr int KC = DH / 32, DB = DH / 16, NSB = 2;
     constexpr int TS = kBwdTileCols + 8;            // LDS row stride of the K/V tile (elements)
-    __shared__ __attribute__((aligned(16))) bf16 kt[32 * TS];
-    __shared__ __attribute__((aligned(16))) bf16 vt[32 * TS];
+    __shared__ __attribute__((aligned(16))) bf16 kt[2][32 * TS];   // double-buffered tiles
+    __shared__ __attribute__((aligned(16))) bf16 vt[2][32 * TS];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, l16 = lane & 15, kq = l16 >> 2, q = l16 & 3;
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(512) void sa_bwd_dp_kernel(BwdArgs a, int NH, int P
     const bf16* Pg = (const bf16*)a.P;
     const bf16* Kg = (const bf16*)a.K;
     const bf16* Vg = (const bf16*)a.V;
-    const uint32_t k_base = (uint32_t)(uintptr_t)(lds_void*)kt;
+    const uint32_t k_base = (uint32_t)(uintptr_t)(lds_void*)&kt[0][0];
     const uint32_t tr_off = (uint32_t)(((4 * g + kq) * TS + hl * DH + 4 * q) * 2);
 
     for (int b = a.users.find(v_lo); b < a.users.B; ++b) {
@@ -276,78 +276,88 @@ __global__ __launch_bounds__(512) void sa_bwd_dp_kernel(BwdArgs a, int NH, int P
                 }
             }
         };
-        load_tile(0);
-        for (int t0 = 0; t0 < n; t0 += 32) {
-            __syncthreads();                         // the previous tile's LDS reads are done
+        auto store_tile = [&](int buf) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int idx = threadIdx.x + u * nthreads;
                 if (u < per && idx < nchunk) {
                     const int r = idx / (cols / 8), c8 = idx - r * (cols / 8);
-                    *(bf16x8*)&kt[r * TS + c8 * 8] = kreg[u];
-                    *(bf16x8*)&vt[r * TS + c8 * 8] = vreg[u];
+                    *(bf16x8*)&kt[buf][r * TS + c8 * 8] = kreg[u];
+                    *(bf16x8*)&vt[buf][r * TS + c8 * 8] = vreg[u];
                 }
             }
+        };
+        // tile t lives in buffer t & 1; tile t + 1 is loaded into registers
+        // while tile t is computed and stored into the other buffer (read by
+        // tile t - 1, done before the previous barrier): one barrier per tile
+        load_tile(0);
+        store_tile(0);
+        __syncthreads();
+        for (int t0 = 0, it = 0; t0 < n; t0 += 32, ++it) {
+            const int cur = it & 1;
+            const bool more = t0 + 32 < n;
+            if (more) load_tile(t0 + 32);
+            if (active) {
+                // validity of the tile's 32 rows (bit r)
+                const int tl = t0 + lane;
+                bool vr = lane < 32 && tl < n;
+                if (a.mask) vr = vr && a.mask[gbase + min(tl, n - 1)] != 0;
+                const uint32_t valid = (uint32_t)__ballot(vr);
+                // S^T = K P^T and dA^T = V dS^T: rows = tokens (two 16-row halves)
+                f32x4 s[2][NSB], da[2][NSB];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+#pragma unroll
+                    for (int sb = 0; sb < NSB; ++sb) s[half][sb] = da[half][sb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kc = 0; kc < KC; ++kc) {
+                        const bf16x8 kr = *(const bf16x8*)&kt[cur][(16 * half + l16) * TS + hl * DH + 32 * kc + 8 * g];
+                        const bf16x8 vr8 = *(const bf16x8*)&vt[cur][(16 * half + l16) * TS + hl * DH + 32 * kc + 8 * g];
+#pragma unroll
+                        for (int sb = 0; sb < NSB; ++sb) {
+                            s[half][sb] = mfma(kr, pf[sb][kc], s[half][sb]);
+                            da[half][sb] = mfma(vr8, gf[sb][kc], da[half][sb]);
+                        }
+                    }
+                }
+                // ds^T packed as the B operand of dP^T += K^T ds^T (k = tokens in the
+                // tok_of order, column = prototype)
+                const uint32_t vj = lane_slots(valid, g);
+                bf16x8 pk[NSB];
+#pragma unroll
+                for (int sb = 0; sb < NSB; ++sb) {
+                    float x[8];
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) {
+                        const float sc = s[jj >> 2][sb][jj & 3], dd = da[jj >> 2][sb][jj & 3];
+                        const float p = __builtin_amdgcn_exp2f(fmaf(sc, a.c2, -l2v[sb]));
+                        x[jj] = ((vj >> jj) & 1) ? p * (dd - dv[sb]) : 0.f;
+                    }
+                    pk[sb] = cat8(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
+                }
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    union {
+                        i16x4 h[2];
+                        bf16x8 v;
+                    } kT;
+                    const uint32_t o = k_base + (uint32_t)(cur * 32 * TS * 2) + tr_off + (uint32_t)(16 * db * 2);
+                    kT.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)o);
+                    kT.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(o + 16 * TS * 2));
+                    if (valid != 0xffffffffu) {
+                        // invalid rows: zero their keys (NaN in masked rows must not leak)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+                            if (!((vj >> jj) & 1)) kT.h[0][jj] = 0;
+                            if (!((vj >> (4 + jj)) & 1)) kT.h[1][jj] = 0;
+                        }
+                    }
+#pragma unroll
+                    for (int sb = 0; sb < NSB; ++sb) acc[sb][db] = mfma(kT.v, pk[sb], acc[sb][db]);
+                }
+            }
+            if (more) store_tile(cur ^ 1);
             __syncthreads();
-            if (t0 + 32 < n) load_tile(t0 + 32);
-            if (!active) continue;
-            // validity of the tile's 32 rows (bit r)
-            const int tl = t0 + lane;
-            bool vr = lane < 32 && tl < n;
-            if (a.mask) vr = vr && a.mask[gbase + min(tl, n - 1)] != 0;
-            const uint32_t valid = (uint32_t)__ballot(vr);
-            // S^T = K P^T and dA^T = V dS^T: rows = tokens (two 16-row halves)
-            f32x4 s[2][NSB], da[2][NSB];
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-#pragma unroll
-                for (int sb = 0; sb < NSB; ++sb) s[half][sb] = da[half][sb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
-                    const bf16x8 kr = *(const bf16x8*)&kt[(16 * half + l16) * TS + hl * DH + 32 * kc + 8 * g];
-                    const bf16x8 vr8 = *(const bf16x8*)&vt[(16 * half + l16) * TS + hl * DH + 32 * kc + 8 * g];
-#pragma unroll
-                    for (int sb = 0; sb < NSB; ++sb) {
-                        s[half][sb] = mfma(kr, pf[sb][kc], s[half][sb]);
-                        da[half][sb] = mfma(vr8, gf[sb][kc], da[half][sb]);
-                    }
-                }
-            }
-            // ds^T packed as the B operand of dP^T += K^T ds^T (k = tokens in the
-            // tok_of order, column = prototype)
-            const uint32_t vj = lane_slots(valid, g);
-            bf16x8 pk[NSB];
-#pragma unroll
-            for (int sb = 0; sb < NSB; ++sb) {
-                float x[8];
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const float sc = s[jj >> 2][sb][jj & 3], dd = da[jj >> 2][sb][jj & 3];
-                    const float p = __builtin_amdgcn_exp2f(fmaf(sc, a.c2, -l2v[sb]));
-                    x[jj] = ((vj >> jj) & 1) ? p * (dd - dv[sb]) : 0.f;
-                }
-                pk[sb] = cat8(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
-            }
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                union {
-                    i16x4 h[2];
-                    bf16x8 v;
-                } kT;
-                const uint32_t o = k_base + tr_off + (uint32_t)(16 * db * 2);
-                kT.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)o);
-                kT.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(o + 16 * TS * 2));
-                if (valid != 0xffffffffu) {
-                    // invalid rows: zero their keys (NaN in masked rows must not leak)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        if (!((vj >> jj) & 1)) kT.h[0][jj] = 0;
-                        if (!((vj >> (4 + jj)) & 1)) kT.h[1][jj] = 0;
-                    }
-                }
-#pragma unroll
-                for (int sb = 0; sb < NSB; ++sb) acc[sb][db] = mfma(kT.v, pk[sb], acc[sb][db]);
-            }
         }
         if (active) {
             const int64_t slot = (int64_t)w + b;
