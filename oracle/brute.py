@@ -145,3 +145,41 @@ def refine(X, P0, layers, cu, H, eps=1e-5):
             Xt = [_layer_norm_row([Xbar[j][e] + F[j][e] for e in range(d)], g2, b2, eps) for j in range(k)]
         out.append(Xt)
     return out
+
+
+# ------------------------------------ STCA single-query attention (tiny)
+def stca(xt, X, Wq, Wk, Wv, cu, tcu, h, windows=None):
+    """Section 2.3 of the SequenceO1 paper written as it stands (no
+    reordering), every number an mpf: per target q and head hh (channels
+    c = [hh dh, (hh+1) dh)), keys K = X W_K[:, c] and values V = X W_V[:, c]
+    of the rows in the target's window, weights softmax(q W_Q[:, c] K^T /
+    sqrt(dh)), output weights V.  Returns [T][D] mpf (0 for targets with no
+    row)."""
+    T, D = len(xt), len(xt[0])
+    dh = D // h
+    sc = 1 / mpmath.sqrt(dh)
+    out = [[mpmath.mpf(0)] * D for _ in range(T)]
+    Wq_, Wk_, Wv_ = _mat(Wq), _mat(Wk), _mat(Wv)
+    for b in range(len(cu) - 1):
+        rows = [_mat([X[r]])[0] for r in range(int(cu[b]), int(cu[b + 1]))]
+        for t in range(int(tcu[b]), int(tcu[b + 1])):
+            lo, hi = 0, len(rows)
+            if windows is not None:
+                lo = min(max(int(windows[t][0]), 0), len(rows))
+                hi = max(lo, min(max(int(windows[t][1]), 0), len(rows)))
+            Xw = rows[lo:hi]
+            if not Xw:
+                continue
+            q = _matmul(_mat([xt[t]]), Wq_)[0]
+            for hh in range(h):
+                c = range(hh * dh, (hh + 1) * dh)
+                qh = [q[e] for e in c]
+                K = [[mpmath.fsum(x[d] * Wk_[d][e] for d in range(D)) for e in c] for x in Xw]
+                V = [[mpmath.fsum(x[d] * Wv_[d][e] for d in range(D)) for e in c] for x in Xw]
+                s = [mpmath.fsum(qh[e] * k[e] for e in range(dh)) * sc for k in K]
+                M = max(s)
+                w = [mpmath.exp(v - M) for v in s]
+                Z = mpmath.fsum(w)
+                for i, e in enumerate(c):
+                    out[t][e] = mpmath.fsum(w[r] * V[r][i] for r in range(len(Xw))) / Z
+    return out

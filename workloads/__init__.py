@@ -297,6 +297,55 @@ def random_refine_case(seed: int, *, B: int, H: int, m: int, dh: int, lengths, n
     return w
 
 
+def random_stca_case(seed: int, *, lengths, targets, D: int = 1024, h: int = 16, windows: str | None = None):
+    """Inputs of STCA single-query attention (bf16): history rows X ~ N(0, 1)
+    [rows, D] packed by ``lengths`` (the adapted sketch, or a recent suffix),
+    target vectors xt ~ N(0, 1) [T, D] grouped by user with ``targets`` per
+    user, and W_Q, W_K, W_V ~ N(0, 1/D) [D, D] (unit-scale projections, so
+    the scaled scores are about unit-scale too).  ``windows``: None (every
+    target sees its user's rows), "random" (a uniform [lo, hi) per target,
+    empty ones included) or "requests" (a user's targets, in order, fall in
+    four equal groups, some possibly empty, standing for four requests;
+    group r sees the first (r+1)/4 of the user's rows).  Windows are int32 [T, 2], relative to the user's first
+    row."""
+    import torch
+    ss = np.random.SeedSequence([seed, 15485863])
+    kids = ss.spawn(3 + len(lengths))
+    g_t, g_w, g_win = (np.random.Generator(np.random.PCG64(k)) for k in kids[:3])
+    lengths = np.asarray(lengths, dtype=np.int64)
+    targets = np.asarray(targets, dtype=np.int64)
+    B = len(lengths)
+    cu = np.zeros(B + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(lengths)
+    tcu = np.zeros(B + 1, dtype=np.int64)
+    tcu[1:] = np.cumsum(targets)
+    T = int(tcu[-1])
+    std = np.float32(1.0 / math.sqrt(D))
+    W = [_to_torch(g_w.standard_normal((D, D), dtype=np.float32) * std, "bf16") for _ in range(3)]
+    xt = _to_torch(g_t.standard_normal((T, D), dtype=np.float32), "bf16")
+    X = torch.empty((int(cu[-1]), D), dtype=torch.bfloat16)
+    for b in range(B):
+        g = np.random.Generator(np.random.PCG64(kids[3 + b]))
+        X[cu[b]:cu[b + 1]] = _to_torch(g.standard_normal((int(lengths[b]), D), dtype=np.float32), "bf16")
+    out = {"B": B, "D": D, "h": h, "T": T, "xt": xt, "X": X, "Wq": W[0], "Wk": W[1], "Wv": W[2],
+           "lengths": torch.from_numpy(lengths.astype(np.int32)), "targets": torch.from_numpy(targets.astype(np.int32)),
+           "cu_offsets": torch.from_numpy(cu.astype(np.int32)), "t_offsets": torch.from_numpy(tcu.astype(np.int32)),
+           "windows": None}
+    if windows is not None:
+        win = np.zeros((T, 2), dtype=np.int32)
+        for b in range(B):
+            n, t0, nt = int(lengths[b]), int(tcu[b]), int(targets[b])
+            for k in range(nt):
+                if windows == "random":
+                    lo = int(g_win.integers(0, n + 1))
+                    win[t0 + k] = (lo, int(g_win.integers(lo, n + 1)))
+                else:
+                    r = 4 * k // nt
+                    win[t0 + k] = (0, (n * (r + 1)) // 4)
+        out["windows"] = torch.from_numpy(win)
+    return out
+
+
 def algorithmic_bytes(w: dict) -> int:
     """HBM bytes one forward must move at minimum: K and V (or X and the two
     projection matrices), the prototypes, the fp32 sketch and the offsets."""
