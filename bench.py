@@ -399,6 +399,80 @@ def bench_production(args):
     }))
 
 
+STCA_METRIC = "targets/sec through STCA single-query attention, reordered (bf16, D=1024, h=16)"
+
+
+def bench_stca(args):
+    """STCA single-query attention (appendix G.2.1's reordering) over the
+    sketch branch: 64 users, each a sketch of 1,024 rows adapted to width
+    D = 1024 and 40 targets (the training-side reuse ratio of appendix G.5),
+    h = 16 heads.  A step is one sa_stca_attention call; the roofline is the
+    fused kernel's (MFMA-bound)."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import sketch_attention_flashsa_amd as sa
+    from oracle import stca as ST
+    dev = torch.device("cuda:0")
+    B, L, R, D, h = 64, args.stca_rows, args.stca_targets, 1024, 16
+    w = W.random_stca_case(9, lengths=[L] * B, targets=[R] * B, D=D, h=h)
+    xt, X, Wq, Wk, Wv, cu, toff = (w[k].to(dev) for k in ("xt", "X", "Wq", "Wk", "Wv", "cu_offsets", "t_offsets"))
+    T = w["T"]
+    pb = sa.SaStcaProblem(B=B, T=T, D=D, h=h, total_rows=B * L, x_row_stride=0, scale=0.0, flags=0)
+    ws = torch.empty(sa.sa_stca_workspace_size(pb), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, D), dtype=torch.float32, device=dev)
+
+    def step():
+        sa.sa_stca_attention(xt, X, Wq, Wk, Wv, cu, toff, h, workspace=ws, out=out)
+
+    ms_per_step, kern_ms = _timed(step, args.steps, args.warmup)
+    kavg = sum(kern_ms) / len(kern_ms)
+    fl = ST.stca_flops([L] * T, D, h)
+    tflops = fl / (kavg / 1e3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+        nu = min(B, 32)
+        n = nu * R
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        t0 = time.perf_counter()
+        ST.stca_attention(w["xt"][:n], w["X"][:nu * L], w["Wq"], w["Wk"], w["Wv"], w["cu_offsets"][:nu + 1].numpy(),
+                          w["t_offsets"][:nu + 1].numpy(), h)
+        dt = time.perf_counter() - t0
+        cpu = {"value": n / dt, "unit": "targets/s", "cores": int(blas), "kind": "oracle",
+               "sample": f"the first {nu} users ({n} targets, {L} rows each, all {h} heads), double precision, "
+                         f"{dt:.1f} s wall"}
+    print(json.dumps({
+        "metric": STCA_METRIC,
+        "value": T / (ms_per_step / 1e3),
+        "unit": "targets/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal draws; random-init projections)",
+        "config": {"workload": f"stca_sketch_L{L}_R{R}_bf16", "B": B, "rows_per_user": L, "targets_per_user": R,
+                   "D": D, "h": h, "dh": D // h, "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "sa_stca_kernel<1024, 64>",
+            "achieved": tflops,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": None,
+            "algorithmic_flops_per_launch": fl,
+            "kernel_ms_avg": kavg,
+            "kernel_ms_min": min(kern_ms),
+        },
+        "cpu_baseline": cpu,
+    }))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -408,7 +482,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=4,
                     help="workload number (default 4: full 100K bf16; 5: fused projection; 6: two refinement "
-                         "layers; 7: backward pass on the 100K workload; 8: production shape d=128, k=1024)")
+                         "layers; 7: backward pass on the 100K workload; 8: production shape d=128, k=1024; "
+                         "9: STCA single-query attention over the sketch)")
+    ap.add_argument("--stca-rows", type=int, default=1024, help="workload 9: rows per user (1024: the sketch)")
+    ap.add_argument("--stca-targets", type=int, default=40, help="workload 9: targets per user")
     ap.add_argument("--cpu-users", type=int, default=4, help="users in the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -434,6 +511,8 @@ def main():
         return bench_backward(args)
     if args.workload == 8:
         return bench_production(args)
+    if args.workload == 9:
+        return bench_stca(args)
     dev = torch.device("cuda:0")
     w = W.make(args.workload)
     spec = w["spec"]

@@ -289,13 +289,78 @@ sa_status sa_refine_forward(const sa_problem* pb, const void* X, int32_t d_model
 size_t sa_refine_workspace_size(const sa_problem* pb, int32_t d_model, int32_t n_layers);
 
 /*
+ * STCA single-query target-to-history cross attention, reordered.
+ *
+ * Operation: section 2.3 of the SequenceO1 paper ("STCA Recap") defines the
+ * attention of one target vector x over a history X [L, D] with h heads of
+ * width dh = D / h as softmax((x W_Q)(X W_K)^T / sqrt(dh)) (X W_V); appendix
+ * G.2.1 evaluates it without the L x dh key and value projections.  Per head
+ * (channels c = [hh*dh, (hh+1)*dh) of the projections):
+ *     u      = (x W_Q[:, c]) W_K[:, c]^T          [D]
+ *     alpha  = softmax(scale * u X^T)             over the target's rows
+ *     out[c] = (alpha X) W_V[:, c]                [dh]
+ * This entry does that for every target of a packed ragged batch in one
+ * fused kernel (plus a weight transpose and a small setup launch): the
+ * targets of one user share the user's rows (the multi-request batching of
+ * section 4.2), so each pass over a user's rows serves 16 of its targets for
+ * two heads.  The products run on MFMA in bf16 with fp32 accumulation; q and
+ * u, the weights and alpha X are rounded to bf16 before their products.  The
+ * output projection W_O and the query-side FFN of a full STCA layer are
+ * one-token transforms outside this entry.
+ *
+ * pb        B users, T targets, width D, heads h, total_rows of X,
+ *           x_row_stride (elements between rows of X; 0 means D), scale (0:
+ *           1/sqrt(dh)), flags (must be 0).
+ * xt        [T, D] bf16 target vectors.
+ * X         [total_rows, D] bf16 history rows (x_row_stride apart); user b
+ *           owns rows [cu_offsets[b], cu_offsets[b+1]).  Rows of a user must
+ *           be finite (a row outside one target's window still meets the
+ *           others' weights).
+ * Wq, Wk, Wv [D, D] bf16 row-major, [in, out]: q = x Wq.
+ * cu_offsets int32 [B+1], non-decreasing, cu_offsets[B] <= total_rows.
+ * t_offsets  int32 [B+1], non-decreasing, t_offsets[B] <= T: the targets of
+ *           user b are t_offsets[b] .. t_offsets[b+1]-1.  Targets outside
+ *           every user get out = 0.
+ * windows   int32 [T, 2] or NULL: target t sees only rows [lo, hi) of its
+ *           user (relative to the user's first row, clipped to the user): the
+ *           request-aware masking of section 4.2.  An empty window gives 0.
+ * out       [T, D] fp32: the h head outputs side by side.
+ * workspace at least sa_stca_workspace_size(pb) bytes, 256-byte aligned.
+ *
+ * Compiled shapes: D == 1024 with h in {16, 8} (dh 64 or 128; the paper's
+ * STCA uses h = 16, appendix G.5).  Others return SA_ERR_UNSUPPORTED.  xt,
+ * X, the matrices and out are 16-byte aligned.  Deterministic.
+ */
+typedef struct sa_stca_problem {
+    int32_t B;              /* users (>= 0) */
+    int32_t T;              /* targets (>= 0) */
+    int32_t D;              /* model width */
+    int32_t h;              /* heads; dh = D / h */
+    int64_t total_rows;     /* rows of X */
+    int64_t x_row_stride;   /* elements between rows of X; 0 means D */
+    float scale;            /* score scale; 0 means 1/sqrt(dh) */
+    int32_t flags;          /* reserved, must be 0 */
+} sa_stca_problem;
+
+sa_status sa_stca_attention(const sa_stca_problem* pb, const void* xt, const void* X, const void* Wq,
+                            const void* Wk, const void* Wv, const int32_t* cu_offsets,
+                            const int32_t* t_offsets, const int32_t* windows, float* out,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace sa_stca_attention needs (0 if the problem is invalid or
+ * unsupported; sa_last_error() says why). */
+size_t sa_stca_workspace_size(const sa_stca_problem* pb);
+
+/*
  * Timing hook for benchmarks and profilers (not part of the computation).
  * When both events are non-NULL, the next sa_forward or sa_forward_fused_proj
  * call made on this host thread records `start` on its stream immediately
  * before the streaming kernel (the pass over K/V or X; on the fused entry's
  * two-pass shapes, before the key projection) and `stop` immediately after
  * it, then forgets both; the next sa_refine_forward or sa_backward call
- * records them before its first and after its last launch.  NULL, NULL clears a pending request.  The
+ * records them before its first and after its last launch; the next
+ * sa_stca_attention call records them around its fused attention kernel.
+ * NULL, NULL clears a pending request.  The
  * events belong to the caller (hipEventCreate); the library never creates,
  * waits on or destroys them.  Returns SA_ERR_INVALID_ARG if exactly one is NULL.
  */

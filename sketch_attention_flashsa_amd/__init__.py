@@ -25,7 +25,7 @@ _NORMS = {"history": SA_NORM_HISTORY, "prototype": SA_NORM_PROTOTYPE}
 
 EXPORTED = ("sa_forward", "sa_forward_workspace_size", "sa_forward_kernel_name", "sa_forward_fused_proj",
             "sa_forward_fused_proj_workspace_size", "sa_refine_forward", "sa_refine_workspace_size",
-            "sa_backward", "sa_backward_workspace_size",
+            "sa_backward", "sa_backward_workspace_size", "sa_stca_attention", "sa_stca_workspace_size",
             "sa_set_timing_events", "sa_status_string", "sa_last_error", "sa_version")
 
 
@@ -44,6 +44,15 @@ class SaProblem(ctypes.Structure):
         ("k_row_stride", ctypes.c_int64), ("v_row_stride", ctypes.c_int64),
         ("q_batch_stride", ctypes.c_int64),
         ("chunk_rows", ctypes.c_int32), ("flags", ctypes.c_int32),
+    ]
+
+
+class SaStcaProblem(ctypes.Structure):
+    """Mirror of ``sa_stca_problem`` in include/sketchattn.h."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("D", ctypes.c_int32), ("h", ctypes.c_int32),
+        ("total_rows", ctypes.c_int64), ("x_row_stride", ctypes.c_int64), ("scale", ctypes.c_float),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -85,6 +94,11 @@ def load_library(path: str | None = None):
     lib.sa_backward_workspace_size.restype = ctypes.c_size_t
     lib.sa_refine_workspace_size.argtypes = [pp, ctypes.c_int32, ctypes.c_int32]
     lib.sa_refine_workspace_size.restype = ctypes.c_size_t
+    sp = ctypes.POINTER(SaStcaProblem)
+    lib.sa_stca_attention.argtypes = [sp] + [vp] * 10 + [ctypes.c_size_t, vp]
+    lib.sa_stca_attention.restype = ctypes.c_int
+    lib.sa_stca_workspace_size.argtypes = [sp]
+    lib.sa_stca_workspace_size.restype = ctypes.c_size_t
     lib.sa_status_string.argtypes = [ctypes.c_int]
     lib.sa_status_string.restype = ctypes.c_char_p
     lib.sa_last_error.argtypes = []
@@ -370,6 +384,38 @@ def sa_backward(P, K, V, S, lse, dS, cu_offsets=None, lengths=None, mask=None, s
                          _stream_handle(dev))
     _check(st)
     return dP, dK, dV
+
+
+def sa_stca_attention(xt, X, Wq, Wk, Wv, cu_offsets, t_offsets, h: int, windows=None, scale: float | None = None,
+                      workspace=None, out=None):
+    """STCA single-query attention, reordered (appendix G.2.1), for every
+    target: xt [T, D] and X [rows, D] bf16, Wq, Wk, Wv [D, D] bf16 ([in,
+    out]), cu_offsets and t_offsets int32 [B+1] (user rows and user
+    targets), windows int32 [T, 2] or None.  Returns out [T, D] fp32."""
+    import torch
+    lib = load_library()
+    dev = xt.device
+    T, D = xt.shape
+    B = t_offsets.numel() - 1
+    xt, X, Wq, Wk, Wv = (t.contiguous() for t in (xt, X, Wq, Wk, Wv))
+    if windows is not None:
+        windows = windows.to(torch.int32).contiguous()
+    pb = SaStcaProblem(B=B, T=T, D=D, h=h, total_rows=X.shape[0], x_row_stride=0, scale=scale or 0.0, flags=0)
+    nws = int(lib.sa_stca_workspace_size(ctypes.byref(pb)))
+    if nws == 0:
+        _check(lib.sa_stca_attention(ctypes.byref(pb), *([None] * 10), 0, None))
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.float32, device=dev)
+    st = lib.sa_stca_attention(ctypes.byref(pb), _ptr(xt), _ptr(X), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(cu_offsets),
+                               _ptr(t_offsets), _ptr(windows), _ptr(out), _ptr(workspace), nws, _stream_handle(dev))
+    _check(st)
+    return out
+
+
+def sa_stca_workspace_size(pb) -> int:
+    return int(load_library().sa_stca_workspace_size(ctypes.byref(pb)))
 
 
 def sa_backward_workspace_size(pb) -> int:

@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "sa_internal.h"
@@ -459,6 +460,115 @@ size_t sa_forward_fused_proj_workspace_size(const sa_problem* pb, int32_t d_mode
     Plan pl;
     if (!pb || make_fused_plan(pb, d_model, &pl) != SA_OK) return 0;
     return pl.total;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of the STCA attention: W_Q and W_V transposed to [out][in], then
+// the block table.
+struct StcaPlan {
+    size_t off_wqt = 0, off_wvt = 0, off_table = 0, total = 0;
+    int grid = 0, dh = 0;
+    int64_t x_stride = 0;
+    float c = 0.f;
+};
+
+sa_status make_stca_plan(const sa_stca_problem* pb, StcaPlan* sp) {
+    if (!pb) return fail(SA_ERR_INVALID_ARG, "problem is NULL");
+    if (pb->flags != 0) return fail(SA_ERR_INVALID_ARG, "flags must be 0");
+    if (pb->B < 0 || pb->T < 0 || pb->total_rows < 0)
+        return fail(SA_ERR_INVALID_ARG, "B, T and total_rows must be >= 0 (got %d, %d, %lld)", pb->B, pb->T,
+                    (long long)pb->total_rows);
+    if (pb->D <= 0 || pb->h <= 0 || pb->D % pb->h != 0)
+        return fail(SA_ERR_INVALID_ARG, "D and h must be positive with h dividing D (got D=%d h=%d)", pb->D, pb->h);
+    const int dh = pb->D / pb->h;
+    if (pb->h % 2 != 0 || !sa::stca_supported(pb->D, dh))
+        return fail(SA_ERR_UNSUPPORTED, "STCA attention: D == 1024 with dh in {64, 128} (got D=%d h=%d)", pb->D,
+                    pb->h);
+    const int64_t xs = pb->x_row_stride == 0 ? pb->D : pb->x_row_stride;
+    if (xs < pb->D || xs % 8 != 0)
+        return fail(SA_ERR_INVALID_ARG, "x_row_stride must be 0 or a multiple of 8 that is >= D (got %lld)",
+                    (long long)pb->x_row_stride);
+    if (!isfinite(pb->scale) || pb->scale < 0.f) return fail(SA_ERR_INVALID_ARG, "scale must be finite and >= 0");
+    const int64_t chunks = ((int64_t)pb->T + sa::kStcaTargets - 1) / sa::kStcaTargets + pb->B;
+    const int64_t grid = (chunks * (pb->h / 2) + 7) / 8 * 8;
+    if (grid > (int64_t)1 << 30) return fail(SA_ERR_UNSUPPORTED, "too many targets and users for one launch");
+    sp->grid = (int)std::max<int64_t>(grid, 8);
+    sp->dh = dh;
+    sp->x_stride = xs;
+    sp->c = (pb->scale == 0.f ? 1.f / sqrtf((float)dh) : pb->scale) * sa::kLog2e;
+    const size_t dd = (size_t)pb->D * pb->D;
+    size_t off = 0;
+    sp->off_wqt = off;
+    off = align_up(off + 2 * dd);
+    sp->off_wvt = off;
+    off = align_up(off + 2 * dd);
+    sp->off_table = off;
+    off = align_up(off + 16 * (size_t)sp->grid);
+    sp->total = off;
+    return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sa_status sa_stca_attention(const sa_stca_problem* pb, const void* xt, const void* X, const void* Wq, const void* Wk,
+                            const void* Wv, const int32_t* cu_offsets, const int32_t* t_offsets,
+                            const int32_t* windows, float* out, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+    g_err[0] = 0;
+    StcaPlan sp;
+    sa_status st = make_stca_plan(pb, &sp);
+    if (st != SA_OK) return st;
+    if (pb->T == 0) return SA_OK;
+    if (!xt || !Wq || !Wk || !Wv || !t_offsets || !out)
+        return fail(SA_ERR_INVALID_ARG, "xt, Wq, Wk, Wv, t_offsets and out must be non-NULL");
+    if (pb->B > 0 && (!cu_offsets || (!X && pb->total_rows > 0)))
+        return fail(SA_ERR_INVALID_ARG, "cu_offsets (and X when total_rows > 0) must be non-NULL");
+    if (!aligned(xt, 16) || !aligned(X, 16) || !aligned(Wq, 16) || !aligned(Wk, 16) || !aligned(Wv, 16) ||
+        !aligned(out, 16) || !aligned(windows, 4) || !aligned(cu_offsets, 4) || !aligned(t_offsets, 4))
+        return fail(SA_ERR_INVALID_ARG, "xt, X, Wq, Wk, Wv and out must be 16-byte aligned");
+    if (!workspace || workspace_bytes < sp.total)
+        return fail(SA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", sp.total, workspace_bytes);
+    if (!aligned(workspace, kAlign)) return fail(SA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+    unsigned char* ws = (unsigned char*)workspace;
+    sa::StcaArgs a{};
+    a.xt = (const sa::bf16*)xt;
+    a.X = (const sa::bf16*)X;
+    a.x_stride = sp.x_stride;
+    a.wqt = (const sa::bf16*)(ws + sp.off_wqt);
+    a.wk = (const sa::bf16*)Wk;
+    a.wvt = (const sa::bf16*)(ws + sp.off_wvt);
+    a.cu = cu_offsets;
+    a.tcu = t_offsets;
+    a.win = windows;
+    a.out = out;
+    a.table = (int4*)(ws + sp.off_table);
+    a.B = pb->B;
+    a.T = pb->T;
+    a.h = pb->h;
+    a.D = pb->D;
+    a.grid = sp.grid;
+    a.c = sp.c;
+
+    const hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
+    g_ev_start = g_ev_stop = nullptr;
+    sa::TransposeArgs ta{};
+    ta.mat[ta.n++] = {(const sa::bf16*)Wq, (sa::bf16*)(ws + sp.off_wqt), pb->D, pb->D};
+    ta.mat[ta.n++] = {(const sa::bf16*)Wv, (sa::bf16*)(ws + sp.off_wvt), pb->D, pb->D};
+    hipError_t e;
+    if ((e = sa::launch_transpose(ta, stream)) != hipSuccess) return hip_fail(e, "weight transpose");
+    if ((e = sa::launch_stca(a, sp.dh, stream, ev0, ev1)) != hipSuccess) return hip_fail(e, "STCA attention");
+    return SA_OK;
+}
+
+size_t sa_stca_workspace_size(const sa_stca_problem* pb) {
+    StcaPlan sp;
+    return make_stca_plan(pb, &sp) == SA_OK ? sp.total : 0;
 }
 
 }  // extern "C"

@@ -82,6 +82,45 @@ __device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t
         : "memory");
 }
 
+// Direct-to-LDS load as dma16s, without the non-temporal hint: for rows that
+// several blocks read in turn, which should stay in the caches.
+__device__ __forceinline__ void dma16c(const void* base, uint32_t voff, uint32_t lds) {
+    const uint64_t bb = (uint64_t)(uintptr_t)base;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(bb >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bb);
+    const uint64_t ub = ((uint64_t)hi << 32) | (uint64_t)lo;
+    base = (const void*)(uintptr_t)ub;
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(base), "s"(lds)
+        : "memory");
+}
+
+// acc *= f in place, for an accumulator kept in AGPRs (the MFMA accumulator
+// registers): each element goes through one VGPR and back, so the common
+// path never copies the accumulator.
+__device__ __forceinline__ void scale_in_place_acc(f32x4& acc, float f) {
+    float t;
+    asm volatile(
+        "v_accvgpr_read_b32 %4, %0\n\t"
+        "v_mul_f32 %4, %5, %4\n\t"
+        "v_accvgpr_write_b32 %0, %4\n\t"
+        "v_accvgpr_read_b32 %4, %1\n\t"
+        "v_mul_f32 %4, %5, %4\n\t"
+        "v_accvgpr_write_b32 %1, %4\n\t"
+        "v_accvgpr_read_b32 %4, %2\n\t"
+        "v_mul_f32 %4, %5, %4\n\t"
+        "v_accvgpr_write_b32 %2, %4\n\t"
+        "v_accvgpr_read_b32 %4, %3\n\t"
+        "v_mul_f32 %4, %5, %4\n\t"
+        "v_accvgpr_write_b32 %3, %4"
+        : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "=&v"(t)
+        : "v"(f));
+}
+
 // acc *= f in place.  A tied-operand ALU asm statement keeps the accumulator
 // in the same registers on the (rare) rescale path, so the common path does
 // not pay register copies to merge two versions of it.

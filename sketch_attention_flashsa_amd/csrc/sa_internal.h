@@ -286,6 +286,26 @@ bool bwd_supported(int dh, int m);
 void bwd_dp_shape(int m, int H, int* NH, int* PB);
 hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
 
+// STCA single-query attention, reordered (sa_stca.hip).
+constexpr int kStcaTargets = 16;     // targets per block (one MFMA column tile)
+struct StcaArgs {
+    const bf16* xt;          // [T][D] target vectors
+    const bf16* X;           // history rows, x_stride elements apart
+    int64_t x_stride;
+    const bf16* wqt;         // [D][D] W_Q transposed ([out][in])
+    const bf16* wk;          // [D][D] W_K as given ([in][out])
+    const bf16* wvt;         // [D][D] W_V transposed
+    const int32_t* cu;       // [B+1] rows of each user
+    const int32_t* tcu;      // [B+1] targets of each user
+    const int32_t* win;      // [T][2] per-target row window, or nullptr
+    float* out;              // [T][D]
+    int4* table;             // [grid] block -> (user, target chunk, head pair); user -1 = idle block
+    int32_t B, T, h, D, grid;
+    float c;                 // score scale * log2(e)
+};
+bool stca_supported(int D, int dh);
+hipError_t launch_stca(const StcaArgs& a, int dh, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+
 bool fused_supported(int d_model, int m, int dh);
 int fused_groups(int H);     // blocks per row range
 hipError_t launch_fused(const FusedArgs& a, hipStream_t s);

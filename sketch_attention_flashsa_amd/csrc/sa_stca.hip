@@ -1,0 +1,480 @@
+// sa_stca.hip -- STCA single-query target-to-history cross attention with the
+// reordering of appendix G.2.1 of the SequenceO1 paper, in one kernel:
+//     q = x W_Q,  u_h = q_h W_K[:, h]^T,  alpha = softmax(u_h X^T / sqrt(dh)),
+//     o_h = (alpha X) W_V[:, h]
+// for every target of every user of a packed batch; a user's targets share
+// its history rows (the multi-request batching of section 4.2), so each block
+// streams the rows once for 16 targets x 2 heads.
+//
+// Block = (user, head pair, 16 targets): 32 query columns, one 16-column MFMA
+// tile per head.  Four waves, one per SIMD; wave w owns channels
+// [w D/4, (w+1) D/4) of the D-wide rows:
+//   * prologue: q for the 16 targets and both heads on MFMA (shared through
+//     LDS), then u^T over the wave's channels (MFMA with W_K), kept in
+//     registers as the score product's B operand;
+//   * loop over 32-row tiles of the rows the block's targets see: the wave's
+//     slice of every row streams through the wave's own two-stage LDS ring by
+//     direct-to-LDS loads (no other wave reads it, so the ring needs no
+//     barrier); partial scores over the wave's channels (MFMA) go to a
+//     double-buffered LDS exchange; after the tile's one block barrier every
+//     wave adds the other three partials to its own (in wave order) and runs
+//     the online softmax on the full scores (lazy maximum, as in the SA
+//     streaming kernel).  The four waves' sums differ only in rounding, and
+//     each wave normalises its channels with its own running sum, so every
+//     output slice is a weighted mean under one consistent set of weights;
+//     alpha X over the wave's channels accumulates on MFMA from transposed
+//     LDS reads of the same ring stage;
+//   * epilogue: (alpha X) W_V over the wave's channels on MFMA, the four
+//     waves' partial products added in wave order through LDS, fp32 out.
+// Ring rows are XOR-swizzled per 16-byte chunk so that the row reads of the
+// score product and the transposed reads of the aggregation are both free of
+// bank conflicts.  A sa_stca_prep_kernel launch first builds the block table
+// from the target offsets on the device (no host reads) and zeroes the
+// outputs of targets outside every user.
+#include "sa_device.h"
+
+namespace sa {
+
+using namespace dev;
+
+namespace {
+
+constexpr int kStcaWaves = 4;
+// fast-loop range of a lane's tile sum of weights 2^(s c) (maximum fixed at 0)
+constexpr float kStcaHiBound = 4294967296.0f;      // 2^32
+constexpr float kStcaLoBound = 2.3283064365e-10f;  // 2^-32
+
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ f32x4 lds_ld4(uint32_t a) { return *(const lds_f32x4*)(uintptr_t)a; }
+__device__ __forceinline__ void lds_st4(uint32_t a, f32x4 v) { *(lds_f32x4*)(uintptr_t)a = v; }
+__device__ __forceinline__ bf16x8 lds_ld8(uint32_t a) { return *(const lds_bf16x8*)(uintptr_t)a; }
+__device__ __forceinline__ void lds_st_b4(uint32_t a, bf16x4 v) { *(lds_bf16x4*)(uintptr_t)a = v; }
+
+// 16-byte chunk swizzle of a ring row (a function of row % 8): rows r..r+7
+// take 8 distinct chunks of a 128-byte bank window, and rows 4k..4k+3 take 4
+// distinct 32-byte chunk pairs
+__device__ __forceinline__ int stca_swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) { return __builtin_convertvector(v, bf16x4); }
+
+}  // namespace
+
+template <int D, int DH>
+__global__ __launch_bounds__(256, 1) void sa_stca_kernel(StcaArgs a) {
+    constexpr int NW = kStcaWaves;
+    constexpr int DW = D / NW;             // channels per wave
+    constexpr int KC = DW / 32;            // 32-channel k-steps of the score product
+    constexpr int DB = DW / 16;            // 16-channel row blocks of the aggregate
+    constexpr int ROWB = DW * 2;           // bytes of a wave's slice of one row
+    constexpr int STAGE = 32 * ROWB;       // bytes of one 32-row ring stage
+    constexpr int OPS = STAGE / 1024;      // direct-to-LDS ops per stage
+    constexpr int ET = DH / 16;            // 16-row blocks of one head's dh outputs
+    constexpr int EK = DH / 32;            // k-steps over dh
+    constexpr int QK = D / 32;             // k-steps of the query projection
+    constexpr int QT = ET / 2;             // query-projection (and output) tiles per wave: 2 heads x ET over 4 waves
+    constexpr int QS = DH + 8;             // LDS row stride (elements) of the shared queries
+    static_assert(DW == 256 && DH % 32 == 0 && OPS * 1024 == STAGE, "compiled for 256 channels per wave");
+    static_assert(2 * 16 * QS * 2 <= NW * 4 * 64 * 16, "queries fit one exchange buffer");
+
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[NW][2][STAGE];
+    __shared__ __attribute__((aligned(1024))) f32x4 xchg[2][NW][4][64];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, l16 = lane & 15;
+
+    // block -> (user, target chunk, head pair): XCD x (blockIdx % 8) takes the
+    // x-th contiguous run of the table, so a user's blocks share one L2
+    const int G = gridDim.x;
+    const int Lb = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
+    const int4 ent = a.table[Lb];
+    const int b = __builtin_amdgcn_readfirstlane(ent.x);
+    if (b < 0) return;
+    const int chunk = __builtin_amdgcn_readfirstlane(ent.y);
+    const int hp = __builtin_amdgcn_readfirstlane(ent.z);
+    const int64_t u0 = a.cu[b];
+    const int nu = a.cu[b + 1] - (int)u0;
+    const int tb = a.tcu[b] + chunk * kStcaTargets;
+    const int nt = min(kStcaTargets, a.tcu[b + 1] - tb);
+
+    // this lane's target (column l16) and its window; the block streams the
+    // union of its targets' windows
+    const bool tv = l16 < nt;
+    const int tl = tb + (tv ? l16 : 0);
+    int wlo = 0, whi = nu;
+    if (a.win != nullptr) {
+        wlo = min(max(a.win[2 * (int64_t)tl], 0), nu);
+        whi = max(wlo, min(max(a.win[2 * (int64_t)tl + 1], 0), nu));
+    }
+    int ulo = (tv && whi > wlo) ? wlo : nu, uhi = (tv && whi > wlo) ? whi : 0;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+        ulo = min(ulo, __shfl_xor(ulo, o, 64));
+        uhi = max(uhi, __shfl_xor(uhi, o, 64));
+    }
+    const int r_lo = __builtin_amdgcn_readfirstlane(ulo);
+    const int nrows = max(0, __builtin_amdgcn_readfirstlane(uhi) - r_lo);
+    const int qlo = tv ? wlo - r_lo : 0, qhi = tv ? whi - r_lo : 0;   // relative to the block's first row
+    const int ntiles = (nrows + 31) / 32;
+
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void*)&ring[0][0][0];
+    const uint32_t my_ring = ring_lds + (uint32_t)(wave * 2 * STAGE);
+    const uint32_t xch_lds = (uint32_t)(uintptr_t)(lds_void*)&xchg[0][0][0][0];
+    const uint32_t qs_lds = xch_lds + (uint32_t)(NW * 4 * 64 * 16);   // exchange buffer 1, free until tile 1
+
+    // ---- prologue 1: Qm^T[e][t] = sum_k W_Q^T[hh dh + e][k] x_t[k] for
+    // tiles (head hsel, 16-row block et) = wave * QT + i
+    {
+        f32x4 qa[QT];
+        const bf16* wrow[QT];
+#pragma unroll
+        for (int i = 0; i < QT; ++i) {
+            qa[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            const int tix = wave * QT + i, hh = 2 * hp + tix / ET, et = tix % ET;
+            wrow[i] = a.wqt + (int64_t)(hh * DH + 16 * et + l16) * D + 8 * g;
+        }
+        const bf16* xrow = a.xt + (int64_t)tl * D + 8 * g;
+#pragma unroll 4
+        for (int kk = 0; kk < QK; ++kk) {
+            const bf16x8 xb = *(const bf16x8*)(xrow + 32 * kk);
+#pragma unroll
+            for (int i = 0; i < QT; ++i) qa[i] = mfma(*(const bf16x8*)(wrow[i] + 32 * kk), xb, qa[i]);
+        }
+        // rows e = 16 et + 4 g + r of column t -> Qs[hsel][t][e] (bf16)
+#pragma unroll
+        for (int i = 0; i < QT; ++i) {
+            const int tix = wave * QT + i, hsel = tix / ET, et = tix % ET;
+            lds_st_b4(qs_lds + (uint32_t)(((hsel * 16 + l16) * QS + 16 * et + 4 * g) * 2), to_bf16x4(qa[i]));
+        }
+    }
+    __syncthreads();
+
+    // ---- prologue 2: u^T[d][t] = sum_e W_K[d][hh dh + e] Qm[t][e] over the
+    // wave's channels d, both heads; staged through the wave's own ring (as
+    // [hsel][t][channel], rows swizzled by t) into the score B operand
+    bf16x8 uf[2][KC];
+    {
+#pragma unroll
+        for (int hsel = 0; hsel < 2; ++hsel) {
+            const int hh = 2 * hp + hsel;
+            bf16x8 qb[EK];
+#pragma unroll
+            for (int ek = 0; ek < EK; ++ek)
+                qb[ek] = lds_ld8(qs_lds + (uint32_t)(((hsel * 16 + l16) * QS + 32 * ek + 8 * g) * 2));
+#pragma unroll 4
+            for (int dt = 0; dt < DB; ++dt) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                const bf16* wk = a.wk + (int64_t)(wave * DW + 16 * dt + l16) * D + hh * DH + 8 * g;
+#pragma unroll
+                for (int ek = 0; ek < EK; ++ek) acc = mfma(*(const bf16x8*)(wk + 32 * ek), qb[ek], acc);
+                const int row = hsel * 16 + l16, ck = (2 * dt + (g >> 1)) ^ (l16 & 7);
+                lds_st_b4(my_ring + (uint32_t)(row * ROWB + ck * 16 + (g & 1) * 8), to_bf16x4(acc));
+            }
+        }
+#pragma unroll
+        for (int hsel = 0; hsel < 2; ++hsel)
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const int row = hsel * 16 + l16, ck = (4 * kc + g) ^ (l16 & 7);
+                uf[hsel][kc] = lds_ld8(my_ring + (uint32_t)(row * ROWB + ck * 16));
+            }
+        // the ring is about to be refilled
+        wait_lgkm0();
+    }
+
+    // ---- streaming
+    const int64_t xrow = a.x_stride * 2;
+    const unsigned char* Xg = (const unsigned char*)a.X + ((u0 + r_lo) * a.x_stride + (int64_t)wave * DW) * 2;
+    auto issue = [&](int t) {
+        const uint32_t dst = my_ring + (uint32_t)((t & 1) * STAGE);
+        const unsigned char* src = Xg + (int64_t)t * 32 * xrow;
+        const int last = nrows - 1 - t * 32;   // rows past the block's end re-read its last row
+#pragma unroll
+        for (int d = 0; d < OPS; ++d) {
+            const int row = 2 * d + (lane >> 5);          // one op = two 512-byte rows
+            const int ck = (lane & 31) ^ stca_swz(row);
+            const int rr = min(row, last);
+            dma16c(src, (uint32_t)(rr * (uint32_t)xrow + ck * 16), __builtin_amdgcn_readfirstlane(dst + d * 1024));
+        }
+    };
+
+    // per-lane LDS offsets inside a stage
+    const int sw = stca_swz(l16);
+    const uint32_t a_even = (uint32_t)(l16 * ROWB + 16 * (g ^ (sw & 3)) + 64 * (sw >> 2));
+    const uint32_t a_odd = (uint32_t)(l16 * ROWB + 16 * (g ^ (sw & 3)) - 64 * (sw >> 2));
+    uint32_t tb4[4];   // transposed reads: row 4g + kq, channels 16 db + 4 q
+    {
+        const int kq = l16 >> 2, q = l16 & 3, row = 4 * g + kq;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            tb4[m] = (uint32_t)(row * ROWB + 32 * (m ^ kq) + 16 * ((q >> 1) ^ (g & 1)) + 8 * (q & 1));
+    }
+    uint32_t xo[3];    // exchange slots of the other three waves, in wave order
+#pragma unroll
+    for (int k = 0; k < 3; ++k) xo[k] = (uint32_t)((k + (k >= wave ? 1 : 0)) * 4 * 64 * 16 + lane * 16);
+
+    // Softmax state per lane (head sb, target l16), in log2 units.  The fast
+    // loop keeps the maximum at M = 0: weights 2^(s c) are used as long as a
+    // lane's tile sum stays within [2^-32, 2^32] (scores of usual scale are far
+    // inside), so the accumulator is only ever written by MFMAs.  A wave whose
+    // tile falls outside that range (or holds NaN or Inf) finishes the block in
+    // the exact loop: running maximum, rescaled accumulator.  Both loops meet
+    // the block barrier once per tile at the same point, so waves may switch
+    // independently.
+    float Mc[2] = {0.f, 0.f}, Zs[2] = {0.f, 0.f};
+    f32x4 acc[2][DB];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[sb][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    const float c = a.c;
+
+    i16x4 lo[DB], hi[DB];
+    f32x4 tot[2][2];
+    // DMA, partial scores, transposed operands and the exchange of tile t,
+    // ending with the full scores in tot
+    auto stage = [&](int t) {
+        // the last tile's transposed reads are done, so slot (t + 1) & 1 is free
+        wait_lgkm0();
+        if (t + 1 < ntiles) {
+            issue(t + 1);
+            wait_vm<OPS>();
+        } else {
+            wait_vm<0>();
+        }
+        const uint32_t st = my_ring + (uint32_t)((t & 1) * STAGE);
+        f32x4 s[2][2];
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            const uint32_t ad = st + ((kc & 1) ? a_odd : a_even) + 64 * kc;
+            const bf16x8 x0 = lds_ld8(ad);
+            const bf16x8 x1 = lds_ld8(ad + 16 * ROWB);
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                const f32x4 z0 = kc == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : s[0][sb];
+                const f32x4 z1 = kc == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : s[1][sb];
+                s[0][sb] = mfma(x0, uf[sb][kc], z0);
+                s[1][sb] = mfma(x1, uf[sb][kc], z1);
+            }
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const uint32_t ad = st + tb4[db & 3] + 128 * (db >> 2);
+            lo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)ad);
+            hi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(ad + 16 * ROWB));
+        }
+        const uint32_t xb = xch_lds + (uint32_t)((t & 1) * NW * 4 * 64 * 16);
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+            lds_st4(xb + (uint32_t)((wave * 4 + r4) * 64 * 16 + lane * 16), s[r4 >> 1][r4 & 1]);
+        wait_lgkm0();
+        block_barrier();
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 l0 = lds_ld4(xb + xo[0] + r4 * 64 * 16);
+            const f32x4 l1 = lds_ld4(xb + xo[1] + r4 * 64 * 16);
+            const f32x4 l2 = lds_ld4(xb + xo[2] + r4 * 64 * 16);
+            tot[r4 >> 1][r4 & 1] = ((s[r4 >> 1][r4 & 1] + l0) + l1) + l2;
+        }
+    };
+    // (alpha X)^T over the wave's channels += X^T p^T
+    auto aggregate = [&](const bf16x8 (&pk)[2]) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            union {
+                i16x4 h[2];
+                bf16x8 v;
+            } vt;
+            vt.h[0] = lo[db];
+            vt.h[1] = hi[db];
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) acc[sb][db] = mfma(vt.v, pk[sb], acc[sb][db]);
+        }
+    };
+    // rows of tile t inside the lane's window: bit j <-> row tok_of(g, j)
+    auto valid_bits = [&](int t) {
+        uint32_t vj = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = t * 32 + tok_of(g, j);
+            vj |= (r >= qlo && r < qhi) ? (1u << j) : 0u;
+        }
+        return vj;
+    };
+
+    if (ntiles > 0) issue(0);
+    int t = 0;
+    for (; t < ntiles; ++t) {
+        stage(t);
+        float p[2][8];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) p[sb][j] = __builtin_amdgcn_exp2f(tot[j >> 2][sb][j & 3] * c);
+        const bool full = t * 32 >= qlo && t * 32 + 32 <= qhi;
+        uint32_t vj = 0xffu;
+        if (!__all(full)) {
+            vj = valid_bits(t);
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) p[sb][j] = ((vj >> j) & 1) ? p[sb][j] : 0.f;
+        }
+        bf16x8 pk[2];
+        float zt[2];
+        bool fits = true;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const bf16x2 q0 = pack2(p[sb][0], p[sb][1]), q1 = pack2(p[sb][2], p[sb][3]);
+            const bf16x2 q2 = pack2(p[sb][4], p[sb][5]), q3 = pack2(p[sb][6], p[sb][7]);
+            pk[sb] = cat8(q0, q1, q2, q3);
+            zt[sb] = dot2sum(q3, dot2sum(q2, dot2sum(q1, dot2sum(q0, 0.f))));
+            // false for NaN and Inf too
+            fits = fits && zt[sb] <= kStcaHiBound && (zt[sb] >= kStcaLoBound || vj == 0u);
+        }
+        if (__builtin_expect(!__all(fits), 0)) break;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) Zs[sb] += zt[sb];
+        aggregate(pk);
+    }
+    // exact loop, entered in the middle of tile t (its scores are in tot)
+    for (bool resume = true; t < ntiles; ++t, resume = false) {
+        if (!resume) stage(t);
+        const uint32_t vj = valid_bits(t);
+        bf16x8 pk[2];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            float x[8];
+            float tm = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                x[j] = ((vj >> j) & 1) ? tot[j >> 2][sb][j & 3] * c : -INFINITY;
+                tm = fmaxf(tm, x[j]);
+            }
+            tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
+            tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+            // with no weight accumulated yet the maximum may also move down
+            const float Mold = Mc[sb];
+            const float Mnew = Zs[sb] > 0.f ? fmaxf(Mold, tm) : tm;
+            const float f = (Zs[sb] > 0.f && Mnew != Mold) ? __builtin_amdgcn_exp2f(Mold - Mnew) : 1.f;
+            float pe[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pe[j] = ((vj >> j) & 1) ? __builtin_amdgcn_exp2f(x[j] - Mnew) : 0.f;
+            const bf16x2 q0 = pack2(pe[0], pe[1]), q1 = pack2(pe[2], pe[3]);
+            const bf16x2 q2 = pack2(pe[4], pe[5]), q3 = pack2(pe[6], pe[7]);
+            pk[sb] = cat8(q0, q1, q2, q3);
+            Zs[sb] = fmaf(Zs[sb], f, dot2sum(q3, dot2sum(q2, dot2sum(q1, dot2sum(q0, 0.f)))));
+            if (tm != -INFINITY || Zs[sb] > 0.f) Mc[sb] = Mnew;
+            if (f != 1.f) {
+#pragma unroll
+                for (int db = 0; db < DB; ++db) scale_in_place_acc(acc[sb][db], f);
+            }
+        }
+        aggregate(pk);
+    }
+    wait_lgkm0();
+
+    // ---- epilogue: y = acc / Z, o^T[e][t] = sum_d W_V^T[hh dh + e][d] y[t][d]
+    // over the wave's channels; k-slot j of chunk kc <-> channel 32 kc + tok_of(g, j)
+    f32x4 ov[2][ET];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+        float z = Zs[sb];
+        z += __shfl_xor(z, 16, 64);
+        z += __shfl_xor(z, 32, 64);
+        const float inv = z > 0.f ? 1.f / z : 0.f;
+        bf16x8 yb[KC];
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            const f32x4 e0 = acc[sb][2 * kc] * inv, e1 = acc[sb][2 * kc + 1] * inv;
+            yb[kc] = cat8(pack2(e0[0], e0[1]), pack2(e0[2], e0[3]), pack2(e1[0], e1[1]), pack2(e1[2], e1[3]));
+        }
+        const int hh = 2 * hp + sb;
+#pragma unroll
+        for (int et = 0; et < ET; ++et) {
+            f32x4 o = {0.f, 0.f, 0.f, 0.f};
+            const bf16* wv = a.wvt + (int64_t)(hh * DH + 16 * et + l16) * D + wave * DW + 4 * g;
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const bf16x4 w0 = *(const bf16x4*)(wv + 32 * kc);
+                const bf16x4 w1 = *(const bf16x4*)(wv + 32 * kc + 16);
+                o = mfma(__builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7), yb[kc], o);
+            }
+            ov[sb][et] = o;
+        }
+    }
+    // the four waves' partial products, added in wave order (each wave's own
+    // ring holds its partials; its loop is over)
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int et = 0; et < ET; ++et) lds_st4(my_ring + (uint32_t)(((sb * ET + et) * 64 + lane) * 16), ov[sb][et]);
+    wait_lgkm0();
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < QT; ++i) {
+        const int j = wave * QT + i, sb = j / ET, et = j % ET;
+        const uint32_t off = (uint32_t)((j * 64 + lane) * 16);
+        f32x4 r = lds_ld4(ring_lds + off);
+#pragma unroll
+        for (int w = 1; w < NW; ++w) r = r + lds_ld4(ring_lds + (uint32_t)(w * 2 * STAGE) + off);
+        if (tv) *(f32x4*)(a.out + (int64_t)tl * D + (2 * hp + sb) * DH + 16 * et + 4 * g) = r;
+    }
+}
+
+// One block: the block table (user b gets ceil(targets_b / 16) x (h / 2)
+// consecutive entries, in user order) and zeros for targets outside every user.
+__global__ __launch_bounds__(1024) void sa_stca_prep_kernel(StcaArgs a) {
+    __shared__ int scan[1024];
+    const int tid = threadIdx.x;
+    const int hpn = a.h / 2;
+    int running = 0;
+    for (int base = 0; base < a.B; base += 1024) {
+        const int b = base + tid;
+        int n = 0;
+        if (b < a.B) {
+            const int nT = a.tcu[b + 1] - a.tcu[b];
+            n = nT > 0 ? (nT + kStcaTargets - 1) / kStcaTargets * hpn : 0;
+        }
+        scan[tid] = n;
+        __syncthreads();
+        for (int o = 1; o < 1024; o <<= 1) {
+            const int v = tid >= o ? scan[tid - o] : 0;
+            __syncthreads();
+            scan[tid] += v;
+            __syncthreads();
+        }
+        const int start = running + scan[tid] - n;
+        for (int k = 0; k < n; ++k)
+            if (start + k < a.grid) a.table[start + k] = make_int4(b, k / hpn, k % hpn, 0);
+        running += scan[1023];
+        __syncthreads();
+    }
+    for (int L = running + tid; L < a.grid; L += 1024) a.table[L] = make_int4(-1, 0, 0, 0);
+    const int t_lo = a.B > 0 ? min(max(a.tcu[0], 0), a.T) : a.T;
+    const int t_hi = a.B > 0 ? min(max(a.tcu[a.B], t_lo), a.T) : a.T;
+    const int d4 = a.D / 4;
+    for (int64_t i = tid; i < (int64_t)a.T * d4; i += 1024) {
+        const int t = (int)(i / d4);
+        if (t < t_lo || t >= t_hi) ((f32x4*)a.out)[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+bool stca_supported(int D, int dh) { return D == 1024 && (dh == 64 || dh == 128); }
+
+hipError_t launch_stca(const StcaArgs& a, int dh, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    hipLaunchKernelGGL(sa_stca_prep_kernel, dim3(1), dim3(1024), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
+    if (dh == 64) hipLaunchKernelGGL((sa_stca_kernel<1024, 64>), dim3(a.grid), dim3(256), 0, s, a);
+    if (dh == 128) hipLaunchKernelGGL((sa_stca_kernel<1024, 128>), dim3(a.grid), dim3(256), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
+    return hipSuccess;
+}
+
+}  // namespace sa

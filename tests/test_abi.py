@@ -220,3 +220,43 @@ def test_fused_two_pass_shapes():
         assert lib.sa_forward_fused_proj_workspace_size(ctypes.byref(p), dm) == 0
     # refinement keeps to the on-chip shapes
     assert lib.sa_refine_workspace_size(ctypes.byref(sa.make_problem(4, 1, 1024, 128, 1000, dtype="bf16")), 128, 2) == 0
+
+
+def test_stca_entry_validation():
+    lib = sa.load_library()
+
+    def P(B=64, T=2560, D=1024, h=16, rows=65536, stride=0, scale=0.0, flags=0):
+        return sa.SaStcaProblem(B=B, T=T, D=D, h=h, total_rows=rows, x_row_stride=stride, scale=scale, flags=flags)
+
+    pb = P()
+    n = lib.sa_stca_workspace_size(ctypes.byref(pb))
+    # W_Q^T and W_V^T (bf16) plus a 16-byte block-table entry per block
+    grid = ((2560 // 16 + 64) * 8 + 7) // 8 * 8
+    assert n >= 2 * 1024 * 1024 * 2 + 16 * grid
+    bad = [(P(D=512, h=8), sa.SA_ERR_UNSUPPORTED), (P(h=32), sa.SA_ERR_UNSUPPORTED),
+           (P(h=15), sa.SA_ERR_INVALID_ARG), (P(B=-1), sa.SA_ERR_INVALID_ARG), (P(T=-3), sa.SA_ERR_INVALID_ARG),
+           (P(stride=1000), sa.SA_ERR_INVALID_ARG), (P(stride=1028), sa.SA_ERR_INVALID_ARG),
+           (P(scale=float("nan")), sa.SA_ERR_INVALID_ARG), (P(flags=1), sa.SA_ERR_INVALID_ARG)]
+    for p, code in bad:
+        assert lib.sa_stca_workspace_size(ctypes.byref(p)) == 0
+        st = lib.sa_stca_attention(ctypes.byref(p), *([FAKE] * 10), 1 << 30, None)
+        assert st == code, (st, sa.sa_last_error())
+    assert lib.sa_stca_workspace_size(ctypes.byref(P(h=8))) > 0            # dh = 128
+    assert lib.sa_stca_workspace_size(ctypes.byref(P(stride=2048))) > 0    # rows 2048 elements apart
+    # required pointers and workspace: rejected before any GPU work; T == 0 is a no-op
+    st = lib.sa_stca_attention(ctypes.byref(pb), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, n, None)
+    assert st == sa.SA_ERR_INVALID_ARG and "t_offsets" in sa.sa_last_error()
+    st = lib.sa_stca_attention(ctypes.byref(pb), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, n - 1,
+                               None)
+    assert st == sa.SA_ERR_WORKSPACE
+    assert lib.sa_stca_attention(ctypes.byref(P(T=0)), *([None] * 10), 0, None) == sa.SA_OK
+
+
+def test_stca_problem_struct_matches_header():
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct sa_stca_problem \{(.*?)\} sa_stca_problem;", text, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"(int32_t|int64_t|float)\s+([\w, ]+);", body)
+    assert [n.strip() for _, grp in fields for n in grp.split(",")] == [f[0] for f in sa.SaStcaProblem._fields_]
+    ctypes_of = {"int32_t": ctypes.c_int32, "int64_t": ctypes.c_int64, "float": ctypes.c_float}
+    assert [ctypes_of[t] for t, grp in fields for _ in grp.split(",")] == [f[1] for f in sa.SaStcaProblem._fields_]
