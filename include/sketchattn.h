@@ -299,8 +299,10 @@ size_t sa_refine_workspace_size(const sa_problem* pb, int32_t d_model, int32_t n
  *     u      = (x W_Q[:, c]) W_K[:, c]^T          [D]
  *     alpha  = softmax(scale * u X^T)             over the target's rows
  *     out[c] = (alpha X) W_V[:, c]                [dh]
- * This entry does that for every target of a packed ragged batch in one
- * fused kernel (plus a weight transpose and a small setup launch): the
+ * This entry does that for every target of a packed ragged batch: q = x W_Q
+ * for all targets (one GEMM), then one fused attention kernel that forms u,
+ * the weights and alpha X on chip, then the per-head products with W_V (one
+ * batched GEMM); plus a weight transpose and a small setup launch.  The
  * targets of one user share the user's rows (the multi-request batching of
  * section 4.2), so each pass over a user's rows serves 16 of its targets for
  * two heads.  The products run on MFMA in bf16 with fp32 accumulation; q and
@@ -359,7 +361,8 @@ size_t sa_stca_workspace_size(const sa_stca_problem* pb);
  * two-pass shapes, before the key projection) and `stop` immediately after
  * it, then forgets both; the next sa_refine_forward or sa_backward call
  * records them before its first and after its last launch; the next
- * sa_stca_attention call records them around its fused attention kernel.
+ * sa_stca_attention call records them around its launches after the weight
+ * transpose (query GEMM, attention, output GEMM).
  * NULL, NULL clears a pending request.  The
  * events belong to the caller (hipEventCreate); the library never creates,
  * waits on or destroys them.  Returns SA_ERR_INVALID_ARG if exactly one is NULL.

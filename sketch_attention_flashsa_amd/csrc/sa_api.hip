@@ -466,10 +466,10 @@ size_t sa_forward_fused_proj_workspace_size(const sa_problem* pb, int32_t d_mode
 
 namespace {
 
-// Workspace of the STCA attention: W_Q and W_V transposed to [out][in], then
-// the block table.
+// Workspace of the STCA attention: W_Q and W_V transposed to [out][in], the
+// block table, the queries q = x W_Q [T][D] and alpha X [T][h][D] (bf16).
 struct StcaPlan {
-    size_t off_wqt = 0, off_wvt = 0, off_table = 0, total = 0;
+    size_t off_wqt = 0, off_wvt = 0, off_table = 0, off_q = 0, off_y = 0, total = 0;
     int grid = 0, dh = 0;
     int64_t x_stride = 0;
     float c = 0.f;
@@ -507,6 +507,10 @@ sa_status make_stca_plan(const sa_stca_problem* pb, StcaPlan* sp) {
     off = align_up(off + 2 * dd);
     sp->off_table = off;
     off = align_up(off + 16 * (size_t)sp->grid);
+    sp->off_q = off;
+    off = align_up(off + 2 * (size_t)pb->T * pb->D);
+    sp->off_y = off;
+    off = align_up(off + 2 * (size_t)pb->T * pb->h * pb->D);
     sp->total = off;
     return SA_OK;
 }
@@ -536,33 +540,65 @@ sa_status sa_stca_attention(const sa_stca_problem* pb, const void* xt, const voi
     if (!aligned(workspace, kAlign)) return fail(SA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
 
     unsigned char* ws = (unsigned char*)workspace;
+    const sa::bf16* wqt = (const sa::bf16*)(ws + sp.off_wqt);
+    const sa::bf16* wvt = (const sa::bf16*)(ws + sp.off_wvt);
+    sa::bf16* q = (sa::bf16*)(ws + sp.off_q);
+    sa::bf16* y = (sa::bf16*)(ws + sp.off_y);
+    const int D = pb->D, h = pb->h, dh = sp.dh, T = pb->T;
     sa::StcaArgs a{};
-    a.xt = (const sa::bf16*)xt;
     a.X = (const sa::bf16*)X;
     a.x_stride = sp.x_stride;
-    a.wqt = (const sa::bf16*)(ws + sp.off_wqt);
+    a.qm = q;
     a.wk = (const sa::bf16*)Wk;
-    a.wvt = (const sa::bf16*)(ws + sp.off_wvt);
     a.cu = cu_offsets;
     a.tcu = t_offsets;
     a.win = windows;
-    a.out = out;
+    a.y = y;
     a.table = (int4*)(ws + sp.off_table);
     a.B = pb->B;
-    a.T = pb->T;
-    a.h = pb->h;
-    a.D = pb->D;
+    a.T = T;
+    a.h = h;
+    a.D = D;
     a.grid = sp.grid;
     a.c = sp.c;
 
     const hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
     g_ev_start = g_ev_stop = nullptr;
-    sa::TransposeArgs ta{};
-    ta.mat[ta.n++] = {(const sa::bf16*)Wq, (sa::bf16*)(ws + sp.off_wqt), pb->D, pb->D};
-    ta.mat[ta.n++] = {(const sa::bf16*)Wv, (sa::bf16*)(ws + sp.off_wvt), pb->D, pb->D};
     hipError_t e;
+    sa::TransposeArgs ta{};
+    ta.mat[ta.n++] = {(const sa::bf16*)Wq, (sa::bf16*)wqt, D, D};
+    ta.mat[ta.n++] = {(const sa::bf16*)Wv, (sa::bf16*)wvt, D, D};
     if ((e = sa::launch_transpose(ta, stream)) != hipSuccess) return hip_fail(e, "weight transpose");
-    if ((e = sa::launch_stca(a, sp.dh, stream, ev0, ev1)) != hipSuccess) return hip_fail(e, "STCA attention");
+    if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return hip_fail(e, "timing event");
+    // q = x W_Q for every target
+    sa::GemmArgs g1{};
+    g1.A = (const sa::bf16*)xt;
+    g1.Bt = wqt;
+    g1.C = q;
+    g1.lda = g1.ldb = g1.ldc = D;
+    g1.M = T;
+    g1.N = D;
+    g1.K = D;
+    g1.batch = 1;
+    if ((e = sa::launch_gemm_nt(g1, true, stream)) != hipSuccess) return hip_fail(e, "query projection");
+    if ((e = sa::launch_stca(a, dh, stream)) != hipSuccess) return hip_fail(e, "STCA attention");
+    // out[:, head block] = (alpha X)[:, head] W_V[:, head block], per head
+    sa::GemmArgs g3{};
+    g3.A = y;
+    g3.lda = (int64_t)h * D;
+    g3.sA = D;
+    g3.Bt = wvt;
+    g3.ldb = D;
+    g3.sB = (int64_t)dh * D;
+    g3.C = out;
+    g3.ldc = D;
+    g3.sC = dh;
+    g3.M = T;
+    g3.N = dh;
+    g3.K = D;
+    g3.batch = h;
+    if ((e = sa::launch_gemm_nt(g3, false, stream)) != hipSuccess) return hip_fail(e, "output projection");
+    if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return hip_fail(e, "timing event");
     return SA_OK;
 }
 

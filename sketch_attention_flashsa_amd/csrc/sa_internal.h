@@ -289,22 +289,32 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
 // STCA single-query attention, reordered (sa_stca.hip).
 constexpr int kStcaTargets = 16;     // targets per block (one MFMA column tile)
 struct StcaArgs {
-    const bf16* xt;          // [T][D] target vectors
     const bf16* X;           // history rows, x_stride elements apart
     int64_t x_stride;
-    const bf16* wqt;         // [D][D] W_Q transposed ([out][in])
+    const bf16* qm;          // [T][D] queries x W_Q (bf16)
     const bf16* wk;          // [D][D] W_K as given ([in][out])
-    const bf16* wvt;         // [D][D] W_V transposed
     const int32_t* cu;       // [B+1] rows of each user
     const int32_t* tcu;      // [B+1] targets of each user
     const int32_t* win;      // [T][2] per-target row window, or nullptr
-    float* out;              // [T][D]
+    bf16* y;                 // [T][h][D] out: alpha X per target and head
     int4* table;             // [grid] block -> (user, target chunk, head pair); user -1 = idle block
     int32_t B, T, h, D, grid;
     float c;                 // score scale * log2(e)
 };
 bool stca_supported(int D, int dh);
-hipError_t launch_stca(const StcaArgs& a, int dh, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_stca(const StcaArgs& a, int dh, hipStream_t s);
+
+// Batched bf16 GEMM, both operands k-contiguous (sa_gemm.hip):
+// C[z][m][n] = sum_k A[z][m][k] Bt[z][n][k]; K a multiple of 32, N of 4,
+// lda and ldb multiples of 8, ldc of 4; C bf16 or fp32.
+struct GemmArgs {
+    const bf16* A;
+    const bf16* Bt;
+    void* C;
+    int64_t lda, ldb, ldc, sA, sB, sC;
+    int32_t M, N, K, batch;
+};
+hipError_t launch_gemm_nt(const GemmArgs& a, bool out_bf16, hipStream_t s);
 
 bool fused_supported(int d_model, int m, int dh);
 int fused_groups(int H);     // blocks per row range

@@ -1,36 +1,37 @@
 // sa_stca.hip -- STCA single-query target-to-history cross attention with the
-// reordering of appendix G.2.1 of the SequenceO1 paper, in one kernel:
+// reordering of appendix G.2.1 of the SequenceO1 paper:
 //     q = x W_Q,  u_h = q_h W_K[:, h]^T,  alpha = softmax(u_h X^T / sqrt(dh)),
 //     o_h = (alpha X) W_V[:, h]
 // for every target of every user of a packed batch; a user's targets share
-// its history rows (the multi-request batching of section 4.2), so each block
-// streams the rows once for 16 targets x 2 heads.
+// its history rows (the multi-request batching of section 4.2).  The host
+// sequence (sa_api.hip) is: q = x W_Q for all targets (sa_gemm.hip), this
+// file's setup launch and fused attention kernel, which writes alpha X per
+// (target, head), then the per-head products with W_V (sa_gemm.hip).
 //
-// Block = (user, head pair, 16 targets): 32 query columns, one 16-column MFMA
-// tile per head.  Four waves, one per SIMD; wave w owns channels
-// [w D/4, (w+1) D/4) of the D-wide rows:
-//   * prologue: q for the 16 targets and both heads on MFMA (shared through
-//     LDS), then u^T over the wave's channels (MFMA with W_K), kept in
-//     registers as the score product's B operand;
+// Attention block = (user, head pair, 16 targets): 32 query columns, one
+// 16-column MFMA tile per head.  Four waves, one per SIMD; wave w owns
+// channels [w D/4, (w+1) D/4) of the D-wide rows:
+//   * prologue: u^T over the wave's channels (MFMA with W_K and q), staged
+//     through LDS into the score product's B operand, kept in registers;
 //   * loop over 32-row tiles of the rows the block's targets see: the wave's
 //     slice of every row streams through the wave's own two-stage LDS ring by
 //     direct-to-LDS loads (no other wave reads it, so the ring needs no
 //     barrier); partial scores over the wave's channels (MFMA) go to a
 //     double-buffered LDS exchange; after the tile's one block barrier every
 //     wave adds the other three partials to its own (in wave order) and runs
-//     the online softmax on the full scores (lazy maximum, as in the SA
-//     streaming kernel).  The four waves' sums differ only in rounding, and
-//     each wave normalises its channels with its own running sum, so every
-//     output slice is a weighted mean under one consistent set of weights;
-//     alpha X over the wave's channels accumulates on MFMA from transposed
-//     LDS reads of the same ring stage;
-//   * epilogue: (alpha X) W_V over the wave's channels on MFMA, the four
-//     waves' partial products added in wave order through LDS, fp32 out.
+//     the online softmax on the full scores.  The four waves' sums differ
+//     only in rounding, and each wave normalises its channels with its own
+//     running sum, so every output slice is a weighted mean under one
+//     consistent set of weights.  alpha X over the wave's channels
+//     accumulates on MFMA from transposed LDS reads of the same ring stage.
+//     The loop is software-pipelined: tile t+1's scores are computed while
+//     tile t's weights are formed;
+//   * epilogue: alpha X normalised, in bf16, written row by row through LDS.
 // Ring rows are XOR-swizzled per 16-byte chunk so that the row reads of the
 // score product and the transposed reads of the aggregation are both free of
 // bank conflicts.  A sa_stca_prep_kernel launch first builds the block table
-// from the target offsets on the device (no host reads) and zeroes the
-// outputs of targets outside every user.
+// from the target offsets on the device (no host reads) and zeroes the rows
+// of targets outside every user.
 #include "sa_device.h"
 
 namespace sa {
@@ -53,10 +54,12 @@ __device__ __forceinline__ void lds_st4(uint32_t a, f32x4 v) { *(lds_f32x4*)(uin
 __device__ __forceinline__ bf16x8 lds_ld8(uint32_t a) { return *(const lds_bf16x8*)(uintptr_t)a; }
 __device__ __forceinline__ void lds_st_b4(uint32_t a, bf16x4 v) { *(lds_bf16x4*)(uintptr_t)a = v; }
 
-// 16-byte chunk swizzle of a ring row (a function of row % 8): rows r..r+7
-// take 8 distinct chunks of a 128-byte bank window, and rows 4k..4k+3 take 4
-// distinct 32-byte chunk pairs
-__device__ __forceinline__ int stca_swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+// 16-byte chunk swizzle of a ring row (XOR on the chunk index, a function of
+// row % 16), for the 64 four-byte banks of an LDS cycle: the 16 rows read by
+// one 16-lane group of the score operand land on 16 distinct chunks of the
+// 256-byte bank window, and the 8 rows read by a 32-lane group of the
+// transposed reads on 8 distinct 32-byte chunk pairs
+__device__ __forceinline__ int stca_swz(int r) { return 2 * (r & 7) + ((r >> 3) & 1); }
 
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) { return __builtin_convertvector(v, bf16x4); }
 
@@ -71,13 +74,8 @@ __global__ __launch_bounds__(256, 1) void sa_stca_kernel(StcaArgs a) {
     constexpr int ROWB = DW * 2;           // bytes of a wave's slice of one row
     constexpr int STAGE = 32 * ROWB;       // bytes of one 32-row ring stage
     constexpr int OPS = STAGE / 1024;      // direct-to-LDS ops per stage
-    constexpr int ET = DH / 16;            // 16-row blocks of one head's dh outputs
     constexpr int EK = DH / 32;            // k-steps over dh
-    constexpr int QK = D / 32;             // k-steps of the query projection
-    constexpr int QT = ET / 2;             // query-projection (and output) tiles per wave: 2 heads x ET over 4 waves
-    constexpr int QS = DH + 8;             // LDS row stride (elements) of the shared queries
     static_assert(DW == 256 && DH % 32 == 0 && OPS * 1024 == STAGE, "compiled for 256 channels per wave");
-    static_assert(2 * 16 * QS * 2 <= NW * 4 * 64 * 16, "queries fit one exchange buffer");
 
     __shared__ __attribute__((aligned(1024))) unsigned char ring[NW][2][STAGE];
     __shared__ __attribute__((aligned(1024))) f32x4 xchg[2][NW][4][64];
@@ -123,38 +121,12 @@ __global__ __launch_bounds__(256, 1) void sa_stca_kernel(StcaArgs a) {
     const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void*)&ring[0][0][0];
     const uint32_t my_ring = ring_lds + (uint32_t)(wave * 2 * STAGE);
     const uint32_t xch_lds = (uint32_t)(uintptr_t)(lds_void*)&xchg[0][0][0][0];
-    const uint32_t qs_lds = xch_lds + (uint32_t)(NW * 4 * 64 * 16);   // exchange buffer 1, free until tile 1
 
-    // ---- prologue 1: Qm^T[e][t] = sum_k W_Q^T[hh dh + e][k] x_t[k] for
-    // tiles (head hsel, 16-row block et) = wave * QT + i
-    {
-        f32x4 qa[QT];
-        const bf16* wrow[QT];
-#pragma unroll
-        for (int i = 0; i < QT; ++i) {
-            qa[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            const int tix = wave * QT + i, hh = 2 * hp + tix / ET, et = tix % ET;
-            wrow[i] = a.wqt + (int64_t)(hh * DH + 16 * et + l16) * D + 8 * g;
-        }
-        const bf16* xrow = a.xt + (int64_t)tl * D + 8 * g;
-#pragma unroll 4
-        for (int kk = 0; kk < QK; ++kk) {
-            const bf16x8 xb = *(const bf16x8*)(xrow + 32 * kk);
-#pragma unroll
-            for (int i = 0; i < QT; ++i) qa[i] = mfma(*(const bf16x8*)(wrow[i] + 32 * kk), xb, qa[i]);
-        }
-        // rows e = 16 et + 4 g + r of column t -> Qs[hsel][t][e] (bf16)
-#pragma unroll
-        for (int i = 0; i < QT; ++i) {
-            const int tix = wave * QT + i, hsel = tix / ET, et = tix % ET;
-            lds_st_b4(qs_lds + (uint32_t)(((hsel * 16 + l16) * QS + 16 * et + 4 * g) * 2), to_bf16x4(qa[i]));
-        }
-    }
-    __syncthreads();
 
-    // ---- prologue 2: u^T[d][t] = sum_e W_K[d][hh dh + e] Qm[t][e] over the
-    // wave's channels d, both heads; staged through the wave's own ring (as
-    // [hsel][t][channel], rows swizzled by t) into the score B operand
+    // ---- prologue: u^T[d][t] = sum_e W_K[d][hh dh + e] q[t][hh dh + e] over
+    // the wave's channels d, both heads (q = x W_Q comes precomputed); staged
+    // through the wave's own ring (as [hsel][t][channel], rows swizzled by t)
+    // into the score B operand
     bf16x8 uf[2][KC];
     {
 #pragma unroll
@@ -162,23 +134,33 @@ __global__ __launch_bounds__(256, 1) void sa_stca_kernel(StcaArgs a) {
             const int hh = 2 * hp + hsel;
             bf16x8 qb[EK];
 #pragma unroll
-            for (int ek = 0; ek < EK; ++ek)
-                qb[ek] = lds_ld8(qs_lds + (uint32_t)(((hsel * 16 + l16) * QS + 32 * ek + 8 * g) * 2));
-#pragma unroll 4
-            for (int dt = 0; dt < DB; ++dt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                const bf16* wk = a.wk + (int64_t)(wave * DW + 16 * dt + l16) * D + hh * DH + 8 * g;
+            for (int ek = 0; ek < EK; ++ek) qb[ek] = *(const bf16x8*)(a.qm + (int64_t)tl * D + hh * DH + 32 * ek + 8 * g);
+            // W_K operands in batches of 32 loads, all in flight at once
+            constexpr int DTB = 32 / EK;
+#pragma unroll 1
+            for (int d0 = 0; d0 < DB; d0 += DTB) {
+                bf16x8 wf[DTB][EK];
 #pragma unroll
-                for (int ek = 0; ek < EK; ++ek) acc = mfma(*(const bf16x8*)(wk + 32 * ek), qb[ek], acc);
-                const int row = hsel * 16 + l16, ck = (2 * dt + (g >> 1)) ^ (l16 & 7);
-                lds_st_b4(my_ring + (uint32_t)(row * ROWB + ck * 16 + (g & 1) * 8), to_bf16x4(acc));
+                for (int u = 0; u < DTB; ++u) {
+                    const bf16* wk = a.wk + (int64_t)(wave * DW + 16 * (d0 + u) + l16) * D + hh * DH + 8 * g;
+#pragma unroll
+                    for (int ek = 0; ek < EK; ++ek) wf[u][ek] = *(const bf16x8*)(wk + 32 * ek);
+                }
+#pragma unroll
+                for (int u = 0; u < DTB; ++u) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ek = 0; ek < EK; ++ek) acc = mfma(wf[u][ek], qb[ek], acc);
+                    const int dt = d0 + u, row = hsel * 16 + l16, ck = (2 * dt + (g >> 1)) ^ l16;
+                    lds_st_b4(my_ring + (uint32_t)(row * ROWB + ck * 16 + (g & 1) * 8), to_bf16x4(acc));
+                }
             }
         }
 #pragma unroll
         for (int hsel = 0; hsel < 2; ++hsel)
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
-                const int row = hsel * 16 + l16, ck = (4 * kc + g) ^ (l16 & 7);
+                const int row = hsel * 16 + l16, ck = (4 * kc + g) ^ l16;
                 uf[hsel][kc] = lds_ld8(my_ring + (uint32_t)(row * ROWB + ck * 16));
             }
         // the ring is about to be refilled
@@ -201,16 +183,22 @@ __global__ __launch_bounds__(256, 1) void sa_stca_kernel(StcaArgs a) {
         }
     };
 
-    // per-lane LDS offsets inside a stage
+    // per-lane LDS offsets inside a stage.  Score operand: row l16, chunk
+    // 4 kc + g; with sw = swz(l16) its swizzled position is
+    // 4 (kc ^ (sw >> 2)) + (g ^ (sw & 3)), i.e. base[kc & 3] + 256 (kc >> 2).
     const int sw = stca_swz(l16);
-    const uint32_t a_even = (uint32_t)(l16 * ROWB + 16 * (g ^ (sw & 3)) + 64 * (sw >> 2));
-    const uint32_t a_odd = (uint32_t)(l16 * ROWB + 16 * (g ^ (sw & 3)) - 64 * (sw >> 2));
-    uint32_t tb4[4];   // transposed reads: row 4g + kq, channels 16 db + 4 q
-    {
-        const int kq = l16 >> 2, q = l16 & 3, row = 4 * g + kq;
+    uint32_t xa[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-            tb4[m] = (uint32_t)(row * ROWB + 32 * (m ^ kq) + 16 * ((q >> 1) ^ (g & 1)) + 8 * (q & 1));
+    for (int m = 0; m < 4; ++m) xa[m] = (uint32_t)(l16 * ROWB + 64 * (m ^ (sw >> 2)) + 16 * (g ^ (sw & 3)));
+    // transposed reads: row 4 g + kq, channels 16 db + 4 q (+0..3); the row's
+    // swizzle is 2 v + (g >> 1) with v = 4 (g & 1) + kq, so chunk pair db sits
+    // at pair db ^ v: tb8[db & 7] + 256 (db >> 3)
+    uint32_t tb8[8];
+    {
+        const int kq = l16 >> 2, q = l16 & 3, row = 4 * g + kq, v = 4 * (g & 1) + kq;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            tb8[m] = (uint32_t)(row * ROWB + 32 * (m ^ v) + 16 * ((q >> 1) ^ (g >> 1)) + 8 * (q & 1));
     }
     uint32_t xo[3];    // exchange slots of the other three waves, in wave order
 #pragma unroll
@@ -232,24 +220,26 @@ __global__ __launch_bounds__(256, 1) void sa_stca_kernel(StcaArgs a) {
         for (int db = 0; db < DB; ++db) acc[sb][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
     const float c = a.c;
 
+    // Software pipeline, per wave: the scores of tile t+1 are computed while
+    // the weights of tile t are formed, and tile t+1's transposed operands
+    // are read after tile t's aggregation, so a ring slot is free two tiles
+    // before it is needed again and its load has a whole tile to land.
+    //   stage_scores(k): tile k landed (own loads), partial scores S(k) -> s
+    //   stage_tail(k):   X^T(k) -> lo/hi, S(k) -> exchange buffer k & 1, slot
+    //                    k & 1 refilled with tile k + 2, block barrier
+    //   iteration t:     full scores of t from the exchange, stage_scores(t+1),
+    //                    weights of t, aggregation of t, stage_tail(t+1)
+    // The last iteration runs both stages on stale ring data (results unused),
+    // so every wave meets ntiles + 1 barriers whichever loop it is in.
     i16x4 lo[DB], hi[DB];
-    f32x4 tot[2][2];
-    // DMA, partial scores, transposed operands and the exchange of tile t,
-    // ending with the full scores in tot
-    auto stage = [&](int t) {
-        // the last tile's transposed reads are done, so slot (t + 1) & 1 is free
-        wait_lgkm0();
-        if (t + 1 < ntiles) {
-            issue(t + 1);
-            wait_vm<OPS>();
-        } else {
-            wait_vm<0>();
-        }
-        const uint32_t st = my_ring + (uint32_t)((t & 1) * STAGE);
-        f32x4 s[2][2];
+    f32x4 s[2][2], tot[2][2];
+    auto stage_scores = [&](int k) {
+        if (k + 1 < ntiles) wait_vm<OPS>();   // tile k + 1 may still be in flight
+        else wait_vm<0>();
+        const uint32_t st = my_ring + (uint32_t)((k & 1) * STAGE);
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-            const uint32_t ad = st + ((kc & 1) ? a_odd : a_even) + 64 * kc;
+            const uint32_t ad = st + xa[kc & 3] + 256 * (kc >> 2);
             const bf16x8 x0 = lds_ld8(ad);
             const bf16x8 x1 = lds_ld8(ad + 16 * ROWB);
 #pragma unroll
@@ -260,25 +250,33 @@ __global__ __launch_bounds__(256, 1) void sa_stca_kernel(StcaArgs a) {
                 s[1][sb] = mfma(x1, uf[sb][kc], z1);
             }
         }
+    };
+    auto stage_tail = [&](int k) {
+        const uint32_t st = my_ring + (uint32_t)((k & 1) * STAGE);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const uint32_t ad = st + tb4[db & 3] + 128 * (db >> 2);
+            const uint32_t ad = st + tb8[db & 7] + 256 * (db >> 3);
             lo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)ad);
             hi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(ad + 16 * ROWB));
         }
-        const uint32_t xb = xch_lds + (uint32_t)((t & 1) * NW * 4 * 64 * 16);
+        const uint32_t xb = xch_lds + (uint32_t)((k & 1) * NW * 4 * 64 * 16);
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
             lds_st4(xb + (uint32_t)((wave * 4 + r4) * 64 * 16 + lane * 16), s[r4 >> 1][r4 & 1]);
+        // every read of slot k & 1 is done, and the partials are in place
         wait_lgkm0();
+        if (k + 2 < ntiles) issue(k + 2);
         block_barrier();
+    };
+    auto read_exchange = [&](int t) {
+        const uint32_t xb = xch_lds + (uint32_t)((t & 1) * NW * 4 * 64 * 16);
+        f32x4 l[3][4];
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 l0 = lds_ld4(xb + xo[0] + r4 * 64 * 16);
-            const f32x4 l1 = lds_ld4(xb + xo[1] + r4 * 64 * 16);
-            const f32x4 l2 = lds_ld4(xb + xo[2] + r4 * 64 * 16);
-            tot[r4 >> 1][r4 & 1] = ((s[r4 >> 1][r4 & 1] + l0) + l1) + l2;
-        }
+        for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+            for (int k = 0; k < 3; ++k) l[k][r4] = lds_ld4(xb + xo[k] + r4 * 64 * 16);
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) tot[r4 >> 1][r4 & 1] = ((tot[r4 >> 1][r4 & 1] + l[0][r4]) + l[1][r4]) + l[2][r4];
     };
     // (alpha X)^T over the wave's channels += X^T p^T
     auto aggregate = [&](const bf16x8 (&pk)[2]) {
@@ -305,10 +303,21 @@ __global__ __launch_bounds__(256, 1) void sa_stca_kernel(StcaArgs a) {
         return vj;
     };
 
-    if (ntiles > 0) issue(0);
+    if (ntiles > 0) {
+        issue(0);
+        if (ntiles > 1) issue(1);
+        stage_scores(0);
+        stage_tail(0);
+    }
     int t = 0;
     for (; t < ntiles; ++t) {
-        stage(t);
+        // the wave's own partial of tile t is still in s: start the sum with it
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) tot[r4 >> 1][r4 & 1] = s[r4 >> 1][r4 & 1];
+        read_exchange(t);
+        // unconditional (the last tile's extra stage reads stale ring data
+        // and is never used) so the MFMAs interleave with the weights below
+        stage_scores(t + 1);
         float p[2][8];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
@@ -339,10 +348,16 @@ __global__ __launch_bounds__(256, 1) void sa_stca_kernel(StcaArgs a) {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) Zs[sb] += zt[sb];
         aggregate(pk);
+        stage_tail(t + 1);
     }
-    // exact loop, entered in the middle of tile t (its scores are in tot)
+    // exact loop, entered after the scores of tile t + 1 (if any) are in s
     for (bool resume = true; t < ntiles; ++t, resume = false) {
-        if (!resume) stage(t);
+        if (!resume) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) tot[r4 >> 1][r4 & 1] = s[r4 >> 1][r4 & 1];
+            read_exchange(t);
+            stage_scores(t + 1);
+        }
         const uint32_t vj = valid_bits(t);
         bf16x8 pk[2];
 #pragma unroll
@@ -374,59 +389,38 @@ __global__ __launch_bounds__(256, 1) void sa_stca_kernel(StcaArgs a) {
             }
         }
         aggregate(pk);
+        stage_tail(t + 1);
     }
     wait_lgkm0();
 
-    // ---- epilogue: y = acc / Z, o^T[e][t] = sum_d W_V^T[hh dh + e][d] y[t][d]
-    // over the wave's channels; k-slot j of chunk kc <-> channel 32 kc + tok_of(g, j)
-    f32x4 ov[2][ET];
+    // ---- epilogue: y = acc / Z in bf16, staged through the wave's own ring
+    // as [head sb * 16 + target][channel] (rows swizzled by target) and
+    // written row by row: 512 contiguous bytes per row
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
         float z = Zs[sb];
         z += __shfl_xor(z, 16, 64);
         z += __shfl_xor(z, 32, 64);
         const float inv = z > 0.f ? 1.f / z : 0.f;
-        bf16x8 yb[KC];
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-            const f32x4 e0 = acc[sb][2 * kc] * inv, e1 = acc[sb][2 * kc + 1] * inv;
-            yb[kc] = cat8(pack2(e0[0], e0[1]), pack2(e0[2], e0[3]), pack2(e1[0], e1[1]), pack2(e1[2], e1[3]));
-        }
-        const int hh = 2 * hp + sb;
-#pragma unroll
-        for (int et = 0; et < ET; ++et) {
-            f32x4 o = {0.f, 0.f, 0.f, 0.f};
-            const bf16* wv = a.wvt + (int64_t)(hh * DH + 16 * et + l16) * D + wave * DW + 4 * g;
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                const bf16x4 w0 = *(const bf16x4*)(wv + 32 * kc);
-                const bf16x4 w1 = *(const bf16x4*)(wv + 32 * kc + 16);
-                o = mfma(__builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7), yb[kc], o);
-            }
-            ov[sb][et] = o;
+        for (int db = 0; db < DB; ++db) {
+            const int row = sb * 16 + l16, ck = (2 * db + (g >> 1)) ^ l16;
+            lds_st_b4(my_ring + (uint32_t)(row * ROWB + ck * 16 + (g & 1) * 8), to_bf16x4(acc[sb][db] * inv));
         }
     }
-    // the four waves' partial products, added in wave order (each wave's own
-    // ring holds its partials; its loop is over)
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int et = 0; et < ET; ++et) lds_st4(my_ring + (uint32_t)(((sb * ET + et) * 64 + lane) * 16), ov[sb][et]);
-    wait_lgkm0();
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < QT; ++i) {
-        const int j = wave * QT + i, sb = j / ET, et = j % ET;
-        const uint32_t off = (uint32_t)((j * 64 + lane) * 16);
-        f32x4 r = lds_ld4(ring_lds + off);
-#pragma unroll
-        for (int w = 1; w < NW; ++w) r = r + lds_ld4(ring_lds + (uint32_t)(w * 2 * STAGE) + off);
-        if (tv) *(f32x4*)(a.out + (int64_t)tl * D + (2 * hp + sb) * DH + 16 * et + 4 * g) = r;
+    for (int it = 0; it < 16; ++it) {
+        const int row = 2 * it + (lane >> 5), c = lane & 31, tt = row & 15;
+        const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(
+            my_ring + (uint32_t)(row * ROWB + ((c ^ tt) * 16)));
+        if (tt < nt)
+            *(u32x4*)(a.y + ((int64_t)(tb + tt) * a.h + 2 * hp + (row >> 4)) * D + wave * DW + 8 * c) = v;
     }
 }
 
 // One block: the block table (user b gets ceil(targets_b / 16) x (h / 2)
-// consecutive entries, in user order) and zeros for targets outside every user.
+// consecutive entries, in user order) and zero y rows for targets outside
+// every user.
 __global__ __launch_bounds__(1024) void sa_stca_prep_kernel(StcaArgs a) {
     __shared__ int scan[1024];
     const int tid = threadIdx.x;
@@ -456,25 +450,21 @@ __global__ __launch_bounds__(1024) void sa_stca_prep_kernel(StcaArgs a) {
     for (int L = running + tid; L < a.grid; L += 1024) a.table[L] = make_int4(-1, 0, 0, 0);
     const int t_lo = a.B > 0 ? min(max(a.tcu[0], 0), a.T) : a.T;
     const int t_hi = a.B > 0 ? min(max(a.tcu[a.B], t_lo), a.T) : a.T;
-    const int d4 = a.D / 4;
-    for (int64_t i = tid; i < (int64_t)a.T * d4; i += 1024) {
-        const int t = (int)(i / d4);
-        if (t < t_lo || t >= t_hi) ((f32x4*)a.out)[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    }
+    const int64_t per = (int64_t)a.h * a.D / 8;    // 16-byte chunks of one target's y rows
+    for (int64_t i = tid; i < (int64_t)t_lo * per; i += 1024) ((u32x4*)a.y)[i] = (u32x4){0u, 0u, 0u, 0u};
+    for (int64_t i = (int64_t)t_hi * per + tid; i < (int64_t)a.T * per; i += 1024)
+        ((u32x4*)a.y)[i] = (u32x4){0u, 0u, 0u, 0u};
 }
 
 bool stca_supported(int D, int dh) { return D == 1024 && (dh == 64 || dh == 128); }
 
-hipError_t launch_stca(const StcaArgs& a, int dh, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+hipError_t launch_stca(const StcaArgs& a, int dh, hipStream_t s) {
     hipLaunchKernelGGL(sa_stca_prep_kernel, dim3(1), dim3(1024), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
     if (dh == 64) hipLaunchKernelGGL((sa_stca_kernel<1024, 64>), dim3(a.grid), dim3(256), 0, s, a);
     if (dh == 128) hipLaunchKernelGGL((sa_stca_kernel<1024, 128>), dim3(a.grid), dim3(256), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
-    return hipSuccess;
+    return hipGetLastError();
 }
 
 }  // namespace sa
