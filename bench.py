@@ -406,8 +406,9 @@ def bench_stca(args):
     """STCA single-query attention (appendix G.2.1's reordering) over the
     sketch branch: 64 users, each a sketch of 1,024 rows adapted to width
     D = 1024 and 40 targets (the training-side reuse ratio of appendix G.5),
-    h = 16 heads.  A step is one sa_stca_attention call; the roofline is the
-    fused kernel's (MFMA-bound)."""
+    h = 16 heads.  A step is one sa_stca_attention call; the roofline covers
+    its launches after the weight transpose (MFMA-bound), timed by the HIP
+    events the library records around them."""
     import numpy as np
     import torch
     import workloads as W
@@ -459,7 +460,7 @@ def bench_stca(args):
                    "D": D, "h": h, "dh": D // h, "parallelism": "single GPU"},
         "roofline": {
             "bound": "mfma",
-            "kernel": "sa_stca_kernel<1024, 64>",
+            "kernel": "sa_stca_attention: query GEMM + sa_stca_kernel<1024, 64> + output GEMM",
             "achieved": tflops,
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
