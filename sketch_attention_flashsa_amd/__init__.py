@@ -397,10 +397,14 @@ def sa_stca_attention(xt, X, Wq, Wk, Wv, cu_offsets, t_offsets, h: int, windows=
     dev = xt.device
     T, D = xt.shape
     B = t_offsets.numel() - 1
-    xt, X, Wq, Wk, Wv = (t.contiguous() for t in (xt, X, Wq, Wk, Wv))
+    xt, Wq, Wk, Wv = (t.contiguous() for t in (xt, Wq, Wk, Wv))
+    # X may be a row view of a wider buffer (unit column stride, rows apart)
+    if X.dim() != 2 or X.stride(1) != 1 or X.stride(0) < D:
+        X = X.contiguous()
     if windows is not None:
         windows = windows.to(torch.int32).contiguous()
-    pb = SaStcaProblem(B=B, T=T, D=D, h=h, total_rows=X.shape[0], x_row_stride=0, scale=scale or 0.0, flags=0)
+    pb = SaStcaProblem(B=B, T=T, D=D, h=h, total_rows=X.shape[0], x_row_stride=X.stride(0), scale=scale or 0.0,
+                       flags=0)
     nws = int(lib.sa_stca_workspace_size(ctypes.byref(pb)))
     if nws == 0:
         _check(lib.sa_stca_attention(ctypes.byref(pb), *([None] * 10), 0, None))

@@ -17,10 +17,11 @@ from gpu_util import assert_parity, device
 pytestmark = pytest.mark.gpu
 
 
-def run_stca(w, windows="default", t_offsets=None, xt=None, h=None):
+def run_stca(w, windows="default", t_offsets=None, xt=None, h=None, X=None):
     dev = device()
     win = w["windows"] if isinstance(windows, str) else windows
-    out = sa.sa_stca_attention((w["xt"] if xt is None else xt).to(dev), w["X"].to(dev), w["Wq"].to(dev),
+    out = sa.sa_stca_attention((w["xt"] if xt is None else xt).to(dev), w["X"].to(dev) if X is None else X,
+                               w["Wq"].to(dev),
                                w["Wk"].to(dev), w["Wv"].to(dev), w["cu_offsets"].to(dev),
                                (w["t_offsets"] if t_offsets is None else t_offsets).to(dev), h or w["h"],
                                windows=None if win is None else win.to(dev))
@@ -108,3 +109,24 @@ def test_stca_sketch_branch_workload_sampled():
         sub["t_offsets"] = torch.tensor([0, R], dtype=torch.int32)
         o = oracle_stca(sub, xt=w["xt"][b * R:(b + 1) * R])
         assert_parity(g[b * R:(b + 1) * R], o, "bf16", f"stca sketch workload user {b}")
+
+
+def test_stca_strided_rows_many_users_dh128():
+    """History rows as a view of a wider buffer (x_row_stride > D), 1,100
+    users (the block table's prefix runs over two 1,024-user passes), a
+    user with no targets between users with targets, and h = 8 (dh = 128)
+    with request windows."""
+    rng = np.random.default_rng(914)
+    B = 1100
+    lengths = rng.integers(0, 40, size=B)
+    targets = rng.integers(0, 3, size=B)
+    targets[[5, 600, 1099]] = [17, 33, 1]
+    w = W.random_stca_case(914, lengths=lengths.tolist(), targets=targets.tolist(), D=1024, h=8, windows="requests")
+    dev = device()
+    wide = torch.zeros((w["X"].shape[0], 1024 + 64), dtype=torch.bfloat16, device=dev)
+    wide[:, :1024] = w["X"].to(dev)
+    wide[:, 1024:] = float("nan")                        # never read
+    g = run_stca(w, X=wide[:, :1024])
+    o = oracle_stca(w)
+    assert np.all(np.isfinite(g))
+    assert_parity(g, o, "bf16", "stca strided rows, 1100 users, h=8")
