@@ -506,7 +506,7 @@ sa_status make_stca_plan(const sa_stca_problem* pb, StcaPlan* sp) {
     sp->off_wvt = off;
     off = align_up(off + 2 * dd);
     sp->off_table = off;
-    off = align_up(off + 16 * (size_t)sp->grid);
+    off = align_up(off + 32 * (size_t)sp->grid);
     sp->off_q = off;
     off = align_up(off + 2 * (size_t)pb->T * pb->D);
     sp->off_y = off;

@@ -297,7 +297,8 @@ struct StcaArgs {
     const int32_t* tcu;      // [B+1] targets of each user
     const int32_t* win;      // [T][2] per-target row window, or nullptr
     bf16* y;                 // [T][h][D] out: alpha X per target and head
-    int4* table;             // [grid] block -> (user, target chunk, head pair); user -1 = idle block
+    int4* table;             // [grid][2] per block: (user, first target, targets, head pair) and
+                             // (first row of the rows its targets see, their count, 0, 0); user -1 = idle
     int32_t B, T, h, D, grid;
     float c;                 // score scale * log2(e)
 };

@@ -88,35 +88,34 @@ __global__ __launch_bounds__(256, 1) void sa_stca_kernel(StcaArgs a) {
     // x-th contiguous run of the table, so a user's blocks share one L2
     const int G = gridDim.x;
     const int Lb = (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8;
-    const int4 ent = a.table[Lb];
+    // (everything the block needs before its first loads comes in its two
+    // table entries, so they can all be issued after one round trip)
+    const int4 ent = a.table[2 * Lb];
     const int b = __builtin_amdgcn_readfirstlane(ent.x);
     if (b < 0) return;
-    const int chunk = __builtin_amdgcn_readfirstlane(ent.y);
-    const int hp = __builtin_amdgcn_readfirstlane(ent.z);
-    const int64_t u0 = a.cu[b];
-    const int nu = a.cu[b + 1] - (int)u0;
-    const int tb = a.tcu[b] + chunk * kStcaTargets;
-    const int nt = min(kStcaTargets, a.tcu[b + 1] - tb);
+    const int tb = __builtin_amdgcn_readfirstlane(ent.y);
+    const int nt = __builtin_amdgcn_readfirstlane(ent.z);
+    const int hp = __builtin_amdgcn_readfirstlane(ent.w);
+    const int4 ent2 = a.table[2 * Lb + 1];
+    const int row0 = __builtin_amdgcn_readfirstlane(ent2.x);   // absolute first row the block streams
+    const int nrows = __builtin_amdgcn_readfirstlane(ent2.y);
+    const int ntiles = (nrows + 31) / 32;
 
-    // this lane's target (column l16) and its window; the block streams the
-    // union of its targets' windows
+    // this lane's target (column l16) and its window, relative to the
+    // block's first row (needed only once the loop starts)
     const bool tv = l16 < nt;
     const int tl = tb + (tv ? l16 : 0);
-    int wlo = 0, whi = nu;
-    if (a.win != nullptr) {
-        wlo = min(max(a.win[2 * (int64_t)tl], 0), nu);
-        whi = max(wlo, min(max(a.win[2 * (int64_t)tl + 1], 0), nu));
+    int qlo = 0, qhi = 0;
+    if (tv) {
+        const int u0 = a.cu[b], nu = a.cu[b + 1] - u0;
+        int wlo = 0, whi = nu;
+        if (a.win != nullptr) {
+            wlo = min(max(a.win[2 * (int64_t)tl], 0), nu);
+            whi = max(wlo, min(max(a.win[2 * (int64_t)tl + 1], 0), nu));
+        }
+        qlo = u0 + wlo - row0;
+        qhi = u0 + whi - row0;
     }
-    int ulo = (tv && whi > wlo) ? wlo : nu, uhi = (tv && whi > wlo) ? whi : 0;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-        ulo = min(ulo, __shfl_xor(ulo, o, 64));
-        uhi = max(uhi, __shfl_xor(uhi, o, 64));
-    }
-    const int r_lo = __builtin_amdgcn_readfirstlane(ulo);
-    const int nrows = max(0, __builtin_amdgcn_readfirstlane(uhi) - r_lo);
-    const int qlo = tv ? wlo - r_lo : 0, qhi = tv ? whi - r_lo : 0;   // relative to the block's first row
-    const int ntiles = (nrows + 31) / 32;
 
     const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void*)&ring[0][0][0];
     const uint32_t my_ring = ring_lds + (uint32_t)(wave * 2 * STAGE);
@@ -135,7 +134,8 @@ __global__ __launch_bounds__(256, 1) void sa_stca_kernel(StcaArgs a) {
             bf16x8 qb[EK];
 #pragma unroll
             for (int ek = 0; ek < EK; ++ek) qb[ek] = *(const bf16x8*)(a.qm + (int64_t)tl * D + hh * DH + 32 * ek + 8 * g);
-            // W_K operands in batches of 32 loads, all in flight at once
+            // W_K operands in batches of 32 loads (all of a head's at once for
+            // dh = 64), every load of a batch in flight together
             constexpr int DTB = 32 / EK;
 #pragma unroll 1
             for (int d0 = 0; d0 < DB; d0 += DTB) {
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256, 1) void sa_stca_kernel(StcaArgs a) {
 
     // ---- streaming
     const int64_t xrow = a.x_stride * 2;
-    const unsigned char* Xg = (const unsigned char*)a.X + ((u0 + r_lo) * a.x_stride + (int64_t)wave * DW) * 2;
+    const unsigned char* Xg = (const unsigned char*)a.X + ((int64_t)row0 * a.x_stride + (int64_t)wave * DW) * 2;
     auto issue = [&](int t) {
         const uint32_t dst = my_ring + (uint32_t)((t & 1) * STAGE);
         const unsigned char* src = Xg + (int64_t)t * 32 * xrow;
@@ -442,12 +442,37 @@ __global__ __launch_bounds__(1024) void sa_stca_prep_kernel(StcaArgs a) {
             __syncthreads();
         }
         const int start = running + scan[tid] - n;
-        for (int k = 0; k < n; ++k)
-            if (start + k < a.grid) a.table[start + k] = make_int4(b, k / hpn, k % hpn, 0);
+        if (n > 0) {
+            const int u0 = a.cu[b], nu = a.cu[b + 1] - u0, t0 = a.tcu[b], nT = a.tcu[b + 1] - t0;
+            for (int c = 0; c * hpn < n; ++c) {
+                // the union of the chunk's target windows (clipped to the user)
+                const int tb = t0 + c * kStcaTargets, nt = min(kStcaTargets, nT - c * kStcaTargets);
+                int lo = nu, hi = 0;
+                for (int k = 0; k < nt; ++k) {
+                    int wlo = 0, whi = nu;
+                    if (a.win != nullptr) {
+                        wlo = min(max(a.win[2 * (int64_t)(tb + k)], 0), nu);
+                        whi = max(wlo, min(max(a.win[2 * (int64_t)(tb + k) + 1], 0), nu));
+                    }
+                    if (whi > wlo) {
+                        lo = min(lo, wlo);
+                        hi = max(hi, whi);
+                    }
+                }
+                const int rows = max(0, hi - lo);
+                for (int p = 0; p < hpn; ++p) {
+                    const int L = start + c * hpn + p;
+                    if (L < a.grid) {
+                        a.table[2 * L] = make_int4(b, tb, nt, p);
+                        a.table[2 * L + 1] = make_int4(u0 + (rows > 0 ? lo : 0), rows, 0, 0);
+                    }
+                }
+            }
+        }
         running += scan[1023];
         __syncthreads();
     }
-    for (int L = running + tid; L < a.grid; L += 1024) a.table[L] = make_int4(-1, 0, 0, 0);
+    for (int L = running + tid; L < a.grid; L += 1024) a.table[2 * L] = make_int4(-1, 0, 0, 0);
     const int t_lo = a.B > 0 ? min(max(a.tcu[0], 0), a.T) : a.T;
     const int t_hi = a.B > 0 ? min(max(a.tcu[a.B], t_lo), a.T) : a.T;
     const int64_t per = (int64_t)a.h * a.D / 8;    // 16-byte chunks of one target's y rows

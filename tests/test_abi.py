@@ -230,10 +230,10 @@ def test_stca_entry_validation():
 
     pb = P()
     n = lib.sa_stca_workspace_size(ctypes.byref(pb))
-    # W_Q^T and W_V^T (bf16), a 16-byte block-table entry per block, the
+    # W_Q^T and W_V^T (bf16), a 32-byte block-table entry per block, the
     # queries [T, D] and alpha X [T, h, D] (bf16)
     grid = ((2560 // 16 + 64) * 8 + 7) // 8 * 8
-    assert n >= 2 * 1024 * 1024 * 2 + 16 * grid + 2 * 2560 * 1024 + 2 * 2560 * 16 * 1024
+    assert n >= 2 * 1024 * 1024 * 2 + 32 * grid + 2 * 2560 * 1024 + 2 * 2560 * 16 * 1024
     bad = [(P(D=512, h=8), sa.SA_ERR_UNSUPPORTED), (P(h=32), sa.SA_ERR_UNSUPPORTED),
            (P(h=15), sa.SA_ERR_INVALID_ARG), (P(B=-1), sa.SA_ERR_INVALID_ARG), (P(T=-3), sa.SA_ERR_INVALID_ARG),
            (P(stride=1000), sa.SA_ERR_INVALID_ARG), (P(stride=1028), sa.SA_ERR_INVALID_ARG),
