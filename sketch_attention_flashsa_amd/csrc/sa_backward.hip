@@ -28,6 +28,8 @@
 // Rows past a segment's end load a clamped valid row; rows that are invalid
 // (past the end, masked) get weight 0 by select, and their K values are
 // zeroed before the dP product, so NaN in masked rows cannot leak.
+#include <stdlib.h>
+
 #include "sa_device.h"
 
 namespace sa {
@@ -371,6 +373,213 @@ __global__ __launch_bounds__(512) void sa_bwd_dp_kernel(BwdArgs a, int NH, int P
     }
 }
 
+// The same dP computation fed by a direct-to-LDS ring (the forward streaming
+// kernel's scheme): K and V rows of the block's heads (CPR 16-byte chunks per
+// row per tensor) stream through kDpStages 32-row stages, kDpStages - 1 of
+// them in flight while one is computed, each wave waiting (counted vmcnt)
+// for its own loads before the block barrier.  K is read row-wise for the
+// scores and transposed for dP^T += K^T ds^T, V row-wise for dA, so both
+// tensors take one XOR swizzle of the 16-byte chunks, dp_swz(row % 16), under
+// which a 16-lane group of row reads touches 16 distinct chunks of the
+// 256-byte bank window and a 32-lane group of transposed reads 8 distinct
+// 32-byte chunk pairs.  Compiled for 8-wave blocks (NH heads x PB prototype
+// blocks = 8) with NH dh = 8 CPR in {128, 256}.
+namespace {
+constexpr int kDpStages = 4;
+__device__ __forceinline__ int dp_swz(int r) { return 2 * (r & 7) + ((r >> 3) & 1); }
+}  // namespace
+
+template <int DH, int CPR>
+__global__ __launch_bounds__(512, CPR == 16 ? 2 : 1) void sa_bwd_dp_stream_kernel(BwdArgs a, int NH, int PB) {
+    constexpr int KC = DH / 32, DB = DH / 16, NSB = 2, NW = 8;
+    constexpr int S = kDpStages, AHEAD = S - 1;
+    constexpr int ROWB = CPR * 16;                   // bytes per row per tensor
+    constexpr int STAGE = 32 * ROWB;                 // bytes per tensor per stage
+    constexpr int D = 32 * CPR / (NW * 64);          // DMA ops per wave per tensor per stage
+    constexpr int VMS = 2 * D;
+    static_assert(D >= 1 && D * NW * 64 == 32 * CPR, "a stage is whole DMA ops per wave");
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[S][2][STAGE];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, l16 = lane & 15, kq = l16 >> 2, q = l16 & 3;
+    const int w = blockIdx.x;
+    const int h0 = blockIdx.y * NH;
+    const int hl = wave / PB, pb = wave - hl * PB;
+    const int head = h0 + hl;
+    const bool active = head < a.H;
+
+    const int64_t total = a.users.total();
+    const RowSplit rs = row_split(total, a.G, a.R_fixed, a.R_min, 50);
+    const int64_t v_lo = rs.lo(w);
+    if (v_lo >= total) return;
+    const int64_t v_hi = min(rs.lo(w + 1), total);
+    const bf16* Pg = (const bf16*)a.P;
+    const unsigned char* Kg = (const unsigned char*)a.K;
+    const unsigned char* Vg = (const unsigned char*)a.V;
+    const int64_t krow = a.k_stride * 2, vrow = a.v_stride * 2;
+
+    // per-lane DMA geometry: op (wave D + d) writes 1 KB of the stage; lane
+    // writes 16 B at row * ROWB + slot * 16 and fetches the logical chunk the
+    // swizzle places there
+    int dma_row[D], dma_ck[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        const int off = (wave * D + d) * 1024 + lane * 16;
+        dma_row[d] = off / ROWB;
+        dma_ck[d] = (((off % ROWB) / 16) ^ dp_swz(dma_row[d] & 15)) * 16;
+    }
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void*)&ring[0][0][0];
+    const int hc = min(h0 + hl, a.H - 1) - h0;      // head column of this wave (clamped for idle waves)
+    uint32_t rd[KC];                                 // row reads: row l16, chunk hc dh/8 + 4 kc + g
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+        rd[kc] = (uint32_t)(l16 * ROWB + (((hc * (DH / 8) + 4 * kc + g) ^ dp_swz(l16)) * 16));
+    uint32_t tr[DB];                                 // transposed reads: row 4 g + kq, channels 16 db + 4 q
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        const int row = 4 * g + kq, c = hc * (DH / 8) + 2 * db + (q >> 1);
+        tr[db] = (uint32_t)(row * ROWB + ((c ^ dp_swz(row)) * 16) + 8 * (q & 1));
+    }
+
+    for (int b = a.users.find(v_lo); b < a.users.B; ++b) {
+        const int64_t us = a.users.vstart(b), ue = a.users.vstart(b + 1);
+        if (us >= v_hi) break;
+        const int64_t s_lo = max(v_lo, us), s_hi = min(v_hi, ue);
+        if (s_hi <= s_lo) continue;
+        const int64_t gbase = a.users.row_base(b) + (s_lo - us);
+        const int n = (int)(s_hi - s_lo);
+        const int ntiles = (n + 31) / 32;
+        const int hh = active ? head : h0;
+        // B operands: column = prototype 32 pb + 16 sb + l16, k = dh
+        bf16x8 pf[NSB][KC], gf[NSB][KC];
+        float l2v[NSB], dv[NSB];
+        const bf16* Pb = Pg + (int64_t)b * a.q_batch_stride + (int64_t)hh * a.m * DH;
+        const bf16* Gb = a.dSb + ((int64_t)b * a.H + hh) * a.m * DH;
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) {
+            const int j = 32 * pb + 16 * sb + l16;
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                pf[sb][kc] = *(const bf16x8*)(Pb + (int64_t)j * DH + 32 * kc + 8 * g);
+                gf[sb][kc] = *(const bf16x8*)(Gb + (int64_t)j * DH + 32 * kc + 8 * g);
+            }
+            l2v[sb] = a.L2v[((int64_t)b * a.H + hh) * a.m + j];
+            dv[sb] = a.Dv[((int64_t)b * a.H + hh) * a.m + j];
+        }
+        // settle these loads before the ring's counted waits start
+        wait_vm<0>();
+        f32x4 acc[NSB][DB];
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[sb][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+        const unsigned char* kseg = Kg + gbase * krow + (int64_t)h0 * DH * 2;
+        const unsigned char* vseg = Vg + gbase * vrow + (int64_t)h0 * DH * 2;
+        auto issue = [&](int t) {
+            const uint32_t slot = ring_lds + (uint32_t)((t % S) * 2 * STAGE) + (uint32_t)(wave * D * 1024);
+            const int last = n - 1 - t * 32;         // rows past the segment end re-read its last row
+            const unsigned char* kb = kseg + (int64_t)t * 32 * krow;
+            const unsigned char* vb = vseg + (int64_t)t * 32 * vrow;
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const int rr = min(dma_row[d], last);
+                dma16c(kb, (uint32_t)(rr * (int)krow + dma_ck[d]), __builtin_amdgcn_readfirstlane(slot + d * 1024));
+                dma16c(vb, (uint32_t)(rr * (int)vrow + dma_ck[d]),
+                       __builtin_amdgcn_readfirstlane(slot + STAGE + d * 1024));
+            }
+        };
+
+#pragma unroll
+        for (int t = 0; t < AHEAD; ++t)
+            if (t < ntiles) issue(t);
+        for (int t = 0; t < ntiles; ++t) {
+            // this wave's part of stage t has landed; the barrier makes the
+            // stage complete and frees slot (t - 1) % S for stage t + AHEAD
+            wait_after<AHEAD - 1, VMS>(min(AHEAD - 1, ntiles - 1 - t));
+            block_barrier();
+            if (t + AHEAD < ntiles) issue(t + AHEAD);
+            if (active) {
+                const uint32_t kst = ring_lds + (uint32_t)((t % S) * 2 * STAGE), vst = kst + STAGE;
+                const int tl = t * 32 + lane;
+                bool vr = lane < 32 && tl < n;
+                if (a.mask) vr = vr && a.mask[gbase + min(tl, n - 1)] != 0;
+                const uint32_t valid = (uint32_t)__ballot(vr);
+                // S^T = K P^T and dA^T = V dS^T: rows = tokens (two 16-row halves)
+                f32x4 s[2][NSB], da[2][NSB];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+#pragma unroll
+                    for (int sb = 0; sb < NSB; ++sb) s[half][sb] = da[half][sb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kc = 0; kc < KC; ++kc) {
+                        const uint32_t o = rd[kc] + (uint32_t)(16 * half * ROWB);
+                        const bf16x8 kr = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(kst + o);
+                        const bf16x8 vr8 = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(vst + o);
+#pragma unroll
+                        for (int sb = 0; sb < NSB; ++sb) {
+                            s[half][sb] = mfma(kr, pf[sb][kc], s[half][sb]);
+                            da[half][sb] = mfma(vr8, gf[sb][kc], da[half][sb]);
+                        }
+                    }
+                }
+                // ds^T packed as the B operand of dP^T += K^T ds^T (k = tokens in
+                // the tok_of order, column = prototype)
+                const uint32_t vj = lane_slots(valid, g);
+                bf16x8 pk[NSB];
+#pragma unroll
+                for (int sb = 0; sb < NSB; ++sb) {
+                    float x[8];
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) {
+                        const float sc = s[jj >> 2][sb][jj & 3], dd = da[jj >> 2][sb][jj & 3];
+                        const float p = __builtin_amdgcn_exp2f(fmaf(sc, a.c2, -l2v[sb]));
+                        x[jj] = ((vj >> jj) & 1) ? p * (dd - dv[sb]) : 0.f;
+                    }
+                    pk[sb] = cat8(pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7]));
+                }
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    union {
+                        i16x4 h[2];
+                        bf16x8 v;
+                    } kT;
+                    kT.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(kst + tr[db]));
+                    kT.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4*)(uintptr_t)(kst + tr[db] + 16 * ROWB));
+                    if (valid != 0xffffffffu) {
+                        // invalid rows: zero their keys (NaN in masked rows must not leak)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+                            if (!((vj >> jj) & 1)) kT.h[0][jj] = 0;
+                            if (!((vj >> (4 + jj)) & 1)) kT.h[1][jj] = 0;
+                        }
+                    }
+#pragma unroll
+                    for (int sb = 0; sb < NSB; ++sb) acc[sb][db] = mfma(kT.v, pk[sb], acc[sb][db]);
+                }
+            }
+            // every LDS read of this stage has completed before the next barrier
+            wait_lgkm0();
+        }
+        if (active) {
+            const int64_t slot = (int64_t)w + b;
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    *(f32x4*)lane_major_acc(a.part, slot, a.H, head, a.m, DH, 2 * pb + sb, db, lane) =
+                        acc[sb][db] * a.c;
+        }
+        // drain this segment's loads and let every wave finish reading the
+        // ring before the next segment's prologue refills it
+        wait_vm<0>();
+        wait_lgkm0();
+        block_barrier();
+    }
+}
+
 // dP = sum of the dP partials of the segments in fixed order: per user (per-user
 // prototypes) or over all users (shared prototypes).  One thread per four
 // outputs (h, j, e..e+3); the partials are lane-major.
@@ -431,7 +640,16 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     int NH, PB;
     bwd_dp_shape(a.m, a.H, &NH, &PB);
     const dim3 g2(a.G, (a.H + NH - 1) / NH), blk2(NH * PB * 64);
-    if (a.dh == 32) hipLaunchKernelGGL(sa_bwd_dp_kernel<32>, g2, blk2, 0, s, a, NH, PB);
+    // the ring-fed kernel for 8-wave blocks whose rows are 128 or 256 elements
+    // (K and V row starts 16-byte aligned), the register-staged one otherwise
+    const int cpr = NH * a.dh / 8;
+    const bool ring_ok = NH * PB == 8 && (cpr == 16 || cpr == 32) && a.k_stride % 8 == 0 && a.v_stride % 8 == 0 &&
+                         getenv("SA_BWD_DP") == nullptr;
+    if (ring_ok && a.dh == 32 && cpr == 16) hipLaunchKernelGGL((sa_bwd_dp_stream_kernel<32, 16>), g2, blk2, 0, s, a, NH, PB);
+    else if (ring_ok && a.dh == 32 && cpr == 32) hipLaunchKernelGGL((sa_bwd_dp_stream_kernel<32, 32>), g2, blk2, 0, s, a, NH, PB);
+    else if (ring_ok && a.dh == 64 && cpr == 16) hipLaunchKernelGGL((sa_bwd_dp_stream_kernel<64, 16>), g2, blk2, 0, s, a, NH, PB);
+    else if (ring_ok && a.dh == 64 && cpr == 32) hipLaunchKernelGGL((sa_bwd_dp_stream_kernel<64, 32>), g2, blk2, 0, s, a, NH, PB);
+    else if (a.dh == 32) hipLaunchKernelGGL(sa_bwd_dp_kernel<32>, g2, blk2, 0, s, a, NH, PB);
     else hipLaunchKernelGGL(sa_bwd_dp_kernel<64>, g2, blk2, 0, s, a, NH, PB);
     const int mq = a.m * (a.dh / 4);
     hipLaunchKernelGGL(sa_bwd_dp_merge_kernel, dim3((mq + 255) / 256, a.H, a.per_user ? a.users.B : 1), dim3(256), 0,
