@@ -35,59 +35,105 @@ __device__ __forceinline__ void lse_merge(float& M, float& Z, float Mo, float Zo
 
 }  // namespace
 
-// One wave per 16 rows of one head; S^T[16 rows x 16 prototypes] blocks by MFMA.
+// bf16: one wave per head (4 heads per block; blocks of the same rows for
+// the other heads are dispatched next to it, so every row is read while it is
+// in the caches), walking 32-row tiles with the next tile's key fragments
+// loaded while the current one is computed.  The wave keeps P for up to 128
+// prototypes in registers (A operands, one 16-prototype block per sb); each
+// 16-row half gives S [16 sb prototypes x 16 rows] by MFMA, a lane holding
+// prototypes 16 sb + 4 g + i of row l16: the row maximum and the sum of
+// 2^(s c - max) take the lane's 4 NSB values, then the 4 lanes of the row
+// (one exponential per score, two shuffles per reduction).  More than 128
+// prototypes are taken 128 at a time with a running (max, sum) merge.
 template <int DH>
 __global__ __launch_bounds__(256) void sa_bf16_tok_lse_kernel(TokLseArgs a) {
     constexpr int KC = DH / 32;
+    constexpr int NSB = 8;                        // 16-prototype blocks held at a time
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, l16 = lane & 15;
-    const int h = blockIdx.y;
-    const int64_t r0 = ((int64_t)blockIdx.x * 4 + wave) * 16;
-    if (r0 >= a.total_rows) return;
-    const bf16* Kg = (const bf16*)a.K;
-    const bf16* Pg = (const bf16*)a.P;
+    const int h = blockIdx.x * 4 + wave;
+    if (h >= a.H) return;
+    const int64_t ntile = (a.total_rows + 31) / 32;
+    const bf16* Kg = (const bf16*)a.K + (int64_t)h * DH + 8 * g;
+    const bf16* Pg = (const bf16*)a.P + (int64_t)h * a.m * DH + 8 * g;
+    const int nchunk = (a.m + 16 * NSB - 1) / (16 * NSB);
 
-    const int64_t arow = r0 + l16;              // row this lane feeds into the A operand
-    const bool aval = row_valid(a, arow);
-    bf16x8 ka[KC];
+    // key fragments of tile t: B operands, column = row 32 t + 16 half + l16 (clamped), k = dh
+    auto load_k = [&](int64_t t, bf16x8 (&kf)[2][KC]) {
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-        if (aval) ka[kc] = *(const bf16x8*)(Kg + arow * a.k_stride + (int64_t)h * DH + 32 * kc + 8 * g);
-        else ka[kc] = (bf16x8){};
-    }
-    float M[4], Z[4];
+        for (int half = 0; half < 2; ++half) {
+            const int64_t row = min(32 * t + 16 * half + l16, a.total_rows - 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        M[i] = -INFINITY;
-        Z[i] = 0.f;
-    }
-    for (int j0 = 0; j0 < a.m; j0 += 16) {
-        const bf16* pr = Pg + ((int64_t)h * a.m + j0 + l16) * DH;
-        f32x4 d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kc], *(const bf16x8*)(pr + 32 * kc + 8 * g), d, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lse_merge(M[i], Z[i], d[i] * a.c, 1.f);
-    }
-    // combine the 16 prototype columns held by the 16 lanes of each group
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-            const float Mo = __shfl_xor(M[i], off, 64);
-            const float Zo = __shfl_xor(Z[i], off, 64);
-            lse_merge(M[i], Z[i], Mo, Zo);
+            for (int kc = 0; kc < KC; ++kc) kf[half][kc] = *(const bf16x8*)(Kg + row * a.k_stride + 32 * kc);
         }
-    }
-    if (l16 == 0) {
+    };
+    // prototype fragments: A operands, row = prototype 16 sb + l16 (clamped), k = dh
+    bf16x8 pf[NSB][KC];
+    auto load_p = [&](int c) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t row = r0 + 4 * g + i;
-            if (row >= a.total_rows) continue;
-            const float v = row_valid(a, row) ? M[i] + log2f(Z[i]) : -INFINITY;
-            a.lse2_tok[row * a.H + h] = v;
-            if (a.lse_out) a.lse_out[row * a.H + h] = v * kLn2;
+        for (int sb = 0; sb < NSB; ++sb) {
+            const int j = min(16 * (NSB * c + sb) + l16, a.m - 1);
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) pf[sb][kc] = *(const bf16x8*)(Pg + (int64_t)j * DH + 32 * kc);
+        }
+    };
+    if (nchunk == 1) load_p(0);
+
+    int64_t t = blockIdx.y;
+    bf16x8 kf[2][KC], kn[2][KC];
+    if (t < ntile) load_k(t, kf);
+    for (; t < ntile; t += gridDim.y) {
+        const bool more = t + gridDim.y < ntile;
+        if (more) load_k(t + gridDim.y, kn);
+        float M[2] = {-INFINITY, -INFINITY}, Z[2] = {0.f, 0.f};
+        for (int c = 0; c < nchunk; ++c) {
+            if (nchunk > 1) load_p(c);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                float x[NSB][4];
+                float mx = -INFINITY;
+#pragma unroll
+                for (int sb = 0; sb < NSB; ++sb) {
+                    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kc = 0; kc < KC; ++kc)
+                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[sb][kc], kf[half][kc], sc, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool ok = 16 * (NSB * c + sb) + 4 * g + i < a.m;
+                        x[sb][i] = ok ? sc[i] * a.c : -INFINITY;
+                        mx = fmaxf(mx, x[sb][i]);
+                    }
+                }
+                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                float z = 0.f;
+#pragma unroll
+                for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) z += __builtin_amdgcn_exp2f(x[sb][i] - mx);
+                z += __shfl_xor(z, 16, 64);
+                z += __shfl_xor(z, 32, 64);
+                lse_merge(M[half], Z[half], mx, z);
+            }
+        }
+        // lanes of group 0 write the 16 rows of each half
+        if (g == 0) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int64_t row = 32 * t + 16 * half + l16;
+                if (row < a.total_rows) {
+                    const float v = row_valid(a, row) ? M[half] + log2f(Z[half]) : -INFINITY;
+                    a.lse2_tok[row * a.H + h] = v;
+                    if (a.lse_out) a.lse_out[row * a.H + h] = v * kLn2;
+                }
+            }
+        }
+        if (more) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) kf[half][kc] = kn[half][kc];
         }
     }
 }
@@ -115,7 +161,12 @@ __global__ __launch_bounds__(256) void sa_f32_tok_lse_kernel(TokLseArgs a) {
 
 hipError_t launch_bf16_tok_lse(const TokLseArgs& a, hipStream_t s) {
     if (a.total_rows == 0) return hipSuccess;
-    dim3 grid((unsigned)((a.total_rows + 63) / 64), a.H);
+    // x: groups of 4 heads (the blocks of one row range run side by side), y:
+    // row tiles, strided; a few waves per SIMD of work per CU
+    const int64_t ntile = (a.total_rows + 31) / 32;
+    const int hg = (a.H + 3) / 4;
+    const int64_t want = (int64_t)2048 / hg;          // ~8 blocks per CU on 256 CUs
+    dim3 grid((unsigned)hg, (unsigned)(ntile < want ? ntile : want));
     switch (a.dh) {
         case 32: hipLaunchKernelGGL(sa_bf16_tok_lse_kernel<32>, grid, dim3(256), 0, s, a); break;
         case 64: hipLaunchKernelGGL(sa_bf16_tok_lse_kernel<64>, grid, dim3(256), 0, s, a); break;
