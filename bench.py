@@ -97,6 +97,31 @@ def copy_calibration(mib: int, steps: int) -> None:
                       "GBps": 4 * n / dt / 1e9}))
 
 
+def hbm_probe(mib: int, steps: int) -> None:
+    """Plain torch kernels over an fp32 buffer of mib MiB, timed with events
+    after a warm-up: a fill (write only), a sum (read only) and a copy_ (read
+    and write).  The rates bound what a kernel with the same read/write mix
+    can reach on this device."""
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    out = {"probe": "hbm", "bytes": 4 * n}
+    for name, fn, nbytes in (("fill", lambda: y.fill_(1.0), 4 * n), ("sum", lambda: x.sum(), 4 * n),
+                             ("copy", lambda: y.copy_(x), 8 * n)):
+        for _ in range(10):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        out[name] = {"ms": ms, "GBps": nbytes / ms / 1e6}
+    print(json.dumps(out))
+
+
 def cpu_baseline(w, n_users: int):
     """The oracle as it stands, on the first n_users users of the workload."""
     import oracle
@@ -291,19 +316,21 @@ def bench_backward(args):
     dS = torch.from_numpy(np.random.default_rng(8).standard_normal((B, H, m, dh), dtype=np.float32)).to(dev)
     pb = sa.make_problem(B, H, m, dh, K.shape[0], dtype="bf16")
     ws = torch.empty(sa.sa_backward_workspace_size(pb), dtype=torch.uint8, device=dev)
-    out = (torch.empty(P.shape, dtype=torch.float32, device=dev), torch.zeros(K.shape, dtype=torch.float32, device=dev),
-           torch.zeros(V.shape, dtype=torch.float32, device=dev))
+    gdt = torch.bfloat16 if args.grad_dtype == "bf16" else torch.float32
+    gsz = 2 if args.grad_dtype == "bf16" else 4
+    out = (torch.empty(P.shape, dtype=torch.float32, device=dev), torch.zeros(K.shape, dtype=gdt, device=dev),
+           torch.zeros(V.shape, dtype=gdt, device=dev))
 
     def step():
         sa.sa_backward(P, K, V, S, lse, dS, cu_offsets=cu, workspace=ws, out=out)
 
     ms_per_step, call_ms = _timed(step, args.steps, args.warmup)
     call_avg = sum(call_ms) / len(call_ms)
-    # every K, V element read once, dK, dV written once (fp32), plus P, dP, S, dS, lse and offsets
-    alg_bytes = tokens * H * dh * (2 + 2 + 4 + 4) + H * m * dh * (2 + 4) + B * H * m * (dh * 8 + 4) + 4 * (B + 1)
+    # every K, V element read once, dK, dV written once (fp32 or bf16), plus P, dP, S, dS, lse and offsets
+    alg_bytes = tokens * H * dh * (2 + 2 + 2 * gsz) + H * m * dh * (2 + 4) + B * H * m * (dh * 8 + 4) + 4 * (B + 1)
     achieved = alg_bytes / (call_avg / 1e3) / 1e9
     print(json.dumps({
-        "metric": BACKWARD_METRIC,
+        "metric": BACKWARD_METRIC + (", bf16 gradients" if args.grad_dtype == "bf16" else ""),
         "value": tokens / (ms_per_step / 1e3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -316,7 +343,8 @@ def bench_backward(args):
         "dtype": "bf16",
         "data": "synthetic (seeded normal draws shaped like the paper's histories)",
         "config": {"workload": "backward_full100k_bf16", "B": B, "sum_L": tokens, "L_max": int(w["lengths"].max()),
-                   "H": H, "m": m, "dh": dh, "layout": "packed", "parallelism": "single GPU"},
+                   "H": H, "m": m, "dh": dh, "layout": "packed", "grad_dtype": args.grad_dtype,
+                   "parallelism": "single GPU"},
         "roofline": {
             "bound": "hbm",
             "kernel": "sa_backward (all launches of one call)",
@@ -489,8 +517,12 @@ def main():
     ap.add_argument("--stca-targets", type=int, default=40, help="workload 9: targets per user")
     ap.add_argument("--norm", choices=("history", "prototype"), default="history",
                     help="workloads 1-4: softmax axis (prototype = the paper's normalisation display, row A9)")
+    ap.add_argument("--grad-dtype", choices=("fp32", "bf16"), default="fp32",
+                    help="workload 7: element type of dK and dV")
     ap.add_argument("--cpu-users", type=int, default=4, help="users in the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hbm-probe-mib", type=int, default=0,
+                    help="time torch fill / sum / copy_ over a buffer of this many MiB and exit")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the forward, time a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -499,6 +531,9 @@ def main():
               "(users shard across GPUs with no exchange; run one process per GPU).", file=sys.stderr)
         sys.exit(2)
 
+    if args.hbm_probe_mib:
+        hbm_probe(args.hbm_probe_mib, args.steps)
+        return
     if args.copy_mib:
         copy_calibration(args.copy_mib, args.steps)
         return

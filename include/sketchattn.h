@@ -101,8 +101,13 @@ typedef struct sa_problem {
                                across users, section 3.1) */
     int32_t chunk_rows;     /* 0: automatic work split over the device; > 0: every work
                                segment covers this many rows (multiple of 32) */
-    int32_t flags;          /* reserved, must be 0 */
+    int32_t flags;          /* 0, or SA_FLAG_BF16_GRADS for sa_backward; every other
+                               entry point requires 0 */
 } sa_problem;
+
+/* sa_problem.flags bit for sa_backward only: dK and dV are written as bf16
+ * (the fp32 sums rounded to nearest even), the element type of K and V. */
+#define SA_FLAG_BF16_GRADS 1
 
 /*
  * Sketch Attention forward over a ragged batch of user histories.
@@ -211,22 +216,22 @@ size_t sa_forward_fused_proj_workspace_size(const sa_problem* pb, int32_t d_mode
  * S, lse   the forward's outputs [B, H, m, dh] and [B, H, m] (lse is required).
  * dS       [B, H, m, dh] fp32 upstream gradient.
  * dP       fp32, shaped like P ([H, m, dh], or [B, H, m, dh] with per-user P).
- * dK, dV   fp32 [rows, H, dh] (packed) or [B, L_max, H, dh] (dense), dh
- *          contiguous, heads contiguous in a row.  Rows of users (valid,
- *          masked or past a dense length) are written; masked rows get 0.
- *          Rows outside every user and dense padding past L_b are left as
- *          they are.
+ * dK, dV   [rows, H, dh] (packed) or [B, L_max, H, dh] (dense), dh
+ *          contiguous, heads contiguous in a row, 16-byte aligned; fp32, or
+ *          bf16 when pb->flags has SA_FLAG_BF16_GRADS.  Every row of a user
+ *          (valid or masked) is written; masked rows get 0.  Rows outside
+ *          every user and dense padding past L_b are left as they are.
  * workspace, workspace_bytes: at least sa_backward_workspace_size(pb).
  *
  * Compiled shapes: bf16, history axis, dh in {32, 64}, m in {32, 64, 128,
  * 256}; any H; P shared or per user.  Others return SA_ERR_UNSUPPORTED.
- * P, K, V, S, dS and dP are 16-byte aligned.  Deterministic: dP's partial
+ * P, K, V, S, dS, dP, dK and dV are 16-byte aligned.  Deterministic: dP's partial
  * sums are added in a fixed order, no float atomics.
  */
 sa_status sa_backward(const sa_problem* pb, const void* P, const void* K, const void* V,
                       const int32_t* cu_offsets, const int32_t* lengths, const uint8_t* mask,
-                      const float* S, const float* lse, const float* dS, float* dP, float* dK,
-                      float* dV, void* workspace, size_t workspace_bytes, hipStream_t stream);
+                      const float* S, const float* lse, const float* dS, float* dP, void* dK,
+                      void* dV, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace sa_backward needs on the current device (0 if the
  * problem is invalid or unsupported; sa_last_error() says why).  pb->L_max

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libsketchattn.so")
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
 SA_DTYPE_F32, SA_DTYPE_BF16 = 0, 1
 SA_NORM_HISTORY, SA_NORM_PROTOTYPE = 0, 1
+SA_FLAG_BF16_GRADS = 1
 _NORMS = {"history": SA_NORM_HISTORY, "prototype": SA_NORM_PROTOTYPE}
 
 EXPORTED = ("sa_forward", "sa_forward_workspace_size", "sa_forward_kernel_name", "sa_forward_fused_proj",
@@ -140,11 +141,11 @@ def _stream_handle(device):
 
 
 def make_problem(B, H, m, dh, total_rows, L_max=0, dtype="bf16", norm="history", scale=0.0,
-                 k_row_stride=0, v_row_stride=0, q_batch_stride=0, chunk_rows=0) -> SaProblem:
+                 k_row_stride=0, v_row_stride=0, q_batch_stride=0, chunk_rows=0, flags=0) -> SaProblem:
     return SaProblem(B=B, H=H, m=m, dh=dh, total_rows=total_rows, L_max=L_max,
                      dtype=SA_DTYPE_BF16 if dtype == "bf16" else SA_DTYPE_F32,
                      norm=_NORMS[norm], scale=float(scale or 0.0), k_row_stride=k_row_stride,
-                     v_row_stride=v_row_stride, q_batch_stride=q_batch_stride, chunk_rows=chunk_rows, flags=0)
+                     v_row_stride=v_row_stride, q_batch_stride=q_batch_stride, chunk_rows=chunk_rows, flags=flags)
 
 
 def sa_forward_workspace_size(pb: SaProblem) -> int:
@@ -345,11 +346,13 @@ def sa_refine_workspace_size(pb, d_model: int, n_layers: int) -> int:
 
 
 def sa_backward(P, K, V, S, lse, dS, cu_offsets=None, lengths=None, mask=None, scale: float | None = None,
-                workspace=None, out=None):
-    """Gradients of the history-axis forward: returns (dP, dK, dV) in fp32.
-    P, K, V, cu_offsets, lengths, mask as given to :func:`sa_forward`; S and
-    lse its outputs; dS [B, H, m, dh] fp32.  dK and dV are zero-initialised
-    here, so rows outside every user come back as 0."""
+                workspace=None, out=None, grad_dtype=None):
+    """Gradients of the history-axis forward: returns (dP, dK, dV), dP in
+    fp32 and dK, dV in ``grad_dtype`` (torch.float32, the default, or
+    torch.bfloat16, the element type of K and V).  P, K, V, cu_offsets,
+    lengths, mask as given to :func:`sa_forward`; S and lse its outputs; dS
+    [B, H, m, dh] fp32.  dK and dV are zero-initialised here, so rows outside
+    every user come back as 0."""
     import torch
     lib = load_library()
     dev = K.device
@@ -366,8 +369,14 @@ def sa_backward(P, K, V, S, lse, dS, cu_offsets=None, lengths=None, mask=None, s
     S, lse, dS = S.contiguous(), lse.contiguous(), dS.to(torch.float32).contiguous()
     if mask is not None:
         mask = (mask.to(torch.uint8) if mask.dtype == torch.bool else mask).contiguous()
+    if out is not None:
+        grad_dtype = out[1].dtype
+    grad_dtype = grad_dtype or torch.float32
+    if grad_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"grad_dtype must be torch.float32 or torch.bfloat16 (got {grad_dtype})")
     pb = make_problem(B, H, m, dh, rows, L_max=L_max, dtype=_dtype_name(K), scale=scale or 0.0,
-                      q_batch_stride=(H * m * dh if per_user else 0))
+                      q_batch_stride=(H * m * dh if per_user else 0),
+                      flags=SA_FLAG_BF16_GRADS if grad_dtype == torch.bfloat16 else 0)
     nws = int(lib.sa_backward_workspace_size(ctypes.byref(pb)))
     if nws == 0:
         _check(lib.sa_backward(ctypes.byref(pb), *([None] * 13), 0, None))
@@ -375,10 +384,12 @@ def sa_backward(P, K, V, S, lse, dS, cu_offsets=None, lengths=None, mask=None, s
         workspace = torch.empty(nws, dtype=torch.uint8, device=dev)
     if out is None:
         dP = torch.empty(P.shape, dtype=torch.float32, device=dev)
-        dK = torch.zeros(K.shape, dtype=torch.float32, device=dev)
-        dV = torch.zeros(V.shape, dtype=torch.float32, device=dev)
+        dK = torch.zeros(K.shape, dtype=grad_dtype, device=dev)
+        dV = torch.zeros(V.shape, dtype=grad_dtype, device=dev)
     else:
         dP, dK, dV = out
+        if dK.dtype != grad_dtype or dV.dtype != grad_dtype:
+            raise ValueError("out: dK and dV must share one dtype")
     st = lib.sa_backward(ctypes.byref(pb), _ptr(P), _ptr(K), _ptr(V), _ptr(cu_offsets), _ptr(lengths), _ptr(mask),
                          _ptr(S), _ptr(lse), _ptr(dS), _ptr(dP), _ptr(dK), _ptr(dV), _ptr(workspace), nws,
                          _stream_handle(dev))

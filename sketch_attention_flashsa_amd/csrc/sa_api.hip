@@ -58,6 +58,8 @@ constexpr int kRowMinF32 = 128;
 // Share (percent) of the rows that the first half of the streaming kernel's
 // row ranges takes when two of its blocks share a CU (measured on MI355X).
 constexpr int kStreamSplit = 64;
+// Blocks per CU of the backward's dK/dV kernel (row ranges x heads).
+constexpr int kDkdvBlocksPerCu = 4;
 
 // Everything the dispatcher derives from the problem.
 struct Plan {
@@ -763,7 +765,13 @@ struct BwdPlan {
     size_t off_vcu = 0, off_D = 0, off_L2 = 0, off_dsb = 0, off_part = 0, total = 0;
 };
 
-sa_status make_bwd_plan(const sa_problem* pb, bool packed, BwdPlan* bp) {
+sa_status make_bwd_plan(const sa_problem* pb_in, bool packed, BwdPlan* bp) {
+    if (!pb_in) return fail(SA_ERR_INVALID_ARG, "problem is NULL");
+    if (pb_in->flags & ~SA_FLAG_BF16_GRADS)
+        return fail(SA_ERR_INVALID_ARG, "backward: flags must be 0 or SA_FLAG_BF16_GRADS (got %d)", pb_in->flags);
+    sa_problem q = *pb_in;      // the forward's checks see flags = 0
+    q.flags = 0;
+    const sa_problem* pb = &q;
     sa_status st = make_plan(pb, packed, &bp->fw);
     if (st != SA_OK) return st;
     if (pb->dtype != SA_DTYPE_BF16) return fail(SA_ERR_UNSUPPORTED, "backward: bf16 inputs only");
@@ -781,7 +789,9 @@ sa_status make_bwd_plan(const sa_problem* pb, bool packed, BwdPlan* bp) {
         bp->G = bp->G1 = (int)(G > 0 ? G : 1);
     } else {
         bp->G = cus * 2 / groups > 0 ? cus * 2 / groups : 1;
-        bp->G1 = cus * 2 / pb->H > 0 ? cus * 2 / pb->H : 1;
+        int bpc = kDkdvBlocksPerCu;
+        if (const char* e = getenv("SA_BWD_BLOCKS_PER_CU")) bpc = atoi(e) > 0 ? atoi(e) : bpc;
+        bp->G1 = cus * bpc / pb->H > 0 ? cus * bpc / pb->H : 1;
     }
     const size_t bhm = (size_t)pb->B * pb->H * pb->m;
     size_t off = 0;
@@ -805,7 +815,7 @@ extern "C" {
 
 sa_status sa_backward(const sa_problem* pb, const void* P, const void* K, const void* V, const int32_t* cu_offsets,
                       const int32_t* lengths, const uint8_t* mask, const float* S, const float* lse, const float* dS,
-                      float* dP, float* dK, float* dV, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                      float* dP, void* dK, void* dV, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     g_err[0] = 0;
     BwdPlan bp;
     const bool packed = cu_offsets != nullptr;
@@ -816,8 +826,8 @@ sa_status sa_backward(const sa_problem* pb, const void* P, const void* K, const 
     if (!P || !K || !V || !S || !lse || !dS || !dP || !dK || !dV)
         return fail(SA_ERR_INVALID_ARG, "P, K, V, S, lse, dS, dP, dK and dV must be non-NULL");
     if (!aligned(P, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(S, 16) || !aligned(dS, 16) ||
-        !aligned(dP, 16) || !aligned(dK, 4) || !aligned(dV, 4) || !aligned(lse, 4))
-        return fail(SA_ERR_INVALID_ARG, "P, K, V, S, dS and dP must be 16-byte aligned");
+        !aligned(dP, 16) || !aligned(dK, 16) || !aligned(dV, 16) || !aligned(lse, 4))
+        return fail(SA_ERR_INVALID_ARG, "P, K, V, S, dS, dP, dK and dV must be 16-byte aligned");
     if (!workspace || workspace_bytes < bp.total)
         return fail(SA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", bp.total, workspace_bytes);
     if (!aligned(workspace, kAlign)) return fail(SA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -864,6 +874,7 @@ sa_status sa_backward(const sa_problem* pb, const void* P, const void* K, const 
     a.dSb = (sa::bf16*)(ws + bp.off_dsb);
     a.dK = dK;
     a.dV = dV;
+    a.grads_bf16 = (pb->flags & SA_FLAG_BF16_GRADS) != 0;
     a.part = sa::Partials{(float*)(ws + bp.off_part), nullptr, nullptr};
     a.dP = dP;
     a.per_user = pb->q_batch_stride != 0;

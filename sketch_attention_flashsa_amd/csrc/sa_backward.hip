@@ -11,14 +11,18 @@
 //   sa_bwd_prep_kernel   D_j, lse_j in log2 units, and dS in bf16 (MFMA operand);
 //   sa_bwd_dkdv_kernel   dK and dV.  A block owns a row range and one head; P_h
 //                        and dS (bf16) of the current user sit in LDS; each wave
-//                        takes 16-row tiles and ALL m prototypes, so the sums
-//                        over j stay inside the wave.  Scores are computed as
+//                        takes 32-row tiles (two 16-row halves that share every
+//                        operand read from LDS) and ALL m prototypes, so the
+//                        sums over j stay inside the wave.  Scores are computed as
 //                        S = P K^T (prototypes in the MFMA output rows), which
 //                        is the layout in which the prototype index can be the
 //                        reduction index of the next two products:
-//                        dV = A^T dS and dK = ds^T P (B operands read with
-//                        ds_read_b64_tr_b16).  K and V fragments come straight
-//                        from memory (16 bytes per lane);
+//                        computed transposed, dV^T = dS^T A^T and dK^T = P^T ds^T
+//                        (dS and P as A operands read with ds_read_b64_tr_b16),
+//                        so a lane's results are four consecutive dh of one row
+//                        and leave in 16-byte (fp32) or 8-byte (bf16) stores.
+//                        K and V fragments come straight from memory (16 bytes
+//                        per lane);
 //   sa_bwd_dp_kernel     dP.  Waves own (head, 32-prototype block) as in the
 //                        forward; scores as S^T = K P^T (rows in the output
 //                        rows), so rows are the reduction index of
@@ -29,6 +33,8 @@
 // (past the end, masked) get weight 0 by select, and their K values are
 // zeroed before the dP product, so NaN in masked rows cannot leak.
 #include <stdlib.h>
+
+#include <type_traits>
 
 #include "sa_device.h"
 
@@ -59,13 +65,13 @@ __global__ __launch_bounds__(256) void sa_bwd_prep_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- dK, dV
 // Waves per SIMD the dK/dV kernel is compiled for (blocks of four waves, one
-// per SIMD): as many as its registers allow, and no more than LDS allows
-// (P and dS of one head take 4 m (dh + 8) bytes).
-constexpr int dkdv_occupancy(int DH, int NKB) {
-    return DH == 32 ? (NKB == 8 ? 3 : 4) : (NKB == 2 || NKB == 4) ? 4 : 2;
-}
+// per SIMD): as many as its registers allow (a wave holds two 16-row halves'
+// K and V fragments, their prefetch and their dK, dV sums: ~250 registers at
+// dh = 64, ~160 at dh = 32), and no more than LDS allows (P and dS of one
+// head take 4 m (dh + 8) bytes).
+constexpr int dkdv_occupancy(int DH, int NKB) { return DH == 32 ? 3 : 2; }
 
-template <int DH, int NKB>
+template <int DH, int NKB, bool GBF16, bool MASKED>
 __global__ __launch_bounds__(256, dkdv_occupancy(DH, NKB)) void sa_bwd_dkdv_kernel(BwdArgs a) {
     constexpr int M = 32 * NKB;
     constexpr int KC = DH / 32, DB = DH / 16;
@@ -111,56 +117,86 @@ __global__ __launch_bounds__(256, dkdv_occupancy(DH, NKB)) void sa_bwd_dkdv_kern
 
         const int64_t gbase = a.users.row_base(b) + (s_lo - us);
         const int n = (int)(s_hi - s_lo);
-        // K and V fragments of a 16-row tile: B operands (column = row l16 of
-        // the tile, k = dh); the next tile's are loaded while this one computes
-        bf16x8 kf[KC], vf[KC];
-        auto load_tile = [&](int t0, bf16x8 (&kk)[KC], bf16x8 (&vv)[KC]) {
-            const int64_t row = gbase + min(t0 + l16, n - 1);
+        // K and V fragments of a 32-row tile, two 16-row halves u: B operands
+        // (column = row 16 u + l16 of the tile, k = dh), and the rows' mask
+        // bytes; the next tile's are loaded while this one computes.  Both
+        // halves share every P and dS operand read from LDS.  Lanes past the
+        // segment end take row n - 1 whole (its values and its mask byte), so
+        // they compute exactly that row's gradients and their stores rewrite
+        // its bytes with the same values: every lane stores, and the number
+        // of memory operations per tile is fixed.
+        bf16x8 kf[2][KC], vf[2][KC];
+        int mf[2] = {1, 1};
+        auto load_tile = [&](int t0, bf16x8 (&kk)[2][KC], bf16x8 (&vv)[2][KC], int (&mm)[2]) {
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                kk[kc] = *(const bf16x8*)(Kg + row * a.k_stride + (int64_t)h * DH + 32 * kc + 8 * g);
-                vv[kc] = *(const bf16x8*)(Vg + row * a.v_stride + (int64_t)h * DH + 32 * kc + 8 * g);
+            for (int u = 0; u < 2; ++u) {
+                const int64_t row = gbase + min(t0 + 16 * u + l16, n - 1);
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) {
+                    kk[u][kc] = *(const bf16x8*)(Kg + row * a.k_stride + (int64_t)h * DH + 32 * kc + 8 * g);
+                    vv[u][kc] = *(const bf16x8*)(Vg + row * a.v_stride + (int64_t)h * DH + 32 * kc + 8 * g);
+                }
+                if (a.mask != nullptr) mm[u] = a.mask[row];
             }
         };
-        if (16 * wave < n) load_tile(16 * wave, kf, vf);
-        for (int t0 = 16 * wave; t0 < n; t0 += 64) {
-            const int tok = t0 + l16;
-            const bool valid = tok < n && (a.mask == nullptr || a.mask[gbase + min(tok, n - 1)] != 0);
-            bf16x8 kn[KC], vn[KC];
-            const bool more = t0 + 64 < n;
-            if (more) load_tile(t0 + 64, kn, vn);
-            f32x4 dva[DB], dka[DB];
+        if (32 * wave < n) load_tile(32 * wave, kf, vf, mf);
+        // settle the first tile here: otherwise the compiler treats kf and vf
+        // as loads in flight at the loop head and waits inside every tile's
+        // prototype loop, which also drains the next tile's prefetch
+        wait_vm<0>();
+        for (int t0 = 32 * wave; t0 < n; t0 += 128) {
+            bool valid[2];
 #pragma unroll
-            for (int db = 0; db < DB; ++db) dva[db] = dka[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            // one block of 32 prototypes at a time: weights and score
-            // gradients packed as the A operands (row = this lane's token, k =
-            // the 32 prototypes in the tok_of order) of dV += A^T dS and
-            // dK += ds^T P
-#pragma unroll 1
-            for (int kb = 0; kb < NKB; ++kb) {
-                float av[8], dv[8];
+            for (int u = 0; u < 2; ++u) valid[u] = mf[u] != 0;
+            bf16x8 kn[2][KC], vn[2][KC];
+            int mn[2] = {1, 1};
+            const bool more = t0 + 128 < n;
+            if (more) load_tile(t0 + 128, kn, vn, mn);
+            f32x4 dva[2][DB], dka[2][DB];
+            // one block of 32 prototypes: weights and score gradients packed
+            // as the B operands (column = this lane's row, k = the 32
+            // prototypes in the tok_of order) of dV^T += dS^T A^T and
+            // dK^T += P^T ds^T; the first block starts the sums (C = 0), so
+            // they need no clearing
+            auto step = [&](int kb, auto first) {
+                float av[2][8], dv[2][8];
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     const int pb = 2 * kb + half;
-                    f32x4 s = {0.f, 0.f, 0.f, 0.f}, da = {0.f, 0.f, 0.f, 0.f};
+                    f32x4 s[2], da[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) s[u] = da[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kc = 0; kc < KC; ++kc) {
                         const bf16x8 pa = *(const bf16x8*)&p_l[(16 * pb + l16) * PS + 32 * kc + 8 * g];
                         const bf16x8 ga = *(const bf16x8*)&g_l[(16 * pb + l16) * PS + 32 * kc + 8 * g];
-                        s = mfma(pa, kf[kc], s);
-                        da = mfma(ga, vf[kc], da);
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            s[u] = mfma(pa, kf[u][kc], s[u]);
+                            da[u] = mfma(ga, vf[u][kc], da[u]);
+                        }
                     }
                     const f32x4 l2 = *(const f32x4*)&l2_l[16 * pb + 4 * g];
                     const f32x4 dd = *(const f32x4*)&d_l[16 * pb + 4 * g];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float x = __builtin_amdgcn_exp2f(fmaf(s[i], a.c2, -l2[i]));
-                        av[4 * half + i] = valid ? x : 0.f;
-                        dv[4 * half + i] = valid ? x * (da[i] - dd[i]) : 0.f;
-                    }
+                    for (int u = 0; u < 2; ++u)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float x = __builtin_amdgcn_exp2f(fmaf(s[u][i], a.c2, -l2[i]));
+                            const float y = x * (da[u][i] - dd[i]);
+                            // masked rows: weight 0 by select (their values may be NaN)
+                            av[u][4 * half + i] = MASKED ? (valid[u] ? x : 0.f) : x;
+                            dv[u][4 * half + i] = MASKED ? (valid[u] ? y : 0.f) : y;
+                        }
                 }
-                const bf16x8 apk = cat8(pack2(av[0], av[1]), pack2(av[2], av[3]), pack2(av[4], av[5]), pack2(av[6], av[7]));
-                const bf16x8 dpk = cat8(pack2(dv[0], dv[1]), pack2(dv[2], dv[3]), pack2(dv[4], dv[5]), pack2(dv[6], dv[7]));
+                bf16x8 apk[2], dpk[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    apk[u] = cat8(pack2(av[u][0], av[u][1]), pack2(av[u][2], av[u][3]), pack2(av[u][4], av[u][5]),
+                                  pack2(av[u][6], av[u][7]));
+                    dpk[u] = cat8(pack2(dv[u][0], dv[u][1]), pack2(dv[u][2], dv[u][3]), pack2(dv[u][4], dv[u][5]),
+                                  pack2(dv[u][6], dv[u][7]));
+                }
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     const uint32_t o = tr_off + (uint32_t)((32 * kb * PS + 16 * db) * 2);
@@ -172,28 +208,49 @@ __global__ __launch_bounds__(256, dkdv_occupancy(DH, NKB)) void sa_bwd_dkdv_kern
                     gt.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(g_base + o + 16 * PS * 2));
                     pt.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(p_base + o));
                     pt.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(p_base + o + 16 * PS * 2));
-                    dva[db] = mfma(apk, gt.v, dva[db]);
-                    dka[db] = mfma(dpk, pt.v, dka[db]);
-                }
-            }
-            // rows 4g + i of the tile, columns 16 db + l16
+                    // transposed products: the lane's four results are four
+                    // consecutive dh of one row
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = t0 + 4 * g + i;
-                if (t >= n) continue;
-                const int64_t r = gbase + t;
+                    for (int u = 0; u < 2; ++u) {
+                        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                        dva[u][db] = mfma(gt.v, apk[u], decltype(first)::value ? zero : dva[u][db]);
+                        dka[u][db] = mfma(pt.v, dpk[u], decltype(first)::value ? zero : dka[u][db]);
+                    }
+                }
+            };
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) dva[u][db] = dka[u][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+            for (int kb = 0; kb < NKB; ++kb) step(kb, std::false_type{});
+            // row t0 + 16 u + l16, columns 16 db + 4 g + 0..3: one 16-byte
+            // (fp32) or 8-byte (bf16) store per tensor and dh block
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int64_t r = gbase + min(t0 + 16 * u + l16, n - 1);
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const int64_t o = (r * a.H + h) * DH + 16 * db + l16;
-                    a.dV[o] = dva[db][i];
-                    a.dK[o] = dka[db][i] * a.c;
+                    const int64_t o = (r * a.H + h) * DH + 16 * db + 4 * g;
+                    const f32x4 dk = dka[u][db] * a.c;
+                    if constexpr (GBF16) {
+                        *(bf16x4*)((bf16*)a.dV + o) = __builtin_convertvector(dva[u][db], bf16x4);
+                        *(bf16x4*)((bf16*)a.dK + o) = __builtin_convertvector(dk, bf16x4);
+                    } else {
+                        *(f32x4*)((float*)a.dV + o) = dva[u][db];
+                        *(f32x4*)((float*)a.dK + o) = dk;
+                    }
                 }
             }
             if (more) {
 #pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
-                    kf[kc] = kn[kc];
-                    vf[kc] = vn[kc];
+                for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                    for (int kc = 0; kc < KC; ++kc) {
+                        kf[u][kc] = kn[u][kc];
+                        vf[u][kc] = vn[u][kc];
+                    }
+                    mf[u] = mn[u];
                 }
             }
         }
@@ -632,8 +689,14 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     const int64_t n = (int64_t)a.users.B * a.H * a.m;
     hipLaunchKernelGGL(sa_bwd_prep_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
     const dim3 g1(a.G1, a.H);
-#define SA_DKDV(D_, K_) \
-    if (a.dh == D_ && a.m == 32 * K_) hipLaunchKernelGGL((sa_bwd_dkdv_kernel<D_, K_>), g1, dim3(256), 0, s, a);
+    const bool masked = a.mask != nullptr;
+#define SA_DKDV(D_, K_)                                                                                          \
+    if (a.dh == D_ && a.m == 32 * K_) {                                                                          \
+        if (a.grads_bf16 && masked) hipLaunchKernelGGL((sa_bwd_dkdv_kernel<D_, K_, true, true>), g1, dim3(256), 0, s, a); \
+        if (a.grads_bf16 && !masked) hipLaunchKernelGGL((sa_bwd_dkdv_kernel<D_, K_, true, false>), g1, dim3(256), 0, s, a); \
+        if (!a.grads_bf16 && masked) hipLaunchKernelGGL((sa_bwd_dkdv_kernel<D_, K_, false, true>), g1, dim3(256), 0, s, a); \
+        if (!a.grads_bf16 && !masked) hipLaunchKernelGGL((sa_bwd_dkdv_kernel<D_, K_, false, false>), g1, dim3(256), 0, s, a); \
+    }
     SA_DKDV(32, 1) SA_DKDV(32, 2) SA_DKDV(32, 4) SA_DKDV(32, 8) SA_DKDV(64, 1) SA_DKDV(64, 2) SA_DKDV(64, 4)
     SA_DKDV(64, 8)
 #undef SA_DKDV

@@ -276,8 +276,9 @@ struct BwdArgs {
     float* Dv;               // [B][H][m] dS . S
     float* L2v;              // [B][H][m] lse in log2 units
     bf16* dSb;               // [B][H][m][dh] dS in bf16
-    float* dK;               // [rows][H][dh]
-    float* dV;
+    void* dK;                // [rows][H][dh], fp32 or (grads_bf16) bf16
+    void* dV;
+    int32_t grads_bf16;
     Partials part;           // dP partials (acc only, lane-major)
     float* dP;               // [H][m][dh] or [B][H][m][dh]
     int32_t per_user;

@@ -201,6 +201,31 @@ def test_backward_entry_validation():
     st = lib.sa_backward(ctypes.byref(pb), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                          FAKE, n, None)
     assert st == sa.SA_ERR_INVALID_ARG and "lengths" in sa.sa_last_error()
+    # dK and dV take 16-byte vector stores
+    odd = ctypes.c_void_p((1 << 20) + 4)
+    st = lib.sa_backward(ctypes.byref(pb), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, odd, FAKE,
+                         FAKE, n, None)
+    assert st == sa.SA_ERR_INVALID_ARG and "aligned" in sa.sa_last_error()
+
+
+def test_bf16_gradient_flag():
+    """SA_FLAG_BF16_GRADS is a backward-only flag: accepted there with the
+    same workspace, rejected by the forward; other bits are rejected."""
+    lib = sa.load_library()
+    pb = sa.make_problem(16, 8, 128, 64, 1_600_000, dtype="bf16")
+    pf = sa.make_problem(16, 8, 128, 64, 1_600_000, dtype="bf16", flags=sa.SA_FLAG_BF16_GRADS)
+    n = lib.sa_backward_workspace_size(ctypes.byref(pb))
+    assert n > 0 and lib.sa_backward_workspace_size(ctypes.byref(pf)) == n
+    st = lib.sa_backward(ctypes.byref(pf), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                         FAKE, n - 1, None)
+    assert st == sa.SA_ERR_WORKSPACE, sa.sa_last_error()
+    bad = sa.make_problem(16, 8, 128, 64, 1_600_000, dtype="bf16", flags=2)
+    assert lib.sa_backward_workspace_size(ctypes.byref(bad)) == 0
+    st = lib.sa_backward(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                         FAKE, n, None)
+    assert st == sa.SA_ERR_INVALID_ARG and "flags" in sa.sa_last_error()
+    assert sa.sa_forward_workspace_size(pf) == 0
+    assert _call(pf, P=FAKE, K=FAKE, V=FAKE, cu=FAKE, S=FAKE) == sa.SA_ERR_INVALID_ARG
 
 
 def test_fused_two_pass_shapes():

@@ -24,7 +24,7 @@ def _upstream(w, seed):
     return torch.from_numpy(g.standard_normal((w["B"], w["H"], w["m"], w["dh"]), dtype=np.float32))
 
 
-def run_bw(w, dS, P=None, K=None, V=None, mask="default"):
+def run_bw(w, dS, P=None, K=None, V=None, mask="default", grad_dtype=None, raw=False):
     dev = device()
     P = (w["P"] if P is None else P).to(dev)
     K = (w["K"] if K is None else K).to(dev)
@@ -33,8 +33,10 @@ def run_bw(w, dS, P=None, K=None, V=None, mask="default"):
     mk = None if mk is None else mk.to(dev)
     kw = {"cu_offsets": w["cu_offsets"].to(dev)} if w["layout"] == "packed" else {"lengths": w["lengths"].to(dev)}
     S, lse = sa.sa_forward(P, K, V, mask=mk, return_lse=True, **kw)
-    dP, dK, dV = sa.sa_backward(P, K, V, S, lse, dS.to(dev), mask=mk, **kw)
+    dP, dK, dV = sa.sa_backward(P, K, V, S, lse, dS.to(dev), mask=mk, grad_dtype=grad_dtype, **kw)
     torch.cuda.synchronize()
+    if raw:
+        return dP.cpu(), dK.cpu(), dV.cpu()
     return tuple(t.double().cpu().numpy() for t in (dP, dK, dV))
 
 
@@ -63,6 +65,24 @@ def test_backward_shapes_ragged(dh, m, H):
     dS = _upstream(w, 1)
     print(f"backward dh={dh} m={m} H={H} rows={sum(lengths)}", flush=True)
     check(run_bw(w, dS), oracle_bw(w, dS), f"dh={dh} m={m} H={H}")
+
+
+@pytest.mark.parametrize("dh,m,H", [(64, 128, 8), (32, 256, 2), (32, 64, 3)])
+def test_backward_bf16_gradients(dh, m, H):
+    """dK and dV written as bf16: the fp32 gradients rounded to nearest even,
+    bitwise (the same sums, only the store differs), and within the bf16 bar
+    of the oracle; dP is unchanged."""
+    lengths = [640, 0, 1, 17, 33, 1100]
+    w = W.random_case(530 + dh + m, B=len(lengths), H=H, m=m, dh=dh, lengths=lengths, dtype="bf16")
+    dS = _upstream(w, 7)
+    print(f"backward bf16 gradients dh={dh} m={m} H={H}", flush=True)
+    f = run_bw(w, dS, raw=True)
+    b = run_bw(w, dS, grad_dtype=torch.bfloat16, raw=True)
+    assert b[1].dtype == torch.bfloat16 and b[2].dtype == torch.bfloat16
+    assert torch.equal(f[0], b[0]), "dP must not depend on the gradient dtype"
+    for n, x, y in (("dK", f[1], b[1]), ("dV", f[2], b[2])):
+        assert torch.equal(x.to(torch.bfloat16).view(torch.int16), y.view(torch.int16)), f"{n}: not the RNE rounding"
+    check(tuple(t.double().numpy() for t in b), oracle_bw(w, dS), f"bf16 gradients dh={dh} m={m} H={H}")
 
 
 def test_backward_workload4_reduced():
