@@ -64,7 +64,9 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
     constexpr int ROWB = CPR * 16;                        // bytes per row per tensor
     constexpr int D = 32 * CPR / (NW * 64);               // DMA ops per wave per tensor per stage
     constexpr int STAGE = 32 * ROWB;                      // bytes per tensor per stage
-    constexpr int VMS = 2 * D;                            // vector-memory ops per wave per stage
+    // vector-memory ops per wave per stage: K and V, and on the prototype axis
+    // one 4-byte load of the rows' normalisers
+    constexpr int VMS = 2 * D + (PROTO ? 1 : 0);
     constexpr int AHEAD = S - 1;                          // stages issued ahead of the one computed
     constexpr int FK = CPR < 16 ? CPR : 16;               // K swizzle period (rows)
     constexpr int FV = (CPR < 16 ? CPR : 16) / 2;         // V swizzle period (rows), chunk pairs
@@ -77,6 +79,9 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
     static_assert((AHEAD - 1) * VMS < 64, "ring depth");
 
     __shared__ __attribute__((aligned(1024))) unsigned char ring[S][2][STAGE];
+    // prototype axis: each wave's 64 dwords of a stage's per-(row, head)
+    // normalisers, entry row * NH + head for the first 32 * NH of them
+    __shared__ __attribute__((aligned(16))) float nlring[PROTO ? S : 1][PROTO ? NW * 64 : 1];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -149,6 +154,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
     // per-lane LDS byte offsets inside one 32-row stage (the swizzle of a row
     // depends on row % 16 only, so both 16-row halves share them)
     const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void*)&ring[0][0][0];
+    const uint32_t nl_lds = (uint32_t)(uintptr_t)(lds_void*)&nlring[0][0];
     uint32_t klane[KC];   // K operand reads, slot 0
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
@@ -192,6 +198,15 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
                 dma16s(kb, (uint32_t)(rr * (int)krow + dma_ck[d]), __builtin_amdgcn_readfirstlane(slot_lds + d * 1024));
                 dma16s(vb, (uint32_t)(rr * (int)vrow + dma_cv[d]),
                        __builtin_amdgcn_readfirstlane(slot_lds + STAGE + d * 1024));
+            }
+            if constexpr (PROTO) {
+                // lane -> entry (wave*64 + lane) mod 32 NH: row e / NH (clamped
+                // to the segment), head hc + e % NH; the entries past 32 NH repeat
+                const int e = (wave * 64 + lane) % (32 * NH);
+                const int rr = min(e / NH, last);
+                const float* nb = a.lse2_tok + (gbase + r0) * a.H + hc;
+                dma4c(nb, (uint32_t)((rr * a.H + min(e % NH, a.H - 1 - hc)) * 4),
+                      __builtin_amdgcn_readfirstlane(nl_lds + (uint32_t)(((t % S) * NW + wave) * 256)));
             }
         };
         // validity bits of stage t (32 rows): rows past the segment end or masked are 0
@@ -242,10 +257,15 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
             bf16x8 pk[NSB];
             if constexpr (PROTO) {
                 // prototype axis: weights 2^(s*c - lse2[row]) with the per-row normaliser
+                // the stage's normalisers arrived with it (direct-to-LDS)
+                const uint32_t nls = nl_lds + (uint32_t)((t % S) * NW * 256);
                 float nl[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    nl[j] = ((vj >> j) & 1) ? a.lse2_tok[(gbase + (int64_t)t * 32 + tok_of(g, j)) * a.H + head] : 0.f;
+                for (int j = 0; j < 8; ++j) {
+                    const float v = *(const __attribute__((address_space(3))) float*)(uintptr_t)(
+                        nls + (uint32_t)((tok_of(g, j) * NH + hl) * 4));
+                    nl[j] = ((vj >> j) & 1) ? v : 0.f;
+                }
 #pragma unroll
                 for (int sb = 0; sb < NSB; ++sb) {
                     float p[8];

@@ -99,6 +99,23 @@ __device__ __forceinline__ void dma16c(const void* base, uint32_t voff, uint32_t
         : "memory");
 }
 
+// Direct-to-LDS load of 4 bytes per lane (lane i's dword lands at lds + 4*i),
+// otherwise as dma16c: for small per-row values that travel with a stage.
+__device__ __forceinline__ void dma4c(const void* base, uint32_t voff, uint32_t lds) {
+    const uint64_t bb = (uint64_t)(uintptr_t)base;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(bb >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bb);
+    const uint64_t ub = ((uint64_t)hi << 32) | (uint64_t)lo;
+    base = (const void*)(uintptr_t)ub;
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %0, %1"
+        :
+        : "v"(voff), "s"(base), "s"(lds)
+        : "memory");
+}
+
 // acc *= f in place, for an accumulator kept in AGPRs (the MFMA accumulator
 // registers): each element goes through one VGPR and back, so the common
 // path never copies the accumulator.
