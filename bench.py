@@ -61,6 +61,12 @@ class _Hip:
         self.lib.hipEventDestroy(e)
 
 
+def _percentiles(xs):
+    """10th, 50th and 90th percentile of a list of launch times (nearest rank)."""
+    ys = sorted(xs)
+    return [ys[min(len(ys) - 1, int(q * len(ys)))] for q in (0.1, 0.5, 0.9)]
+
+
 def _kernel_hash() -> str:
     from sketch_attention_flashsa_amd.build import sources_hash
     return sources_hash()
@@ -615,6 +621,7 @@ def main():
             "algorithmic_bytes_per_launch": alg_bytes,
             "kernel_ms_avg": kern_avg_ms,
             "kernel_ms_min": min(kern_ms),
+            "kernel_ms_p10_p50_p90": _percentiles(kern_ms),
             "mfma_tflops": flops.sa_forward_flops(tokens, H, m, dh) / (kern_avg_ms / 1e3) / 1e12,
         },
         "cpu_baseline": None,
