@@ -275,6 +275,31 @@ def test_prototype_axis_workloads(cfg, B, max_len):
     assert_lse(lse.reshape(rows, -1), lo, dt, f"prototype axis lse, workload {cfg}")
 
 
+def test_prototype_axis_full_size_sampled():
+    """The 100K workload on the prototype axis in the launch configuration
+    the benchmark times: one whole user (100,000 rows) against the oracle run
+    on that user alone, and the per-row normalisers of sampled rows of every
+    user against the oracle run on each row alone."""
+    w = W.make(4)
+    S, lse = run(w, norm="prototype")
+    assert np.all(np.isfinite(S)) and np.all(np.isfinite(lse))
+    cu = w["cu_offsets"].numpy()
+    H = w["H"]
+    lse = lse.reshape(-1, H)
+    b = w["B"] - 1
+    lo_, hi_ = int(cu[b]), int(cu[b + 1])
+    one = torch.tensor([0, hi_ - lo_], dtype=torch.int32)
+    So, lo = oracle.forward(w["P"], w["K"][lo_:hi_], w["V"][lo_:hi_], cu_offsets=one, norm="prototype")
+    assert_parity(S[b], So[0], "bf16", f"prototype axis, user {b} of the 100K workload")
+    assert_lse(lse[lo_:hi_], lo, "bf16", f"prototype axis lse, user {b}")
+    rng = np.random.default_rng(44)
+    rows = [int(cu[u]) + int(rng.integers(0, cu[u + 1] - cu[u])) for u in range(w["B"]) for _ in range(2)]
+    single = torch.tensor([0, 1], dtype=torch.int32)
+    for r in rows:
+        _, lr = oracle.forward(w["P"], w["K"][r:r + 1], w["V"][r:r + 1], cu_offsets=single, norm="prototype")
+        assert_lse(lse[r:r + 1], lr, "bf16", f"prototype axis lse, row {r}")
+
+
 def test_prototype_axis_masked_and_dense():
     w = W.random_case(109, B=3, H=2, m=64, dh=64, lengths=[600, 0, 130], dtype="bf16", layout="dense", mask_p=0.2)
     S, lse = run(w, norm="prototype")
