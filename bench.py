@@ -523,6 +523,8 @@ def main():
     ap.add_argument("--stca-targets", type=int, default=40, help="workload 9: targets per user")
     ap.add_argument("--norm", choices=("history", "prototype"), default="history",
                     help="workloads 1-4: softmax axis (prototype = the paper's normalisation display, row A9)")
+    ap.add_argument("--mask-p", type=float, default=0.0,
+                    help="workloads 1-4: pass a seeded per-row mask that excludes each row with this probability")
     ap.add_argument("--grad-dtype", choices=("fp32", "bf16"), default="fp32",
                     help="workload 7: element type of dK and dV")
     ap.add_argument("--cpu-users", type=int, default=4, help="users in the CPU oracle sample")
@@ -565,6 +567,13 @@ def main():
     if "X" in w:
         return bench_fused(args, w)
     P, K, V = w["P"].to(dev), w["K"].to(dev), w["V"].to(dev)
+    mask = None
+    if args.mask_p > 0:
+        # seeded per-row mask over the K/V buffer rows: each row excluded with probability mask_p
+        import numpy as np
+        nrow = K.shape[0] if w["layout"] == "packed" else K.shape[0] * K.shape[1]
+        keep = np.random.default_rng(77).uniform(size=nrow) >= args.mask_p
+        mask = torch.from_numpy(keep.astype(np.uint8)).to(dev)
     cu = w["cu_offsets"].to(dev) if w["layout"] == "packed" else None
     lengths = w["lengths"].to(dev) if w["layout"] == "dense" else None
     S = torch.empty((B, H, m, dh), dtype=torch.float32, device=dev)
@@ -578,7 +587,7 @@ def main():
     kernel = sa.sa_forward_kernel_name(pb)
 
     def step():
-        sa.sa_forward(P, K, V, cu_offsets=cu, lengths=lengths, out=S, workspace=ws, **pb_kw)
+        sa.sa_forward(P, K, V, cu_offsets=cu, lengths=lengths, mask=mask, out=S, workspace=ws, **pb_kw)
 
     ms_per_step, kern_ms = _timed(step, args.steps, args.warmup)
     value = tokens / (ms_per_step / 1e3)
@@ -591,11 +600,11 @@ def main():
         kernel = "sa_forward, prototype axis (row log-sum-exp pass + " + kernel + " + merge)"
     el = 2 if w["dtype"] == "bf16" else 4
     # algorithmic bytes of the streaming kernel: every K and V element once, plus P and offsets
-    alg_bytes = 2 * tokens * H * dh * el + H * m * dh * el + 4 * (B + 1)
+    alg_bytes = 2 * tokens * H * dh * el + H * m * dh * el + 4 * (B + 1) + (tokens if mask is not None else 0)
     achieved = alg_bytes / (kern_avg_ms / 1e3) / 1e9
     step_bytes = W.algorithmic_bytes(w)
     out = {
-        "metric": METRIC if not proto else METRIC + ", prototype axis",
+        "metric": METRIC + (", prototype axis" if proto else "") + (", masked rows" if mask is not None else ""),
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -608,7 +617,7 @@ def main():
         "dtype": w["dtype"],
         "data": "synthetic (seeded normal draws shaped like the paper's histories)",
         "config": {"workload": spec.name, "B": B, "sum_L": tokens, "L_max": int(w["lengths"].max()), "H": H,
-                   "m": m, "dh": dh, "layout": w["layout"], "parallelism": "single GPU"},
+                   "m": m, "dh": dh, "layout": w["layout"], "mask_p": args.mask_p, "parallelism": "single GPU"},
         "hbm_frac_step": step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
         "roofline": {
             "bound": "hbm",
@@ -617,7 +626,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": _traffic(kernel) if spec.name == "full100k_bf16" and not proto else None,
+            "traffic": _traffic(kernel) if spec.name == "full100k_bf16" and not proto and mask is None else None,
             "algorithmic_bytes_per_launch": alg_bytes,
             "kernel_ms_avg": kern_avg_ms,
             "kernel_ms_min": min(kern_ms),

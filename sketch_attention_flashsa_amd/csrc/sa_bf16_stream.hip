@@ -28,9 +28,11 @@
 //   * rows past the segment end are loaded from a clamped, valid row and
 //     masked rows are loaded as they are; both get weight 0 and their V
 //     values are zeroed in registers before the aggregation, so neither can
-//     leak, NaN included.  The mask bytes of a stage are read when the stage
-//     is consumed (a plain load the compiler waits for), so masked inputs
-//     keep less of the ring in flight than unmasked ones.
+//     leak, NaN included.  A stage's mask bytes (and, on the prototype axis,
+//     its rows' normalisers) come into LDS with the stage, by 4-byte
+//     direct-to-LDS loads counted with its other loads: plain loads at the
+//     point of use would make the compiler, which cannot count the ring's
+//     asm loads, wait for all of them, draining the ring once per stage.
 #include <stdlib.h>
 #include <string.h>
 
@@ -64,9 +66,9 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
     constexpr int ROWB = CPR * 16;                        // bytes per row per tensor
     constexpr int D = 32 * CPR / (NW * 64);               // DMA ops per wave per tensor per stage
     constexpr int STAGE = 32 * ROWB;                      // bytes per tensor per stage
-    // vector-memory ops per wave per stage: K and V, and on the prototype axis
-    // one 4-byte load of the rows' normalisers
-    constexpr int VMS = 2 * D + (PROTO ? 1 : 0);
+    // vector-memory ops per wave per stage: K and V, on the prototype axis one
+    // 4-byte load of the rows' normalisers, with a mask one of its bytes
+    constexpr int VMS = 2 * D + (PROTO ? 1 : 0) + (MASKED ? 1 : 0);
     constexpr int AHEAD = S - 1;                          // stages issued ahead of the one computed
     constexpr int FK = CPR < 16 ? CPR : 16;               // K swizzle period (rows)
     constexpr int FV = (CPR < 16 ? CPR : 16) / 2;         // V swizzle period (rows), chunk pairs
@@ -82,6 +84,9 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
     // prototype axis: each wave's 64 dwords of a stage's per-(row, head)
     // normalisers, entry row * NH + head for the first 32 * NH of them
     __shared__ __attribute__((aligned(16))) float nlring[PROTO ? S : 1][PROTO ? NW * 64 : 1];
+    // with a mask: each wave's own copy of a stage's mask bytes, lane i < 32
+    // holding the 4-byte word that contains row i's byte
+    __shared__ __attribute__((aligned(16))) uint32_t mkring[MASKED ? S : 1][MASKED ? NW * 64 : 1];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -155,6 +160,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
     // depends on row % 16 only, so both 16-row halves share them)
     const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void*)&ring[0][0][0];
     const uint32_t nl_lds = (uint32_t)(uintptr_t)(lds_void*)&nlring[0][0];
+    const uint32_t mk_lds = (uint32_t)(uintptr_t)(lds_void*)&mkring[0][0];
     uint32_t klane[KC];   // K operand reads, slot 0
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
@@ -199,6 +205,15 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
                 dma16s(vb, (uint32_t)(rr * (int)vrow + dma_cv[d]),
                        __builtin_amdgcn_readfirstlane(slot_lds + STAGE + d * 1024));
             }
+            if constexpr (MASKED) {
+                // lane -> row (lane % 32) clamped to the segment; the load takes
+                // the aligned 4-byte word holding the row's mask byte (it stays
+                // in the byte's 4-byte-aligned word, so in the byte's page)
+                const uintptr_t m0 = (uintptr_t)(a.mask + gbase + r0);
+                const int rr = min(lane & 31, last);
+                dma4c((const void*)(m0 & ~(uintptr_t)3), (uint32_t)((int)(m0 & 3) + rr) & ~3u,
+                      __builtin_amdgcn_readfirstlane(mk_lds + (uint32_t)(((t % S) * NW + wave) * 256)));
+            }
             if constexpr (PROTO) {
                 // lane -> entry (wave*64 + lane) mod 32 NH: row e / NH (clamped
                 // to the segment), head hc + e % NH; the entries past 32 NH repeat
@@ -214,7 +229,14 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
             const int64_t r0 = (int64_t)t * 32;
             const int rows_here = (int)min((int64_t)32, nrows - r0);
             bool v = lane < rows_here;
-            if constexpr (MASKED) v = v && a.mask[gbase + r0 + min(lane, rows_here - 1)] != 0;
+            if constexpr (MASKED) {
+                // the stage's mask words arrived with it (this wave's own copy)
+                const uint32_t m0 = (uint32_t)((uintptr_t)(a.mask + gbase + r0) & 3);
+                const int sh = 8 * (int)((m0 + (uint32_t)min(lane & 31, rows_here - 1)) & 3);
+                const uint32_t wd = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)(
+                    mk_lds + (uint32_t)(((t % S) * NW + wave) * 256 + 4 * lane));
+                v = v && ((wd >> sh) & 0xffu) != 0;
+            }
             return (uint32_t)__ballot(v);
         };
 
@@ -283,7 +305,12 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
                     const float nm = -Mc[sb];
                     float p[8];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(s[j >> 2][sb][j & 3], a.c, nm));
+                    for (int j = 0; j < 8; ++j) {
+                        p[j] = __builtin_amdgcn_exp2f(fmaf(s[j >> 2][sb][j & 3], a.c, nm));
+                        // with a mask, invalid rows (masked or past the end) get
+                        // weight 0 here, so they do not force the exact path
+                        if constexpr (MASKED) p[j] = ((vj >> j) & 1) ? p[j] : 0.f;
+                    }
                     const bf16x2 q0 = pack2(p[0], p[1]), q1 = pack2(p[2], p[3]);
                     const bf16x2 q2 = pack2(p[4], p[5]), q3 = pack2(p[6], p[7]);
                     pk[sb] = cat8(q0, q1, q2, q3);
@@ -293,7 +320,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
                 }
                 // rare exact path (then-only, so the common path keeps its
                 // values in place): validity, running-maximum update, rescale
-                if (__builtin_expect(!(__all(fits) && valid == 0xffffffffu), 0)) {
+                if (__builtin_expect(!(__all(fits) && (MASKED || valid == 0xffffffffu)), 0)) {
 #pragma unroll
                     for (int sb = 0; sb < NSB; ++sb) {
                         float x[8];
