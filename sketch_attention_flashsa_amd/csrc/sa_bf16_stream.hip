@@ -252,6 +252,9 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
 
         // one 32-row stage: scores, weights, aggregation
         auto unit = [&](int t, uint32_t valid) {
+            // all 32 rows of the stage are inside the segment (without a mask
+            // that is valid == all ones)
+            const bool seg_full = MASKED ? (t + 1) * 32 <= nrows32 : valid == 0xffffffffu;
             const uint32_t sbase = (uint32_t)((t % S) * 2 * STAGE);
             // S^T = K P^T (two 16-row halves)
             f32x4 s[2][NSB];
@@ -307,8 +310,9 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         p[j] = __builtin_amdgcn_exp2f(fmaf(s[j >> 2][sb][j & 3], a.c, nm));
-                        // with a mask, invalid rows (masked or past the end) get
-                        // weight 0 here, so they do not force the exact path
+                        // with a mask, masked rows get weight 0 here, so they
+                        // do not force the exact path (a no-op where the mask
+                        // is all ones, which keeps that bitwise equal to no mask)
                         if constexpr (MASKED) p[j] = ((vj >> j) & 1) ? p[j] : 0.f;
                     }
                     const bf16x2 q0 = pack2(p[0], p[1]), q1 = pack2(p[2], p[3]);
@@ -320,7 +324,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
                 }
                 // rare exact path (then-only, so the common path keeps its
                 // values in place): validity, running-maximum update, rescale
-                if (__builtin_expect(!(__all(fits) && (MASKED || valid == 0xffffffffu)), 0)) {
+                if (__builtin_expect(!(__all(fits) && seg_full), 0)) {
 #pragma unroll
                     for (int sb = 0; sb < NSB; ++sb) {
                         float x[8];

@@ -149,6 +149,36 @@ def test_mask_poisoned_rows_bit_exact(dtype):
     assert np.array_equal(S4, S5), "all-ones mask must equal no mask"
 
 
+@pytest.mark.parametrize("H,m,dh", [(8, 128, 64), (8, 64, 32)])
+@pytest.mark.parametrize("norm", ["history", "prototype"])
+def test_streaming_kernel_masks_bit_exact(H, m, dh, norm):
+    """The same properties on shapes the streaming kernel serves (its masked
+    instances carry the mask bytes in the ring): masked rows match the oracle,
+    NaN/Inf in masked rows change nothing bitwise, an all-ones mask equals no
+    mask bitwise.  Ragged users put masked rows in segment tails too."""
+    lengths = [700, 1, 33, 1000, 64, 0, 95]
+    w = W.random_case(120 + dh, B=len(lengths), H=H, m=m, dh=dh, lengths=lengths, dtype="bf16", mask_p=0.3)
+    pb = sa.make_problem(w["B"], H, m, dh, w["K"].shape[0], dtype="bf16", norm=norm)
+    assert sa.sa_forward_kernel_name(pb) == "sa_bf16_stream_kernel"
+    S_ref, l_ref = run(w, norm=norm)
+    So, lo = _oracle(w, norm=norm)
+    assert_parity(S_ref, So, "bf16", f"streaming masked {norm} dh={dh}")
+    assert_lse(l_ref.reshape(lo.shape), lo, "bf16", f"streaming masked {norm} dh={dh}")
+    bad = ~w["mask"].bool()
+    K, V = w["K"].clone(), w["V"].clone()
+    K[bad] = float("nan")
+    V[bad] = float("inf")
+    S2, l2 = run(dict(w, K=K, V=V), norm=norm)
+    assert np.array_equal(S2, S_ref), "masked rows must not leak"
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(fin, np.isfinite(l2)) and np.array_equal(l2[fin], l_ref[fin])
+    w4 = dict(w)
+    w4.pop("mask")
+    S4, _ = run(w4, norm=norm)
+    S5, _ = run(w4, norm=norm, mask=torch.ones(w["K"].shape[0], dtype=torch.uint8))
+    assert np.array_equal(S4, S5), "all-ones mask must equal no mask"
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_packed_equals_dense_bitwise(dtype):
     lengths = [500, 3, 0, 1200, 64]
