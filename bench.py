@@ -318,7 +318,11 @@ def bench_backward(args):
     B, H, m, dh = w["B"], w["H"], w["m"], w["dh"]
     tokens = int(w["lengths"].sum())
     P, K, V, cu = (w[k].to(dev) for k in ("P", "K", "V", "cu_offsets"))
-    S, lse = sa.sa_forward(P, K, V, cu_offsets=cu, return_lse=True)
+    mask = None
+    if args.mask_p > 0:
+        keep = np.random.default_rng(77).uniform(size=K.shape[0]) >= args.mask_p
+        mask = torch.from_numpy(keep.astype(np.uint8)).to(dev)
+    S, lse = sa.sa_forward(P, K, V, cu_offsets=cu, mask=mask, return_lse=True)
     dS = torch.from_numpy(np.random.default_rng(8).standard_normal((B, H, m, dh), dtype=np.float32)).to(dev)
     pb = sa.make_problem(B, H, m, dh, K.shape[0], dtype="bf16")
     ws = torch.empty(sa.sa_backward_workspace_size(pb), dtype=torch.uint8, device=dev)
@@ -328,7 +332,7 @@ def bench_backward(args):
            torch.zeros(V.shape, dtype=gdt, device=dev))
 
     def step():
-        sa.sa_backward(P, K, V, S, lse, dS, cu_offsets=cu, workspace=ws, out=out)
+        sa.sa_backward(P, K, V, S, lse, dS, cu_offsets=cu, mask=mask, workspace=ws, out=out)
 
     ms_per_step, call_ms = _timed(step, args.steps, args.warmup)
     call_avg = sum(call_ms) / len(call_ms)
@@ -336,7 +340,8 @@ def bench_backward(args):
     alg_bytes = tokens * H * dh * (2 + 2 + 2 * gsz) + H * m * dh * (2 + 4) + B * H * m * (dh * 8 + 4) + 4 * (B + 1)
     achieved = alg_bytes / (call_avg / 1e3) / 1e9
     print(json.dumps({
-        "metric": BACKWARD_METRIC + (", bf16 gradients" if args.grad_dtype == "bf16" else ""),
+        "metric": BACKWARD_METRIC + (", bf16 gradients" if args.grad_dtype == "bf16" else "")
+        + (", masked rows" if mask is not None else ""),
         "value": tokens / (ms_per_step / 1e3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -349,7 +354,7 @@ def bench_backward(args):
         "dtype": "bf16",
         "data": "synthetic (seeded normal draws shaped like the paper's histories)",
         "config": {"workload": "backward_full100k_bf16", "B": B, "sum_L": tokens, "L_max": int(w["lengths"].max()),
-                   "H": H, "m": m, "dh": dh, "layout": "packed", "grad_dtype": args.grad_dtype,
+                   "H": H, "m": m, "dh": dh, "layout": "packed", "grad_dtype": args.grad_dtype, "mask_p": args.mask_p,
                    "parallelism": "single GPU"},
         "roofline": {
             "bound": "hbm",
@@ -524,7 +529,7 @@ def main():
     ap.add_argument("--norm", choices=("history", "prototype"), default="history",
                     help="workloads 1-4: softmax axis (prototype = the paper's normalisation display, row A9)")
     ap.add_argument("--mask-p", type=float, default=0.0,
-                    help="workloads 1-4: pass a seeded per-row mask that excludes each row with this probability")
+                    help="workloads 1-4 and 7: pass a seeded per-row mask that excludes each row with this probability")
     ap.add_argument("--grad-dtype", choices=("fp32", "bf16"), default="fp32",
                     help="workload 7: element type of dK and dV")
     ap.add_argument("--cpu-users", type=int, default=4, help="users in the CPU oracle sample")

@@ -446,16 +446,22 @@ constexpr int kDpStages = 4;
 __device__ __forceinline__ int dp_swz(int r) { return 2 * (r & 7) + ((r >> 3) & 1); }
 }  // namespace
 
-template <int DH, int CPR>
+template <int DH, int CPR, bool MASKED>
 __global__ __launch_bounds__(512, CPR == 16 ? 2 : 1) void sa_bwd_dp_stream_kernel(BwdArgs a, int NH, int PB) {
     constexpr int KC = DH / 32, DB = DH / 16, NSB = 2, NW = 8;
     constexpr int S = kDpStages, AHEAD = S - 1;
     constexpr int ROWB = CPR * 16;                   // bytes per row per tensor
     constexpr int STAGE = 32 * ROWB;                 // bytes per tensor per stage
     constexpr int D = 32 * CPR / (NW * 64);          // DMA ops per wave per tensor per stage
-    constexpr int VMS = 2 * D;
+    // K and V, and with a mask one 4-byte load of the stage's mask words
+    constexpr int VMS = 2 * D + (MASKED ? 1 : 0);
     static_assert(D >= 1 && D * NW * 64 == 32 * CPR, "a stage is whole DMA ops per wave");
     __shared__ __attribute__((aligned(1024))) unsigned char ring[S][2][STAGE];
+    // with a mask: each wave's own copy of a stage's mask words, lane i < 32
+    // holding the aligned 4-byte word that contains row i's byte (a plain
+    // load at the point of use would make the compiler, which cannot count
+    // the ring's asm loads, drain the ring)
+    __shared__ __attribute__((aligned(16))) uint32_t mkring[MASKED ? S : 1][MASKED ? NW * 64 : 1];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -487,6 +493,7 @@ __global__ __launch_bounds__(512, CPR == 16 ? 2 : 1) void sa_bwd_dp_stream_kerne
         dma_ck[d] = (((off % ROWB) / 16) ^ dp_swz(dma_row[d] & 15)) * 16;
     }
     const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void*)&ring[0][0][0];
+    const uint32_t mk_lds = (uint32_t)(uintptr_t)(lds_void*)&mkring[0][0];
     const int hc = min(h0 + hl, a.H - 1) - h0;      // head column of this wave (clamped for idle waves)
     uint32_t rd[KC];                                 // row reads: row l16, chunk hc dh/8 + 4 kc + g
 #pragma unroll
@@ -546,6 +553,14 @@ __global__ __launch_bounds__(512, CPR == 16 ? 2 : 1) void sa_bwd_dp_stream_kerne
                 dma16c(vb, (uint32_t)(rr * (int)vrow + dma_ck[d]),
                        __builtin_amdgcn_readfirstlane(slot + STAGE + d * 1024));
             }
+            if constexpr (MASKED) {
+                // lane -> row (lane % 32) clamped to the segment: the aligned
+                // word around its mask byte (never leaves the byte's page)
+                const uintptr_t m0 = (uintptr_t)(a.mask + gbase + (int64_t)t * 32);
+                const int rr = min(lane & 31, last);
+                dma4c((const void*)(m0 & ~(uintptr_t)3), (uint32_t)((int)(m0 & 3) + rr) & ~3u,
+                      __builtin_amdgcn_readfirstlane(mk_lds + (uint32_t)(((t % S) * NW + wave) * 256)));
+            }
         };
 
 #pragma unroll
@@ -561,7 +576,13 @@ __global__ __launch_bounds__(512, CPR == 16 ? 2 : 1) void sa_bwd_dp_stream_kerne
                 const uint32_t kst = ring_lds + (uint32_t)((t % S) * 2 * STAGE), vst = kst + STAGE;
                 const int tl = t * 32 + lane;
                 bool vr = lane < 32 && tl < n;
-                if (a.mask) vr = vr && a.mask[gbase + min(tl, n - 1)] != 0;
+                if constexpr (MASKED) {
+                    const uint32_t m0 = (uint32_t)((uintptr_t)(a.mask + gbase + (int64_t)t * 32) & 3);
+                    const int sh = 8 * (int)((m0 + (uint32_t)min(lane & 31, n - 1 - t * 32)) & 3);
+                    const uint32_t wd = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)(
+                        mk_lds + (uint32_t)(((t % S) * NW + wave) * 256 + 4 * lane));
+                    vr = vr && ((wd >> sh) & 0xffu) != 0;
+                }
                 const uint32_t valid = (uint32_t)__ballot(vr);
                 // S^T = K P^T and dA^T = V dS^T: rows = tokens (two 16-row halves)
                 f32x4 s[2][NSB], da[2][NSB];
@@ -708,10 +729,14 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     const int cpr = NH * a.dh / 8;
     const bool ring_ok = NH * PB == 8 && (cpr == 16 || cpr == 32) && a.k_stride % 8 == 0 && a.v_stride % 8 == 0 &&
                          getenv("SA_BWD_DP") == nullptr;
-    if (ring_ok && a.dh == 32 && cpr == 16) hipLaunchKernelGGL((sa_bwd_dp_stream_kernel<32, 16>), g2, blk2, 0, s, a, NH, PB);
-    else if (ring_ok && a.dh == 32 && cpr == 32) hipLaunchKernelGGL((sa_bwd_dp_stream_kernel<32, 32>), g2, blk2, 0, s, a, NH, PB);
-    else if (ring_ok && a.dh == 64 && cpr == 16) hipLaunchKernelGGL((sa_bwd_dp_stream_kernel<64, 16>), g2, blk2, 0, s, a, NH, PB);
-    else if (ring_ok && a.dh == 64 && cpr == 32) hipLaunchKernelGGL((sa_bwd_dp_stream_kernel<64, 32>), g2, blk2, 0, s, a, NH, PB);
+#define SA_DP_RING(D_, C_)                                                                                   \
+    if (masked) hipLaunchKernelGGL((sa_bwd_dp_stream_kernel<D_, C_, true>), g2, blk2, 0, s, a, NH, PB);      \
+    else hipLaunchKernelGGL((sa_bwd_dp_stream_kernel<D_, C_, false>), g2, blk2, 0, s, a, NH, PB);
+    if (ring_ok && a.dh == 32 && cpr == 16) { SA_DP_RING(32, 16) }
+    else if (ring_ok && a.dh == 32 && cpr == 32) { SA_DP_RING(32, 32) }
+    else if (ring_ok && a.dh == 64 && cpr == 16) { SA_DP_RING(64, 16) }
+    else if (ring_ok && a.dh == 64 && cpr == 32) { SA_DP_RING(64, 32) }
+#undef SA_DP_RING
     else if (a.dh == 32) hipLaunchKernelGGL(sa_bwd_dp_kernel<32>, g2, blk2, 0, s, a, NH, PB);
     else hipLaunchKernelGGL(sa_bwd_dp_kernel<64>, g2, blk2, 0, s, a, NH, PB);
     const int mq = a.m * (a.dh / 4);
