@@ -54,7 +54,11 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
     constexpr int STAGE = 32 * ROWB;           // one 32-row tile
     constexpr int OPS = STAGE / 1024;          // 1 KB DMA ops per tile
     constexpr int D = OPS / kFWaves;           // per wave
-    constexpr int VMS = D;                     // vector-memory ops per wave per tile
+    // with a mask, its words travel with the tile (MDMA) where the LDS has room
+    // for them: every shape but d_model = 256 with m = 256, whose ring,
+    // exchange and prototypes fill the LDS
+    constexpr bool MDMA = MASKED && !(DM == 256 && MB == 128);
+    constexpr int VMS = D + (MDMA ? 1 : 0);   // vector-memory ops per wave per tile
     constexpr int AHEAD = S - 1;
     constexpr int KCX = DM / 32;               // 32-wide chunks of the model dimension
     constexpr int NSB = MB / 16;               // prototype blocks of one wave
@@ -64,6 +68,11 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
     static_assert((AHEAD - 1) * VMS < 64, "vmcnt range");
 
     __shared__ __attribute__((aligned(1024))) unsigned char ring[S][STAGE];
+    // with a mask: each wave's own copy of a tile's mask words, lane i < 32
+    // holding the aligned 4-byte word that contains row i's byte (a plain
+    // load at the point of use would make the compiler, which cannot count
+    // the ring's asm loads, drain the ring)
+    __shared__ __attribute__((aligned(16))) uint32_t mkring[MDMA ? S : 1][MDMA ? kFWaves * 64 : 1];
     // exchange: [tile parity][head][role][fragment][lane]
     __shared__ __attribute__((aligned(16))) bf16x8 xchg[2][HPB][2][2][64];
 
@@ -142,6 +151,7 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
         dma_off[d] = (slot ^ (dma_row[d] & 15)) * 16;   // byte offset of the fetched chunk in its row
     }
     const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void*)&ring[0][0];
+    const uint32_t mk_lds = (uint32_t)(uintptr_t)(lds_void*)&mkring[0][0];
     // LDS address of this lane's X fragment (row block 0, chunk 0) in slot 0
     const uint32_t xlane = ring_lds + (uint32_t)(l16 * ROWB);
 
@@ -172,12 +182,29 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
                 const uint32_t voff = (uint32_t)(min(dma_row[d], last) * ROWB + dma_off[d]);
                 dma16s(tbase, voff, __builtin_amdgcn_readfirstlane(slot_lds + d * 1024));
             }
+            if constexpr (MDMA) {
+                // lane -> row (lane % 32) clamped to the segment: the aligned
+                // word around its mask byte (never leaves the byte's page)
+                const uintptr_t m0 = (uintptr_t)(a.mask + gbase + r0);
+                const int rr = min(lane & 31, last);
+                dma4c((const void*)(m0 & ~(uintptr_t)3), (uint32_t)((int)(m0 & 3) + rr) & ~3u,
+                      __builtin_amdgcn_readfirstlane(mk_lds + (uint32_t)(((t % S) * kFWaves + wave) * 256)));
+            }
         };
         auto tile_valid = [&](int t) -> uint32_t {
             const int64_t r0 = (int64_t)t * 32;
             const int rows_here = (int)min((int64_t)32, nrows - r0);
             bool v = lane < rows_here;
-            if constexpr (MASKED) v = v && a.mask[gbase + r0 + min(lane, rows_here - 1)] != 0;
+            if constexpr (MDMA) {
+                // the tile's mask words arrived with it (this wave's own copy)
+                const uint32_t m0 = (uint32_t)((uintptr_t)(a.mask + gbase + r0) & 3);
+                const int sh = 8 * (int)((m0 + (uint32_t)min(lane & 31, rows_here - 1)) & 3);
+                const uint32_t wd = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)(
+                    mk_lds + (uint32_t)(((t % S) * kFWaves + wave) * 256 + 4 * lane));
+                v = v && ((wd >> sh) & 0xffu) != 0;
+            } else if constexpr (MASKED) {
+                v = v && a.mask[gbase + r0 + min(lane, rows_here - 1)] != 0;
+            }
             return (uint32_t)__ballot(v);
         };
 

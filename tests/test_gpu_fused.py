@@ -86,10 +86,14 @@ def test_fused_small_chunks_match_default_split():
     assert_parity(S1, So, "bf16", "fused, default split")
 
 
-def test_fused_mask_poison_is_bit_exact():
+@pytest.mark.parametrize("H,m,d_model", [(8, 256, 256), (8, 128, 256), (4, 256, 128)])
+def test_fused_mask_poison_is_bit_exact(H, m, d_model):
     """Masked rows are never read as numbers: NaN in X at masked rows leaves
-    the output bitwise unchanged; the result matches the oracle's mask."""
-    w = W.random_fused_case(312, B=4, H=8, m=256, dh=32, d_model=256, lengths=[400, 77, 1000, 33], mask_p=0.3)
+    the output bitwise unchanged; the result matches the oracle's mask.  The
+    shapes cover both ways a tile's mask reaches the kernel (with the tile
+    through LDS, and read directly where the LDS is full)."""
+    w = W.random_fused_case(312 + m + d_model, B=4, H=H, m=m, dh=32, d_model=d_model,
+                            lengths=[400, 77, 1000, 33], mask_p=0.3)
     S, lse = run_fused(w)
     X2 = w["X"].clone()
     X2[w["mask"] == 0] = float("nan")
