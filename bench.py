@@ -153,27 +153,42 @@ def cpu_baseline(w, n_users: int):
     }
 
 
-def _timed(step, steps: int, warmup: int):
-    """Run warmup + timed steps; returns (ms per step by wall clock, the
-    streaming kernel's HIP-event durations in ms)."""
+def _timed(step, steps: int, warmup: int, flush_mib: int = 0):
+    """Run warmup + timed steps; returns (ms per step, the streaming kernel's
+    HIP-event durations in ms).  ms per step is the wall clock over the timed
+    loop; with flush_mib > 0 a buffer of that size is overwritten before every
+    step (so no input is left in the L2 or the 256 MB MALL) and ms per step is
+    the mean of per-step event times, which exclude the flush."""
     import torch
     import sketch_attention_flashsa_amd as sa
     hip = _Hip()
+    scratch = torch.empty(flush_mib << 18, dtype=torch.float32, device="cuda:0") if flush_mib > 0 else None
     for _ in range(warmup):
+        if scratch is not None:
+            scratch.fill_(1.0)
         step()
     torch.cuda.synchronize()
     evs = [(hip.event(), hip.event()) for _ in range(steps)]
+    step_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(steps if scratch is not None else 0)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
+        if scratch is not None:
+            scratch.fill_(1.0)
+            step_evs[i][0].record()
         sa.sa_set_timing_events(evs[i][0], evs[i][1])
         step()
+        if scratch is not None:
+            step_evs[i][1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kern_ms = [hip.elapsed_ms(a, b) for a, b in evs]
     for a, b in evs:
         hip.destroy(a)
         hip.destroy(b)
+    if scratch is not None:
+        return sum(a.elapsed_time(b) for a, b in step_evs) / steps, kern_ms
     return (t1 - t0) * 1e3 / steps, kern_ms
 
 
@@ -530,6 +545,11 @@ def main():
                     help="workloads 1-4: softmax axis (prototype = the paper's normalisation display, row A9)")
     ap.add_argument("--mask-p", type=float, default=0.0,
                     help="workloads 1-4 and 7: pass a seeded per-row mask that excludes each row with this probability")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="workloads 1-4: overwrite a buffer of this many MiB before every step (cold caches)")
+    ap.add_argument("--cold-mib", type=int, default=1024,
+                    help="workloads 1-4: after the timed steps, time the kernel again with this many MiB "
+                         "overwritten before each launch (0: skip); reported as cold_cache")
     ap.add_argument("--grad-dtype", choices=("fp32", "bf16"), default="fp32",
                     help="workload 7: element type of dK and dV")
     ap.add_argument("--cpu-users", type=int, default=4, help="users in the CPU oracle sample")
@@ -594,7 +614,7 @@ def main():
     def step():
         sa.sa_forward(P, K, V, cu_offsets=cu, lengths=lengths, mask=mask, out=S, workspace=ws, **pb_kw)
 
-    ms_per_step, kern_ms = _timed(step, args.steps, args.warmup)
+    ms_per_step, kern_ms = _timed(step, args.steps, args.warmup, args.flush_mib)
     value = tokens / (ms_per_step / 1e3)
     kern_avg_ms = sum(kern_ms) / len(kern_ms)
     if proto:
@@ -622,7 +642,8 @@ def main():
         "dtype": w["dtype"],
         "data": "synthetic (seeded normal draws shaped like the paper's histories)",
         "config": {"workload": spec.name, "B": B, "sum_L": tokens, "L_max": int(w["lengths"].max()), "H": H,
-                   "m": m, "dh": dh, "layout": w["layout"], "mask_p": args.mask_p, "parallelism": "single GPU"},
+                   "m": m, "dh": dh, "layout": w["layout"], "mask_p": args.mask_p, "flush_mib": args.flush_mib,
+                   "parallelism": "single GPU"},
         "hbm_frac_step": step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
         "roofline": {
             "bound": "hbm",
@@ -640,6 +661,16 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.flush_mib == 0 and args.cold_mib > 0 and not proto:
+        # the same launches with a buffer overwritten before each one (after
+        # the timed region above, which it does not affect): no input left in
+        # the L2 or the MALL, and the kernel not launched back to back
+        _, cold_ms = _timed(step, args.steps, args.warmup, args.cold_mib)
+        cold_avg = sum(cold_ms) / len(cold_ms)
+        out["cold_cache"] = {"flush_mib": args.cold_mib, "kernel_ms_avg": cold_avg,
+                             "kernel_ms_p10_p50_p90": _percentiles(cold_ms),
+                             "achieved": alg_bytes / (cold_avg / 1e3) / 1e9,
+                             "frac": alg_bytes / (cold_avg / 1e3) / 1e9 / HBM_PEAK_GBS}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_users)
     print(json.dumps(out))
