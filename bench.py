@@ -153,19 +153,27 @@ def cpu_baseline(w, n_users: int):
     }
 
 
-def _timed(step, steps: int, warmup: int, flush_mib: int = 0):
+def _timed(step, steps: int, warmup: int, flush_mib: int = 0, flush_kind: str = "write"):
     """Run warmup + timed steps; returns (ms per step, the streaming kernel's
     HIP-event durations in ms).  ms per step is the wall clock over the timed
     loop; with flush_mib > 0 a buffer of that size is overwritten before every
-    step (so no input is left in the L2 or the 256 MB MALL) and ms per step is
-    the mean of per-step event times, which exclude the flush."""
+    step (so no input is left in the L2 or the 256 MB MALL; flush_kind "read"
+    sums it instead) and ms per step is the mean of per-step event times,
+    which exclude the flush."""
     import torch
     import sketch_attention_flashsa_amd as sa
     hip = _Hip()
-    scratch = torch.empty(flush_mib << 18, dtype=torch.float32, device="cuda:0") if flush_mib > 0 else None
+    scratch = torch.ones(flush_mib << 18, dtype=torch.float32, device="cuda:0") if flush_mib > 0 else None
+
+    def flush():
+        if flush_kind == "read":
+            scratch.sum()
+        else:
+            scratch.fill_(1.0)
+
     for _ in range(warmup):
         if scratch is not None:
-            scratch.fill_(1.0)
+            flush()
         step()
     torch.cuda.synchronize()
     evs = [(hip.event(), hip.event()) for _ in range(steps)]
@@ -175,7 +183,7 @@ def _timed(step, steps: int, warmup: int, flush_mib: int = 0):
     t0 = time.perf_counter()
     for i in range(steps):
         if scratch is not None:
-            scratch.fill_(1.0)
+            flush()
             step_evs[i][0].record()
         sa.sa_set_timing_events(evs[i][0], evs[i][1])
         step()
@@ -547,6 +555,8 @@ def main():
                     help="workloads 1-4 and 7: pass a seeded per-row mask that excludes each row with this probability")
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="workloads 1-4: overwrite a buffer of this many MiB before every step (cold caches)")
+    ap.add_argument("--flush-kind", choices=("write", "read"), default="write",
+                    help="--flush-mib: overwrite (write) or sum (read) the buffer before each step")
     ap.add_argument("--cold-mib", type=int, default=1024,
                     help="workloads 1-4: after the timed steps, time the kernel again with this many MiB "
                          "overwritten before each launch (0: skip); reported as cold_cache")
@@ -614,7 +624,7 @@ def main():
     def step():
         sa.sa_forward(P, K, V, cu_offsets=cu, lengths=lengths, mask=mask, out=S, workspace=ws, **pb_kw)
 
-    ms_per_step, kern_ms = _timed(step, args.steps, args.warmup, args.flush_mib)
+    ms_per_step, kern_ms = _timed(step, args.steps, args.warmup, args.flush_mib, args.flush_kind)
     value = tokens / (ms_per_step / 1e3)
     kern_avg_ms = sum(kern_ms) / len(kern_ms)
     if proto:
@@ -643,6 +653,7 @@ def main():
         "data": "synthetic (seeded normal draws shaped like the paper's histories)",
         "config": {"workload": spec.name, "B": B, "sum_L": tokens, "L_max": int(w["lengths"].max()), "H": H,
                    "m": m, "dh": dh, "layout": w["layout"], "mask_p": args.mask_p, "flush_mib": args.flush_mib,
+                   "flush_kind": args.flush_kind if args.flush_mib else None,
                    "parallelism": "single GPU"},
         "hbm_frac_step": step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,
         "roofline": {
