@@ -395,8 +395,9 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
         }
 
         // ---- segment epilogue: partial statistics at slot w + b (the sums in
-        // lane order, 1 KB per store, non-temporal: every block ends at about
-        // the same time, and these writes are the kernel's tail)
+        // lane order, 1 KB per store, written through to memory: these writes
+        // are the kernel's tail, and lines left dirty in the caches would be
+        // written back during the next launch's reads, ~1 % slower)
         if (active) {
             const int64_t slot = (int64_t)w + b;
 #pragma unroll
@@ -414,8 +415,8 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
                 }
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
-                    __builtin_nontemporal_store(
-                        acc[sb][db], (f32x4*)lane_major_acc(a.part, slot, a.H, head, a.m, DH, (pb * MB) / 16 + sb, db, lane));
+                    store16_wt((f32x4*)lane_major_acc(a.part, slot, a.H, head, a.m, DH, (pb * MB) / 16 + sb, db, lane),
+                               acc[sb][db]);
             }
         }
         // drain this segment's memory traffic and let every wave finish reading

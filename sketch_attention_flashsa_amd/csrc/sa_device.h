@@ -116,6 +116,22 @@ __device__ __forceinline__ void dma4c(const void* base, uint32_t voff, uint32_t 
         : "memory");
 }
 
+// 16-byte store that writes through to memory (system scope, non-temporal):
+// for results written once at a kernel's end and read by the next kernel, so
+// that they do not stay dirty in the caches and get written back in the
+// middle of the following launch's reads.  The compiler's hazard tracking
+// does not see into asm, and a VALU write of a store's data registers right
+// after a store of more than 8 bytes is a hazard, so the asm ends with wait
+// states before the compiler may reuse them.
+__device__ __forceinline__ void store16_wt(f32x4* p, f32x4 v) {
+    asm volatile(
+        "global_store_dwordx4 %0, %1, off sc0 sc1 nt\n\t"
+        "s_nop 7"
+        :
+        : "v"(p), "v"(v)
+        : "memory");
+}
+
 // acc *= f in place, for an accumulator kept in AGPRs (the MFMA accumulator
 // registers): each element goes through one VGPR and back, so the common
 // path never copies the accumulator.
