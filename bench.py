@@ -128,6 +128,35 @@ def hbm_probe(mib: int, steps: int) -> None:
     print(json.dumps(out))
 
 
+def hbm_reference(mib: int = 2048, read_iters: int = 400, copy_iters: int = 150, timed: int = 100):
+    """The device's own streaming rates, measured in this process just before
+    the benchmark's warm-up: torch's sum over an fp32 buffer of `mib` MiB
+    (reads only) and its copy_ into a second buffer (reads and writes), each
+    run `read_iters` / `copy_iters` times back to back with the last `timed`
+    launches timed by events.  The kernel is compared with these rates as well
+    as with the nominal 8 TB/s.  The ~0.3 s of streaming also brings the chip
+    from idle to its loaded clock state, the state the timed steps then run
+    in (the first few tens of back-to-back launches after idle run slower)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    out = {"buffer_mib": mib}
+    for name, fn, iters, nbytes in (("read", lambda: x.sum(), read_iters, 4 * n),
+                                    ("copy", lambda: y.copy_(x), copy_iters, 8 * n)):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(iters):
+            if i == iters - timed:
+                a.record()
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / timed
+        out[f"{name}_GBps"] = nbytes / ms / 1e6
+    del x, y
+    return out
+
+
 def cpu_baseline(w, n_users: int):
     """The oracle as it stands, on the first n_users users of the workload."""
     import oracle
@@ -146,7 +175,9 @@ def cpu_baseline(w, n_users: int):
     return {
         "value": rows / dt,
         "unit": "tokens/s",
+        # OpenMP threads the oracle ran (its loop has n * H iterations)
         "cores": int(min(oracle.threads(), pairs)),
+        "host_cores": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": f"first {n} users of the workload ({rows} history rows, all {w['H']} heads and {w['m']} "
                   f"prototypes), double precision, {dt:.1f} s wall",
@@ -475,7 +506,7 @@ def bench_stca(args):
     import torch
     import workloads as W
     import sketch_attention_flashsa_amd as sa
-    from oracle import stca as ST
+    from sketch_attention_flashsa_amd import flops
     dev = torch.device("cuda:0")
     B, L, R, D, h = 64, args.stca_rows, args.stca_targets, 1024, 16
     w = W.random_stca_case(9, lengths=[L] * B, targets=[R] * B, D=D, h=h)
@@ -490,11 +521,12 @@ def bench_stca(args):
 
     ms_per_step, kern_ms = _timed(step, args.steps, args.warmup)
     kavg = sum(kern_ms) / len(kern_ms)
-    fl = ST.stca_flops([L] * T, D, h)
+    fl = flops.stca_attention_flops([L] * T, D, h)
     tflops = fl / (kavg / 1e3) / 1e12
     cpu = None
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_info
+        from oracle import stca as ST
         nu = min(B, 32)
         n = nu * R
         blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
@@ -564,6 +596,9 @@ def main():
                     help="workload 7: element type of dK and dV")
     ap.add_argument("--cpu-users", type=int, default=4, help="users in the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ref-mib", type=int, default=2048,
+                    help="workloads 1-4: before the warm-up, measure the device's read and copy rates over a "
+                         "buffer of this many MiB (0: skip); reported as hbm_reference")
     ap.add_argument("--hbm-probe-mib", type=int, default=0,
                     help="time torch fill / sum / copy_ over a buffer of this many MiB and exit")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -624,6 +659,7 @@ def main():
     def step():
         sa.sa_forward(P, K, V, cu_offsets=cu, lengths=lengths, mask=mask, out=S, workspace=ws, **pb_kw)
 
+    ref = hbm_reference(args.ref_mib) if args.ref_mib > 0 else None
     ms_per_step, kern_ms = _timed(step, args.steps, args.warmup, args.flush_mib, args.flush_kind)
     value = tokens / (ms_per_step / 1e3)
     kern_avg_ms = sum(kern_ms) / len(kern_ms)
@@ -672,6 +708,10 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if ref is not None:
+        out["hbm_reference"] = ref
+        out["roofline"]["frac_of_measured_read"] = achieved / ref["read_GBps"]
+        out["roofline"]["frac_of_measured_copy"] = achieved / ref["copy_GBps"]
     if args.flush_mib == 0 and args.cold_mib > 0 and not proto:
         # the same launches with a buffer overwritten before each one (after
         # the timed region above, which it does not affect): no input left in

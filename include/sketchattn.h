@@ -25,18 +25,19 @@
  *     masks stay on the device).
  *   - Results are deterministic: the same call on the same device gives
  *     bitwise-identical outputs (fixed reduction order, no float atomics).
- *     The row segmentation depends on the device's CU count and on the
- *     tuning variables SA_KERNEL, SA_STREAM_NW, SA_BLOCKS_PER_CU,
- *     SA_BF16_TILE and SA_RANGE_SPLIT (read when a call is planned); other
- *     settings round differently, within the stated tolerances.
+ *     The row segmentation depends only on the problem and the device's CU
+ *     count (and on sa_set_tuning(), which nothing calls unless a caller
+ *     asks for a non-default work split); the environment plays no part.
  *   - Errors that the host can detect (null or misaligned pointers, bad
  *     sizes, unsupported shapes, a short workspace) return a non-zero status
  *     before anything is enqueued; sa_last_error() then describes it.  No C++
- *     exception crosses this interface.  Offsets and lengths are NOT checked
- *     on the device: they must satisfy the stated rules or results are
- *     undefined.
+ *     exception crosses this interface.  Offsets live in device memory and
+ *     are trusted by default: they must satisfy the stated rules or results
+ *     are undefined.  SA_FLAG_CHECK_OFFSETS (below) makes the forward entry
+ *     points validate them on the device first.
  *   - Thread safety: calls may be made from several host threads; the only
- *     per-thread state is the error text and the timing events below.
+ *     per-thread state is the error text, the timing events and the tuning
+ *     below.
  */
 #ifndef SKETCHATTN_H
 #define SKETCHATTN_H
@@ -101,13 +102,43 @@ typedef struct sa_problem {
                                across users, section 3.1) */
     int32_t chunk_rows;     /* 0: automatic work split over the device; > 0: every work
                                segment covers this many rows (multiple of 32) */
-    int32_t flags;          /* 0, or SA_FLAG_BF16_GRADS for sa_backward; every other
-                               entry point requires 0 */
+    int32_t flags;          /* OR of the SA_FLAG_* bits below that the entry point
+                               accepts; 0 for the default behaviour */
 } sa_problem;
 
 /* sa_problem.flags bit for sa_backward only: dK and dV are written as bf16
  * (the fp32 sums rounded to nearest even), the element type of K and V. */
 #define SA_FLAG_BF16_GRADS 1
+
+/*
+ * sa_problem.flags bit for sa_forward and sa_forward_fused_proj (a debug
+ * aid): before any kernel reads an offset, a small kernel checks cu_offsets
+ * on the device against the rules of sa_forward (the batching of ragged user
+ * histories that section 4.4 of the SequenceO1 paper serves in one pass):
+ *     rule 1 (bit 1)  cu_offsets[0] >= 0
+ *     rule 2 (bit 2)  cu_offsets[b] <= cu_offsets[b+1] for every b
+ *     rule 3 (bit 4)  cu_offsets[B] <= total_rows
+ * and writes the result into the first 8 bytes of the workspace: int32
+ * status (0 = valid, else the OR of the violated rules' bits) and int32
+ * index (the smallest b at which a rule fails: 0 for rule 1, the b of the
+ * first decreasing pair for rule 2, B for rule 3; -1 when valid).  Every
+ * later kernel of the call reads the status first; when it is non-zero none
+ * of them reads K, V, X or the mask, and S_out and lse_out are filled with
+ * NaN.  The host never reads the status on the call path (the call stays
+ * asynchronous): read it from the workspace after synchronising.  The
+ * dense layout (cu_offsets == NULL) has nothing to check (lengths are
+ * clamped) and always gets status 0.  The flag adds 256 bytes to the
+ * workspace size; the rest of the workspace follows the status section.
+ */
+#define SA_FLAG_CHECK_OFFSETS 2
+
+/*
+ * The rules of SA_FLAG_CHECK_OFFSETS evaluated on the host, for offsets the
+ * caller holds in host memory (the device check runs the same rule code).
+ * cu_offsets_host has B+1 entries.  Returns the status word described above
+ * and stores the index of the first violation in *first_bad (if non-NULL).
+ */
+int32_t sa_check_offsets_host(const int32_t* cu_offsets_host, int32_t B, int64_t total_rows, int32_t* first_bad);
 
 /*
  * Sketch Attention forward over a ragged batch of user histories.
@@ -359,6 +390,32 @@ sa_status sa_stca_attention(const sa_stca_problem* pb, const void* xt, const voi
 size_t sa_stca_workspace_size(const sa_stca_problem* pb);
 
 /*
+ * Work-split tuning for sweeps and benchmarks (not part of the computation).
+ * Each field left 0 keeps the library's default, which is what every call
+ * uses unless this is called.  The settings change which rows a work segment
+ * covers, and so the order in which sums are rounded: results move within
+ * the stated tolerances and stay bitwise repeatable for fixed settings.
+ * Thread-local: they apply to the calls this host thread makes until the next
+ * sa_set_tuning(); NULL restores the defaults.  Invalid values return
+ * SA_ERR_INVALID_ARG and leave the settings unchanged.
+ */
+typedef struct sa_tuning {
+    int32_t register_staged;   /* 1: bf16 forward on the register-staged kernel
+                                  instead of the direct-to-LDS streaming kernel */
+    int32_t stream_waves;      /* 8 or 16: preferred streaming block size */
+    int32_t blocks_per_cu;     /* > 0: occupancy that sizes the forward's row split */
+    int32_t range_split;       /* 1..99: percent of the rows that the first half of
+                                  the streaming kernel's row ranges takes when two
+                                  blocks share a CU (50 = equal ranges) */
+    int32_t bf16_tile_mb;      /* register-staged kernel: prototypes per wave (16, 32, 64) */
+    int32_t bf16_tile_nw;      /* register-staged kernel: waves per block (4, 8) */
+    int32_t bwd_blocks_per_cu; /* > 0: occupancy that sizes the backward's dK/dV row split */
+    int32_t bwd_dp_register_staged; /* 1: backward dP pass on the register-staged kernel */
+} sa_tuning;
+
+sa_status sa_set_tuning(const sa_tuning* tuning);
+
+/*
  * Timing hook for benchmarks and profilers (not part of the computation).
  * When both events are non-NULL, the next sa_forward or sa_forward_fused_proj
  * call made on this host thread records `start` on its stream immediately
@@ -368,9 +425,11 @@ size_t sa_stca_workspace_size(const sa_stca_problem* pb);
  * records them before its first and after its last launch; the next
  * sa_stca_attention call records them around its launches after the weight
  * transpose (query GEMM, attention, output GEMM).
- * NULL, NULL clears a pending request.  The
- * events belong to the caller (hipEventCreate); the library never creates,
- * waits on or destroys them.  Returns SA_ERR_INVALID_ARG if exactly one is NULL.
+ * NULL, NULL clears a pending request, and so does the next call of any
+ * entry point above, including one that fails before launching anything.
+ * The events belong to the caller (hipEventCreate); the library never
+ * creates, waits on or destroys them.  Returns SA_ERR_INVALID_ARG if exactly
+ * one is NULL.
  */
 sa_status sa_set_timing_events(hipEvent_t start, hipEvent_t stop);
 

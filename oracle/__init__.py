@@ -187,7 +187,8 @@ def _problem(P, K, cu, L_max, norm, scale, p_user_stride=0):
 def forward(P, K, V, cu_offsets=None, lengths=None, mask=None, norm="history", scale=None):
     """Full SA forward in double.
 
-    P: [H, m, dh]; K, V: packed [rows, H, dh] with ``cu_offsets`` [B+1], or
+    P: [H, m, dh] shared by every user, or [B, H, m, dh] with a prototype set
+    per user (user b's scores use P[b]); K, V: packed [rows, H, dh] with ``cu_offsets`` [B+1], or
     dense [B, L_max, H, dh] with optional ``lengths`` [B].  ``mask``: per row
     (packed: [rows]; dense: [B, L_max]), 0 = excluded.
     Returns (S [B, H, m, dh] float64, lse): lse is [B, H, m] for the history
@@ -203,7 +204,7 @@ def forward(P, K, V, cu_offsets=None, lengths=None, mask=None, norm="history", s
     cu = _opt_int32(cu_offsets)
     ln = _opt_int32(lengths)
     mk = _opt_u8(mask)
-    pb = _problem(Pr, Kr, cu, None, norm, scale)
+    pb = _problem(Pr, Kr, cu, None, norm, scale, p_user_stride=_user_stride(Pr, cu, Kr))
     pb.in_dtype = dt
     S = np.zeros((pb.B, pb.H, pb.m, pb.dh), dtype=np.float64)
     if pb.norm == HISTORY:
@@ -217,6 +218,19 @@ def forward(P, K, V, cu_offsets=None, lengths=None, mask=None, norm="history", s
     return S, lse
 
 
+def _user_stride(Pr, cu, Kr):
+    """p_user_stride of the C problem: 0 for shared P [H, m, dh], H*m*dh for
+    per-user P [B, H, m, dh] (which must have one set per user)."""
+    if Pr.ndim == 3:
+        return 0
+    if Pr.ndim != 4:
+        raise ValueError("P must be [H, m, dh] or [B, H, m, dh]")
+    B = len(cu) - 1 if cu is not None else Kr.shape[0]
+    if Pr.shape[0] != B:
+        raise ValueError(f"per-user P has {Pr.shape[0]} sets for {B} users")
+    return int(Pr.shape[1] * Pr.shape[2] * Pr.shape[3])
+
+
 def forward_sample(P, K, V, bhj, cu_offsets=None, lengths=None, mask=None, scale=None):
     """History axis: rows S[b, h, j, :] for each (b, h, j) in ``bhj`` -> ([n, dh], lse [n])."""
     lib = load()
@@ -226,7 +240,7 @@ def forward_sample(P, K, V, bhj, cu_offsets=None, lengths=None, mask=None, scale
     cu = _opt_int32(cu_offsets)
     ln = _opt_int32(lengths)
     mk = _opt_u8(mask)
-    pb = _problem(Pr, Kr, cu, None, "history", scale)
+    pb = _problem(Pr, Kr, cu, None, "history", scale, p_user_stride=_user_stride(Pr, cu, Kr))
     pb.in_dtype = dt
     idx = np.ascontiguousarray(np.asarray(bhj, dtype=np.int32).reshape(-1, 3))
     out = np.zeros((idx.shape[0], pb.dh), dtype=np.float64)

@@ -14,6 +14,11 @@ import mpmath
 mpmath.mp.dps = 50
 
 
+def _mp(x):
+    """An mpf for a stored float (exact) or an mpf computed here (kept as is)."""
+    return x if isinstance(x, mpmath.mpf) else mpmath.mpf(float(x))
+
+
 def _user_rows(b, cu, lengths, L_max, mask):
     if cu is not None:
         rows = list(range(int(cu[b]), int(cu[b + 1])))
@@ -36,21 +41,27 @@ def sketch_dense(P, K, V, B, L_max, lengths=None, mask=None, norm="history", sca
 
 
 def _sketch(P, K, V, B, rows_of, norm, scale):
-    """P [H][m][dh]; K, V [rows][H][dh] (any nested indexable of floats).
+    """P [H][m][dh], or [B][H][m][dh] with one prototype set per user (a
+    numpy array of 4 dimensions); K, V [rows][H][dh] (any nested indexable of
+    floats).
 
     Returns (S [B][H][m][dh], A, lse) as mpf: A[b][h] is the materialised
     [m][n_valid] assignment matrix; lse[b][h] is per prototype (history axis)
     or per valid token (prototype axis), natural log, scale included.
     """
-    H, m, dh = len(P), len(P[0]), len(P[0][0])
+    per_user = getattr(P, "ndim", 3) == 4
+    P0 = P[0] if per_user else P
+    H, m, dh = len(P0), len(P0[0]), len(P0[0][0])
     sc = mpmath.mpf(1) / mpmath.sqrt(dh) if scale is None else mpmath.mpf(scale)
     S, W, LSE = [], [], []
+    P_all = P
     for b in range(B):
+        P = P_all[b] if per_user else P_all
         rows = rows_of(b)
         Sb, Wb, Lb = [], [], []
         for h in range(H):
             # scores s[j][t] = scale * <P[h][j], K[row_t][h]>
-            s = [[sc * mpmath.fsum(mpmath.mpf(float(P[h][j][e])) * mpmath.mpf(float(K[r][h][e]))
+            s = [[sc * mpmath.fsum(_mp(P[h][j][e]) * _mp(K[r][h][e])
                                    for e in range(dh)) for r in rows] for j in range(m)]
             n = len(rows)
             if norm == "history":
@@ -73,7 +84,7 @@ def _sketch(P, K, V, B, rows_of, norm, scale):
                     for j in range(m):
                         A[j][t] = e_[j] / Z
                     lse.append(mpmath.log(Z))
-            Sbh = [[mpmath.fsum(A[j][t] * mpmath.mpf(float(V[rows[t]][h][e])) for t in range(n))
+            Sbh = [[mpmath.fsum(A[j][t] * _mp(V[rows[t]][h][e]) for t in range(n))
                     for e in range(dh)] for j in range(m)]
             Sb.append(Sbh)
             Wb.append(A)
@@ -82,6 +93,22 @@ def _sketch(P, K, V, B, rows_of, norm, scale):
         W.append(Wb)
         LSE.append(Lb)
     return S, W, LSE
+
+
+# ------------------------------------------- fused projection (tiny)
+def fused(X, Wk, Wv, P, cu, mask=None, scale=None):
+    """Keys K = X Wk and values V = X Wv -- or V = X itself when ``Wv`` is
+    None, the paper's sketch of X (section 3.1) -- every product an mpf, then
+    the history-axis sketch of :func:`sketch_packed`.  X [rows][d_model],
+    Wk (and Wv) [d_model][H dh], P [H][m][dh]; head h is columns
+    [h dh, (h+1) dh) of K and V (of X when V = X).  Returns (S, A, lse)."""
+    H, dh = len(P), len(P[0][0])
+    Xm = _mat(X)
+    Km = _matmul(Xm, _mat(Wk))
+    Vm = _matmul(Xm, _mat(Wv)) if Wv is not None else Xm
+    K3 = [[[Km[r][h * dh + e] for e in range(dh)] for h in range(H)] for r in range(len(Xm))]
+    V3 = [[[Vm[r][h * dh + e] for e in range(dh)] for h in range(H)] for r in range(len(Xm))]
+    return sketch_packed(P, K3, V3, cu, mask=mask, scale=scale)
 
 
 # ------------------------------------------------- stacked refinement (tiny)

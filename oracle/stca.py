@@ -78,10 +78,3 @@ def stca_attention(xt, X, Wq, Wk, Wv, cu_offsets, t_offsets, h, windows=None, sc
                 out[t, cols] = y @ Wv[:, cols]
     return out
 
-
-def stca_flops(n_rows_per_target, D, h):
-    """Appendix G.2.1's count for one target: 2 D dh for each of q W_Q,
-    (q W_Q) W_K^T and (alpha X) W_V, and 2 L D for each of u X^T and alpha X,
-    per head: 6 D^2 + 4 L D h in total (dh = D / h)."""
-    L = np.asarray(n_rows_per_target, dtype=np.float64)
-    return float(np.sum(6.0 * D * D + 4.0 * L * D * h))

@@ -22,12 +22,14 @@ SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = ra
 SA_DTYPE_F32, SA_DTYPE_BF16 = 0, 1
 SA_NORM_HISTORY, SA_NORM_PROTOTYPE = 0, 1
 SA_FLAG_BF16_GRADS = 1
+SA_FLAG_CHECK_OFFSETS = 2
 _NORMS = {"history": SA_NORM_HISTORY, "prototype": SA_NORM_PROTOTYPE}
 
 EXPORTED = ("sa_forward", "sa_forward_workspace_size", "sa_forward_kernel_name", "sa_forward_fused_proj",
             "sa_forward_fused_proj_workspace_size", "sa_refine_forward", "sa_refine_workspace_size",
             "sa_backward", "sa_backward_workspace_size", "sa_stca_attention", "sa_stca_workspace_size",
-            "sa_set_timing_events", "sa_status_string", "sa_last_error", "sa_version")
+            "sa_set_timing_events", "sa_set_tuning", "sa_check_offsets_host", "sa_status_string", "sa_last_error",
+            "sa_version")
 
 
 class SaRefineLayer(ctypes.Structure):
@@ -46,6 +48,13 @@ class SaProblem(ctypes.Structure):
         ("q_batch_stride", ctypes.c_int64),
         ("chunk_rows", ctypes.c_int32), ("flags", ctypes.c_int32),
     ]
+
+
+class SaTuning(ctypes.Structure):
+    """Mirror of ``sa_tuning`` in include/sketchattn.h (0 = the default)."""
+    _fields_ = [(n, ctypes.c_int32) for n in ("register_staged", "stream_waves", "blocks_per_cu", "range_split",
+                                              "bf16_tile_mb", "bf16_tile_nw", "bwd_blocks_per_cu",
+                                              "bwd_dp_register_staged")]
 
 
 class SaStcaProblem(ctypes.Structure):
@@ -108,6 +117,10 @@ def load_library(path: str | None = None):
     lib.sa_version.restype = ctypes.c_int
     lib.sa_set_timing_events.argtypes = [vp, vp]
     lib.sa_set_timing_events.restype = ctypes.c_int
+    lib.sa_set_tuning.argtypes = [ctypes.POINTER(SaTuning)]
+    lib.sa_set_tuning.restype = ctypes.c_int
+    lib.sa_check_offsets_host.argtypes = [vp, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)]
+    lib.sa_check_offsets_host.restype = ctypes.c_int32
     if path is None:
         _lib = lib
     return lib
@@ -117,6 +130,32 @@ def sa_set_timing_events(start, stop) -> None:
     """Record HIP events ``start``/``stop`` (raw hipEvent_t handles, or None)
     around the streaming kernel of the next forward call on this thread."""
     _check(load_library().sa_set_timing_events(start, stop))
+
+
+def sa_set_tuning(**fields) -> None:
+    """Work-split tuning for the calls this thread makes (``sa_tuning``
+    fields as keywords; no keywords restores the defaults)."""
+    lib = load_library()
+    if not fields:
+        _check(lib.sa_set_tuning(None))
+        return
+    t = SaTuning()
+    for k, v in fields.items():
+        if k not in dict(SaTuning._fields_):
+            raise TypeError(f"unknown tuning field {k!r}")
+        setattr(t, k, int(v))
+    _check(lib.sa_set_tuning(ctypes.byref(t)))
+
+
+def sa_check_offsets_host(cu_offsets, total_rows: int):
+    """The offsets rules on host memory: returns (status bits, first bad
+    index or -1) for an int32 sequence of B+1 offsets."""
+    import numpy as np
+    cu = np.ascontiguousarray(np.asarray(cu_offsets), dtype=np.int32)
+    first = ctypes.c_int32(0)
+    bits = load_library().sa_check_offsets_host(cu.ctypes.data_as(ctypes.c_void_p), cu.size - 1, int(total_rows),
+                                                ctypes.byref(first))
+    return int(bits), int(first.value)
 
 
 def sa_status_string(status: int) -> str:
@@ -176,7 +215,7 @@ def _dtype_name(t):
 
 def sa_forward(P, K, V, cu_offsets=None, lengths=None, mask=None, norm: str = "history",
                return_lse: bool = False, scale: float | None = None, chunk_rows: int = 0,
-               workspace=None, out=None):
+               workspace=None, out=None, check_offsets: bool = False):
     """Sketch Attention forward on the GPU.
 
     P: [H, m, dh] (or [B, H, m, dh] per-user prototypes), bf16 or fp32.
@@ -185,6 +224,9 @@ def sa_forward(P, K, V, cu_offsets=None, lengths=None, mask=None, norm: str = "h
     ``mask``: uint8/bool per buffer row ([rows] or [B, L_max]), 0 = excluded.
     Returns S [B, H, m, dh] float32, and lse when ``return_lse``
     ([B, H, m] history axis; [rows, H] prototype axis).
+    ``check_offsets`` sets SA_FLAG_CHECK_OFFSETS: the offsets are validated
+    on the device and the verdict lands in ``workspace[:8]`` (int32 status,
+    int32 first bad index); pass ``workspace`` to read it.
     """
     import torch
     lib = load_library()
@@ -234,7 +276,7 @@ def sa_forward(P, K, V, cu_offsets=None, lengths=None, mask=None, norm: str = "h
         mask = mask.contiguous()
     pb = make_problem(B, H, m, dh, rows, L_max=L_max, dtype=dt, norm=norm, scale=scale or 0.0,
                       k_row_stride=ks, v_row_stride=vs, q_batch_stride=(H * m * dh if per_user else 0),
-                      chunk_rows=chunk_rows)
+                      chunk_rows=chunk_rows, flags=SA_FLAG_CHECK_OFFSETS if check_offsets else 0)
     nws = sa_forward_workspace_size(pb)
     if nws == 0:
         _check(lib.sa_forward(ctypes.byref(pb), None, None, None, None, None, None, None, None, None, 0, None))

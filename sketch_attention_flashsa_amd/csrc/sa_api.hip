@@ -18,6 +18,24 @@ namespace {
 
 thread_local char g_err[512] = "";
 thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+thread_local sa_tuning g_tune = {};
+
+// The timing events of a call: taken (and forgotten) at the top of every
+// compute entry point, before anything can fail.
+struct Events {
+    hipEvent_t start, stop;
+};
+Events take_events() {
+    const Events ev{g_ev_start, g_ev_stop};
+    g_ev_start = g_ev_stop = nullptr;
+    return ev;
+}
+
+// A launch reports its error through the runtime's per-thread "last error",
+// which an earlier, unrelated HIP call may have left set: clear it first, so
+// that a call's status reflects its own launches only.  (Errors that poison
+// the device context persist in the runtime and still fail the launches.)
+void clear_stale_error() { (void)hipGetLastError(); }
 
 sa_status fail(sa_status st, const char* fmt, ...) {
     va_list ap;
@@ -77,16 +95,18 @@ struct Plan {
     bool stream = false;      // bf16: the direct-to-LDS streaming kernel serves this shape
     sa::StreamConfig scfg{};
     int groups = 1;           // bf16: unit groups per row range
+    bool check_offsets = false;  // SA_FLAG_CHECK_OFFSETS: status section first
     // workspace layout (byte offsets)
-    size_t off_vcu = 0, off_M = 0, off_Z = 0, off_acc = 0, off_tok = 0, total = 0;
+    size_t off_status = 0, off_vcu = 0, off_M = 0, off_Z = 0, off_acc = 0, off_tok = 0, total = 0;
 };
 
 void set_layout(const sa_problem* pb, Plan* pl);
 
 // Validation and work split shared by every entry point.  The workspace size
 // depends only on the problem description, never on which optional pointers
-// a call passes, so the size query and the call always agree.
-sa_status make_plan(const sa_problem* pb, bool packed, Plan* pl) {
+// a call passes, so the size query and the call always agree.  `flags_ok`
+// are the sa_problem.flags bits the calling entry point accepts.
+sa_status make_plan(const sa_problem* pb, bool packed, Plan* pl, int32_t flags_ok = SA_FLAG_CHECK_OFFSETS) {
     if (!pb) return fail(SA_ERR_INVALID_ARG, "problem is NULL");
     if (pb->B < 0 || pb->H < 1 || pb->m < 1 || pb->dh < 1)
         return fail(SA_ERR_INVALID_ARG, "need B >= 0, H >= 1, m >= 1, dh >= 1 (got B=%d H=%d m=%d dh=%d)", pb->B,
@@ -95,7 +115,9 @@ sa_status make_plan(const sa_problem* pb, bool packed, Plan* pl) {
         return fail(SA_ERR_INVALID_ARG, "unknown dtype %d", pb->dtype);
     if (pb->norm != SA_NORM_HISTORY && pb->norm != SA_NORM_PROTOTYPE)
         return fail(SA_ERR_INVALID_ARG, "unknown norm %d", pb->norm);
-    if (pb->flags != 0) return fail(SA_ERR_INVALID_ARG, "flags must be 0");
+    if (pb->flags & ~flags_ok)
+        return fail(SA_ERR_INVALID_ARG, "flags %d: this entry point accepts only the bits %d", pb->flags, flags_ok);
+    pl->check_offsets = (pb->flags & SA_FLAG_CHECK_OFFSETS) != 0;
     if (pb->total_rows < 0 || pb->total_rows > INT32_MAX)
         return fail(SA_ERR_INVALID_ARG, "total_rows must be in [0, 2^31)");
     if (pb->chunk_rows < 0 || pb->chunk_rows % sa::kRowAlign != 0)
@@ -126,7 +148,8 @@ sa_status make_plan(const sa_problem* pb, bool packed, Plan* pl) {
         if (!(pb->dh == 32 || pb->dh == 64 || pb->dh == 128) || pb->m % 16 != 0)
             return fail(SA_ERR_UNSUPPORTED, "bf16: dh must be 32, 64 or 128 and m a multiple of 16 (got dh=%d m=%d)",
                         pb->dh, pb->m);
-        if (!sa::bf16_config(pb->dh, pb->m, pb->H, device_info().lds, &pl->cfg))
+        if (!sa::bf16_config(pb->dh, pb->m, pb->H, device_info().lds, g_tune.bf16_tile_mb, g_tune.bf16_tile_nw,
+                             &pl->cfg))
             return fail(SA_ERR_UNSUPPORTED, "bf16: tile needs %zu bytes of LDS, device allows %zu",
                         pl->cfg.lds_bytes, device_info().lds);
         const int64_t ks = pb->k_row_stride ? pb->k_row_stride : hd;
@@ -142,8 +165,8 @@ sa_status make_plan(const sa_problem* pb, bool packed, Plan* pl) {
         blocks_per_cu = 4;
         pl->R_min = kRowMinF32;
     } else {
-        const char* kern = getenv("SA_KERNEL");
-        pl->stream = !(kern && strcmp(kern, "v1") == 0) && sa::stream_config(pb->dh, pb->m, pb->H, &pl->scfg);
+        pl->stream =
+            !g_tune.register_staged && sa::stream_config(pb->dh, pb->m, pb->H, g_tune.stream_waves, &pl->scfg);
         if (pl->stream) {
             pl->groups = pl->scfg.groups;
             blocks_per_cu = pl->scfg.blocks_per_cu;
@@ -161,14 +184,13 @@ sa_status make_plan(const sa_problem* pb, bool packed, Plan* pl) {
         const int64_t G = (rows_upper + pb->chunk_rows - 1) / pb->chunk_rows;
         pl->G = (int)(G > 0 ? G : 1);
     } else {
-        if (const char* e = getenv("SA_BLOCKS_PER_CU")) blocks_per_cu = atoi(e) > 0 ? atoi(e) : blocks_per_cu;
+        if (g_tune.blocks_per_cu > 0) blocks_per_cu = g_tune.blocks_per_cu;
         const int64_t G = (int64_t)dev.cus * blocks_per_cu / per_row_range;
         pl->G = (int)(G > 0 ? G : 1);
         // two streaming blocks per CU: the older one (first half of the
         // ranges in dispatch order) gets the larger share of the rows
         if (pl->stream && blocks_per_cu == 2) {
-            pl->split = kStreamSplit;
-            if (const char* e = getenv("SA_RANGE_SPLIT")) pl->split = atoi(e);
+            pl->split = g_tune.range_split > 0 ? g_tune.range_split : kStreamSplit;
         }
     }
 
@@ -181,6 +203,8 @@ void set_layout(const sa_problem* pb, Plan* pl) {
     const size_t nslot = (size_t)pl->G + (size_t)pb->B;
     const size_t hm = (size_t)pb->H * pb->m;
     size_t off = 0;
+    pl->off_status = off;
+    if (pl->check_offsets) off = align_up(off + 2 * sizeof(int32_t));
     pl->off_vcu = off;
     off = align_up(off + sizeof(int32_t) * ((size_t)pb->B + 1));
     pl->off_M = off;
@@ -260,6 +284,8 @@ sa_status sa_forward(const sa_problem* pb, const void* P, const void* K, const v
                      const int32_t* lengths, const uint8_t* mask, float* S_out, float* lse_out, void* workspace,
                      size_t workspace_bytes, hipStream_t stream) {
     g_err[0] = 0;
+    const Events ev = take_events();
+    clear_stale_error();
     Plan pl;
     const bool packed = cu_offsets != nullptr;
     sa_status st = make_plan(pb, packed, &pl);
@@ -286,6 +312,13 @@ sa_status sa_forward(const sa_problem* pb, const void* P, const void* K, const v
     const float scale = pb->scale > 0.f ? pb->scale : 1.0f / sqrtf((float)pb->dh);
 
     hipError_t e;
+    const int32_t* status = nullptr;
+    if (pl.check_offsets) {
+        int32_t* sw = (int32_t*)(ws + pl.off_status);
+        if ((e = sa::launch_check_offsets(cu_offsets, pb->B, pb->total_rows, sw, stream)) != hipSuccess)
+            return hip_fail(e, "offsets check");
+        status = sw;
+    }
     if (!packed && lengths) {
         users.vcu = (int32_t*)(ws + pl.off_vcu);
         e = sa::launch_dense_vcu(lengths, pb->B, pb->L_max, (int32_t*)(ws + pl.off_vcu), stream);
@@ -308,6 +341,7 @@ sa_status sa_forward(const sa_problem* pb, const void* P, const void* K, const v
         t.c = scale * sa::kLog2e;
         t.lse2_tok = lse2_tok;
         t.lse_out = lse_out;
+        t.status = status;
         if (pb->q_batch_stride != 0)
             return fail(SA_ERR_UNSUPPORTED, "prototype axis with per-user prototypes is not supported");
         e = pl.f32 ? sa::launch_f32_tok_lse(t, stream) : sa::launch_bf16_tok_lse(t, stream);
@@ -334,14 +368,13 @@ sa_status sa_forward(const sa_problem* pb, const void* P, const void* K, const v
     a.part = part;
     a.lse2_tok = lse2_tok;
     a.norm = pb->norm;
-    const hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
-    g_ev_start = g_ev_stop = nullptr;
-    if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return hip_fail(e, "timing event");
+    a.status = status;
+    if (ev.start && (e = hipEventRecord(ev.start, stream)) != hipSuccess) return hip_fail(e, "timing event");
     if (pl.f32) e = sa::launch_f32_forward(a, stream);
     else if (pl.stream) e = sa::launch_bf16_stream(a, pl.scfg, stream);
     else e = sa::launch_bf16_forward(a, pl.cfg, stream);
     if (e != hipSuccess) return hip_fail(e, "forward");
-    if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return hip_fail(e, "timing event");
+    if (ev.stop && (e = hipEventRecord(ev.stop, stream)) != hipSuccess) return hip_fail(e, "timing event");
 
     sa::MergeArgs mg{};
     mg.users = users;
@@ -357,6 +390,7 @@ sa_status sa_forward(const sa_problem* pb, const void* P, const void* K, const v
     mg.lse = pb->norm == SA_NORM_HISTORY ? lse_out : nullptr;
     mg.norm = pb->norm;
     mg.lane_major = !pl.f32;   // the MFMA kernels store their accumulators lane-major
+    mg.status = status;
     e = sa::launch_merge(mg, stream);
     if (e != hipSuccess) return hip_fail(e, "merge");
     return SA_OK;
@@ -366,6 +400,8 @@ sa_status sa_forward_fused_proj(const sa_problem* pb, const void* X, int32_t d_m
                                 const void* P, const int32_t* cu_offsets, const uint8_t* mask, float* S_out,
                                 float* lse_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     g_err[0] = 0;
+    const Events ev = take_events();
+    clear_stale_error();
     Plan pl;
     sa_status st = make_fused_plan(pb, d_model, &pl);
     if (st != SA_OK) return st;
@@ -388,10 +424,8 @@ sa_status sa_forward_fused_proj(const sa_problem* pb, const void* X, int32_t d_m
         const int hd = pb->H * pb->dh;
         sa::bf16* kbuf = (sa::bf16*)(ws + pl.off_kproj);
         sa::bf16* wt = (sa::bf16*)(ws + pl.off_wt);
-        const hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
-        g_ev_start = g_ev_stop = nullptr;
         hipError_t e;
-        if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return hip_fail(e, "timing event");
+        if (ev.start && (e = hipEventRecord(ev.start, stream)) != hipSuccess) return hip_fail(e, "timing event");
         sa::TransposeArgs ta{};
         ta.mat[ta.n++] = {(const sa::bf16*)Wk, wt, d_model, hd};
         if ((e = sa::launch_transpose(ta, stream)) != hipSuccess) return hip_fail(e, "weight transpose");
@@ -406,7 +440,7 @@ sa_status sa_forward_fused_proj(const sa_problem* pb, const void* X, int32_t d_m
         sa_problem fp = *pb;
         fp.k_row_stride = hd;
         fp.v_row_stride = d_model;
-        g_ev_stop = ev1;                 // stop after the streaming pass (start is above)
+        g_ev_stop = ev.stop;             // stop after the streaming pass (start is above)
         return sa_forward(&fp, P, kbuf, X, cu_offsets, nullptr, mask, S_out, lse_out, workspace, pl.fwd_total, stream);
     }
     sa::Users users{};
@@ -432,12 +466,18 @@ sa_status sa_forward_fused_proj(const sa_problem* pb, const void* X, int32_t d_m
     a.R_min = pl.R_min;
     a.part = part;
     hipError_t e;
-    const hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
-    g_ev_start = g_ev_stop = nullptr;
-    if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return hip_fail(e, "timing event");
+    const int32_t* status = nullptr;
+    if (pl.check_offsets) {
+        int32_t* sw = (int32_t*)(ws + pl.off_status);
+        if ((e = sa::launch_check_offsets(cu_offsets, pb->B, pb->total_rows, sw, stream)) != hipSuccess)
+            return hip_fail(e, "offsets check");
+        status = sw;
+    }
+    a.status = status;
+    if (ev.start && (e = hipEventRecord(ev.start, stream)) != hipSuccess) return hip_fail(e, "timing event");
     e = sa::launch_fused(a, stream);
     if (e != hipSuccess) return hip_fail(e, "fused forward");
-    if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return hip_fail(e, "timing event");
+    if (ev.stop && (e = hipEventRecord(ev.stop, stream)) != hipSuccess) return hip_fail(e, "timing event");
 
     sa::MergeArgs mg{};
     mg.users = users;
@@ -453,6 +493,7 @@ sa_status sa_forward_fused_proj(const sa_problem* pb, const void* X, int32_t d_m
     mg.lse = lse_out;
     mg.norm = SA_NORM_HISTORY;
     mg.lane_major = 1;
+    mg.status = status;
     e = sa::launch_merge(mg, stream);
     if (e != hipSuccess) return hip_fail(e, "merge");
     return SA_OK;
@@ -526,6 +567,8 @@ sa_status sa_stca_attention(const sa_stca_problem* pb, const void* xt, const voi
                             const int32_t* windows, float* out, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
     g_err[0] = 0;
+    const Events ev = take_events();
+    clear_stale_error();
     StcaPlan sp;
     sa_status st = make_stca_plan(pb, &sp);
     if (st != SA_OK) return st;
@@ -564,14 +607,12 @@ sa_status sa_stca_attention(const sa_stca_problem* pb, const void* xt, const voi
     a.grid = sp.grid;
     a.c = sp.c;
 
-    const hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
-    g_ev_start = g_ev_stop = nullptr;
     hipError_t e;
     sa::TransposeArgs ta{};
     ta.mat[ta.n++] = {(const sa::bf16*)Wq, (sa::bf16*)wqt, D, D};
     ta.mat[ta.n++] = {(const sa::bf16*)Wv, (sa::bf16*)wvt, D, D};
     if ((e = sa::launch_transpose(ta, stream)) != hipSuccess) return hip_fail(e, "weight transpose");
-    if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return hip_fail(e, "timing event");
+    if (ev.start && (e = hipEventRecord(ev.start, stream)) != hipSuccess) return hip_fail(e, "timing event");
     // q = x W_Q for every target
     sa::GemmArgs g1{};
     g1.A = (const sa::bf16*)xt;
@@ -600,7 +641,7 @@ sa_status sa_stca_attention(const sa_stca_problem* pb, const void* xt, const voi
     g3.K = D;
     g3.batch = h;
     if ((e = sa::launch_gemm_nt(g3, false, stream)) != hipSuccess) return hip_fail(e, "output projection");
-    if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return hip_fail(e, "timing event");
+    if (ev.stop && (e = hipEventRecord(ev.stop, stream)) != hipSuccess) return hip_fail(e, "timing event");
     return SA_OK;
 }
 
@@ -625,6 +666,7 @@ struct RefinePlan {
 
 sa_status make_refine_plan(const sa_problem* pb, int32_t d_model, int32_t n_layers, RefinePlan* rp) {
     if (!pb) return fail(SA_ERR_INVALID_ARG, "problem is NULL");
+    if (pb->flags != 0) return fail(SA_ERR_INVALID_ARG, "refinement: flags must be 0");
     if (pb->q_batch_stride != 0 || pb->L_max != 0 || pb->k_row_stride != 0 || pb->v_row_stride != 0)
         return fail(SA_ERR_INVALID_ARG, "refinement: q_batch_stride, L_max and the row strides must be 0");
     if (n_layers < 1 || n_layers > kMaxRefineLayers)
@@ -661,6 +703,8 @@ sa_status sa_refine_forward(const sa_problem* pb, const void* X, int32_t d_model
                             const sa_refine_layer* layers, float eps, const int32_t* cu_offsets, const uint8_t* mask,
                             float* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     g_err[0] = 0;
+    const Events ev = take_events();
+    clear_stale_error();
     RefinePlan rp;
     sa_status st = make_refine_plan(pb, d_model, n_layers, &rp);
     if (st != SA_OK) return st;
@@ -697,10 +741,8 @@ sa_status sa_refine_forward(const sa_problem* pb, const void* X, int32_t d_model
     auto w3_t = [&](int l) { return wt + 7 * dd * l + 3 * dd; };
     auto w2_t = [&](int l) { return wt + 7 * dd * l + 5 * dd; };
 
-    const hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
-    g_ev_start = g_ev_stop = nullptr;
     hipError_t e;
-    if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return hip_fail(e, "timing event");
+    if (ev.start && (e = hipEventRecord(ev.start, stream)) != hipSuccess) return hip_fail(e, "timing event");
 
     // weights to [out][in]
     sa::TransposeArgs ta{};
@@ -749,7 +791,7 @@ sa_status sa_refine_forward(const sa_problem* pb, const void* X, int32_t d_model
         u.out = out;
         if ((e = sa::launch_sketch(u, D, stream)) != hipSuccess) return hip_fail(e, "sketch update");
     }
-    if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return hip_fail(e, "timing event");
+    if (ev.stop && (e = hipEventRecord(ev.stop, stream)) != hipSuccess) return hip_fail(e, "timing event");
     return SA_OK;
 }
 
@@ -772,7 +814,7 @@ sa_status make_bwd_plan(const sa_problem* pb_in, bool packed, BwdPlan* bp) {
     sa_problem q = *pb_in;      // the forward's checks see flags = 0
     q.flags = 0;
     const sa_problem* pb = &q;
-    sa_status st = make_plan(pb, packed, &bp->fw);
+    sa_status st = make_plan(pb, packed, &bp->fw, 0);
     if (st != SA_OK) return st;
     if (pb->dtype != SA_DTYPE_BF16) return fail(SA_ERR_UNSUPPORTED, "backward: bf16 inputs only");
     if (pb->norm != SA_NORM_HISTORY) return fail(SA_ERR_UNSUPPORTED, "backward: history axis only");
@@ -790,7 +832,7 @@ sa_status make_bwd_plan(const sa_problem* pb_in, bool packed, BwdPlan* bp) {
     } else {
         bp->G = cus * 2 / groups > 0 ? cus * 2 / groups : 1;
         int bpc = kDkdvBlocksPerCu;
-        if (const char* e = getenv("SA_BWD_BLOCKS_PER_CU")) bpc = atoi(e) > 0 ? atoi(e) : bpc;
+        if (g_tune.bwd_blocks_per_cu > 0) bpc = g_tune.bwd_blocks_per_cu;
         bp->G1 = cus * bpc / pb->H > 0 ? cus * bpc / pb->H : 1;
     }
     const size_t bhm = (size_t)pb->B * pb->H * pb->m;
@@ -817,6 +859,8 @@ sa_status sa_backward(const sa_problem* pb, const void* P, const void* K, const 
                       const int32_t* lengths, const uint8_t* mask, const float* S, const float* lse, const float* dS,
                       float* dP, void* dK, void* dV, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     g_err[0] = 0;
+    const Events ev = take_events();
+    clear_stale_error();
     BwdPlan bp;
     const bool packed = cu_offsets != nullptr;
     sa_status st = make_bwd_plan(pb, packed, &bp);
@@ -838,9 +882,7 @@ sa_status sa_backward(const sa_problem* pb, const void* P, const void* K, const 
     users.B = pb->B;
     users.L_max = pb->L_max;
     hipError_t e;
-    const hipEvent_t ev0 = g_ev_start, ev1 = g_ev_stop;
-    g_ev_start = g_ev_stop = nullptr;
-    if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return hip_fail(e, "timing event");
+    if (ev.start && (e = hipEventRecord(ev.start, stream)) != hipSuccess) return hip_fail(e, "timing event");
     if (!packed && lengths) {
         users.vcu = (int32_t*)(ws + bp.off_vcu);
         e = sa::launch_dense_vcu(lengths, pb->B, pb->L_max, (int32_t*)(ws + bp.off_vcu), stream);
@@ -878,8 +920,9 @@ sa_status sa_backward(const sa_problem* pb, const void* P, const void* K, const 
     a.part = sa::Partials{(float*)(ws + bp.off_part), nullptr, nullptr};
     a.dP = dP;
     a.per_user = pb->q_batch_stride != 0;
+    a.dp_register_staged = g_tune.bwd_dp_register_staged != 0;
     if ((e = sa::launch_backward(a, stream)) != hipSuccess) return hip_fail(e, "backward");
-    if (ev1 && (e = hipEventRecord(ev1, stream)) != hipSuccess) return hip_fail(e, "timing event");
+    if (ev.stop && (e = hipEventRecord(ev.stop, stream)) != hipSuccess) return hip_fail(e, "timing event");
     return SA_OK;
 }
 
@@ -900,6 +943,41 @@ sa_status sa_set_timing_events(hipEvent_t start, hipEvent_t stop) {
     g_ev_start = start;
     g_ev_stop = stop;
     return SA_OK;
+}
+
+sa_status sa_set_tuning(const sa_tuning* t) {
+    if (!t) {
+        g_tune = sa_tuning{};
+        return SA_OK;
+    }
+    if (t->register_staged < 0 || t->register_staged > 1 || t->bwd_dp_register_staged < 0 ||
+        t->bwd_dp_register_staged > 1)
+        return fail(SA_ERR_INVALID_ARG, "register_staged flags must be 0 or 1");
+    if (!(t->stream_waves == 0 || t->stream_waves == 8 || t->stream_waves == 16))
+        return fail(SA_ERR_INVALID_ARG, "stream_waves must be 0, 8 or 16 (got %d)", t->stream_waves);
+    if (t->blocks_per_cu < 0 || t->blocks_per_cu > 64 || t->bwd_blocks_per_cu < 0 || t->bwd_blocks_per_cu > 64)
+        return fail(SA_ERR_INVALID_ARG, "blocks per CU must be in 0..64");
+    if (t->range_split < 0 || t->range_split > 99)
+        return fail(SA_ERR_INVALID_ARG, "range_split must be in 0..99 (got %d)", t->range_split);
+    if (!(t->bf16_tile_mb == 0 || t->bf16_tile_mb == 16 || t->bf16_tile_mb == 32 || t->bf16_tile_mb == 64) ||
+        !(t->bf16_tile_nw == 0 || t->bf16_tile_nw == 4 || t->bf16_tile_nw == 8) ||
+        ((t->bf16_tile_mb == 0) != (t->bf16_tile_nw == 0)))
+        return fail(SA_ERR_INVALID_ARG, "bf16 tile: mb in {16, 32, 64} and nw in {4, 8}, or both 0");
+    g_tune = *t;
+    return SA_OK;
+}
+
+int32_t sa_check_offsets_host(const int32_t* cu, int32_t B, int64_t total_rows, int32_t* first_bad) {
+    int32_t bits = 0, first = -1;
+    if (cu && B >= 0) {
+        for (int32_t b = 0; b <= B; ++b) {
+            const int32_t x = sa::offsets_entry_bits(cu, b, B, total_rows);
+            if (x && first < 0) first = b;
+            bits |= x;
+        }
+    }
+    if (first_bad) *first_bad = first;
+    return bits;
 }
 
 const char* sa_status_string(sa_status status) {

@@ -728,7 +728,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
     // (K and V row starts 16-byte aligned), the register-staged one otherwise
     const int cpr = NH * a.dh / 8;
     const bool ring_ok = NH * PB == 8 && (cpr == 16 || cpr == 32) && a.k_stride % 8 == 0 && a.v_stride % 8 == 0 &&
-                         getenv("SA_BWD_DP") == nullptr;
+                         !a.dp_register_staged;
 #define SA_DP_RING(D_, C_)                                                                                   \
     if (masked) hipLaunchKernelGGL((sa_bwd_dp_stream_kernel<D_, C_, true>), g2, blk2, 0, s, a, NH, PB);      \
     else hipLaunchKernelGGL((sa_bwd_dp_stream_kernel<D_, C_, false>), g2, blk2, 0, s, a, NH, PB);

@@ -74,6 +74,7 @@ __global__ __launch_bounds__(NW * 64) void sa_bf16_fwd_kernel(FwdArgs a, int PB,
     constexpr int LPT = (DH / 16 + 0);    // max 16-byte loads per thread per tensor (heads <= NW)
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
+    if (offsets_rejected(a.status)) return;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 4;              // lane group: row quad / k octet
@@ -359,8 +360,8 @@ void fill_config(int dh, int H, int mb, int nw, int pb, Bf16Config* cfg) {
 // Tile selection.  Register budget decides it: at 8 waves per block a wave
 // has 256 VGPRs, at 4 waves (one per SIMD) 512 with the accumulation
 // registers; the choices below are the instantiations that do not spill.
-// SA_BF16_TILE="mb,nw" overrides the choice (tuning sweeps), when valid.
-bool bf16_config(int dh, int m, int H, size_t lds_limit, Bf16Config* cfg) {
+// A requested tile (tile_mb, tile_nw) overrides the choice when valid.
+bool bf16_config(int dh, int m, int H, size_t lds_limit, int tile_mb, int tile_nw, Bf16Config* cfg) {
     if (!(dh == 32 || dh == 64 || dh == 128) || m % 16 != 0) return false;
     int mb, nw;
     if (dh == 32) {
@@ -370,10 +371,10 @@ bool bf16_config(int dh, int m, int H, size_t lds_limit, Bf16Config* cfg) {
     }
     int units = H * (m / mb);
     nw = (units % 8 == 0 && dh <= 64) ? 8 : 4;
-    if (const char* env = getenv("SA_BF16_TILE")) {
-        int emb = 0, enw = 0;
-        if (sscanf(env, "%d,%d", &emb, &enw) == 2 && (emb == 16 || emb == 32 || emb == 64) && m % emb == 0 &&
-            (enw == 4 || enw == 8) && !(dh == 128 && (emb == 64 || enw == 8))) {
+    {
+        const int emb = tile_mb, enw = tile_nw;
+        if ((emb == 16 || emb == 32 || emb == 64) && m % emb == 0 && (enw == 4 || enw == 8) &&
+            !(dh == 128 && (emb == 64 || enw == 8))) {
             mb = emb;
             nw = enw;
         }

@@ -33,9 +33,6 @@
 //     direct-to-LDS loads counted with its other loads: plain loads at the
 //     point of use would make the compiler, which cannot count the ring's
 //     asm loads, wait for all of them, draining the ring once per stage.
-#include <stdlib.h>
-#include <string.h>
-
 #include "sa_device.h"
 
 namespace sa {
@@ -88,6 +85,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
     // holding the 4-byte word that contains row i's byte
     __shared__ __attribute__((aligned(16))) uint32_t mkring[MASKED ? S : 1][MASKED ? NW * 64 : 1];
 
+    if (offsets_rejected(a.status)) return;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, l16 = lane & 15;
@@ -454,8 +452,8 @@ constexpr Shape kShapes[] = {{64, 16, 4, 32}, {64, 8, 2, 32}, {64, 8, 4, 32}, {3
 // (NW, NH) with NW = NH * m / 32 (one wave per (head, 32-prototype) unit) and
 // H a multiple of NH.  Preference: 8 waves (two blocks per CU, four waves per
 // SIMD, independent barriers), then 16 waves (one block per CU);
-// SA_STREAM_NW=16 reverses the order.
-bool stream_config(int dh, int m, int H, StreamConfig* cfg) {
+// prefer_nw = 16 reverses the order.
+bool stream_config(int dh, int m, int H, int prefer_nw, StreamConfig* cfg) {
     if (dh == 128) {
         // one head per block, 8 waves = 256 prototypes; m / 256 blocks per head
         if (m % 256 != 0) return false;
@@ -468,8 +466,7 @@ bool stream_config(int dh, int m, int H, StreamConfig* cfg) {
         return true;
     }
     if (!(dh == 32 || dh == 64) || m % 32 != 0) return false;
-    int prefer = 8;
-    if (const char* e = getenv("SA_STREAM_NW")) prefer = atoi(e) == 16 ? 16 : 8;
+    const int prefer = prefer_nw == 16 ? 16 : 8;
     const int MB = 32, PB = m / MB;
     for (int pass = 0; pass < 2; ++pass) {
         const int NW = pass == 0 ? prefer : 24 - prefer;

@@ -55,6 +55,15 @@ __device__ __forceinline__ void wait_after(int n) {
     }
 }
 
+// The three direct-to-LDS loads below set M0 themselves and name it in their
+// clobber lists, so that the compiler treats each asm statement as a writer
+// of M0 and never keeps a value of its own there across one.  M0 is a
+// register the compiler reserves, and clang warns about every reserved
+// register in a clobber list; that warning is silenced for these statements
+// only.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+
 // One direct-to-LDS load of 16 bytes per lane: lane i's 16 bytes land at LDS
 // address lds + 16*i (lds is wave-uniform; it goes through M0).  Written as
 // asm so the compiler does not know that the ring is a DMA target and
@@ -79,7 +88,7 @@ __device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t
         "global_load_lds_dwordx4 %0, %1 nt"
         :
         : "v"(voff), "s"(base), "s"(lds)
-        : "memory");
+        : "memory", "m0");
 }
 
 // Direct-to-LDS load as dma16s, without the non-temporal hint: for rows that
@@ -96,7 +105,7 @@ __device__ __forceinline__ void dma16c(const void* base, uint32_t voff, uint32_t
         "global_load_lds_dwordx4 %0, %1"
         :
         : "v"(voff), "s"(base), "s"(lds)
-        : "memory");
+        : "memory", "m0");
 }
 
 // Direct-to-LDS load of 4 bytes per lane (lane i's dword lands at lds + 4*i),
@@ -113,8 +122,10 @@ __device__ __forceinline__ void dma4c(const void* base, uint32_t voff, uint32_t 
         "global_load_lds_dword %0, %1"
         :
         : "v"(voff), "s"(base), "s"(lds)
-        : "memory");
+        : "memory", "m0");
 }
+
+#pragma clang diagnostic pop
 
 // 16-byte store that writes through to memory (system scope, non-temporal):
 // for results written once at a kernel's end and read by the next kernel, so

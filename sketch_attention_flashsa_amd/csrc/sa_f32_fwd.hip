@@ -19,6 +19,7 @@ __global__ __launch_bounds__(256) void sa_f32_fwd_kernel(FwdArgs a) {
     __shared__ float Vt[kTile][DH];
     __shared__ float Lt[kTile];
     __shared__ int Ok[kTile];
+    if (offsets_rejected(a.status)) return;
     const int w = blockIdx.x, h = blockIdx.y;
     const int j = blockIdx.z * 256 + threadIdx.x;
     const bool active = j < a.m;

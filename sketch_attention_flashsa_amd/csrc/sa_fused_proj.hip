@@ -76,6 +76,7 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
     // exchange: [tile parity][head][role][fragment][lane]
     __shared__ __attribute__((aligned(16))) bf16x8 xchg[2][HPB][2][2][64];
 
+    if (offsets_rejected(a.status)) return;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, l16 = lane & 15;

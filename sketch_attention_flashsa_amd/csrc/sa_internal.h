@@ -61,6 +61,25 @@ struct Users {
     }
 };
 
+// Rules of the debug offsets check (SA_FLAG_CHECK_OFFSETS), evaluated for
+// entry b of cu[B+1]: bit 1 cu[0] < 0, bit 2 cu[b+1] < cu[b], bit 4
+// cu[B] > total_rows.  Host and device run this same code.
+constexpr int32_t kOffNegative = 1, kOffDecreasing = 2, kOffPastEnd = 4;
+__host__ __device__ __forceinline__ int32_t offsets_entry_bits(const int32_t* cu, int32_t b, int32_t B,
+                                                                  int64_t total_rows) {
+    int32_t bits = 0;
+    if (b == 0 && cu[0] < 0) bits |= kOffNegative;
+    if (b < B && cu[b + 1] < cu[b]) bits |= kOffDecreasing;
+    if (b == B && (int64_t)cu[B] > total_rows) bits |= kOffPastEnd;
+    return bits;
+}
+
+// A kernel of a call made with the offsets check runs only when the check
+// found nothing: status[0] is the check kernel's verdict (nullptr: no check).
+__device__ __forceinline__ bool offsets_rejected(const int32_t* status) {
+    return status != nullptr && *status != 0;
+}
+
 // Rows per segment: fixed by the caller, or spread evenly over G blocks.
 // Row counts are below 2^31 (the entry points check), so the divisions by
 // run-time values are 32-bit.
@@ -137,6 +156,7 @@ struct FwdArgs {
     Partials part;
     const float* lse2_tok;   // prototype axis: per (row, head) log2 normaliser
     int32_t norm;            // 0 history, 1 prototype
+    const int32_t* status;   // offsets check verdict, or nullptr
 };
 
 struct MergeArgs {
@@ -148,6 +168,7 @@ struct MergeArgs {
     float* lse;              // [B][H][m] or nullptr (history axis only)
     int32_t norm;
     int32_t lane_major;      // acc layout written by the forward kernel
+    const int32_t* status;   // offsets check verdict, or nullptr (bad: S, lse = NaN)
 };
 
 struct TokLseArgs {
@@ -161,10 +182,13 @@ struct TokLseArgs {
     float c;
     float* lse2_tok;         // [total_rows][H], log2 units
     float* lse_out;          // [total_rows][H], natural log, or nullptr
+    const int32_t* status;   // offsets check verdict, or nullptr (bad: lse_out = NaN)
 };
 
 // ---- launchers (return hipGetLastError() of the launch) ----
 hipError_t launch_dense_vcu(const int32_t* lengths, int32_t B, int32_t L_max, int32_t* vcu, hipStream_t s);
+// status[0] = OR of offsets_entry_bits over b, status[1] = first b with bits (-1: none)
+hipError_t launch_check_offsets(const int32_t* cu, int32_t B, int64_t total_rows, int32_t* status, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_f32_forward(const FwdArgs& a, hipStream_t s);
 hipError_t launch_f32_tok_lse(const TokLseArgs& a, hipStream_t s);
@@ -179,7 +203,8 @@ struct Bf16Config {
     int k_row, v_row;        // LDS row strides (bytes) of the K and V tiles
     size_t lds_bytes;        // dynamic LDS per block
 };
-bool bf16_config(int dh, int m, int H, size_t lds_limit, Bf16Config* cfg);
+// tile_mb, tile_nw: a requested tile (0, 0 = the default choice)
+bool bf16_config(int dh, int m, int H, size_t lds_limit, int tile_mb, int tile_nw, Bf16Config* cfg);
 hipError_t launch_bf16_forward(const FwdArgs& a, const Bf16Config& cfg, hipStream_t s);
 
 // bf16 streaming kernel with the direct-to-LDS ring (sa_bf16_stream.hip):
@@ -192,7 +217,8 @@ struct StreamConfig {
     int groups;              // blocks per row range
     int blocks_per_cu;
 };
-bool stream_config(int dh, int m, int H, StreamConfig* cfg);
+// prefer_nw: 8 or 16, the block size tried first
+bool stream_config(int dh, int m, int H, int prefer_nw, StreamConfig* cfg);
 hipError_t launch_bf16_stream(const FwdArgs& a, const StreamConfig& cfg, hipStream_t s);
 
 // Fused key/value projection + forward (sa_fused_proj.hip): X [rows, d_model]
@@ -209,6 +235,7 @@ struct FusedArgs {
     float c;                 // scale * log2(e)
     int32_t G, R_fixed, R_min;
     Partials part;
+    const int32_t* status;   // offsets check verdict, or nullptr
 };
 // One sketch-update launch of stacked refinement (sa_refine.hip).
 struct SketchArgs {
@@ -282,6 +309,7 @@ struct BwdArgs {
     Partials part;           // dP partials (acc only, lane-major)
     float* dP;               // [H][m][dh] or [B][H][m][dh]
     int32_t per_user;
+    int32_t dp_register_staged;  // 1: the register-staged dP kernel for every shape
 };
 bool bwd_supported(int dh, int m);
 void bwd_dp_shape(int m, int H, int* NH, int* PB);

@@ -40,6 +40,13 @@ __global__ __launch_bounds__(256) void sa_merge_kernel(MergeArgs a) {
         e = (q - j * (a.dh / 4)) * 4;
         qoff = (int64_t)j * a.dh + e;
     }
+    if (offsets_rejected(a.status)) {
+        // offsets failed the check: no partial was written; the outputs say so
+        const float nan = __builtin_nanf("");
+        *(f32x4*)(a.S + (((int64_t)b * a.H + h) * a.m + j) * a.dh + e) = (f32x4){nan, nan, nan, nan};
+        if (e == 0 && a.lse) a.lse[((int64_t)b * a.H + h) * a.m + j] = nan;
+        return;
+    }
     const int64_t total = a.users.total();
     const RowSplit rs = row_split(total, a.G, a.R_fixed, a.R_min, a.split);
     const int64_t us = a.users.vstart(b), ue = a.users.vstart(b + 1);
@@ -152,6 +159,42 @@ __global__ __launch_bounds__(1024) void sa_dense_vcu_kernel(const int32_t* lengt
 
 hipError_t launch_dense_vcu(const int32_t* lengths, int32_t B, int32_t L_max, int32_t* vcu, hipStream_t s) {
     hipLaunchKernelGGL(sa_dense_vcu_kernel, dim3(1), dim3(1024), 0, s, lengths, B, L_max, vcu);
+    return hipGetLastError();
+}
+
+// The debug offsets check: one block walks cu[0..B] (cu == nullptr: dense
+// layout, nothing to check), ORs the rule bits of every entry and keeps the
+// smallest entry that has any; status[0] = bits, status[1] = that entry or -1.
+__global__ __launch_bounds__(256) void sa_check_offsets_kernel(const int32_t* cu, int32_t B, int64_t total_rows,
+                                                                int32_t* status) {
+    __shared__ int32_t bits_all;
+    __shared__ int32_t first;
+    if (threadIdx.x == 0) {
+        bits_all = 0;
+        first = INT32_MAX;
+    }
+    __syncthreads();
+    if (cu) {
+        int32_t bits = 0, mine = INT32_MAX;
+        for (int32_t b = threadIdx.x; b <= B; b += 256) {
+            const int32_t x = offsets_entry_bits(cu, b, B, total_rows);
+            bits |= x;
+            if (x && b < mine) mine = b;
+        }
+        if (bits) {
+            atomicOr(&bits_all, bits);
+            atomicMin(&first, mine);
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        status[0] = bits_all;
+        status[1] = bits_all ? first : -1;
+    }
+}
+
+hipError_t launch_check_offsets(const int32_t* cu, int32_t B, int64_t total_rows, int32_t* status, hipStream_t s) {
+    hipLaunchKernelGGL(sa_check_offsets_kernel, dim3(1), dim3(256), 0, s, cu, B, total_rows, status);
     return hipGetLastError();
 }
 

@@ -54,6 +54,14 @@ __global__ __launch_bounds__(256) void sa_bf16_tok_lse_kernel(TokLseArgs a) {
     const int h = blockIdx.x * 4 + wave;
     if (h >= a.H) return;
     const int64_t ntile = (a.total_rows + 31) / 32;
+    if (offsets_rejected(a.status)) {
+        // offsets failed the check: no key is read, the row normalisers are NaN
+        for (int64_t t = blockIdx.y; t < ntile; t += gridDim.y) {
+            const int64_t row = 32 * t + (lane & 31);
+            if (lane < 32 && row < a.total_rows && a.lse_out) a.lse_out[row * a.H + h] = __builtin_nanf("");
+        }
+        return;
+    }
     const bf16* Kg = (const bf16*)a.K + (int64_t)h * DH + 8 * g;
     const bf16* Pg = (const bf16*)a.P + (int64_t)h * a.m * DH + 8 * g;
     const int nchunk = (a.m + 16 * NSB - 1) / (16 * NSB);
@@ -143,6 +151,10 @@ __global__ __launch_bounds__(256) void sa_f32_tok_lse_kernel(TokLseArgs a) {
     const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int h = blockIdx.y;
     if (row >= a.total_rows) return;
+    if (offsets_rejected(a.status)) {
+        if (a.lse_out) a.lse_out[row * a.H + h] = __builtin_nanf("");
+        return;
+    }
     float M = -INFINITY, Z = 0.f;
     const bool ok = row_valid(a, row);
     if (ok) {

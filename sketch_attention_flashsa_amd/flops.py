@@ -98,6 +98,12 @@ def projection_flops(total_tokens: int, d_model: int, n_cols: int, n_mats: int =
     return 2.0 * total_tokens * d_model * n_cols * n_mats
 
 
+def stca_attention_flops(rows_per_target, D: int, h: int) -> float:
+    """Reordered single-query attention (G.2.1) summed over targets: target t
+    sees rows_per_target[t] history rows and costs attn_reordered(L_t, D, h)."""
+    return float(sum(attn_reordered(float(L), D, h) for L in rows_per_target))
+
+
 def refine_flops(total_tokens: int, B: int, m: int, d: int, n_layers: int) -> float:
     """Stacked refinement over a batch (G.3's SA layer summed over users, with
     L the user's rows and L_s = m): n_sa * (2 L d^2 + 14 L_s d^2 + 4 L_s L d)

@@ -9,6 +9,12 @@
 --stats --output-format csv -d DIR`` writes and prints a markdown table of
 every kernel (calls, average / min / max duration).
 
+``trace`` reads the ``*kernel_trace.csv`` of the same run and splits one
+kernel's dispatches, in dispatch order, into the benchmark's legs: the first
+``--warmup`` are warm-up launches, the next ``--timed`` the timed ones, the
+rest (if any) later legs; it prints each leg's count, average, median, min
+and max duration, so the timed average can be recomputed from the trace.
+
 ``traffic`` reads four ``--pmc`` runs (``*counter_collection.csv``): the
 kernel's FETCH_SIZE and WRITE_SIZE runs, and the same two counters for a
 plain copy kernel that reads and writes ``copy_bytes`` each.  The counters
@@ -80,6 +86,37 @@ def counter_avg(d: str, counter: str, kernel: str) -> tuple[float, int]:
     return statistics.fmean(per.values()), len(per)
 
 
+def kernel_durations(d: str, kernel: str) -> list[float]:
+    """Durations (us) of every dispatch of kernel (substring match), in
+    dispatch order, from the kernel trace."""
+    rows = []
+    for r in _rows(d, "kernel_trace.csv"):
+        if kernel not in _pick(r, "Kernel_Name", "KERNEL_NAME"):
+            continue
+        start = int(_pick(r, "Start_Timestamp", "START_TIMESTAMP"))
+        end = int(_pick(r, "End_Timestamp", "END_TIMESTAMP"))
+        rows.append((int(_pick(r, "Dispatch_Id", "DISPATCH_ID")), (end - start) / 1e3))
+    if not rows:
+        raise SystemExit(f"no dispatch of a kernel matching {kernel!r} under {d}")
+    rows.sort()
+    return [us for _, us in rows]
+
+
+def _trace_main(a) -> None:
+    us = kernel_durations(a.dir, a.kernel)
+    legs = [("warm-up", us[:a.warmup]), ("timed", us[a.warmup:a.warmup + a.timed]),
+            ("after the timed steps", us[a.warmup + a.timed:])]
+    if a.cmd:
+        print(f"Command: `{a.cmd}`\n")
+    print(f"Dispatches of `{a.kernel}`: {len(us)}\n")
+    print("| leg | launches | avg (us) | median (us) | min (us) | max (us) |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for name, xs in legs:
+        if xs:
+            print(f"| {name} | {len(xs)} | {statistics.fmean(xs):.1f} | {statistics.median(xs):.1f} | "
+                  f"{min(xs):.1f} | {max(xs):.1f} |")
+
+
 def _stats_main(a) -> None:
     rows = kernel_stats(a.dir)
     if a.cmd:
@@ -136,6 +173,12 @@ def main(argv=None) -> None:
     s.add_argument("dir")
     s.add_argument("--kernel", default="")
     s.add_argument("--cmd", default="")
+    tr = sub.add_parser("trace")
+    tr.add_argument("dir")
+    tr.add_argument("--kernel", required=True)
+    tr.add_argument("--warmup", type=int, required=True)
+    tr.add_argument("--timed", type=int, required=True)
+    tr.add_argument("--cmd", default="")
     t = sub.add_parser("traffic")
     for n in ("fetch", "write", "copy-fetch", "copy-write"):
         t.add_argument(f"--{n}", required=True)
@@ -146,7 +189,7 @@ def main(argv=None) -> None:
     t.add_argument("--cmd", default="")
     t.add_argument("--json", default="")
     a = ap.parse_args(argv)
-    (_stats_main if a.what == "stats" else _traffic_main)(a)
+    {"stats": _stats_main, "trace": _trace_main, "traffic": _traffic_main}[a.what](a)
 
 
 if __name__ == "__main__":

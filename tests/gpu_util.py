@@ -9,9 +9,16 @@ import sketch_attention_flashsa_amd as sa
 
 # Parity bars: fp32 inputs -> max |g - o| / max |o| <= 1e-5 over the output;
 # bf16 inputs -> relative L2 error <= 1e-2 over the output, oracle fed the
-# same bf16 tensors.
+# same bf16 tensors, and every output row (last axis: one (user, head,
+# prototype) sketch row, one target's output, one gradient row) within a
+# relative L2 error of 5e-2 on its own, so that one wrong row cannot hide in
+# a large output.  Rows the oracle gives as exactly zero have no relative
+# error; the tests whose contract makes them exactly zero (empty users) assert
+# that directly, and others (a single-row user's key gradient, zero only by
+# the cancellation of two terms) are left to the global bar.
 TOL_F32 = 1e-5
 TOL_BF16 = 1e-2
+ROW_TOL_BF16 = 5e-2
 
 
 def device():
@@ -58,13 +65,29 @@ def rel_inf(g, o):
     return float(np.max(np.abs(g - o)) / (den if den > 0 else 1.0)) if o.size else 0.0
 
 
-def assert_parity(g, o, dtype, what=""):
+def row_rel_l2(g, o):
+    """Relative L2 error of every row (last axis) and the rows' oracle norms."""
+    g, o = np.asarray(g, np.float64), np.asarray(o, np.float64)
+    n = o.shape[-1] if o.ndim else 1
+    g2, o2 = g.reshape(-1, n), o.reshape(-1, n)
+    den = np.linalg.norm(o2, axis=1)
+    num = np.linalg.norm(g2 - o2, axis=1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), num), den
+
+
+def assert_parity(g, o, dtype, what="", row_tol=ROW_TOL_BF16):
     if dtype == "f32":
         e = rel_inf(g, o)
         assert e <= TOL_F32, f"{what}: fp32 max relative error {e:.3e} > {TOL_F32}"
     else:
         e = rel_l2(g, o)
         assert e <= TOL_BF16, f"{what}: bf16 relative L2 error {e:.3e} > {TOL_BF16}"
+        if row_tol is not None and np.asarray(o).size:
+            r, den = row_rel_l2(g, o)
+            zero = den == 0
+            worst = int(np.argmax(np.where(zero, 0.0, r)))
+            assert r[worst] <= row_tol or zero[worst], \
+                f"{what}: row {worst} relative L2 error {r[worst]:.3e} > {row_tol} (whole output {e:.3e})"
     return e
 
 

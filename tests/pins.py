@@ -95,6 +95,50 @@ def brute_bf16_inputs():
     _brute_compare(_case(17, dtype="bf16", lengths=(7, 2, 5)), "history")
 
 
+def brute_per_user_prototypes():
+    """P [B, H, m, dh] (one prototype set per user, as stacked refinement
+    feeds them): the full forward and sampled rows against brute force."""
+    w = _case(18, lengths=(6, 1, 9), mask_p=0.2)
+    rng = np.random.default_rng(18)
+    Pu = torch.from_numpy(rng.standard_normal((3, 2, 3, 4)).astype(np.float32))
+    K, V, cu, mk = w["K"], w["V"], w["cu_offsets"], w["mask"]
+    S_b, _, L_b = brute.sketch_packed(Pu.double().numpy(), K.double().numpy(), V.double().numpy(), cu.numpy(),
+                                      mask=mk.numpy())
+    S_b, L_b = _mp_to_np(S_b), _mp_to_np(L_b)
+    S_o, l_o = oracle.forward(Pu, K, V, cu_offsets=cu, mask=mk)
+    assert _rel(S_o, S_b) <= 1e-12, f"per-user P vs brute force: {_rel(S_o, S_b):.3e}"
+    fin = np.isfinite(L_b)
+    assert np.array_equal(fin, np.isfinite(l_o)) and np.max(np.abs(l_o[fin] - L_b[fin]), initial=0.0) <= 1e-12
+    bhj = [(0, 1, 2), (2, 0, 1), (1, 1, 0)]
+    o, ls = oracle.forward_sample(Pu, K, V, bhj, cu_offsets=cu, mask=mk)
+    for t, (b, h, j) in enumerate(bhj):
+        assert _rel(o[t], S_b[b, h, j]) <= 1e-12, "per-user P: sampled row vs brute force"
+
+
+def brute_fused_values_are_x():
+    """The fused entry with Wv = None (V = X: the paper's sketch aggregates X
+    itself, section 3.1): full forward and sampled rows, with and without a
+    mask, against brute force with every product an mpf."""
+    rng = np.random.default_rng(6)
+    bf = torch.bfloat16
+    X = torch.from_numpy(rng.standard_normal((11, 8)).astype(np.float32)).to(bf)
+    Wk = torch.from_numpy((rng.standard_normal((8, 8)) / 3).astype(np.float32)).to(bf)
+    P = torch.from_numpy(rng.standard_normal((2, 3, 4)).astype(np.float32)).to(bf)
+    cu = torch.tensor([0, 4, 4, 11], dtype=torch.int32)
+    mk = torch.from_numpy((rng.uniform(size=11) > 0.3).astype(np.uint8))
+    for mask in (None, mk):
+        S_b, _, _ = brute.fused(X.double().numpy(), Wk.double().numpy(), None, P.double().numpy(), cu.numpy(),
+                                mask=None if mask is None else mask.numpy())
+        S_b = _mp_to_np(S_b)
+        S_o, _ = oracle.fused_forward(X, Wk, None, P, cu, mask=mask)
+        assert _rel(S_o, S_b) <= 1e-12, f"fused V = X vs brute force: {_rel(S_o, S_b):.3e}"
+        bhj = [(0, 1, 2), (2, 0, 0), (2, 1, 1), (1, 0, 0)]
+        o, _ = oracle.fused_forward_sample(X, Wk, None, P, cu, bhj, mask=mask)
+        for t, (b, h, j) in enumerate(bhj):
+            assert np.max(np.abs(o[t] - S_b[b, h, j])) <= 1e-12 * max(1.0, np.max(np.abs(S_b))), \
+                "fused V = X: sampled row vs brute force"
+
+
 # -------------------------------------------------------- library routines
 def library_sdpa_history():
     """History axis == attention with the prototypes as queries (torch SDPA, float64)."""
@@ -341,7 +385,7 @@ def inv_sample_equals_full():
 
 ALL_PINS = [
     brute_history_packed, brute_history_dense_lengths, brute_history_masked, brute_prototype_packed,
-    brute_bf16_inputs, library_sdpa_history, library_scipy_both_axes, library_projection,
+    brute_bf16_inputs, brute_per_user_prototypes, brute_fused_values_are_x, library_sdpa_history, library_scipy_both_axes, library_projection,
     closed_p_zero_is_mean, closed_single_row_is_identity, closed_two_rows_logistic, closed_constant_v,
     inv_weights_sum_to_one, inv_shift, inv_large_scores_no_overflow, inv_permutation,
     inv_linearity_and_hull, inv_padding_and_masking, inv_cross_user_isolation_and_empty,

@@ -64,6 +64,7 @@ FAKE = ctypes.c_void_p(1 << 20)   # never dereferenced: every case below fails v
     ("dtype", 7, sa.SA_ERR_INVALID_ARG),
     ("norm", 5, sa.SA_ERR_INVALID_ARG),
     ("flags", 1, sa.SA_ERR_INVALID_ARG),
+    ("flags", 4, sa.SA_ERR_INVALID_ARG),
     ("chunk_rows", 33, sa.SA_ERR_INVALID_ARG),
     ("dh", 48, sa.SA_ERR_UNSUPPORTED),
     ("m", 40, sa.SA_ERR_UNSUPPORTED),
@@ -286,3 +287,83 @@ def test_stca_problem_struct_matches_header():
     assert [n.strip() for _, grp in fields for n in grp.split(",")] == [f[0] for f in sa.SaStcaProblem._fields_]
     ctypes_of = {"int32_t": ctypes.c_int32, "int64_t": ctypes.c_int64, "float": ctypes.c_float}
     assert [ctypes_of[t] for t, grp in fields for _ in grp.split(",")] == [f[1] for f in sa.SaStcaProblem._fields_]
+
+
+def test_tuning_struct_matches_header():
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct sa_tuning \{(.*?)\} sa_tuning;", text, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    names = re.findall(r"int32_t\s+(\w+);", body)
+    assert names == [f[0] for f in sa.SaTuning._fields_]
+
+
+def test_tuning_is_explicit_validated_and_thread_local():
+    """The work split follows sa_set_tuning() only (never the environment):
+    blocks per CU change the row ranges and so the workspace; invalid values
+    are rejected without changing the settings; NULL restores the defaults;
+    another thread keeps its own (default) settings."""
+    import threading
+    pb = sa.make_problem(16, 8, 128, 64, 1_600_000, dtype="bf16")
+    base = sa.sa_forward_workspace_size(pb)
+    os.environ["SA_BLOCKS_PER_CU"] = "8"      # must have no effect
+    try:
+        assert sa.sa_forward_workspace_size(pb) == base
+    finally:
+        del os.environ["SA_BLOCKS_PER_CU"]
+    try:
+        sa.sa_set_tuning(blocks_per_cu=8)
+        tuned = sa.sa_forward_workspace_size(pb)
+        assert tuned > base
+        other = []
+        t = threading.Thread(target=lambda: other.append(sa.sa_forward_workspace_size(pb)))
+        t.start()
+        t.join()
+        assert other == [base], "tuning must be per thread"
+        for bad in ({"stream_waves": 12}, {"range_split": 100}, {"blocks_per_cu": -1}, {"bf16_tile_mb": 32},
+                    {"bf16_tile_mb": 24, "bf16_tile_nw": 4}, {"register_staged": 2}):
+            with pytest.raises(sa.SketchAttnError):
+                sa.sa_set_tuning(**bad)
+            assert sa.sa_forward_workspace_size(pb) == tuned
+        sa.sa_set_tuning(register_staged=1)
+        assert sa.sa_forward_kernel_name(pb) == "sa_bf16_fwd_kernel"
+    finally:
+        sa.sa_set_tuning()
+    assert sa.sa_forward_workspace_size(pb) == base
+    assert sa.sa_forward_kernel_name(pb) == "sa_bf16_stream_kernel"
+
+
+def test_check_offsets_flag_accepted_where_documented():
+    """SA_FLAG_CHECK_OFFSETS: the forward entries accept it and need 256 bytes
+    more workspace; refinement and the backward pass reject it."""
+    pb = sa.make_problem(4, 8, 128, 64, 10_000, dtype="bf16")
+    pc = sa.make_problem(4, 8, 128, 64, 10_000, dtype="bf16", flags=sa.SA_FLAG_CHECK_OFFSETS)
+    assert sa.sa_forward_workspace_size(pc) == sa.sa_forward_workspace_size(pb) + 256
+    lib = sa.load_library()
+    f = sa.make_problem(4, 8, 64, 32, 10_000, dtype="bf16")
+    fc = sa.make_problem(4, 8, 64, 32, 10_000, dtype="bf16", flags=sa.SA_FLAG_CHECK_OFFSETS)
+    assert lib.sa_forward_fused_proj_workspace_size(ctypes.byref(fc), 256) == \
+        lib.sa_forward_fused_proj_workspace_size(ctypes.byref(f), 256) + 256
+    r = sa.make_problem(4, 8, 64, 32, 10_000, dtype="bf16", flags=sa.SA_FLAG_CHECK_OFFSETS)
+    assert sa.sa_refine_workspace_size(r, 256, 2) == 0 and "flags" in sa.sa_last_error()
+    assert sa.sa_backward_workspace_size(pc) == 0 and "flags" in sa.sa_last_error()
+    g = sa.make_problem(4, 8, 128, 64, 10_000, dtype="bf16", flags=sa.SA_FLAG_BF16_GRADS)
+    assert sa.sa_backward_workspace_size(g) > 0
+    assert sa.sa_forward_workspace_size(g) == 0 and "flags" in sa.sa_last_error()
+
+
+@pytest.mark.parametrize("cu,total,bits,first", [
+    ([0, 10, 20, 30], 30, 0, -1),
+    ([0], 0, 0, -1),
+    ([5, 5, 5], 5, 0, -1),
+    ([-1, 10, 20], 30, 1, 0),
+    ([0, 10, 5, 30], 30, 2, 1),
+    ([0, 10, 20, 31], 30, 4, 3),
+    ([3, 2, 9], 8, 6, 0),
+    ([-4, -5, 40], 30, 7, 0),
+    ([0, 10, 20, 15, 30, 2], 100, 2, 2),
+])
+def test_check_offsets_rules_on_host(cu, total, bits, first):
+    """The rules the device check applies (same rule code): bit 1 a negative
+    first offset, bit 2 a decreasing pair, bit 4 an end past total_rows; the
+    index is the first entry that breaks any rule."""
+    assert sa.sa_check_offsets_host(cu, total) == (bits, first)

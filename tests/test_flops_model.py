@@ -28,3 +28,16 @@ def test_on_path_counter_is_the_affinity_aggregation_term():
     # one head of the G.3 layer at d = dh, L_s = m: 4 L_s L d
     assert flops.sa_forward_flops(1000, 1, 64, 32) == 4 * 64 * 1000 * 32
     assert flops.sa_forward_flops(1000, 8, 64, 32) == 8 * flops.sa_forward_flops(1000, 1, 64, 32)
+
+
+def test_stca_attention_counter_is_the_reordered_attention_term():
+    # G.2: the reordered attention is the part of the pinned STCA layer total
+    # 12LD^2 + 4LDh + 20D^2 left after the two SwiGLU FFNs (history rows and
+    # the one query token, 12LD^2 + 12D^2) and the output projection 2D^2
+    D, h = 1024, 16
+    for L in (1, 1024, 10_000):
+        attn = flops.stca_layer(L, D, h) - flops.swiglu(L, D, 2 * D) - flops.swiglu(1, D, 2 * D) - 2 * D * D
+        assert flops.stca_attention_flops([L], D, h) == attn == 6 * D * D + 4 * L * D * h
+    # summed over targets, each with its own window
+    assert flops.stca_attention_flops([10, 20, 30], D, 8) == sum(flops.attn_reordered(L, D, 8) for L in (10, 20, 30))
+    assert flops.stca_attention_flops([], D, h) == 0.0

@@ -196,7 +196,7 @@ def test_packed_equals_dense_bitwise(dtype):
     assert np.array_equal(Sn, Sd), "dense padding must not leak"
 
 
-def test_uneven_row_split(monkeypatch):
+def test_uneven_row_split():
     """About 118K rows (H=8, m=128, dh=64, bf16): enough rows that the
     streaming kernel gives the first half of its row ranges a larger share
     (R1 > R2), so ranges straddle user boundaries at uneven places.  Checked
@@ -208,9 +208,11 @@ def test_uneven_row_split(monkeypatch):
     So, lo = _oracle(wp)
     assert_parity(S, So, "bf16", "uneven row split")
     assert_lse(lse, lo, "bf16", "uneven row split")
-    monkeypatch.setenv("SA_RANGE_SPLIT", "50")
-    Su, lu = run(wp)
-    monkeypatch.delenv("SA_RANGE_SPLIT")
+    sa.sa_set_tuning(range_split=50)
+    try:
+        Su, lu = run(wp)
+    finally:
+        sa.sa_set_tuning()
     assert_parity(Su, So, "bf16", "uniform row split")
     assert not np.array_equal(S, Su), "the default split should segment these users differently"
     wd = W.random_case(106, B=len(lengths), H=8, m=128, dh=64, lengths=lengths, dtype="bf16", layout="dense")
@@ -282,13 +284,19 @@ def test_peaked_and_shifted_scores(scale_p, offset):
     assert_lse(lse, lo, "bf16", f"peaked x{scale_p} offset {offset}")
 
 
-def test_per_user_prototypes():
-    """P [B, H, m, dh] (stacked refinement feeds per-user queries): each user
-    equals a shared-P call with that user's prototypes."""
-    w = W.random_case(108, B=3, H=2, m=32, dh=32, lengths=[700, 1, 300], dtype="bf16")
-    Pu = torch.stack([w["P"], -w["P"], w["P"].flip(-1)])
-    S, _ = run(dict(w, P=Pu))
-    for b in range(3):
+@pytest.mark.parametrize("H,m,dh", [(2, 32, 32), (8, 128, 64), (3, 48, 32)])
+def test_per_user_prototypes(H, m, dh):
+    """P [B, H, m, dh] (stacked refinement feeds per-user queries) against the
+    oracle with the same per-user sets, on the streaming kernel's shapes and a
+    register-staged one; and each user equals a shared-P call with that
+    user's prototypes, bitwise."""
+    w = W.random_case(108 + m, B=4, H=H, m=m, dh=dh, lengths=[700, 1, 0, 1300], dtype="bf16")
+    Pu = torch.stack([w["P"], -w["P"], w["P"].flip(-1), 0.5 * w["P"]]).to(torch.bfloat16)
+    S, lse = run(dict(w, P=Pu))
+    So, lo = oracle.forward(Pu, w["K"], w["V"], cu_offsets=w["cu_offsets"])
+    assert_parity(S, So, "bf16", f"per-user prototypes H={H} m={m} dh={dh}")
+    assert_lse(lse, lo, "bf16", f"per-user prototypes H={H} m={m} dh={dh}")
+    for b in (0, 1, 3):
         Sb, _ = run(dict(w, P=Pu[b]))
         assert np.array_equal(S[b], Sb[b]), "per-user prototypes must match the shared call"
 

@@ -1,9 +1,11 @@
-"""Plant plausible mistakes in copies of the oracle's C source (CPU only) and
-check that at least one pin rejects each copy.  This is what shows the pins
-are strong enough to trust the oracle: a dropped term, a wrong sign, a wrong
-index or a transposed operand anywhere in it must fail some pin."""
+"""Plant plausible mistakes in copies of the oracle's C source and of its
+Python layer (CPU only) and check that at least one pin rejects each copy.
+This is what shows the pins are strong enough to trust the oracle: a dropped
+term, a wrong sign, a wrong index or a transposed operand anywhere in it must
+fail some pin."""
 import os
 import tempfile
+import types
 
 import pytest
 
@@ -11,6 +13,7 @@ import oracle
 from pins import ALL_PINS
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "sa_oracle.c")
+PY_SRC = os.path.join(os.path.dirname(oracle.__file__), "__init__.py")
 
 # (name, text in sa_oracle.c, replacement)
 MUTANTS = [
@@ -35,6 +38,20 @@ MUTANTS = [
      "        }\n        double Z = 0.0;\n        for (int j = 0; j < m; ++j) Z += exp(s[j] - M);"),
     ("value_used_as_key", "acc += widen(P, pb->in_dtype, pbase + e) * widen(K, pb->in_dtype, kbase + e);",
      "acc += widen(P, pb->in_dtype, pbase + e) * widen(K, pb->in_dtype, kbase + (pb->dh - 1 - e));"),
+    ("per_user_prototypes_shared", "const int64_t pbase = (int64_t)b * pb->p_user_stride + ",
+     "const int64_t pbase = "),
+]
+
+# Mistakes in the Python layer (oracle/__init__.py): the fused entry's
+# projections and head split, and the per-user prototype stride.
+PY_MUTANTS = [
+    ("fused_head_split_transposed", "Vd.reshape(rows, H, dh)", "Vd.reshape(rows, dh, H).transpose(0, 2, 1)"),
+    ("fused_values_x_are_keys", "Vd = project(X, Wv) if Wv is not None else _widen64(X)",
+     "Vd = project(X, Wv) if Wv is not None else Kd"),
+    ("fused_sample_x_head_offset", "_widen64(X)[rows, h * dh:(h + 1) * dh]", "_widen64(X)[rows, h:h + dh]"),
+    ("fused_sample_keys_as_values", "Vd = project(X, Wv, rows=rows, c0=h * dh, nc=dh) if Wv is not None",
+     "Vd = Kd if Wv is not None"),
+    ("per_user_stride_ignored", "return int(Pr.shape[1] * Pr.shape[2] * Pr.shape[3])", "return 0"),
 ]
 
 
@@ -56,3 +73,36 @@ def test_mutant_is_caught(name, old, new):
                 except Exception as e:  # AssertionError, or a crash-free error path
                     failed.append((pin.__name__, type(e).__name__))
         assert failed, f"no pin rejects the mutant '{name}'"
+
+
+@pytest.mark.parametrize("name,old,new", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_python_mutant_is_caught(name, old, new, monkeypatch):
+    src = open(PY_SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mod = types.ModuleType("oracle_mutant")
+    mod.__file__ = PY_SRC
+    exec(compile(src.replace(old, new, 1), PY_SRC, "exec"), mod.__dict__)
+    for fn in ("forward", "forward_sample", "assignment", "project", "fused_forward", "fused_forward_sample",
+               "_user_stride"):
+        monkeypatch.setattr(oracle, fn, getattr(mod, fn))
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin()
+        except Exception as e:
+            failed.append((pin.__name__, type(e).__name__))
+    assert failed, f"no pin rejects the mutant '{name}'"
+
+
+def test_python_copy_unmutated_passes_every_pin(monkeypatch):
+    """Control for the Python mutants: the same loading mechanism with no
+    mistake planted passes every pin, so the mutants above fail for their
+    mistake and not for the way they are loaded."""
+    mod = types.ModuleType("oracle_copy")
+    mod.__file__ = PY_SRC
+    exec(compile(open(PY_SRC).read(), PY_SRC, "exec"), mod.__dict__)
+    for fn in ("forward", "forward_sample", "assignment", "project", "fused_forward", "fused_forward_sample",
+               "_user_stride"):
+        monkeypatch.setattr(oracle, fn, getattr(mod, fn))
+    for pin in ALL_PINS:
+        pin()
