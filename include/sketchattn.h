@@ -190,6 +190,32 @@ sa_status sa_forward(const sa_problem* pb, const void* P, const void* K, const v
  * (0 if the problem itself is invalid; sa_last_error() then says why). */
 size_t sa_forward_workspace_size(const sa_problem* pb);
 
+/*
+ * sa_forward without a caller workspace and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * kernels, results (bitwise) and errors as sa_forward, minus workspace and
+ * workspace_bytes: the workspace is an array of
+ * sa_forward_noalloc_max_workspace() bytes (64 MiB) that the library holds
+ * on each device it runs on, from the first call on that device until the
+ * process ends.  A problem whose sa_forward_workspace_size() exceeds it
+ * returns SA_ERR_WORKSPACE before anything is enqueued (the 100K-row
+ * workload of the benchmark needs about 39 MB on the history axis).
+ * The array is shared by every call on a device and keeps the last call's
+ * contents: calls that overlap on one device (different streams or threads
+ * without ordering between them) race on it, so order them on one stream or
+ * use sa_forward.  Nothing in it needs to start zeroed.  With
+ * SA_FLAG_CHECK_OFFSETS the status words are the first 8 bytes of that
+ * array, which the caller cannot read: use sa_forward to inspect them (S_out
+ * and lse_out still come back NaN on bad offsets).
+ */
+sa_status sa_forward_noalloc(const sa_problem* pb, const void* P, const void* K, const void* V,
+                             const int32_t* cu_offsets, const int32_t* lengths, const uint8_t* mask, float* S_out,
+                             float* lse_out, hipStream_t stream);
+
+/* Bytes of the per-device workspace array of sa_forward_noalloc. */
+size_t sa_forward_noalloc_max_workspace(void);
+
 /* Name of the kernel that performs the pass over K/V for this problem on the
  * current device (the one the timing events below bracket): a static string,
  * or NULL if the problem is invalid or unsupported (sa_last_error() says why).

@@ -25,7 +25,8 @@ SA_FLAG_BF16_GRADS = 1
 SA_FLAG_CHECK_OFFSETS = 2
 _NORMS = {"history": SA_NORM_HISTORY, "prototype": SA_NORM_PROTOTYPE}
 
-EXPORTED = ("sa_forward", "sa_forward_workspace_size", "sa_forward_kernel_name", "sa_forward_fused_proj",
+EXPORTED = ("sa_forward", "sa_forward_workspace_size", "sa_forward_noalloc", "sa_forward_noalloc_max_workspace",
+            "sa_forward_kernel_name", "sa_forward_fused_proj",
             "sa_forward_fused_proj_workspace_size", "sa_refine_forward", "sa_refine_workspace_size",
             "sa_backward", "sa_backward_workspace_size", "sa_stca_attention", "sa_stca_workspace_size",
             "sa_set_timing_events", "sa_set_tuning", "sa_check_offsets_host", "sa_status_string", "sa_last_error",
@@ -89,6 +90,10 @@ def load_library(path: str | None = None):
     lib.sa_forward.restype = ctypes.c_int
     lib.sa_forward_workspace_size.argtypes = [pp]
     lib.sa_forward_workspace_size.restype = ctypes.c_size_t
+    lib.sa_forward_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.sa_forward_noalloc.restype = ctypes.c_int
+    lib.sa_forward_noalloc_max_workspace.argtypes = []
+    lib.sa_forward_noalloc_max_workspace.restype = ctypes.c_size_t
     lib.sa_forward_kernel_name.argtypes = [pp]
     lib.sa_forward_kernel_name.restype = ctypes.c_char_p
     lib.sa_forward_fused_proj.argtypes = [pp, vp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]

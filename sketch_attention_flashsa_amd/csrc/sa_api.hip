@@ -996,3 +996,84 @@ const char* sa_last_error(void) { return g_err; }
 int sa_version(void) { return SA_VERSION_MAJOR * 10000 + SA_VERSION_MINOR * 100 + SA_VERSION_PATCH; }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// sa_forward_noalloc: sa_forward with a workspace the library holds itself,
+// for callers that cannot allocate device memory.  The workspace is a
+// file-scope device array; every device the library runs on holds its own
+// copy from the first call until the process ends.  In host code the array's
+// name is only a stand-in for the symbol, never a device address: the address
+// of a device's copy comes from hipGetSymbolAddress, taken once per device
+// with that device current, and only that address is handed to kernels.
+
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;   // 64 MiB per device
+
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+// The device address of `scratch` on the current device (nullptr on failure,
+// with the error text set).
+void* scratch_on_current_device() {
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        fail(SA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        fail(SA_ERR_HIP, "device %d is beyond the %d devices this entry point serves", dev, kMaxDevices);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            fail(SA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+            return nullptr;
+        }
+        addr[dev] = p;
+    }
+    return addr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sa_forward_noalloc_max_workspace(void) { return kNoAllocScratchBytes; }
+
+sa_status sa_forward_noalloc(const sa_problem* pb, const void* P, const void* K, const void* V,
+                             const int32_t* cu_offsets, const int32_t* lengths, const uint8_t* mask, float* S_out,
+                             float* lse_out, hipStream_t stream) {
+    g_err[0] = 0;
+    Plan pl;
+    sa_status st = make_plan(pb, cu_offsets != nullptr, &pl);
+    if (st != SA_OK) {
+        take_events();
+        return st;
+    }
+    if (pl.total > kNoAllocScratchBytes) {
+        take_events();
+        return fail(SA_ERR_WORKSPACE,
+                    "this problem needs %zu bytes of workspace; sa_forward_noalloc holds %zu (use sa_forward with a "
+                    "caller-allocated workspace)", pl.total, kNoAllocScratchBytes);
+    }
+    void* ws = nullptr;
+    if (pb->B > 0 && pl.total > 0) {
+        ws = scratch_on_current_device();
+        if (!ws) {
+            take_events();
+            return SA_ERR_HIP;
+        }
+    }
+    return sa_forward(pb, P, K, V, cu_offsets, lengths, mask, S_out, lse_out, ws, ws ? kNoAllocScratchBytes : 0,
+                      stream);
+}
+
+}  // extern "C"
