@@ -134,8 +134,23 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc)
-                pf[sb][kc] = *(const bf16x8*)(base + (int64_t)(16 * sb + l16) * DH + 32 * kc + 8 * g);
+            for (int kc = 0; kc < KC; ++kc) {
+                const bf16x8 v = *(const bf16x8*)(base + (int64_t)(16 * sb + l16) * DH + 32 * kc + 8 * g);
+                if constexpr (PROTO) {
+                    pf[sb][kc] = v;
+                } else {
+                    // history axis: scale * log2(e) folded into the prototypes
+                    // (rounded to bf16 once), so the products are base-2 scores
+                    bf16x8 w;
+#pragma unroll
+                    for (int e = 0; e < 8; e += 2) {
+                        const bf16x2 q = pack2((float)v[e] * a.c, (float)v[e + 1] * a.c);
+                        w[e] = q[0];
+                        w[e + 1] = q[1];
+                    }
+                    pf[sb][kc] = w;
+                }
+            }
         // settle the loads here (no ring traffic is in flight yet) so that the
         // compiler does not re-wait for them, and with them for the ring, in the loop
         wait_vm<0>();
@@ -145,32 +160,39 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
     // per-lane DMA geometry: op (wave*D + d) writes 1 KB; lane writes 16 B at
     // LDS offset op*1024 + lane*16 = row * ROWB + slot * 16, fetching the
     // global chunk that the swizzle places in that slot
-    int dma_row[D], dma_ck[D], dma_cv[D];
+    // (the byte offsets of full stages are computed once; the last stage of a
+    // segment clamps rows past its end)
+    int dma_row[D];
+    uint32_t koff[D], voff[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
         const int off = (wave * D + d) * 1024 + lane * 16;
         dma_row[d] = off / ROWB;
         const int slot = (off % ROWB) / 16;
-        dma_ck[d] = (slot ^ (dma_row[d] % FK)) * 16;
-        dma_cv[d] = (slot ^ (2 * (dma_row[d] % FV))) * 16;
+        koff[d] = (uint32_t)(dma_row[d] * (int)krow + (slot ^ (dma_row[d] % FK)) * 16);
+        voff[d] = (uint32_t)(dma_row[d] * (int)vrow + (slot ^ (2 * (dma_row[d] % FV))) * 16);
     }
     // per-lane LDS byte offsets inside one 32-row stage (the swizzle of a row
     // depends on row % 16 only, so both 16-row halves share them)
     const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void*)&ring[0][0][0];
     const uint32_t nl_lds = (uint32_t)(uintptr_t)(lds_void*)&nlring[0][0];
     const uint32_t mk_lds = (uint32_t)(uintptr_t)(lds_void*)&mkring[0][0];
-    uint32_t klane[KC];   // K operand reads, slot 0
+    // (typed LDS pointers: the slot and half offsets of a stage are then
+    // constant indices that fold into the reads' instruction offsets)
+    typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+    lds_bf16x8* klane[KC];   // K operand reads, slot 0
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
         const int row = l16, c = hl * (DH / 8) + 4 * kc + g;
-        klane[kc] = ring_lds + row * ROWB + ((c ^ (row % FK)) * 16);
+        klane[kc] = (lds_bf16x8*)(uintptr_t)(ring_lds + row * ROWB + ((c ^ (row % FK)) * 16));
     }
-    uint32_t vlane[DB];   // V^T transposed reads, slot 0
+    lds_i16x4* vlane[DB];   // V^T transposed reads, slot 0
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
         const int kq = l16 >> 2, q = l16 & 3;
         const int row = 4 * g + kq, colb = hl * DH * 2 + (16 * db + 4 * q) * 2;
-        vlane[db] = ring_lds + STAGE + row * ROWB + (((colb >> 4) ^ (2 * (row % FV))) * 16) + (colb & 15);
+        vlane[db] = (lds_i16x4*)(uintptr_t)(ring_lds + STAGE + row * ROWB + (((colb >> 4) ^ (2 * (row % FV))) * 16) +
+                                            (colb & 15));
     }
 
     int b = a.users.find(v_lo);
@@ -184,24 +206,38 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
         const int64_t nrows = s_hi - s_lo;
         const int ntiles = (int)((nrows + 31) / 32);
         const int nrows32 = (int)nrows;
-        const unsigned char* kseg = Kg + gbase * krow + (int64_t)h0 * DH * 2;
-        const unsigned char* vseg = Vg + gbase * vrow + (int64_t)h0 * DH * 2;
+        // segment bases, wave-uniform: moved to scalar registers once, so that
+        // the per-stage advance below is scalar arithmetic
+        const unsigned char* kseg = uniform_ptr(Kg + gbase * krow + (int64_t)h0 * DH * 2);
+        const unsigned char* vseg = uniform_ptr(Vg + gbase * vrow + (int64_t)h0 * DH * 2);
 
-        // ---- issue stage t into ring slot t % S (every lane of every wave,
-        // always): a wave-uniform base per stage, 32-bit lane offsets; rows
-        // past the segment end re-read its last row
-        auto issue = [&](int t) {
-            const uint32_t slot_lds = ring_lds + (uint32_t)((t % S) * 2 * STAGE) + (uint32_t)(wave * D * 1024);
+        // ---- issue stage t into ring slot `slot` (t % S; callers pass it as a
+        // literal so that every ring address folds into instruction offsets).
+        // Every lane of every wave issues; stages are issued in order, so the
+        // wave-uniform bases advance by 32 rows per stage (scalar registers);
+        // lane offsets are the precomputed ones, clamped in the last stage so
+        // that rows past the segment end re-read its last row
+        const unsigned char* knext = kseg;
+        const unsigned char* vnext = vseg;
+        auto issue = [&](int t, int slot) {
+            const uint32_t slot_lds = ring_lds + (uint32_t)(slot * 2 * STAGE) + (uint32_t)(wave * D * 1024);
             const int r0 = t * 32;
             const int last = nrows32 - 1 - r0;
-            const unsigned char* kb = kseg + (int64_t)r0 * krow;
-            const unsigned char* vb = vseg + (int64_t)r0 * vrow;
+            const unsigned char* kb = knext;
+            const unsigned char* vb = vnext;
+            knext += 32 * krow;
+            vnext += 32 * vrow;
+            const bool tail = last < 31;
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                const int rr = min(dma_row[d], last);
-                dma16s(kb, (uint32_t)(rr * (int)krow + dma_ck[d]), __builtin_amdgcn_readfirstlane(slot_lds + d * 1024));
-                dma16s(vb, (uint32_t)(rr * (int)vrow + dma_cv[d]),
-                       __builtin_amdgcn_readfirstlane(slot_lds + STAGE + d * 1024));
+                uint32_t ko = koff[d], vo = voff[d];
+                if (tail) {
+                    const int over = max(dma_row[d] - last, 0);
+                    ko -= (uint32_t)(over * (int)krow);
+                    vo -= (uint32_t)(over * (int)vrow);
+                }
+                dma16s(kb, ko, __builtin_amdgcn_readfirstlane(slot_lds + d * 1024));
+                dma16s(vb, vo, __builtin_amdgcn_readfirstlane(slot_lds + STAGE + d * 1024));
             }
             if constexpr (MASKED) {
                 // lane -> row (lane % 32) clamped to the segment; the load takes
@@ -210,7 +246,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
                 const uintptr_t m0 = (uintptr_t)(a.mask + gbase + r0);
                 const int rr = min(lane & 31, last);
                 dma4c((const void*)(m0 & ~(uintptr_t)3), (uint32_t)((int)(m0 & 3) + rr) & ~3u,
-                      __builtin_amdgcn_readfirstlane(mk_lds + (uint32_t)(((t % S) * NW + wave) * 256)));
+                      __builtin_amdgcn_readfirstlane(mk_lds + (uint32_t)((slot * NW + wave) * 256)));
             }
             if constexpr (PROTO) {
                 // lane -> entry (wave*64 + lane) mod 32 NH: row e / NH (clamped
@@ -219,11 +255,11 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
                 const int rr = min(e / NH, last);
                 const float* nb = a.lse2_tok + (gbase + r0) * a.H + hc;
                 dma4c(nb, (uint32_t)((rr * a.H + min(e % NH, a.H - 1 - hc)) * 4),
-                      __builtin_amdgcn_readfirstlane(nl_lds + (uint32_t)(((t % S) * NW + wave) * 256)));
+                      __builtin_amdgcn_readfirstlane(nl_lds + (uint32_t)((slot * NW + wave) * 256)));
             }
         };
         // validity bits of stage t (32 rows): rows past the segment end or masked are 0
-        auto unit_valid = [&](int t) -> uint32_t {
+        auto unit_valid = [&](int t, int slot) -> uint32_t {
             const int64_t r0 = (int64_t)t * 32;
             const int rows_here = (int)min((int64_t)32, nrows - r0);
             bool v = lane < rows_here;
@@ -232,39 +268,48 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
                 const uint32_t m0 = (uint32_t)((uintptr_t)(a.mask + gbase + r0) & 3);
                 const int sh = 8 * (int)((m0 + (uint32_t)min(lane & 31, rows_here - 1)) & 3);
                 const uint32_t wd = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)(
-                    mk_lds + (uint32_t)(((t % S) * NW + wave) * 256 + 4 * lane));
+                    mk_lds + (uint32_t)((slot * NW + wave) * 256 + 4 * lane));
                 v = v && ((wd >> sh) & 0xffu) != 0;
             }
             return (uint32_t)__ballot(v);
         };
 
-        float Mc[NSB], Zs[NSB];
+        // history axis: the running maximum M of each of the lane's prototypes
+        // is kept negated in all four entries of a tuple that is the first
+        // score product's accumulator input, so the products come out as
+        // s - M and a weight is one exp2 (the tuple changes only when M does).
+        // Until the prototype meets a valid row, M is 0 (so the products are
+        // the scores themselves) and Zs is -1, which sends every tile to the
+        // exact path that sets M from the scores.
+        float Zs[NSB];
+        f32x4 nM[NSB];
         f32x4 acc[NSB][DB];
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb) {
-            Mc[sb] = -INFINITY;
-            Zs[sb] = 0.f;
+            nM[sb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            Zs[sb] = PROTO ? 0.f : -1.f;
 #pragma unroll
             for (int db = 0; db < DB; ++db) acc[sb][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
         }
 
         // one 32-row stage: scores, weights, aggregation
-        auto unit = [&](int t, uint32_t valid) {
+        auto unit = [&](int t, int slot, uint32_t valid) {
             // all 32 rows of the stage are inside the segment (without a mask
             // that is valid == all ones)
             const bool seg_full = MASKED ? (t + 1) * 32 <= nrows32 : valid == 0xffffffffu;
-            const uint32_t sbase = (uint32_t)((t % S) * 2 * STAGE);
+            const uint32_t sbase = (uint32_t)(slot * 2 * STAGE);
             // S^T = K P^T (two 16-row halves)
             f32x4 s[2][NSB];
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
-                const auto* p0 = (const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(klane[kc] + sbase);
+                lds_bf16x8* p0 = klane[kc] + sbase / 16;
                 const bf16x8 k0 = p0[0];
                 const bf16x8 k1 = p0[16 * ROWB / 16];
 #pragma unroll
                 for (int sb = 0; sb < NSB; ++sb) {
-                    const f32x4 z0 = kc == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : s[0][sb];
-                    const f32x4 z1 = kc == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : s[1][sb];
+                    const f32x4 zc = PROTO ? (f32x4){0.f, 0.f, 0.f, 0.f} : nM[sb];
+                    const f32x4 z0 = kc == 0 ? zc : s[0][sb];
+                    const f32x4 z1 = kc == 0 ? zc : s[1][sb];
                     s[0][sb] = mfma(k0, pf[sb][kc], z0);
                     s[1][sb] = mfma(k1, pf[sb][kc], z1);
                 }
@@ -273,15 +318,15 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
             i16x4 lo[DB], hi[DB];
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                lo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vlane[db] + sbase));
-                hi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vlane[db] + sbase + 16 * ROWB));
+                lo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vlane[db] + sbase / 8);
+                hi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vlane[db] + (sbase + 16 * ROWB) / 8);
             }
             const uint32_t vj = lane_slots(valid, g);
             bf16x8 pk[NSB];
             if constexpr (PROTO) {
                 // prototype axis: weights 2^(s*c - lse2[row]) with the per-row normaliser
                 // the stage's normalisers arrived with it (direct-to-LDS)
-                const uint32_t nls = nl_lds + (uint32_t)((t % S) * NW * 256);
+                const uint32_t nls = nl_lds + (uint32_t)(slot * NW * 256);
                 float nl[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
@@ -303,11 +348,10 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
                 bool fits = true;
 #pragma unroll
                 for (int sb = 0; sb < NSB; ++sb) {
-                    const float nm = -Mc[sb];
                     float p[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        p[j] = __builtin_amdgcn_exp2f(fmaf(s[j >> 2][sb][j & 3], a.c, nm));
+                        p[j] = __builtin_amdgcn_exp2f(s[j >> 2][sb][j & 3]);
                         // with a mask, masked rows get weight 0 here, so they
                         // do not force the exact path (a no-op where the mask
                         // is all ones, which keeps that bitwise equal to no mask)
@@ -318,33 +362,41 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
                     pk[sb] = cat8(q0, q1, q2, q3);
                     zt[sb] = dot2sum(q3, dot2sum(q2, dot2sum(q1, dot2sum(q0, 0.f))));
                     f[sb] = 1.f;
-                    fits = fits && (zt[sb] <= kLazyBound);    // false for NaN and Inf too
+                    // false for NaN and Inf too, and before the first valid row
+                    fits = fits && (zt[sb] <= kLazyBound) && (Zs[sb] >= 0.f);
                 }
                 // rare exact path (then-only, so the common path keeps its
                 // values in place): validity, running-maximum update, rescale
                 if (__builtin_expect(!(__all(fits) && seg_full), 0)) {
 #pragma unroll
                     for (int sb = 0; sb < NSB; ++sb) {
+                        // scores relative to 0 again (the tuple held -M; before
+                        // the first valid row M = 0 and the products are the scores)
+                        const float Mold = -nM[sb][0];
+                        const bool none = Zs[sb] < 0.f;         // no valid row met yet
                         float x[8];
                         float tm = -INFINITY;
 #pragma unroll
                         for (int j = 0; j < 8; ++j) {
-                            x[j] = ((vj >> j) & 1) ? s[j >> 2][sb][j & 3] * a.c : -INFINITY;
+                            x[j] = ((vj >> j) & 1) ? s[j >> 2][sb][j & 3] + Mold : -INFINITY;
                             tm = fmaxf(tm, x[j]);
                         }
                         tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
                         tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
-                        const float Mold = Mc[sb];
-                        const float Mnew = fmaxf(Mold, tm);
-                        f[sb] = (Mnew == Mold) ? 1.f : __builtin_amdgcn_exp2f(Mold - Mnew);
+                        const float Mnew = none ? tm : fmaxf(Mold, tm);
+                        const bool found = Mnew != -INFINITY;   // the prototype has a valid row
+                        // (while it has none, M stays 0 and Zs -1)
+                        const float Mset = found ? Mnew : 0.f;
+                        f[sb] = none ? 0.f : (Mset == Mold ? 1.f : __builtin_amdgcn_exp2f(Mold - Mset));
                         float p[8];
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) p[j] = ((vj >> j) & 1) ? __builtin_amdgcn_exp2f(x[j] - Mnew) : 0.f;
+                        for (int j = 0; j < 8; ++j) p[j] = ((vj >> j) & 1) ? __builtin_amdgcn_exp2f(x[j] - Mset) : 0.f;
                         const bf16x2 q0 = pack2(p[0], p[1]), q1 = pack2(p[2], p[3]);
                         const bf16x2 q2 = pack2(p[4], p[5]), q3 = pack2(p[6], p[7]);
                         pk[sb] = cat8(q0, q1, q2, q3);
                         zt[sb] = dot2sum(q3, dot2sum(q2, dot2sum(q1, dot2sum(q0, 0.f))));
-                        Mc[sb] = Mnew;
+                        if (none && !found) zt[sb] = -1.f;      // Zs = -1 * 0 - 1 keeps the sentinel
+                        nM[sb] = (f32x4){-Mset, -Mset, -Mset, -Mset};
 #pragma unroll
                         for (int db = 0; db < DB; ++db) acc[sb][db] *= f[sb];
                     }
@@ -377,20 +429,32 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
             }
         };
 
-#pragma unroll
-        for (int t = 0; t < AHEAD; ++t)
-            if (t < ntiles) issue(t);
-        for (int t = 0; t < ntiles; ++t) {
+        // stage t, in ring slot `slot` (= t % S, a literal at every call)
+        auto stage = [&](int t, int slot) {
             // this wave's part of stage t has landed; the barrier makes the
             // stage complete and frees slot (t - 1) % S for stage t + AHEAD
             wait_after<AHEAD - 1, VMS>(min(AHEAD - 1, ntiles - 1 - t));
             block_barrier();
-            if (t + AHEAD < ntiles) issue(t + AHEAD);
-            const uint32_t valid = unit_valid(t);
-            if (active) unit(t, valid);
+            if (t + AHEAD < ntiles) issue(t + AHEAD, (slot + AHEAD) % S);
+            const uint32_t valid = unit_valid(t, slot);
+            if (active) unit(t, slot, valid);
             // every LDS read of this stage has completed before the next barrier
             wait_lgkm0();
+        };
+        static_assert(S == 4, "the stage loop is unrolled by the ring size");
+        if (0 < ntiles) issue(0, 0);
+        if (1 < ntiles) issue(1, 1);
+        if (2 < ntiles) issue(2, 2);
+        int t = 0;
+        for (; t + S <= ntiles; t += S) {
+            stage(t, 0);
+            stage(t + 1, 1);
+            stage(t + 2, 2);
+            stage(t + 3, 3);
         }
+        if (t < ntiles) stage(t, 0);
+        if (t + 1 < ntiles) stage(t + 1, 1);
+        if (t + 2 < ntiles) stage(t + 2, 2);
 
         // ---- segment epilogue: partial statistics at slot w + b (the sums in
         // lane order, 1 KB per store, written through to memory: these writes
@@ -403,11 +467,12 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
                 const int j = pb * MB + 16 * sb + l16;
                 const int64_t base = (slot * a.H + head) * a.m + j;
                 if constexpr (!PROTO) {
-                    float z = Zs[sb];
+                    float z = fmaxf(Zs[sb], 0.f);     // the -1 of a prototype with no valid row
                     z += __shfl_xor(z, 16, 64);
                     z += __shfl_xor(z, 32, 64);
                     if (g == 0) {
-                        a.part.M[base] = Mc[sb];
+                        // no valid row in the segment: M = -inf, as the merge expects
+                        a.part.M[base] = z > 0.f ? -nM[sb][0] : -INFINITY;
                         a.part.Z[base] = z;
                     }
                 }

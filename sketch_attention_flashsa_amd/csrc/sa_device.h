@@ -55,6 +55,16 @@ __device__ __forceinline__ void wait_after(int n) {
     }
 }
 
+// A wave-uniform pointer moved to scalar registers (readfirstlane of each
+// half; the low half goes through uint32_t so it is zero-extended).
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+    const uint64_t bb = (uint64_t)(uintptr_t)p;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(bb >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bb);
+    return (T*)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
 // The three direct-to-LDS loads below set M0 themselves and name it in their
 // clobber lists, so that the compiler treats each asm statement as a writer
 // of M0 and never keeps a value of its own there across one.  M0 is a
