@@ -67,9 +67,9 @@ def _percentiles(xs):
     return [ys[min(len(ys) - 1, int(q * len(ys)))] for q in (0.1, 0.5, 0.9)]
 
 
-def _kernel_hash() -> str:
-    from sketch_attention_flashsa_amd.build import sources_hash
-    return sources_hash()
+def _kernel_hash(kernel: str = "sa_bf16_stream_kernel") -> str:
+    from sketch_attention_flashsa_amd.build import KERNEL_SOURCES, sources_hash
+    return sources_hash(KERNEL_SOURCES.get(kernel))
 
 
 def _traffic(kernel: str):
@@ -80,7 +80,7 @@ def _traffic(kernel: str):
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sources_sha256_16") != _kernel_hash() or t.get("kernel") != kernel:
+    if t.get("kernel_sources_sha256_16") != _kernel_hash(kernel) or t.get("kernel") != kernel:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -128,22 +128,30 @@ def hbm_probe(mib: int, steps: int) -> None:
     print(json.dumps(out))
 
 
-def hbm_reference(mib: int = 2048, read_iters: int = 400, copy_iters: int = 150, timed: int = 100):
-    """The device's own streaming rates, measured in this process just before
-    the benchmark's warm-up: torch's sum over an fp32 buffer of `mib` MiB
-    (reads only) and its copy_ into a second buffer (reads and writes), each
-    run `read_iters` / `copy_iters` times back to back with the last `timed`
-    launches timed by events.  The kernel is compared with these rates as well
-    as with the nominal 8 TB/s.  The ~0.3 s of streaming also brings the chip
-    from idle to its loaded clock state, the state the timed steps then run
-    in (the first few tens of back-to-back launches after idle run slower)."""
+def device_reference(mib: int = 2048, read_iters: int = 400, copy_iters: int = 150, gemm_n: int = 8192,
+                     gemm_iters: int = 60, timed: int = 40):
+    """The device's own rates, measured in this process just before the
+    benchmark's warm-up, with torch's kernels: a sum over an fp32 buffer of
+    `mib` MiB (reads only), its copy_ into a second buffer (reads and
+    writes) and a dense bf16 GEMM of size gemm_n^3 (the vendor BLAS), each
+    run back to back with the last `timed` launches timed by events.  The
+    streaming kernel is compared with the read and copy rates as well as with
+    the nominal 8 TB/s.  The ~0.4 s of work, the last part of it at the
+    board's power limit, also brings the chip from idle into the loaded power
+    state that the timed steps run in: after idle, the power controller lets
+    the first launches run at full clock, then cuts the clock hard for a few
+    tens of launches before it settles (the `from_idle` object of the result
+    line shows that transient for the same launches)."""
     import torch
     n = mib * (1 << 20) // 4
     x = torch.ones(n, dtype=torch.float32, device="cuda:0")
     y = torch.empty_like(x)
-    out = {"buffer_mib": mib}
+    ga = torch.randn(gemm_n, gemm_n, dtype=torch.bfloat16, device="cuda:0")
+    gb = torch.randn(gemm_n, gemm_n, dtype=torch.bfloat16, device="cuda:0")
+    out = {"buffer_mib": mib, "gemm_n": gemm_n}
     for name, fn, iters, nbytes in (("read", lambda: x.sum(), read_iters, 4 * n),
-                                    ("copy", lambda: y.copy_(x), copy_iters, 8 * n)):
+                                    ("copy", lambda: y.copy_(x), copy_iters, 8 * n),
+                                    ("gemm", lambda: ga @ gb, gemm_iters, 0)):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for i in range(iters):
             if i == iters - timed:
@@ -152,9 +160,36 @@ def hbm_reference(mib: int = 2048, read_iters: int = 400, copy_iters: int = 150,
         b.record()
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / timed
-        out[f"{name}_GBps"] = nbytes / ms / 1e6
-    del x, y
+        if nbytes:
+            out[f"{name}_GBps"] = nbytes / ms / 1e6
+        else:
+            out["gemm_bf16_TFLOPs"] = 2.0 * gemm_n ** 3 / ms / 1e9
+    del x, y, ga, gb
     return out
+
+
+def from_idle(step, steps: int, warmup: int, idle_s: float = 1.0):
+    """The same warm-up and timed launches after `idle_s` seconds of idle
+    device: per-launch durations of the streaming kernel (HIP events), the
+    power-management transient that the reference work above removes."""
+    import torch
+    import sketch_attention_flashsa_amd as sa
+    hip = _Hip()
+    torch.cuda.synchronize()
+    time.sleep(idle_s)
+    n = warmup + steps
+    evs = [(hip.event(), hip.event()) for _ in range(n)]
+    for i in range(n):
+        sa.sa_set_timing_events(evs[i][0], evs[i][1])
+        step()
+    torch.cuda.synchronize()
+    ms = [hip.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+    timed = ms[warmup:]
+    return {"idle_s": idle_s, "kernel_ms_first_launches": [round(x, 4) for x in ms[:min(n, 30)]],
+            "kernel_ms_avg_timed_launches": sum(timed) / len(timed)}
 
 
 def cpu_baseline(w, n_users: int):
@@ -598,7 +633,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ref-mib", type=int, default=2048,
                     help="workloads 1-4: before the warm-up, measure the device's read and copy rates over a "
-                         "buffer of this many MiB (0: skip); reported as hbm_reference")
+                         "buffer of this many MiB and its dense bf16 GEMM rate (0: skip); reported as "
+                         "device_reference")
+    ap.add_argument("--no-from-idle", dest="from_idle", action="store_false",
+                    help="workloads 1-4: skip the launches timed after an idle second (from_idle)")
     ap.add_argument("--hbm-probe-mib", type=int, default=0,
                     help="time torch fill / sum / copy_ over a buffer of this many MiB and exit")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -659,7 +697,8 @@ def main():
     def step():
         sa.sa_forward(P, K, V, cu_offsets=cu, lengths=lengths, mask=mask, out=S, workspace=ws, **pb_kw)
 
-    ref = hbm_reference(args.ref_mib) if args.ref_mib > 0 else None
+    idle = from_idle(step, args.steps, args.warmup) if args.from_idle else None
+    ref = device_reference(args.ref_mib) if args.ref_mib > 0 else None
     ms_per_step, kern_ms = _timed(step, args.steps, args.warmup, args.flush_mib, args.flush_kind)
     value = tokens / (ms_per_step / 1e3)
     kern_avg_ms = sum(kern_ms) / len(kern_ms)
@@ -709,9 +748,12 @@ def main():
         "cpu_baseline": None,
     }
     if ref is not None:
-        out["hbm_reference"] = ref
+        out["device_reference"] = ref
         out["roofline"]["frac_of_measured_read"] = achieved / ref["read_GBps"]
         out["roofline"]["frac_of_measured_copy"] = achieved / ref["copy_GBps"]
+    if idle is not None:
+        idle["frac"] = alg_bytes / (idle["kernel_ms_avg_timed_launches"] / 1e3) / 1e9 / HBM_PEAK_GBS
+        out["from_idle"] = idle
     if args.flush_mib == 0 and args.cold_mib > 0 and not proto:
         # the same launches with a buffer overwritten before each one (after
         # the timed region above, which it does not affect): no input left in

@@ -29,15 +29,23 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-
          f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
-def sources_hash() -> str:
-    """First 16 hex digits of the sha256 over every csrc/*.hip and *.h, in
-    name order: tags measurements taken on one version of the kernels."""
+# The sources a kernel's measurements depend on (its own file and the headers
+# it includes); a measurement stays valid while these are unchanged.
+KERNEL_SOURCES = {
+    "sa_bf16_stream_kernel": ("sa_bf16_stream.hip", "sa_device.h", "sa_internal.h"),
+}
+
+
+def sources_hash(files=None) -> str:
+    """First 16 hex digits of the sha256 over the given csrc files (default:
+    every csrc/*.hip and *.h), in name order: tags measurements taken on one
+    version of the kernels."""
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".h")):
-            with open(os.path.join(CSRC, f), "rb") as fh:
-                h.update(fh.read())
+    names = sorted(files) if files is not None else sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
+    for f in names:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 

@@ -158,8 +158,9 @@ def _traffic_main(a) -> None:
         "command": a.cmd,
     }
     if a.json:
-        from .build import sources_hash
-        res["kernel_sources_sha256_16"] = sources_hash()
+        from .build import KERNEL_SOURCES, sources_hash
+        res["kernel_sources"] = list(KERNEL_SOURCES.get(a.kernel, ()))
+        res["kernel_sources_sha256_16"] = sources_hash(KERNEL_SOURCES.get(a.kernel))
         with open(a.json, "w") as fh:
             json.dump(res, fh, indent=1)
             fh.write("\n")

@@ -37,7 +37,7 @@ def test_traffic_only_for_matching_sources(monkeypatch):
     b = _load()
     with open(b.TRAFFIC_FILE) as f:
         rec = json.load(f)
-    monkeypatch.setattr(b, "_kernel_hash", lambda: rec["kernel_sources_sha256_16"])
+    monkeypatch.setattr(b, "_kernel_hash", lambda k="": rec["kernel_sources_sha256_16"])
     assert b._traffic(rec["kernel"]) == rec["hbm_bytes_per_launch"]
-    monkeypatch.setattr(b, "_kernel_hash", lambda: "0" * 16)
+    monkeypatch.setattr(b, "_kernel_hash", lambda k="": "0" * 16)
     assert b._traffic(rec["kernel"]) is None
