@@ -15,6 +15,10 @@ kernel's dispatches, in dispatch order, into the benchmark's legs: the first
 rest (if any) later legs; it prints each leg's count, average, median, min
 and max duration, so the timed average can be recomputed from the trace.
 
+``counters`` reads one ``--pmc`` run and prints, for every counter it
+holds, the per-dispatch value of one kernel (summed over the rows a dispatch
+reports, averaged over its dispatches).
+
 ``traffic`` reads four ``--pmc`` runs (``*counter_collection.csv``): the
 kernel's FETCH_SIZE and WRITE_SIZE runs, and the same two counters for a
 plain copy kernel that reads and writes ``copy_bytes`` each.  The counters
@@ -84,6 +88,31 @@ def counter_avg(d: str, counter: str, kernel: str) -> tuple[float, int]:
     if not per:
         raise SystemExit(f"no {counter} rows for a kernel matching {kernel!r} under {d}")
     return statistics.fmean(per.values()), len(per)
+
+
+def all_counters(d: str, kernel: str) -> dict:
+    """{counter: (per-dispatch average, dispatches)} for kernel (substring match)."""
+    per = {}
+    for r in _rows(d, "counter_collection.csv"):
+        if kernel not in _pick(r, "Kernel_Name", "KERNEL_NAME"):
+            continue
+        name = _pick(r, "Counter_Name", "COUNTER_NAME")
+        k = _pick(r, "Dispatch_Id", "DISPATCH_ID")
+        per.setdefault(name, {})
+        per[name][k] = per[name].get(k, 0.0) + float(_pick(r, "Counter_Value", "COUNTER_VALUE"))
+    if not per:
+        raise SystemExit(f"no counters for a kernel matching {kernel!r} under {d}")
+    return {n: (statistics.fmean(v.values()), len(v)) for n, v in sorted(per.items())}
+
+
+def _counters_main(a) -> None:
+    res = all_counters(a.dir, a.kernel)
+    if a.cmd:
+        print(f"Command: `{a.cmd}`\n")
+    print(f"| counter ({a.kernel}) | per dispatch | dispatches |")
+    print("|---|---:|---:|")
+    for n, (v, k) in res.items():
+        print(f"| {n} | {v:.6g} | {k} |")
 
 
 def kernel_durations(d: str, kernel: str) -> list[float]:
@@ -180,6 +209,10 @@ def main(argv=None) -> None:
     tr.add_argument("--warmup", type=int, required=True)
     tr.add_argument("--timed", type=int, required=True)
     tr.add_argument("--cmd", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--cmd", default="")
     t = sub.add_parser("traffic")
     for n in ("fetch", "write", "copy-fetch", "copy-write"):
         t.add_argument(f"--{n}", required=True)
@@ -190,7 +223,7 @@ def main(argv=None) -> None:
     t.add_argument("--cmd", default="")
     t.add_argument("--json", default="")
     a = ap.parse_args(argv)
-    {"stats": _stats_main, "trace": _trace_main, "traffic": _traffic_main}[a.what](a)
+    {"stats": _stats_main, "trace": _trace_main, "counters": _counters_main, "traffic": _traffic_main}[a.what](a)
 
 
 if __name__ == "__main__":
