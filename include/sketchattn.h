@@ -459,8 +459,10 @@ sa_status sa_set_tuning(const sa_tuning* tuning);
  */
 sa_status sa_set_timing_events(hipEvent_t start, hipEvent_t stop);
 
-/* Static text for a status code. */
-const char* sa_status_string(sa_status status);
+/* Static text for a status code.  Takes any integer (a code read back from a
+ * log or another language need not be one of the sa_status values): codes
+ * outside sa_status give "unknown status".  Never NULL; the text is static. */
+const char* sa_status_string(int32_t status);
 
 /* Detail of the last failing call on this host thread ("" if none). */
 const char* sa_last_error(void);

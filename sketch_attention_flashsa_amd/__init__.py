@@ -114,7 +114,7 @@ def load_library(path: str | None = None):
     lib.sa_stca_attention.restype = ctypes.c_int
     lib.sa_stca_workspace_size.argtypes = [sp]
     lib.sa_stca_workspace_size.restype = ctypes.c_size_t
-    lib.sa_status_string.argtypes = [ctypes.c_int]
+    lib.sa_status_string.argtypes = [ctypes.c_int32]
     lib.sa_status_string.restype = ctypes.c_char_p
     lib.sa_last_error.argtypes = []
     lib.sa_last_error.restype = ctypes.c_char_p

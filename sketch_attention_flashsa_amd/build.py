@@ -56,8 +56,8 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, extra: list[str], out_dir: str = BUILD) -> str:
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
     cmd = [_hipcc(), *FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
@@ -69,22 +69,24 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(jobs: int = 8, extra: list[str] | None = None, verbose: bool = False) -> str:
-    """Compile every csrc/*.hip and link libsketchattn.so; return its path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int = 8, extra: list[str] | None = None, verbose: bool = False,
+          out_dir: str = BUILD, lib: str = LIB) -> str:
+    """Compile every csrc/*.hip with ``extra`` flags into ``out_dir`` and link
+    ``lib`` (default: the in-tree libsketchattn.so); return its path."""
+    os.makedirs(out_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     extra = list(extra or [])
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, extra, out_dir), srcs))
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":

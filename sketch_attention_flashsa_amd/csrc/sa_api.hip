@@ -980,7 +980,7 @@ int32_t sa_check_offsets_host(const int32_t* cu, int32_t B, int64_t total_rows, 
     return bits;
 }
 
-const char* sa_status_string(sa_status status) {
+const char* sa_status_string(int32_t status) {
     switch (status) {
         case SA_OK: return "ok";
         case SA_ERR_INVALID_ARG: return "invalid argument";
