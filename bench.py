@@ -702,9 +702,11 @@ def main():
     ms_per_step, kern_ms = _timed(step, args.steps, args.warmup, args.flush_mib, args.flush_kind)
     value = tokens / (ms_per_step / 1e3)
     kern_avg_ms = sum(kern_ms) / len(kern_ms)
-    if proto:
-        # the prototype axis adds a per-row log-sum-exp pass over K before the
-        # streaming kernel: its roofline covers the whole call
+    # shapes the one-pass prototype-axis kernel does not serve add a per-row
+    # log-sum-exp pass over K before the streaming kernel: their roofline
+    # covers the whole call
+    two_pass = proto and kernel != "sa_proto_stream_kernel"
+    if two_pass:
         kern_ms = [ms_per_step]
         kern_avg_ms = ms_per_step
         kernel = "sa_forward, prototype axis (row log-sum-exp pass + " + kernel + " + merge)"
@@ -754,7 +756,7 @@ def main():
     if idle is not None:
         idle["frac"] = alg_bytes / (idle["kernel_ms_avg_timed_launches"] / 1e3) / 1e9 / HBM_PEAK_GBS
         out["from_idle"] = idle
-    if args.flush_mib == 0 and args.cold_mib > 0 and not proto:
+    if args.flush_mib == 0 and args.cold_mib > 0 and not two_pass:
         # the same launches with a buffer overwritten before each one (after
         # the timed region above, which it does not affect): no input left in
         # the L2 or the MALL, and the kernel not launched back to back

@@ -12,6 +12,7 @@
 #include <mutex>
 
 #include "sa_internal.h"
+#include "sa_proto.h"
 #include "sketchattn.h"
 
 namespace {
@@ -93,6 +94,7 @@ struct Plan {
     size_t off_kproj = 0, off_wt = 0, fwd_total = 0;
     sa::Bf16Config cfg{};
     bool stream = false;      // bf16: the direct-to-LDS streaming kernel serves this shape
+    bool proto1 = false;      // prototype axis in one pass (sa_proto_stream_kernel), no row-normaliser pass
     sa::StreamConfig scfg{};
     int groups = 1;           // bf16: unit groups per row range
     bool check_offsets = false;  // SA_FLAG_CHECK_OFFSETS: status section first
@@ -167,6 +169,7 @@ sa_status make_plan(const sa_problem* pb, bool packed, Plan* pl, int32_t flags_o
     } else {
         pl->stream =
             !g_tune.register_staged && sa::stream_config(pb->dh, pb->m, pb->H, g_tune.stream_waves, &pl->scfg);
+        pl->proto1 = pl->stream && pb->norm == SA_NORM_PROTOTYPE && sa::proto_one_pass(pl->scfg, pb->dh);
         if (pl->stream) {
             pl->groups = pl->scfg.groups;
             blocks_per_cu = pl->scfg.blocks_per_cu;
@@ -214,7 +217,9 @@ void set_layout(const sa_problem* pb, Plan* pl) {
     pl->off_acc = off;
     off = align_up(off + sizeof(float) * nslot * hm * pb->dh);
     pl->off_tok = off;
-    if (pb->norm == SA_NORM_PROTOTYPE) off = align_up(off + sizeof(float) * (size_t)pl->buf_rows * pb->H);
+    // the two-pass prototype axis keeps every row's normaliser between its passes
+    if (pb->norm == SA_NORM_PROTOTYPE && !pl->proto1)
+        off = align_up(off + sizeof(float) * (size_t)pl->buf_rows * pb->H);
     pl->total = off;
 }
 
@@ -277,6 +282,7 @@ const char* sa_forward_kernel_name(const sa_problem* pb) {
     Plan pl;
     if (!pb || make_plan(pb, pb->L_max == 0, &pl) != SA_OK) return nullptr;
     if (pl.f32) return "sa_f32_fwd_kernel";
+    if (pl.proto1) return "sa_proto_stream_kernel";
     return pl.stream ? "sa_bf16_stream_kernel" : "sa_bf16_fwd_kernel";
 }
 
@@ -327,7 +333,15 @@ sa_status sa_forward(const sa_problem* pb, const void* P, const void* K, const v
     sa::Partials part{(float*)(ws + pl.off_acc), (float*)(ws + pl.off_M), (float*)(ws + pl.off_Z)};
     float* lse2_tok = (float*)(ws + pl.off_tok);
 
-    if (pb->norm == SA_NORM_PROTOTYPE) {
+    if (pb->norm == SA_NORM_PROTOTYPE && pb->q_batch_stride != 0)
+        return fail(SA_ERR_UNSUPPORTED, "prototype axis with per-user prototypes is not supported");
+    if (pl.proto1 && lse_out) {
+        // the one-pass kernel writes the normalisers of the rows it visits;
+        // rows outside every user get -inf here first
+        e = sa::launch_fill_lse(lse_out, pl.buf_rows * (int64_t)pb->H, status, stream);
+        if (e != hipSuccess) return hip_fail(e, "row normaliser fill");
+    }
+    if (pb->norm == SA_NORM_PROTOTYPE && !pl.proto1) {
         sa::TokLseArgs t{};
         t.users = users;
         t.total_rows = pl.buf_rows;
@@ -342,8 +356,6 @@ sa_status sa_forward(const sa_problem* pb, const void* P, const void* K, const v
         t.lse2_tok = lse2_tok;
         t.lse_out = lse_out;
         t.status = status;
-        if (pb->q_batch_stride != 0)
-            return fail(SA_ERR_UNSUPPORTED, "prototype axis with per-user prototypes is not supported");
         e = pl.f32 ? sa::launch_f32_tok_lse(t, stream) : sa::launch_bf16_tok_lse(t, stream);
         if (e != hipSuccess) return hip_fail(e, "row normaliser");
     }
@@ -371,6 +383,7 @@ sa_status sa_forward(const sa_problem* pb, const void* P, const void* K, const v
     a.status = status;
     if (ev.start && (e = hipEventRecord(ev.start, stream)) != hipSuccess) return hip_fail(e, "timing event");
     if (pl.f32) e = sa::launch_f32_forward(a, stream);
+    else if (pl.proto1) e = sa::launch_proto_stream(a, lse_out, pl.scfg, stream);
     else if (pl.stream) e = sa::launch_bf16_stream(a, pl.scfg, stream);
     else e = sa::launch_bf16_forward(a, pl.cfg, stream);
     if (e != hipSuccess) return hip_fail(e, "forward");

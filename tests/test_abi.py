@@ -102,7 +102,12 @@ def test_empty_batch_is_a_no_op():
 def test_workspace_size_is_layout_independent_and_monotone():
     a = sa.sa_forward_workspace_size(sa.make_problem(16, 8, 128, 64, 1_600_000, dtype="bf16"))
     b = sa.sa_forward_workspace_size(sa.make_problem(16, 8, 128, 64, 1_600_000, dtype="bf16", norm="prototype"))
-    assert 0 < a < b          # the prototype axis adds the per-row normaliser
+    # the one-pass prototype axis keeps no per-row state between passes
+    assert 0 < a == b
+    # a two-pass shape (m not a multiple of 32) adds the per-row normaliser
+    c = sa.sa_forward_workspace_size(sa.make_problem(16, 8, 48, 64, 1_600_000, dtype="bf16"))
+    d = sa.sa_forward_workspace_size(sa.make_problem(16, 8, 48, 64, 1_600_000, dtype="bf16", norm="prototype"))
+    assert d == c + ((1_600_000 * 8 * 4 + 255) // 256) * 256
     # partials stay a small fraction of the K/V bytes at the 100K workload
     assert a < 0.05 * (2 * 1_600_000 * 8 * 64 * 2)
 
@@ -111,6 +116,11 @@ def test_kernel_name_query():
     # the streaming kernel serves the 64- and 32-wide heads; f32 has its own kernel
     assert sa.sa_forward_kernel_name(sa.make_problem(16, 8, 128, 64, 1_600_000, dtype="bf16")) == "sa_bf16_stream_kernel"
     assert sa.sa_forward_kernel_name(sa.make_problem(8, 4, 64, 32, 4096, dtype="bf16")) == "sa_bf16_stream_kernel"
+    # their prototype axis runs in one pass
+    assert sa.sa_forward_kernel_name(sa.make_problem(16, 8, 128, 64, 1_600_000, dtype="bf16", norm="prototype")) == \
+        "sa_proto_stream_kernel"
+    assert sa.sa_forward_kernel_name(sa.make_problem(8, 4, 64, 32, 4096, dtype="bf16", norm="prototype")) == \
+        "sa_proto_stream_kernel"
     assert sa.sa_forward_kernel_name(sa.make_problem(8, 2, 16, 16, 4096, dtype="f32")) == "sa_f32_fwd_kernel"
     # dh = 128 is outside the streaming kernel's shapes and uses the tiled kernel
     assert sa.sa_forward_kernel_name(sa.make_problem(8, 2, 64, 128, 4096, dtype="bf16")) == "sa_bf16_fwd_kernel"

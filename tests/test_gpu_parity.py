@@ -159,7 +159,7 @@ def test_streaming_kernel_masks_bit_exact(H, m, dh, norm):
     lengths = [700, 1, 33, 1000, 64, 0, 95]
     w = W.random_case(120 + dh, B=len(lengths), H=H, m=m, dh=dh, lengths=lengths, dtype="bf16", mask_p=0.3)
     pb = sa.make_problem(w["B"], H, m, dh, w["K"].shape[0], dtype="bf16", norm=norm)
-    assert sa.sa_forward_kernel_name(pb) == "sa_bf16_stream_kernel"
+    assert sa.sa_forward_kernel_name(pb) == ("sa_bf16_stream_kernel" if norm == "history" else "sa_proto_stream_kernel")
     S_ref, l_ref = run(w, norm=norm)
     So, lo = _oracle(w, norm=norm)
     assert_parity(S_ref, So, "bf16", f"streaming masked {norm} dh={dh}")
@@ -336,6 +336,70 @@ def test_prototype_axis_full_size_sampled():
     for r in rows:
         _, lr = oracle.forward(w["P"], w["K"][r:r + 1], w["V"][r:r + 1], cu_offsets=single, norm="prototype")
         assert_lse(lse[r:r + 1], lr, "bf16", f"prototype axis lse, row {r}")
+
+
+def _s_only(w, norm="prototype"):
+    """S from a call that passes no lse output (the kernel instances that
+    write no row normalisers)."""
+    d = to_dev(w, device())
+    S = sa.sa_forward(d["P"], d["K"], d["V"], cu_offsets=d["cu_offsets"], mask=d.get("mask"), norm=norm)
+    torch.cuda.synchronize()
+    return S.double().cpu().numpy()
+
+
+@pytest.mark.parametrize("H,m,dh,waves", [(8, 128, 64, 8), (2, 128, 64, 8), (4, 64, 64, 8), (4, 64, 32, 8),
+                                          (8, 32, 32, 8), (8, 128, 64, 16), (8, 64, 32, 16)])
+@pytest.mark.parametrize("masked", [False, True])
+def test_prototype_one_pass_shapes(H, m, dh, waves, masked):
+    """Every block shape of the one-pass prototype-axis kernel (8- and
+    16-wave blocks; 1, 2 and 4 prototype blocks per head), ragged users,
+    with and without a mask: S against the oracle from a call without lse
+    and from one with lse (the same S bitwise), lse against the oracle."""
+    lengths = [700, 1, 33, 0, 1000, 64, 95, 31]
+    w = W.random_case(130 + m + dh + H, B=len(lengths), H=H, m=m, dh=dh, lengths=lengths, dtype="bf16",
+                      mask_p=0.25 if masked else 0.0)
+    sa.sa_set_tuning(stream_waves=waves)
+    try:
+        pb = sa.make_problem(w["B"], H, m, dh, w["K"].shape[0], dtype="bf16", norm="prototype")
+        assert sa.sa_forward_kernel_name(pb) == "sa_proto_stream_kernel"
+        S1 = _s_only(w)
+        S, lse = run(w, norm="prototype")
+    finally:
+        sa.sa_set_tuning()
+    So, lo = _oracle(w, norm="prototype")
+    tag = f"one pass H={H} m={m} dh={dh} waves={waves} masked={masked}"
+    assert_parity(S1, So, "bf16", tag + " (no lse)")
+    assert_parity(S, So, "bf16", tag)
+    assert_lse(lse.reshape(lo.shape), lo, "bf16", tag)
+    assert np.array_equal(S, S1), "S must not depend on whether lse is written"
+
+
+@pytest.mark.parametrize("offset", [50.0, 120.0, -200.0])
+def test_prototype_exact_path(offset):
+    """Rows whose scores all move by `offset` (channel 0 of every prototype
+    set to 4, channel 0 of the key shifted by offset*sqrt(dh)/4): their
+    partial row sums leave [2^-60, 2^60] (2^72 at +50, past the fp32 range at
+    +120 and -200), so the stages that hold them take the exact path.  The
+    shifted rows come in blocks of 96, so fast and exact stages alternate
+    inside one segment; within a row the offset cancels, the normaliser
+    carries it."""
+    H, m, dh = 8, 128, 64
+    lengths = [3000, 1, 0, 700, 40]
+    w = W.random_case(140, B=len(lengths), H=H, m=m, dh=dh, lengths=lengths, dtype="bf16")
+    P = w["P"].float()
+    K = w["K"].float()
+    P[:, :, 0] = 4.0
+    shifted = (torch.arange(K.shape[0]) // 96) % 2 == 1
+    K[shifted, :, 0] += offset * np.sqrt(dh) / 4.0
+    w = dict(w, P=P.to(torch.bfloat16), K=K.to(torch.bfloat16))
+    S1 = _s_only(w)
+    S, lse = run(w, norm="prototype")
+    So, lo = _oracle(w, norm="prototype")
+    assert np.all(np.isfinite(S))
+    assert_parity(S1, So, "bf16", f"exact path offset {offset} (no lse)")
+    assert_parity(S, So, "bf16", f"exact path offset {offset}")
+    assert_lse(lse.reshape(lo.shape), lo, "bf16", f"exact path offset {offset}")
+    assert np.array_equal(S, S1)
 
 
 def test_prototype_axis_masked_and_dense():

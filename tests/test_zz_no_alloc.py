@@ -59,14 +59,15 @@ def test_noalloc_equals_sa_forward_two_calls(dtype, H, m, dh, norm, layout, big,
 
 
 def test_noalloc_rejects_problems_beyond_its_array():
-    """The prototype axis of the full 100K workload needs ~90 MB of workspace,
-    more than the 64 MiB array: SA_ERR_WORKSPACE, outputs untouched."""
+    """2,000 users of the 100K workload's head shape need one partial-sum
+    slot per user and row range, ~0.5 GB of workspace, more than the 64 MiB
+    array: SA_ERR_WORKSPACE, outputs untouched."""
     dev = device()
     lib = sa.load_library()
     assert lib.sa_forward_noalloc_max_workspace() == 64 << 20
-    pb = sa.make_problem(16, 8, 128, 64, 1_600_000, norm="prototype")
+    pb = sa.make_problem(2000, 8, 128, 64, 1_600_000)
     assert sa.sa_forward_workspace_size(pb) > 64 << 20
-    S = torch.full((16, 8, 128, 64), 3.0, dtype=torch.float32, device=dev)
+    S = torch.full((2000, 8, 128, 64), 3.0, dtype=torch.float32, device=dev)
     fake = ctypes.c_void_p(1 << 20)      # never used: the call fails on the host first
     st = lib.sa_forward_noalloc(ctypes.byref(pb), fake, fake, fake, fake, None, None, _ptr(S), None,
                                 ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
