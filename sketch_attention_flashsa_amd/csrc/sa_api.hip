@@ -12,6 +12,7 @@
 #include <mutex>
 
 #include "sa_internal.h"
+#include "sa_fold.h"
 #include "sa_proto.h"
 #include "sketchattn.h"
 
@@ -91,7 +92,8 @@ struct Plan {
     // fused entry, shapes outside the on-chip kernel: K = X Wk is projected
     // into the workspace (after the forward's own sections), then sa_forward
     bool two_pass = false;
-    size_t off_kproj = 0, off_wt = 0, fwd_total = 0;
+    bool fold_keys = false;   // one head, dh == d_model: W_K folded into the prototypes, no K pass
+    size_t off_kproj = 0, off_wt = 0, off_pfold = 0, fwd_total = 0;
     sa::Bf16Config cfg{};
     bool stream = false;      // bf16: the direct-to-LDS streaming kernel serves this shape
     bool proto1 = false;      // prototype axis in one pass (sa_proto_stream_kernel), no row-normaliser pass
@@ -235,6 +237,16 @@ sa_status make_fused_plan(const sa_problem* pb, int32_t d_model, Plan* pl) {
         // two passes: the projection kernel, then the streaming forward on
         // K (workspace) and V = X; make_plan above planned that forward
         const int64_t hd = (int64_t)pb->H * pb->dh;
+        if (pl->stream && pb->H == 1 && hd == d_model && pb->q_batch_stride == 0) {
+            // one head as wide as the model: the scores are (P W_K^T) X^T,
+            // so K is never formed; the workspace holds the folded prototypes
+            pl->two_pass = true;
+            pl->fold_keys = true;
+            pl->fwd_total = pl->total;
+            pl->off_pfold = align_up(pl->total);
+            pl->total = align_up(pl->off_pfold + 2 * (size_t)pb->m * d_model);
+            return SA_OK;
+        }
         if (!(pl->stream && hd == d_model && sa::project_supported(d_model, (int)hd) && pb->q_batch_stride == 0))
             return fail(SA_ERR_UNSUPPORTED,
                         "fused projection: needs dh == 32, d_model in {128, 256}, m in {64, 128, 256}, or (two "
@@ -432,6 +444,26 @@ sa_status sa_forward_fused_proj(const sa_problem* pb, const void* X, int32_t d_m
     if (workspace && !aligned(workspace, kAlign)) return fail(SA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
 
     unsigned char* ws = (unsigned char*)workspace;
+    if (pl.fold_keys) {
+        if (Wv) return fail(SA_ERR_UNSUPPORTED, "fused projection, one head of width d_model: V = X only (Wv must be NULL)");
+        // scores P (X W_K)^T = (P W_K^T) X^T: the prototypes, scaled by
+        // scale * log2(e) and rounded to bf16 once, then the streaming forward
+        // over K = V = X with a unit scale (its prototypes are already scaled)
+        static_assert((1.0f / sa::kLog2e) * sa::kLog2e == 1.0f, "the unit scale is exact");
+        const float scale = pb->scale > 0.f ? pb->scale : 1.0f / sqrtf((float)pb->dh);
+        sa::bf16* pf = (sa::bf16*)(ws + pl.off_pfold);
+        hipError_t e;
+        if (ev.start && (e = hipEventRecord(ev.start, stream)) != hipSuccess) return hip_fail(e, "timing event");
+        if ((e = sa::launch_fold_keys((const sa::bf16*)P, (const sa::bf16*)Wk, pb->H, pb->m, pb->dh, d_model,
+                                      scale * sa::kLog2e, pf, stream)) != hipSuccess)
+            return hip_fail(e, "prototype fold");
+        sa_problem fp = *pb;
+        fp.k_row_stride = d_model;
+        fp.v_row_stride = d_model;
+        fp.scale = 1.0f / sa::kLog2e;
+        g_ev_stop = ev.stop;             // stop after the streaming pass (start is above)
+        return sa_forward(&fp, pf, X, X, cu_offsets, nullptr, mask, S_out, lse_out, workspace, pl.fwd_total, stream);
+    }
     if (pl.two_pass) {
         if (Wv) return fail(SA_ERR_UNSUPPORTED, "fused projection, two-pass shapes: V = X only (Wv must be NULL)");
         const int hd = pb->H * pb->dh;

@@ -26,6 +26,9 @@
 //      lanes.  One step later (after the next barrier) each wave takes its
 //      partner's half and runs, for its prototypes: S^T = K P^T, the online
 //      softmax (base 2, lazy maximum) per 16-prototype block, O^T += V^T p^T.
+//      As in the streaming kernel, the prototypes are pre-scaled by
+//      scale * log2(e) (rounded to bf16 once) and the negated running maximum
+//      is the score product's accumulator input, so a weight is one exp2.
 // The projection of tile t and the softmax of tile t-1 share a step, so one
 // barrier per tile orders both the ring and the exchange.
 #include <stdio.h>
@@ -34,6 +37,7 @@
 #include <type_traits>
 
 #include "sa_device.h"
+#include "sa_fold.h"
 
 namespace sa {
 
@@ -123,8 +127,10 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
         }
     }
     // ---- prototype fragments, contraction index permuted: element j of lane
-    // (g, l16) in block sb is P[h, pbase + 16 sb + l16, tok_of(g, j)].  They
-    // live in LDS in lane order (one conflict-free 16-byte read each).
+    // (g, l16) in block sb is P[h, pbase + 16 sb + l16, tok_of(g, j)] * c
+    // (scale * log2(e), rounded to bf16 once, so the products are base-2
+    // scores).  They live in LDS in lane order (one conflict-free 16-byte
+    // read each).
     __shared__ __attribute__((aligned(16))) bf16x8 pl[kFWaves][NSB][64];
     auto load_p = [&](int b) {
         const bf16* base = (const bf16*)a.P + (int64_t)b * a.q_batch_stride + ((int64_t)hh * a.m + pbase) * DH;
@@ -133,7 +139,15 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
             const bf16* row = base + (int64_t)(16 * sb + l16) * DH;
             const bf16x4 lo = *(const bf16x4*)(row + 4 * g);
             const bf16x4 hi = *(const bf16x4*)(row + 16 + 4 * g);
-            pl[wave][sb][lane] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            bf16x8 q;
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const bf16x2 t = pack2((float)v[e] * a.c, (float)v[e + 1] * a.c);
+                q[e] = t[0];
+                q[e + 1] = t[1];
+            }
+            pl[wave][sb][lane] = q;
         }
         wait_vm<0>();   // settle before any ring traffic is counted
     };
@@ -209,12 +223,18 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
             return (uint32_t)__ballot(v);
         };
 
-        float Mc[NSB], Zs[NSB];
+        // the running maximum M of each of the lane's prototypes is kept
+        // negated and broadcast into the score products' accumulator input
+        // (one scalar per block: the four-wide tuples would not fit beside
+        // the weight fragments); until the prototype meets a valid row M = 0
+        // and Zs = -1, which sends every tile to the exact path that sets M
+        float nM[NSB];
+        float Zs[NSB];
         f32x4 acc[NSB][2];
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb) {
-            Mc[sb] = -INFINITY;
-            Zs[sb] = 0.f;
+            nM[sb] = 0.f;
+            Zs[sb] = -1.f;
             acc[sb][0] = acc[sb][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
         }
 
@@ -266,16 +286,18 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
             const uint32_t vj = lane_slots(valid, g);
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
-                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
                 const bf16x8 pf = pl[wave][sb][lane];
-                const f32x4 s0 = mfma(ka[0], pf, zero);
-                const f32x4 s1 = mfma(ka[1], pf, zero);
+                // base-2 scores minus the running maximum
+                float m1 = nM[sb];
+                asm volatile("" : "+v"(m1));   // rebuilt per use, not hoisted
+                const f32x4 c4 = {m1, m1, m1, m1};
+                const f32x4 s0 = mfma(ka[0], pf, c4);
+                const f32x4 s1 = mfma(ka[1], pf, c4);
                 float p[8];
-                const float nm = -Mc[sb];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    p[j] = __builtin_amdgcn_exp2f(fmaf(s0[j], a.c, nm));
-                    p[4 + j] = __builtin_amdgcn_exp2f(fmaf(s1[j], a.c, nm));
+                    p[j] = __builtin_amdgcn_exp2f(s0[j]);
+                    p[4 + j] = __builtin_amdgcn_exp2f(s1[j]);
                 }
                 const bf16x2 q0 = pack2(p[0], p[1]), q1 = pack2(p[2], p[3]);
                 const bf16x2 q2 = pack2(p[4], p[5]), q3 = pack2(p[6], p[7]);
@@ -283,30 +305,36 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
                 // fast path: the running maximum stays; Z += the tile's sum
                 float zadd = dot2sum(q3, dot2sum(q2, dot2sum(q1, dot2sum(q0, 0.f))));
                 float f = 1.f;
-                const bool fits = zadd <= kLazyBound;   // false for NaN and Inf too
+                // false for NaN and Inf too, and before the first valid row
+                const bool fits = zadd <= kLazyBound && Zs[sb] >= 0.f;
                 // rare exact path (then-only, so the common path keeps its
                 // values in place): validity, running-maximum update, rescale
                 if (__builtin_expect(!(__all(fits) && valid == 0xffffffffu), 0)) {
+                    // scores relative to 0 again (the products held s - M)
+                    const float Mold = -nM[sb];
+                    const bool none = Zs[sb] < 0.f;         // no valid row met yet
                     float x[8];
                     float tm = -INFINITY;
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         const float sv = j < 4 ? s0[j] : s1[j - 4];
-                        x[j] = ((vj >> j) & 1) ? sv * a.c : -INFINITY;
+                        x[j] = ((vj >> j) & 1) ? sv + Mold : -INFINITY;
                         tm = fmaxf(tm, x[j]);
                     }
                     tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
                     tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
-                    const float Mold = Mc[sb];
-                    const float Mnew = fmaxf(Mold, tm);
-                    f = (Mnew == Mold) ? 1.f : __builtin_amdgcn_exp2f(Mold - Mnew);
+                    const float Mnew = none ? tm : fmaxf(Mold, tm);
+                    const bool found = Mnew != -INFINITY;   // the prototype has a valid row
+                    const float Mset = found ? Mnew : 0.f;
+                    f = none ? 0.f : (Mset == Mold ? 1.f : __builtin_amdgcn_exp2f(Mold - Mset));
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) p[j] = ((vj >> j) & 1) ? __builtin_amdgcn_exp2f(x[j] - Mnew) : 0.f;
+                    for (int j = 0; j < 8; ++j) p[j] = ((vj >> j) & 1) ? __builtin_amdgcn_exp2f(x[j] - Mset) : 0.f;
                     const bf16x2 e0 = pack2(p[0], p[1]), e1 = pack2(p[2], p[3]);
                     const bf16x2 e2 = pack2(p[4], p[5]), e3 = pack2(p[6], p[7]);
                     pk = cat8(e0, e1, e2, e3);
                     zadd = dot2sum(e3, dot2sum(e2, dot2sum(e1, dot2sum(e0, 0.f))));
-                    Mc[sb] = Mnew;
+                    if (none && !found) zadd = -1.f;        // Zs = -1 * 0 - 1 keeps the sentinel
+                    nM[sb] = -Mset;
                     acc[sb][0] *= f;
                     acc[sb][1] *= f;
                 }
@@ -350,11 +378,12 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
             for (int sb = 0; sb < NSB; ++sb) {
                 const int j = pbase + 16 * sb + l16;
                 const int64_t base = (slot * a.H + head) * a.m + j;
-                float z = Zs[sb];
+                float z = fmaxf(Zs[sb], 0.f);     // the -1 of a prototype with no valid row
                 z += __shfl_xor(z, 16, 64);
                 z += __shfl_xor(z, 32, 64);
                 if (g == 0) {
-                    a.part.M[base] = Mc[sb];
+                    // no valid row in the segment: M = -inf, as the merge expects
+                    a.part.M[base] = z > 0.f ? -nM[sb] : -INFINITY;
                     a.part.Z[base] = z;
                 }
 #pragma unroll
@@ -381,6 +410,31 @@ void launch_fused_t(const FusedArgs& a, bool masked, bool vx, hipStream_t s) {
 }
 
 }  // namespace
+
+// One thread per output element; W's row e and P's row j are read along k.
+__global__ void sa_fold_keys_kernel(const bf16* P, const bf16* W, int H, int m, int dh, int d_model, float c,
+                                    bf16* out) {
+    const int64_t n = (int64_t)H * m * d_model;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int e = (int)(i % d_model);
+        const int64_t hj = i / d_model;
+        const int h = (int)(hj / m);
+        const bf16* pr = P + hj * dh;
+        const bf16* wr = W + (int64_t)e * H * dh + (int64_t)h * dh;
+        float acc = 0.f;
+        for (int k = 0; k < dh; ++k) acc = fmaf((float)pr[k], (float)wr[k], acc);
+        out[i] = (bf16)(acc * c);
+    }
+}
+
+hipError_t launch_fold_keys(const bf16* P, const bf16* W, int H, int m, int dh, int d_model, float c, bf16* out,
+                            hipStream_t s) {
+    const int64_t n = (int64_t)H * m * d_model;
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = min((n + 255) / 256, (int64_t)4096);
+    hipLaunchKernelGGL(sa_fold_keys_kernel, dim3((unsigned)blocks), dim3(256), 0, s, P, W, H, m, dh, d_model, c, out);
+    return hipGetLastError();
+}
 
 bool fused_supported(int d_model, int m, int dh) {
     return dh == 32 && (d_model == 128 || d_model == 256) && (m == 64 || m == 128 || m == 256);

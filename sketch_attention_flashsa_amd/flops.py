@@ -98,6 +98,14 @@ def projection_flops(total_tokens: int, d_model: int, n_cols: int, n_mats: int =
     return 2.0 * total_tokens * d_model * n_cols * n_mats
 
 
+def fold_keys_flops(H: int, m: int, dh: int, d_model: int) -> float:
+    """Prototypes moved through the key projection once per call,
+    P_h W_K,h^T for every head: 2 * m * dh * d_model per head.  With it the
+    scores P_h (X W_K,h)^T are (P_h W_K,h^T) X^T and the per-row projection
+    (projection_flops) is not performed (appendix G.2.1's reordering)."""
+    return 2.0 * H * m * dh * d_model
+
+
 def stca_attention_flops(rows_per_target, D: int, h: int) -> float:
     """Reordered single-query attention (G.2.1) summed over targets: target t
     sees rows_per_target[t] history rows and costs attn_reordered(L_t, D, h)."""

@@ -241,14 +241,20 @@ def test_bf16_gradient_flag():
 
 def test_fused_two_pass_shapes():
     """Single head of width 128 with 1024 prototypes (the paper's production
-    shape) takes the two-pass path: accepted with V = X, rejected with Wv."""
+    shape) folds W_K into the prototypes: its workspace is the streaming
+    forward's plus the folded prototypes, no K; accepted with V = X, rejected
+    with Wv.  Two heads of width 128 over d_model = 256 project K into the
+    workspace instead."""
     lib = sa.load_library()
     pb = sa.make_problem(16, 1, 1024, 128, 1_600_000, dtype="bf16")
     n = lib.sa_forward_fused_proj_workspace_size(ctypes.byref(pb), 128)
-    # the streaming forward's workspace plus K (bf16, rows x 128) and W^T
-    assert n >= lib.sa_forward_workspace_size(ctypes.byref(pb)) + 1_600_000 * 128 * 2 + 128 * 128 * 2
+    assert n == lib.sa_forward_workspace_size(ctypes.byref(pb)) + 1024 * 128 * 2
     st = lib.sa_forward_fused_proj(ctypes.byref(pb), FAKE, 128, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, n, None)
     assert st == sa.SA_ERR_UNSUPPORTED and "V = X only" in sa.sa_last_error()
+    p2 = sa.make_problem(16, 2, 256, 128, 1_600_000, dtype="bf16")
+    n2 = lib.sa_forward_fused_proj_workspace_size(ctypes.byref(p2), 256)
+    # the streaming forward's workspace plus K (bf16, rows x 256) and W^T
+    assert n2 >= lib.sa_forward_workspace_size(ctypes.byref(p2)) + 1_600_000 * 256 * 2 + 256 * 256 * 2
     # per-user P, H*dh != d_model, or a shape the streaming kernel does not take: unsupported
     for p, dm in ((sa.make_problem(4, 1, 1024, 128, 1000, dtype="bf16", q_batch_stride=1024 * 128), 128),
                   (sa.make_problem(4, 1, 1024, 128, 1000, dtype="bf16"), 256),

@@ -41,3 +41,16 @@ def test_stca_attention_counter_is_the_reordered_attention_term():
     # summed over targets, each with its own window
     assert flops.stca_attention_flops([10, 20, 30], D, 8) == sum(flops.attn_reordered(L, D, 8) for L in (10, 20, 30))
     assert flops.stca_attention_flops([], D, h) == 0.0
+
+
+def test_folded_keys_replace_the_per_row_projection():
+    # G.3's SA layer at the production shape (one head, d = 128, L_s = k = 1024):
+    # its 2 L d^2 key projection and the 4 L_s L d products; folding W_K into
+    # the prototypes costs 2 L_s d^2 once instead of 2 L d^2 per call
+    L, Ls, d = 100_000, 1024, 128
+    folded = flops.sa_forward_flops(L, 1, Ls, d) + flops.fold_keys_flops(1, Ls, d, d)
+    original = flops.sa_forward_flops(L, 1, Ls, d) + flops.projection_flops(L, d, d, 1)
+    assert flops.fold_keys_flops(1, Ls, d, d) == 2 * Ls * d * d
+    assert original - folded == 2 * L * d * d - 2 * Ls * d * d
+    assert flops.sa_layer(L, Ls, d) - original == flops.sa_layer(L, Ls, d) - 2 * L * d * d - 4 * Ls * L * d
+    assert flops.fold_keys_flops(3, 64, 32, 96) == 3 * flops.fold_keys_flops(1, 64, 32, 96)

@@ -145,8 +145,9 @@ def test_fused_per_user_prototypes():
 @pytest.mark.parametrize("H,dh,d_model,m", [(1, 128, 128, 1024), (2, 128, 256, 256)])
 def test_fused_two_pass_production_shape(H, dh, d_model, m):
     """The paper's production shape (one head of width 128, 1024 prototypes,
-    values = X, appendix G.5) and a two-head variant: K = X Wk is projected
-    into the workspace, then the streaming forward runs on it."""
+    values = X, appendix G.5), where W_K is folded into the prototypes and K
+    is never formed, and a two-head variant, where K = X Wk is projected into
+    the workspace and the streaming forward runs on it."""
     lengths = [1200, 0, 1, 31, 33, 700, 64]
     w = W.random_fused_case(316 + m, B=len(lengths), H=H, m=m, dh=dh, d_model=d_model, lengths=lengths,
                             w_var=1.0 / d_model, mask_p=0.15)
@@ -160,6 +161,28 @@ def test_fused_two_pass_production_shape(H, dh, d_model, m):
     X2[w["mask"] == 0] = float("nan")
     S2, lse2 = run_fused(dict(w, X=X2), use_wv=False)
     assert np.array_equal(S, S2) and np.array_equal(lse, lse2), "masked NaN rows leaked"
+
+
+def test_production_shape_full_size_sampled():
+    """The production shape at the benchmark's size and launch configuration
+    (16 users x 100,000 rows, one head of width 128, 1024 prototypes, V = X,
+    keys X W_K folded into the prototypes): sampled (user, prototype) rows of
+    the longest users against the oracle, which projects K itself."""
+    B, L, m, dm = 16, 100_000, 1024, 128
+    w = W.random_fused_case(8, B=1, H=1, m=m, dh=dm, d_model=dm, lengths=[1], w_var=1.0 / dm)
+    g = torch.Generator().manual_seed(8)
+    X = torch.randn(B * L, dm, generator=g).to(torch.bfloat16)
+    cu = torch.arange(0, B * L + 1, L, dtype=torch.int32)
+    full = dict(w, X=X, cu_offsets=cu, B=B, lengths=torch.full((B,), L, dtype=torch.int64))
+    S, lse = run_fused(full, use_wv=False)
+    assert np.all(np.isfinite(S))
+    rng = np.random.default_rng(88)
+    bhj = [(b, 0, int(rng.integers(m))) for b in (0, 7, 15) for _ in range(4)]
+    o, lo = oracle.fused_forward_sample(X, w["Wk"], None, w["P"], cu, bhj)
+    gsel = np.stack([S[b, h, j] for b, h, j in bhj])
+    gl = np.array([lse[b, h, j] for b, h, j in bhj])
+    assert_parity(gsel, o, "bf16", "production shape, sampled rows")
+    assert_lse(gl, lo, "bf16", "production shape, sampled lse")
 
 
 @pytest.mark.slow
