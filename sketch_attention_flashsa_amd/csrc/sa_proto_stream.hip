@@ -37,7 +37,7 @@ using namespace dev;
 namespace {
 
 constexpr int kPStages = 4;            // ring slots, as the history kernel
-constexpr int kTileRow = 40;           // bytes per row of a transposition tile (16 bf16 + 8 pad)
+constexpr int kTileRow = 32;           // bytes per row of a transposition tile (16 bf16)
 constexpr float kFitLo = 0x1p-60f;     // fast path: partial row sums inside [2^-60, 2^60]
 constexpr float kFitHi = 0x1p60f;
 
@@ -183,10 +183,15 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * proto_blocks_per_cu(DH, NW, NH)) 
     }
     // transposition tile: lane (g, l16) writes the 4 weights of prototypes
     // 4g..4g+3 of row 16 half + l16, and reads back (transposed) prototype
-    // l16 of rows 16 half + 4g .. + 3, the B operand's k-slots
+    // l16 of rows 16 half + 4g .. + 3, the B operand's k-slots.  The 8-byte
+    // chunk c of row r sits at chunk c ^ ((r >> 2) & 3): the rows that share
+    // banks (4 apart with 32-byte rows) then hold different chunks, so each
+    // 16-lane pass of the writes (16 rows, one chunk each) and of the
+    // transposed reads (4 rows x 4 chunks) touches distinct banks
     const uint32_t tile = (uint32_t)(uintptr_t)(lds_void*)&ptile[wave][0];
-    const uint32_t twr = tile + (uint32_t)(l16 * kTileRow + 8 * g);
-    const uint32_t trd = tile + (uint32_t)((4 * g + (l16 >> 2)) * kTileRow + 8 * (l16 & 3));
+    const uint32_t twr = tile + (uint32_t)(l16 * kTileRow + 8 * (g ^ ((l16 >> 2) & 3)));
+    // the read rows are 4g .. 4g + 3, so (row >> 2) & 3 == g
+    const uint32_t trd = tile + (uint32_t)((4 * g + (l16 >> 2)) * kTileRow + 8 * ((l16 & 3) ^ g));
 
     // the row normalisers are written by the first wave of each head (an
     // instance of its own: the writes' addresses would otherwise hold registers)
