@@ -408,3 +408,25 @@ def test_prototype_axis_masked_and_dense():
     So, lo = _oracle(w, norm="prototype")
     assert_parity(S, So, "bf16", "prototype masked dense")
     assert_lse(lse, lo, "bf16", "prototype masked dense")
+
+
+@pytest.mark.parametrize("H,m,dh", [(8, 128, 64), (4, 64, 32), (1, 1024, 128)])
+@pytest.mark.parametrize("masked", [False, True])
+def test_same_buffer_keys_and_values(H, m, dh, masked):
+    """K and V given as one buffer (as the production shape's folded path
+    passes X for both): the oracle with V = K, and bitwise the same result as
+    two separate copies."""
+    lengths = [900, 0, 1, 31, 33, 257, 1500]
+    w = W.random_case(150 + m + dh, B=len(lengths), H=H, m=m, dh=dh, lengths=lengths, dtype="bf16",
+                      mask_p=0.2 if masked else 0.0)
+    w = dict(w, V=w["K"])
+    d = to_dev(w, device())
+    S1, l1 = sa.sa_forward(d["P"], d["K"], d["K"], cu_offsets=d["cu_offsets"], mask=d.get("mask"), return_lse=True)
+    S2, l2 = sa.sa_forward(d["P"], d["K"], d["K"].clone(), cu_offsets=d["cu_offsets"], mask=d.get("mask"),
+                           return_lse=True)
+    torch.cuda.synchronize()
+    S1, l1, S2, l2 = (x.double().cpu().numpy() for x in (S1, l1, S2, l2))
+    So, lo = _oracle(w)
+    assert_parity(S1, So, "bf16", f"K = V buffer H={H} m={m} dh={dh}")
+    assert_lse(l1, lo, "bf16", f"K = V buffer H={H} m={m} dh={dh}")
+    assert np.array_equal(S1, S2) and np.array_equal(l1, l2), "one copy of K = V must equal two copies"
