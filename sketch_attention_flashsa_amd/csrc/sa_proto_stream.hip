@@ -12,7 +12,8 @@
 // 32-prototype) unit per wave, so a block holds all m prototypes of its heads
 // and every row's normaliser is finished inside the block.  Per 32-row stage:
 //   * scores S = P K^T on v_mfma_f32_16x16x32_bf16 (P fragments as the A
-//     operand), so a lane holds 8 prototypes of each of two rows (row l16 of
+//     operand; pre-scaled by c unless the row normalisers are written out),
+//     so a lane holds 8 prototypes of each of two rows (row l16 of
 //     both 16-row halves): the wave's partial row sums of 2^(s c) are seven
 //     adds per row, then two lane-row swaps (v_permlane16/32_swap);
 //   * the PB waves of a head exchange their partial sums through LDS (a
@@ -141,17 +142,37 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * proto_blocks_per_cu(DH, NW, NH)) 
     const int64_t krow = a.k_stride * 2, vrow = a.v_stride * 2;
 
     // P fragments as the score product's A operand: lane (g, l16) holds
-    // prototype 32 pbi + 16 sb + l16, channels 32 kc + 8 g .. + 7 (exact bf16)
+    // prototype 32 pbi + 16 sb + l16, channels 32 kc + 8 g .. + 7.  Without
+    // the lse output they are pre-scaled by c (rounded to bf16 once, as on
+    // the history axis: the rounding shifts a row's scores by amounts that
+    // mostly cancel in its normalisation), so the products are base-2 scores;
+    // the row normaliser itself would keep that shift, so the instance that
+    // writes it keeps P exact and scales each product.
+    constexpr bool PRESCALE = !LSE;
     bf16x8 pf[NSB][KC];
     {
         const bf16* base = (const bf16*)a.P + ((int64_t)head * a.m + pbi * 32) * DH;
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc)
-                pf[sb][kc] = *(const bf16x8*)(base + (int64_t)(16 * sb + l16) * DH + 32 * kc + 8 * g);
+            for (int kc = 0; kc < KC; ++kc) {
+                const bf16x8 v = *(const bf16x8*)(base + (int64_t)(16 * sb + l16) * DH + 32 * kc + 8 * g);
+                if constexpr (PRESCALE) {
+                    bf16x8 w;
+#pragma unroll
+                    for (int e = 0; e < 8; e += 2) {
+                        const bf16x2 q = pack2((float)v[e] * a.c, (float)v[e + 1] * a.c);
+                        w[e] = q[0];
+                        w[e + 1] = q[1];
+                    }
+                    pf[sb][kc] = w;
+                } else {
+                    pf[sb][kc] = v;
+                }
+            }
         wait_vm<0>();
     }
+    const float cs = PRESCALE ? 1.f : a.c;   // what the products still need
 
     // DMA geometry (as the history kernel)
     int dma_row[D];
@@ -304,7 +325,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * proto_blocks_per_cu(DH, NW, NH)) 
                 for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        e[h][sb][r] = __builtin_amdgcn_exp2f(s[h][sb][r] * a.c);
+                        e[h][sb][r] = __builtin_amdgcn_exp2f(PRESCALE ? s[h][sb][r] : s[h][sb][r] * cs);
                         z[h] += e[h][sb][r];
                     }
             }
@@ -346,7 +367,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * proto_blocks_per_cu(DH, NW, NH)) 
                     for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            x[h][sb][r] = vh ? s[h][sb][r] * a.c : -INFINITY;
+                            x[h][sb][r] = vh ? s[h][sb][r] * cs : -INFINITY;
                             mx[h] = fmaxf(mx[h], x[h][sb][r]);
                         }
                 }

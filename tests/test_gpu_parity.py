@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_util import assert_lse, assert_parity, run, to_dev, device
+from gpu_util import assert_lse, assert_parity, rel_l2, run, to_dev, device
 import sketch_attention_flashsa_amd as sa
 
 pytestmark = pytest.mark.gpu
@@ -354,7 +354,8 @@ def test_prototype_one_pass_shapes(H, m, dh, waves, masked):
     """Every block shape of the one-pass prototype-axis kernel (8- and
     16-wave blocks; 1, 2 and 4 prototype blocks per head), ragged users,
     with and without a mask: S against the oracle from a call without lse
-    and from one with lse (the same S bitwise), lse against the oracle."""
+    (pre-scaled prototypes) and from one with lse (exact prototypes), lse
+    against the oracle."""
     lengths = [700, 1, 33, 0, 1000, 64, 95, 31]
     w = W.random_case(130 + m + dh + H, B=len(lengths), H=H, m=m, dh=dh, lengths=lengths, dtype="bf16",
                       mask_p=0.25 if masked else 0.0)
@@ -371,7 +372,9 @@ def test_prototype_one_pass_shapes(H, m, dh, waves, masked):
     assert_parity(S1, So, "bf16", tag + " (no lse)")
     assert_parity(S, So, "bf16", tag)
     assert_lse(lse.reshape(lo.shape), lo, "bf16", tag)
-    assert np.array_equal(S, S1), "S must not depend on whether lse is written"
+    # the instance without lse pre-scales P (one more bf16 rounding): the two
+    # agree to the bf16 bar, not bitwise
+    assert rel_l2(S1, S) < 1e-2, f"{tag}: S with and without lse differ by {rel_l2(S1, S):.2e}"
 
 
 @pytest.mark.parametrize("offset", [50.0, 120.0, -200.0])
@@ -399,7 +402,7 @@ def test_prototype_exact_path(offset):
     assert_parity(S1, So, "bf16", f"exact path offset {offset} (no lse)")
     assert_parity(S, So, "bf16", f"exact path offset {offset}")
     assert_lse(lse.reshape(lo.shape), lo, "bf16", f"exact path offset {offset}")
-    assert np.array_equal(S, S1)
+    assert rel_l2(S1, S) < 1e-2
 
 
 def test_prototype_axis_masked_and_dense():
