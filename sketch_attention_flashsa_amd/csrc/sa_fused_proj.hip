@@ -411,28 +411,39 @@ void launch_fused_t(const FusedArgs& a, bool masked, bool vx, hipStream_t s) {
 
 }  // namespace
 
-// One thread per output element; W's row e and P's row j are read along k.
-__global__ void sa_fold_keys_kernel(const bf16* P, const bf16* W, int H, int m, int dh, int d_model, float c,
-                                    bf16* out) {
-    const int64_t n = (int64_t)H * m * d_model;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-        const int e = (int)(i % d_model);
-        const int64_t hj = i / d_model;
-        const int h = (int)(hj / m);
-        const bf16* pr = P + hj * dh;
-        const bf16* wr = W + (int64_t)e * H * dh + (int64_t)h * dh;
-        float acc = 0.f;
-        for (int k = 0; k < dh; ++k) acc = fmaf((float)pr[k], (float)wr[k], acc);
-        out[i] = (bf16)(acc * c);
-    }
+// P_h W_K,h^T on MFMA (m and d_model multiples of 16, dh of 32): one wave
+// per 16 x 16 output tile (prototypes j0.., model channels e0..), the
+// operands read straight from memory (both are k-contiguous):
+// A = 16 prototype rows of P_h, B = 16 rows of W restricted to head h's
+// columns; the lane's four results (prototypes j0 + 4g .. + 3, channel
+// e0 + l16) are scaled and rounded once.
+__global__ __launch_bounds__(256) void sa_fold_keys_mfma_kernel(const bf16* P, const bf16* W, int H, int m, int dh,
+                                                                int d_model, float c, bf16* out) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
+    const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int tn = d_model / 16, tm = m / 16;
+    if (tile >= (int64_t)H * tm * tn) return;
+    const int e0 = (int)(tile % tn) * 16;
+    const int64_t hj = tile / tn;
+    const int j0 = (int)(hj % tm) * 16, h = (int)(hj / tm);
+    const bf16* pa = P + ((int64_t)h * m + j0 + l16) * dh + 8 * g;
+    const bf16* wb = W + (int64_t)(e0 + l16) * H * dh + (int64_t)h * dh + 8 * g;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < dh; k += 32)
+        acc = mfma(*(const bf16x8*)(pa + k), *(const bf16x8*)(wb + k), acc);
+    bf16* o = out + ((int64_t)h * m + j0 + 4 * g) * d_model + e0 + l16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[(int64_t)r * d_model] = (bf16)(acc[r] * c);
 }
 
 hipError_t launch_fold_keys(const bf16* P, const bf16* W, int H, int m, int dh, int d_model, float c, bf16* out,
                             hipStream_t s) {
     const int64_t n = (int64_t)H * m * d_model;
     if (n <= 0) return hipSuccess;
-    const int64_t blocks = min((n + 255) / 256, (int64_t)4096);
-    hipLaunchKernelGGL(sa_fold_keys_kernel, dim3((unsigned)blocks), dim3(256), 0, s, P, W, H, m, dh, d_model, c, out);
+    if (m % 16 != 0 || d_model % 16 != 0 || dh % 32 != 0) return hipErrorInvalidValue;
+    const int64_t tiles = (int64_t)H * (m / 16) * (d_model / 16);
+    hipLaunchKernelGGL(sa_fold_keys_mfma_kernel, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, s, P, W, H, m, dh,
+                       d_model, c, out);
     return hipGetLastError();
 }
 
