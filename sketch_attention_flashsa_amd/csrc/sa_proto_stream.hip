@@ -106,11 +106,13 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * proto_blocks_per_cu(DH, NW, NH)) 
     __shared__ __attribute__((aligned(16))) uint32_t mkring[MASKED ? S : 1][64];
     // per wave: one 32-row x 16-prototype bf16 tile of weights being transposed
     __shared__ __attribute__((aligned(16))) unsigned char ptile[NW][32 * kTileRow];
-    // per (head, prototype block, row): partial row sums, and maxima on the exact path
-    __shared__ __attribute__((aligned(16))) float xsum[NH][PB][32];
+    // per (stage parity, head, prototype block, row): partial row sums (a
+    // stage's are written one loop step before they are read), and maxima
+    // on the exact path
+    __shared__ __attribute__((aligned(16))) float xsum[2][NH][PB][32];
     __shared__ __attribute__((aligned(16))) float xmax[NH][PB][32];
-    // per stage parity: some wave of the block needs the exact path
-    __shared__ uint32_t xflag[2];
+    // per stage (t & 3): some wave of the block needs the exact path
+    __shared__ uint32_t xflag[4];
 
     if (offsets_rejected(a.status)) return;
     const int lane = threadIdx.x & 63;
@@ -231,9 +233,9 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * proto_blocks_per_cu(DH, NW, NH)) 
         const unsigned char* kseg = uniform_ptr(Kg + gbase * krow + (int64_t)h0 * DH * 2);
         const unsigned char* vseg = uniform_ptr(Vg + gbase * vrow + (int64_t)h0 * DH * 2);
 
-        // both flag words start clear (every wave has passed the previous
+        // the flag words start clear (every wave has passed the previous
         // segment's final barrier, so none still reads them)
-        if (wave == 0 && lane < 2) xflag[lane] = 0u;
+        if (wave == 0 && lane < 4) xflag[lane] = 0u;
         wait_lgkm0();
 
         const unsigned char* knext = kseg;
@@ -304,19 +306,25 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * proto_blocks_per_cu(DH, NW, NH)) 
             }
         };
 
-        auto unit = [&](int t, int slot, uint32_t valid) {
-            const uint32_t sbase = (uint32_t)(slot * 2 * STAGE);
-            const bool full = valid == 0xffffffffu;
-            const bool v0 = (valid >> l16) & 1u, v1 = (valid >> (16 + l16)) & 1u;
+        // The stage loop is software-pipelined: step t (after the step's one
+        // block barrier) finishes stage t -- the row sums its waves published
+        // in the previous step, the normalised weights, the aggregation --
+        // and starts stage t + 1 -- scores, exponentials, partial row sums
+        // into the other exchange buffer.  One barrier per step then orders
+        // both the ring and the exchange; the ring runs two stages ahead.
+        float e[2][NSB][4];       // a started stage's weights 2^(s c), front() -> back()
+        uint32_t valid_c = 0;     // and its validity bits
+
+        // start stage t (ring slot `slot`): scores, weights before
+        // normalisation, this wave's partial row sums and its exact-path flag
+        auto front = [&](int t, int slot) {
+            const uint32_t valid = unit_valid(t, slot);
+            valid_c = valid;
             // the row whose total this lane holds after rows_sum
             const int rr = l16 + 16 * (g & 1);
             const bool vr = (valid >> rr) & 1u;
-
             f32x4 s[2][NSB];
-            scores(sbase, s);
-
-            // unnormalised weights 2^(s c) and the wave's partial row sums
-            float e[2][NSB][4];
+            scores((uint32_t)(slot * 2 * STAGE), s);
             float z[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -332,14 +340,21 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * proto_blocks_per_cu(DH, NW, NH)) 
             const float zr = rows_sum(z[0], z[1]);
             // false for NaN and Inf too
             const bool fits = !vr || (zr >= kFitLo && zr <= kFitHi);
-            if (__ballot(!fits) != 0 && lane == 0) xflag[t & 1] = 1u;
-            if (lane < 32) xsum[hl][pbi][lane] = zr;
-            wait_lgkm0();
-            block_barrier();
-            const bool exact = xflag[t & 1] != 0u;
-            // the other parity's flag: read by every wave before the barrier
-            // that opened this stage, next set after the next one
-            if (wave == 0 && lane == 0) xflag[(t + 1) & 1] = 0u;
+            if (__ballot(!fits) != 0 && lane == 0) xflag[t & 3] = 1u;
+            if (lane < 32) xsum[t & 1][hl][pbi][lane] = zr;
+        };
+
+        // finish stage t (its row sums published before this step's barrier)
+        auto back = [&](int t, int slot) {
+            const uint32_t sbase = (uint32_t)(slot * 2 * STAGE);
+            const uint32_t valid = valid_c;
+            const bool full = valid == 0xffffffffu;
+            const bool v0 = (valid >> l16) & 1u, v1 = (valid >> (16 + l16)) & 1u;
+            const int xb = t & 1;
+            const bool exact = xflag[t & 3] != 0u;
+            // stage t + 2's flag: last read (stage t - 2) before this step's
+            // barrier, next set in the following step
+            if (wave == 0 && lane == 0) xflag[(t + 2) & 3] = 0u;
 
             // rows l16 and 16 + l16: 1 / Z, and Z with the maximum it is relative to
             float rz[2], Zr[2], Mr[2] = {0.f, 0.f};
@@ -347,8 +362,8 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * proto_blocks_per_cu(DH, NW, NH)) 
                 float Z0 = 0.f, Z1 = 0.f;
 #pragma unroll
                 for (int q = 0; q < PB; ++q) {
-                    Z0 += xsum[hl][q][l16];
-                    Z1 += xsum[hl][q][16 + l16];
+                    Z0 += xsum[xb][hl][q][l16];
+                    Z1 += xsum[xb][hl][q][16 + l16];
                 }
                 Zr[0] = Z0;
                 Zr[1] = Z1;
@@ -356,9 +371,10 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * proto_blocks_per_cu(DH, NW, NH)) 
                 // exact path for the stage (all waves of the block): row
                 // maxima first, then sums of 2^(s c - max); the stage's keys
                 // are still in the ring (its slot is refilled after the next
-                // stage's barrier)
+                // step's barrier)
+                f32x4 s[2][NSB];
                 scores(sbase, s);
-                float x[2][NSB][4], mx[2];
+                float x[2][NSB][4], mx[2], z[2];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const bool vh = h ? v1 : v0;
@@ -393,15 +409,16 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * proto_blocks_per_cu(DH, NW, NH)) 
                             z[h] += e[h][sb][r];
                         }
                 }
+                // this buffer's fast-path sums are not read on the exact path
                 const float zx = rows_sum(z[0], z[1]);
-                if (lane < 32) xsum[hl][pbi][lane] = zx;
+                if (lane < 32) xsum[xb][hl][pbi][lane] = zx;
                 wait_lgkm0();
                 block_barrier();
                 float Z0 = 0.f, Z1 = 0.f;
 #pragma unroll
                 for (int q = 0; q < PB; ++q) {
-                    Z0 += xsum[hl][q][l16];
-                    Z1 += xsum[hl][q][16 + l16];
+                    Z0 += xsum[xb][hl][q][l16];
+                    Z1 += xsum[xb][hl][q][16 + l16];
                 }
                 Zr[0] = Z0;
                 Zr[1] = Z1;
@@ -413,13 +430,6 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * proto_blocks_per_cu(DH, NW, NH)) 
             // there; masked rows may hold anything and are selected below
             rz[0] = v0 ? __builtin_amdgcn_rcpf(Zr[0]) : 0.f;
             rz[1] = v1 ? __builtin_amdgcn_rcpf(Zr[1]) : 0.f;
-            // V^T operands (read here, not before the barrier: fewer registers live across it)
-            i16x4 lo[DB], hi[DB];
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                lo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vlane[db] + sbase / 8);
-                hi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vlane[db] + (sbase + 16 * ROWB) / 8);
-            }
             if (lse_writer) {
                 // the row normaliser, natural log (-inf for masked rows)
                 const int rows_here = (int)min((int64_t)32, nrows - (int64_t)t * 32);
@@ -456,6 +466,14 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * proto_blocks_per_cu(DH, NW, NH)) 
                 pk[sb] = pt.v;
             }
 
+            // V^T operands (read after the weights, so that they and the fp32
+            // weights are never live together)
+            i16x4 lo[DB], hi[DB];
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                lo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vlane[db] + sbase / 8);
+                hi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(vlane[db] + (sbase + 16 * ROWB) / 8);
+            }
             if (!full) {
                 // rows outside the segment or masked: zero their values (NaN must not leak)
                 const uint32_t vj = lane_slots(valid, g);
@@ -482,28 +500,38 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * proto_blocks_per_cu(DH, NW, NH)) 
             }
         };
 
-        auto stage = [&](int t, int slot) {
-            wait_after<AHEAD - 1, VMS>(min(AHEAD - 1, ntiles - 1 - t));
+        // step t (stage t in ring slot `slot` = t % S, a literal at every
+        // call): stage t + 1 has landed and stage t's row sums are published
+        // once every wave passes the barrier, which also frees slot
+        // (t - 1) % S (read by step t - 1) for stage t + 3
+        auto step = [&](int t, int slot) {
+            wait_after<1, VMS>(max(0, min(1, ntiles - 2 - t)));
             block_barrier();
-            if (t + AHEAD < ntiles) issue(t + AHEAD, (slot + AHEAD) % S);
-            const uint32_t valid = unit_valid(t, slot);
-            unit(t, slot, valid);
+            if (t + 3 < ntiles) issue(t + 3, (slot + 3) % S);
+            back(t, slot);
+            if (t + 1 < ntiles) front(t + 1, (slot + 1) % S);
+            // every LDS access of this step has completed before the next barrier
             wait_lgkm0();
         };
-        static_assert(S == 4, "the stage loop is unrolled by the ring size");
+        static_assert(S == 4, "the step loop is unrolled by the ring size");
         if (0 < ntiles) issue(0, 0);
         if (1 < ntiles) issue(1, 1);
         if (2 < ntiles) issue(2, 2);
+        // stage 0 has landed; then start it
+        wait_after<2, VMS>(min(2, ntiles - 1));
+        block_barrier();
+        front(0, 0);
+        wait_lgkm0();
         int t = 0;
         for (; t + S <= ntiles; t += S) {
-            stage(t, 0);
-            stage(t + 1, 1);
-            stage(t + 2, 2);
-            stage(t + 3, 3);
+            step(t, 0);
+            step(t + 1, 1);
+            step(t + 2, 2);
+            step(t + 3, 3);
         }
-        if (t < ntiles) stage(t, 0);
-        if (t + 1 < ntiles) stage(t + 1, 1);
-        if (t + 2 < ntiles) stage(t + 2, 2);
+        if (t < ntiles) step(t, 0);
+        if (t + 1 < ntiles) step(t + 1, 1);
+        if (t + 2 < ntiles) step(t + 2, 2);
 
         // segment epilogue: the weighted sums at slot w + b, lane order
         {
