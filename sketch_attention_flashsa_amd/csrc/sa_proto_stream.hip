@@ -218,7 +218,8 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * proto_blocks_per_cu(DH, NW, NH)) 
 
     // the row normalisers are written by the first wave of each head (an
     // instance of its own: the writes' addresses would otherwise hold registers)
-    const bool lse_writer = LSE && pbi == 0 && g == 0;
+    // (lanes g = 0 and 1 of the head's first wave: row 16 g + l16, = lane)
+    const bool lse_writer = LSE && pbi == 0 && g < 2;
 
     int b = a.users.find(v_lo);
     for (; b < a.users.B; ++b) {
@@ -431,11 +432,12 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * proto_blocks_per_cu(DH, NW, NH)) 
             rz[0] = v0 ? __builtin_amdgcn_rcpf(Zr[0]) : 0.f;
             rz[1] = v1 ? __builtin_amdgcn_rcpf(Zr[1]) : 0.f;
             if (lse_writer) {
-                // the row normaliser, natural log (-inf for masked rows)
+                // the row normaliser of row `lane`, natural log (-inf for masked rows)
                 const int rows_here = (int)min((int64_t)32, nrows - (int64_t)t * 32);
                 float* lrow = uniform_ptr(lse_out + (gbase + (int64_t)t * 32) * a.H + head);
-                if (l16 < rows_here) lrow[l16 * a.H] = v0 ? (Mr[0] + __log2f(Zr[0])) * kLn2 : -INFINITY;
-                if (16 + l16 < rows_here) lrow[(16 + l16) * a.H] = v1 ? (Mr[1] + __log2f(Zr[1])) * kLn2 : -INFINITY;
+                const bool vl = g ? v1 : v0;
+                const float zl = g ? Zr[1] : Zr[0], ml = g ? Mr[1] : Mr[0];
+                if (lane < rows_here) lrow[lane * a.H] = vl ? (ml + __log2f(zl)) * kLn2 : -INFINITY;
             }
 
             // normalised bf16 weights, transposed through the wave's tile into
