@@ -14,6 +14,7 @@
 #include "sa_internal.h"
 #include "sa_fold.h"
 #include "sa_proto.h"
+#include "sa_stream_d128.h"
 #include "sketchattn.h"
 
 namespace {
@@ -97,6 +98,7 @@ struct Plan {
     sa::Bf16Config cfg{};
     bool stream = false;      // bf16: the direct-to-LDS streaming kernel serves this shape
     bool proto1 = false;      // prototype axis in one pass (sa_proto_stream_kernel), no row-normaliser pass
+    bool d128 = false;        // history axis, dh = 128: the pipelined streaming kernel (sa_stream_d128.hip)
     sa::StreamConfig scfg{};
     int groups = 1;           // bf16: unit groups per row range
     bool check_offsets = false;  // SA_FLAG_CHECK_OFFSETS: status section first
@@ -172,6 +174,8 @@ sa_status make_plan(const sa_problem* pb, bool packed, Plan* pl, int32_t flags_o
         pl->stream =
             !g_tune.register_staged && sa::stream_config(pb->dh, pb->m, pb->H, g_tune.stream_waves, &pl->scfg);
         pl->proto1 = pl->stream && pb->norm == SA_NORM_PROTOTYPE && sa::proto_one_pass(pl->scfg, pb->dh);
+        pl->d128 = pl->stream && pb->norm == SA_NORM_HISTORY && pb->dh == 128 &&
+                   sa::stream_d128_config(pb->m, pb->H, &pl->scfg);
         if (pl->stream) {
             pl->groups = pl->scfg.groups;
             blocks_per_cu = pl->scfg.blocks_per_cu;
@@ -295,6 +299,7 @@ const char* sa_forward_kernel_name(const sa_problem* pb) {
     if (!pb || make_plan(pb, pb->L_max == 0, &pl) != SA_OK) return nullptr;
     if (pl.f32) return "sa_f32_fwd_kernel";
     if (pl.proto1) return "sa_proto_stream_kernel";
+    if (pl.d128) return "sa_bf16_stream_d128_kernel";
     return pl.stream ? "sa_bf16_stream_kernel" : "sa_bf16_fwd_kernel";
 }
 
@@ -396,6 +401,7 @@ sa_status sa_forward(const sa_problem* pb, const void* P, const void* K, const v
     if (ev.start && (e = hipEventRecord(ev.start, stream)) != hipSuccess) return hip_fail(e, "timing event");
     if (pl.f32) e = sa::launch_f32_forward(a, stream);
     else if (pl.proto1) e = sa::launch_proto_stream(a, lse_out, pl.scfg, stream);
+    else if (pl.d128) e = sa::launch_stream_d128(a, pl.scfg, stream);
     else if (pl.stream) e = sa::launch_bf16_stream(a, pl.scfg, stream);
     else e = sa::launch_bf16_forward(a, pl.cfg, stream);
     if (e != hipSuccess) return hip_fail(e, "forward");

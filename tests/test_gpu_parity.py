@@ -227,7 +227,7 @@ def test_dh128_streaming(H, m):
     lengths = [900, 0, 1, 31, 33, 257, 1500]
     w = W.random_case(107 + m + H, B=len(lengths), H=H, m=m, dh=128, lengths=lengths, dtype="bf16", mask_p=0.2)
     assert sa.sa_forward_kernel_name(sa.make_problem(len(lengths), H, m, 128, int(sum(lengths)))) == \
-        "sa_bf16_stream_kernel"
+        "sa_bf16_stream_d128_kernel"
     S, lse = run(w)
     So, lo = _oracle(w)
     assert_parity(S, So, "bf16", f"dh=128 H={H} m={m}")
@@ -284,7 +284,43 @@ def test_peaked_and_shifted_scores(scale_p, offset):
     assert_lse(lse, lo, "bf16", f"peaked x{scale_p} offset {offset}")
 
 
-@pytest.mark.parametrize("H,m,dh", [(2, 32, 32), (8, 128, 64), (3, 48, 32)])
+@pytest.mark.parametrize("ramp,masked", [(0.0, False), (1.0, False), (-1.0, False), (1.0, True)])
+def test_dh128_pipeline_segments_and_moving_maximum(ramp, masked):
+    """The dh = 128 kernel forms a stage's weights while the next stage's
+    score products run, shifting those products when the weights move the
+    running maximum.  Segments of 1 .. 14 stages (every remainder of the
+    six-slot ring, ragged tails) and a score ramp along the rows: channel 0 of
+    every prototype is 4 and channel 0 of key row r is ramp * r / 4, so base-2
+    scores move by about `ramp` per row (the maximum moves in almost every
+    stage when ramp > 0, never after the first when ramp < 0).  The scale is
+    the float nearest 1 / log2(e), for which scale * log2(e) is exactly 1 in
+    float, so the prototypes enter the products unrounded and the scores of
+    several hundred stay exact enough for the lse bar."""
+    dh, m = 128, 256
+    unit = float(np.float32(1.0) / np.float32(np.log2(np.e)))
+    lengths = [1, 32, 33, 64, 95, 160, 191, 192, 193, 224, 385, 448]
+    w = W.random_case(131 + int(ramp * 10) + masked, B=len(lengths), H=1, m=m, dh=dh, lengths=lengths,
+                      dtype="bf16", mask_p=0.2 if masked else 0.0)
+    P = w["P"].float()
+    K = w["K"].float()
+    if ramp:
+        P[:, :, 0] = 4.0
+        cu = w["cu_offsets"].tolist()
+        for b in range(len(lengths)):
+            r = torch.arange(cu[b + 1] - cu[b], dtype=torch.float32)
+            K[cu[b]:cu[b + 1], :, 0] = (ramp * r / 4.0)[:, None]
+    w = dict(w, P=P.to(torch.bfloat16), K=K.to(torch.bfloat16))
+    assert sa.sa_forward_kernel_name(sa.make_problem(len(lengths), 1, m, dh, int(sum(lengths)))) == \
+        "sa_bf16_stream_d128_kernel"
+    So, lo = oracle.forward(w["P"], w["K"], w["V"], cu_offsets=w["cu_offsets"], mask=w.get("mask"), scale=unit)
+    for chunk in (0, 96):
+        S, lse = run(w, chunk_rows=chunk, scale=unit)
+        assert np.all(np.isfinite(S))
+        assert_parity(S, So, "bf16", f"dh=128 ramp {ramp} masked {masked} chunk {chunk}")
+        assert_lse(lse, lo, "bf16", f"dh=128 ramp {ramp} masked {masked} chunk {chunk}")
+
+
+@pytest.mark.parametrize("H,m,dh", [(2, 32, 32), (8, 128, 64), (3, 48, 32), (1, 256, 128)])
 def test_per_user_prototypes(H, m, dh):
     """P [B, H, m, dh] (stacked refinement feeds per-user queries) against the
     oracle with the same per-user sets, on the streaming kernel's shapes and a
