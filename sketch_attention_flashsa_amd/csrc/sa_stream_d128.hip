@@ -243,9 +243,27 @@ __global__ __launch_bounds__(kNW * 64, 2) void sa_bf16_stream_d128_kernel(FwdArg
             }
         };
 
-        // weights and aggregation of stage t (slot), with the score products
-        // of stage t + 1 (nslot) in between when NEXT
-        auto step = [&](int t, int slot, int nslot, auto next_tag) {
+        // K fragments of the stage in `slot` (8 reads), for its score products
+        typedef bf16x8 KFrag[KC][2];
+        auto kreads = [&](int slot, KFrag& kf) {
+            const uint32_t base = (uint32_t)(slot * 2 * STAGE);
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                lds_bf16x8* p0 = klane[kc] + base / 16;
+                kf[kc][0] = p0[0];
+                kf[kc][1] = p0[16 * ROWB / 16];
+            }
+        };
+        // K fragments of the stage after the one being weighed (read one step
+        // ahead, during the previous aggregation, so their latency is hidden)
+        KFrag kf;
+
+        // step t: weights and aggregation of stage t (slot).  With NEXT (a
+        // stage t + 1 exists) the score products of stage t + 1 run beside the
+        // weights; then, once every wave is past its reads of slot t, the
+        // barrier that certifies stage t + 2 lets slot t take stage t + S, and
+        // stage t + 2's K fragments are read while stage t is aggregated.
+        auto step = [&](int t, int slot, int n2slot, auto next_tag) {
             constexpr bool NEXT = decltype(next_tag)::value;
             const uint32_t valid = unit_valid(t, slot);
             const bool seg_full = MASKED ? (t + 1) * 32 <= nrows32 : valid == 0xffffffffu;
@@ -275,18 +293,10 @@ __global__ __launch_bounds__(kNW * 64, 2) void sa_bf16_stream_d128_kernel(FwdArg
             };
             f32x4 sn[2][NSB];
             if constexpr (NEXT) {
-                // stage t + 1's K fragments, then four rounds of (its score
-                // products of one 32-wide slice of dh, one quarter of stage t's
-                // weights, two V^T column blocks), in this order: a wave's
-                // vector instructions overlap its own independent MFMAs
-                const uint32_t nbase = (uint32_t)(nslot * 2 * STAGE);
-                bf16x8 kf[KC][2];
-#pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
-                    lds_bf16x8* p0 = klane[kc] + nbase / 16;
-                    kf[kc][0] = p0[0];
-                    kf[kc][1] = p0[16 * ROWB / 16];
-                }
+                // four rounds of (one quarter of stage t's weights, stage t + 1's
+                // score products of one 32-wide slice of dh, two V^T column
+                // blocks), in this order: a wave's vector instructions overlap
+                // its own independent MFMAs
 #pragma unroll
                 for (int kc = 0; kc < KC; ++kc) {
                     __builtin_amdgcn_sched_barrier(0);
@@ -347,10 +357,10 @@ __global__ __launch_bounds__(kNW * 64, 2) void sa_bf16_stream_d128_kernel(FwdArg
                     float p[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) p[j] = ((vj >> j) & 1) ? __builtin_amdgcn_exp2f(x[j] - Mset) : 0.f;
-                    const bf16x2 q0 = pack2(p[0], p[1]), q1 = pack2(p[2], p[3]);
-                    const bf16x2 q2 = pack2(p[4], p[5]), q3 = pack2(p[6], p[7]);
-                    pk[sb] = cat8(q0, q1, q2, q3);
-                    zt[sb] = dot2sum(q3, dot2sum(q2, dot2sum(q1, dot2sum(q0, 0.f))));
+                    const bf16x2 e0 = pack2(p[0], p[1]), e1 = pack2(p[2], p[3]);
+                    const bf16x2 e2 = pack2(p[4], p[5]), e3 = pack2(p[6], p[7]);
+                    pk[sb] = cat8(e0, e1, e2, e3);
+                    zt[sb] = dot2sum(e3, dot2sum(e2, dot2sum(e1, dot2sum(e0, 0.f))));
                     if (none && !found) zt[sb] = -1.f;      // Zs = -1 * 0 - 1 keeps the sentinel
                     nM[sb] = (f32x4){-Mset, -Mset, -Mset, -Mset};
                     if constexpr (NEXT) {
@@ -365,6 +375,18 @@ __global__ __launch_bounds__(kNW * 64, 2) void sa_bf16_stream_d128_kernel(FwdArg
             }
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) Zs[sb] = fmaf(Zs[sb], f[sb], zt[sb]);
+            if constexpr (NEXT) {
+                // this wave's reads of slot t (V^T above, K again on the exact
+                // path) have completed; wait for its part of stage t + 2 (stages
+                // up to t + S - 1 have been issued); the barrier then certifies
+                // stage t + 2 and frees slot t for stage t + S
+                wait_lgkm0();
+                const int after = min(t + S - 1, ntiles - 1) - (t + 2);
+                wait_after<S - 3, VMS>(max(0, min(S - 3, after)));
+                block_barrier();
+                if (t + S < ntiles) issue(t + S, slot);
+                if (t + 2 < ntiles) kreads(n2slot, kf);
+            }
             if (valid != 0xffffffffu) {
                 // rows outside the segment or masked: zero their values (NaN must not leak)
 #pragma unroll
@@ -396,39 +418,33 @@ __global__ __launch_bounds__(kNW * 64, 2) void sa_bf16_stream_d128_kernel(FwdArg
             }
         };
 
-        // step t of a stage t + 1 that exists: wait for this wave's part of
-        // stage t + 1; the barrier makes it complete and frees slot
-        // (t - 1) % S (its V was read by step t - 1, its K by step t - 2)
-        auto full = [&](int t, int slot, int nslot, int islot) {
-            wait_after<S - 3, VMS>(min(S - 3, ntiles - 2 - t));
-            block_barrier();
-            if (t + S - 1 < ntiles) issue(t + S - 1, islot);
-            step(t, slot, nslot, Next{});
-            // every LDS read of this step has completed before the next barrier
-            wait_lgkm0();
-        };
-
-        // prologue: stages 0 .. S - 2 in flight, the scores of stage 0
+        // prologue: all S slots filled (stages 0 .. S - 1), the scores of
+        // stage 0 and the K fragments of stage 1
 #pragma unroll
-        for (int i = 0; i < S - 1; ++i)
+        for (int i = 0; i < S; ++i)
             if (i < ntiles) issue(i, i);
-        wait_after<S - 2, VMS>(min(S - 2, ntiles - 1));
+        wait_after<S - 1, VMS>(min(S - 1, ntiles - 1));
         block_barrier();
         scores(0, sc);
+        if (1 < ntiles) {
+            wait_after<S - 2, VMS>(min(S - 2, ntiles - 2));
+            block_barrier();
+            kreads(1, kf);
+        }
         int t = 0;
         static_assert(S == 6, "the step loop is unrolled by the ring size");
         for (; t + S < ntiles; t += S) {
-            full(t, 0, 1, 5);
-            full(t + 1, 1, 2, 0);
-            full(t + 2, 2, 3, 1);
-            full(t + 3, 3, 4, 2);
-            full(t + 4, 4, 5, 3);
-            full(t + 5, 5, 0, 4);
+            step(t, 0, 2, Next{});
+            step(t + 1, 1, 3, Next{});
+            step(t + 2, 2, 4, Next{});
+            step(t + 3, 3, 5, Next{});
+            step(t + 4, 4, 0, Next{});
+            step(t + 5, 5, 1, Next{});
         }
-        // at most S - 1 more full steps, then the last stage (slot = t % S = step index)
+        // at most S - 1 more steps with a next stage, then the last stage
         for (; t + 1 < ntiles; ++t) {
             const int sl = t % S;
-            full(t, sl, sl + 1 == S ? 0 : sl + 1, sl == 0 ? S - 1 : sl - 1);
+            step(t, sl, sl + 2 >= S ? sl + 2 - S : sl + 2, Next{});
         }
         step(t, t % S, 0, Last{});
 
