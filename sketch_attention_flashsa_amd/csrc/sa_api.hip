@@ -398,6 +398,11 @@ sa_status sa_forward(const sa_problem* pb, const void* P, const void* K, const v
     a.lse2_tok = lse2_tok;
     a.norm = pb->norm;
     a.status = status;
+    // a requested per-prototype lse keeps any rounding of the scaled
+    // prototypes (the shift cancels in the weights, not in the normaliser), so
+    // the streaming kernels then scale unrounded products; a unit scale
+    // (the folded production shape) pre-scales exactly
+    a.exact_scale = pb->norm == SA_NORM_HISTORY && lse_out != nullptr && a.c != 1.0f;
     if (ev.start && (e = hipEventRecord(ev.start, stream)) != hipSuccess) return hip_fail(e, "timing event");
     if (pl.f32) e = sa::launch_f32_forward(a, stream);
     else if (pl.proto1) e = sa::launch_proto_stream(a, lse_out, pl.scfg, stream);

@@ -55,7 +55,7 @@ constexpr int blocks_per_cu(int DH, int NW, int NH) {
 
 }  // namespace
 
-template <int DH, int NW, int NH, int MB, bool MASKED, bool PROTO>
+template <int DH, int NW, int NH, int MB, bool MASKED, bool PROTO, bool EXACT>
 __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void sa_bf16_stream_kernel(FwdArgs a,
                                                                                                         int PB) {
     constexpr int S = kStages;
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 const bf16x8 v = *(const bf16x8*)(base + (int64_t)(16 * sb + l16) * DH + 32 * kc + 8 * g);
-                if constexpr (PROTO) {
+                if constexpr (PROTO || EXACT) {
                     pf[sb][kc] = v;
                 } else {
                     // history axis: scale * log2(e) folded into the prototypes
@@ -280,7 +280,9 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
         // s - M and a weight is one exp2 (the tuple changes only when M does).
         // Until the prototype meets a valid row, M is 0 (so the products are
         // the scores themselves) and Zs is -1, which sends every tile to the
-        // exact path that sets M from the scores.
+        // exact path that sets M from the scores.  With EXACT the prototypes
+        // are not pre-scaled: products and M are in units of the raw scores
+        // s, a weight is 2^(c (s - M)) and the stored maximum c M.
         float Zs[NSB];
         f32x4 nM[NSB];
         f32x4 acc[NSB][DB];
@@ -351,7 +353,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
                     float p[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        p[j] = __builtin_amdgcn_exp2f(s[j >> 2][sb][j & 3]);
+                        p[j] = __builtin_amdgcn_exp2f(EXACT ? s[j >> 2][sb][j & 3] * a.c : s[j >> 2][sb][j & 3]);
                         // with a mask, masked rows get weight 0 here, so they
                         // do not force the exact path (a no-op where the mask
                         // is all ones, which keeps that bitwise equal to no mask)
@@ -387,10 +389,12 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
                         const bool found = Mnew != -INFINITY;   // the prototype has a valid row
                         // (while it has none, M stays 0 and Zs -1)
                         const float Mset = found ? Mnew : 0.f;
-                        f[sb] = none ? 0.f : (Mset == Mold ? 1.f : __builtin_amdgcn_exp2f(Mold - Mset));
+                        f[sb] = none ? 0.f
+                                     : (Mset == Mold ? 1.f : __builtin_amdgcn_exp2f(EXACT ? (Mold - Mset) * a.c : Mold - Mset));
                         float p[8];
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) p[j] = ((vj >> j) & 1) ? __builtin_amdgcn_exp2f(x[j] - Mset) : 0.f;
+                        for (int j = 0; j < 8; ++j)
+                            p[j] = ((vj >> j) & 1) ? __builtin_amdgcn_exp2f(EXACT ? (x[j] - Mset) * a.c : x[j] - Mset) : 0.f;
                         const bf16x2 q0 = pack2(p[0], p[1]), q1 = pack2(p[2], p[3]);
                         const bf16x2 q2 = pack2(p[4], p[5]), q3 = pack2(p[6], p[7]);
                         pk[sb] = cat8(q0, q1, q2, q3);
@@ -472,7 +476,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
                     z += __shfl_xor(z, 32, 64);
                     if (g == 0) {
                         // no valid row in the segment: M = -inf, as the merge expects
-                        a.part.M[base] = z > 0.f ? -nM[sb][0] : -INFINITY;
+                        a.part.M[base] = z > 0.f ? (EXACT ? -nM[sb][0] * a.c : -nM[sb][0]) : -INFINITY;
                         a.part.Z[base] = z;
                     }
                 }
@@ -495,11 +499,23 @@ namespace {
 template <int DH, int NW, int NH, int MB>
 hipError_t launch_stream(const FwdArgs& a, bool masked, int PB, hipStream_t s) {
     dim3 grid(a.G, PB > NW ? a.H * (PB / NW) : a.H / NH), block(NW * 64);
-    const bool proto = a.norm == 1;
-    if (!masked && !proto) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, NW, NH, MB, false, false>), grid, block, 0, s, a, PB);
-    if (masked && !proto) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, NW, NH, MB, true, false>), grid, block, 0, s, a, PB);
-    if (!masked && proto) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, NW, NH, MB, false, true>), grid, block, 0, s, a, PB);
-    if (masked && proto) hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, NW, NH, MB, true, true>), grid, block, 0, s, a, PB);
+    const bool proto = a.norm == 1, exact = !proto && a.exact_scale;
+#define SA_LAUNCH(M_, P_, E_) \
+    hipLaunchKernelGGL((sa_bf16_stream_kernel<DH, NW, NH, MB, M_, P_, E_>), grid, block, 0, s, a, PB)
+    if (proto) {
+        if (masked) SA_LAUNCH(true, true, false);
+        else SA_LAUNCH(false, true, false);
+    } else if constexpr (DH == 128) {
+        // the history axis at this width runs sa_bf16_stream_d128_kernel
+        return hipErrorInvalidValue;
+    } else if (exact) {
+        if (masked) SA_LAUNCH(true, false, true);
+        else SA_LAUNCH(false, false, true);
+    } else {
+        if (masked) SA_LAUNCH(true, false, false);
+        else SA_LAUNCH(false, false, false);
+    }
+#undef SA_LAUNCH
     return hipGetLastError();
 }
 

@@ -157,6 +157,12 @@ struct FwdArgs {
     const float* lse2_tok;   // prototype axis: per (row, head) log2 normaliser
     int32_t norm;            // 0 history, 1 prototype
     const int32_t* status;   // offsets check verdict, or nullptr
+    // history axis, streaming kernels: 0 = P * c rounded to bf16 once in the
+    // prototype fragments (base-2 products, one rounding of every P element
+    // relative to the exact scores); 1 = P enters unrounded and every score
+    // is multiplied by c in fp32 (set when the per-prototype lse is requested,
+    // whose value keeps the shift that rounding gives the scores)
+    int32_t exact_scale;
 };
 
 struct MergeArgs {

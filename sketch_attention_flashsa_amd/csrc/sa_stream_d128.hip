@@ -53,7 +53,7 @@ using Last = Tag<false>;   // the segment's last stage
 
 }  // namespace
 
-template <bool MASKED>
+template <bool MASKED, bool EXACT>
 __global__ __launch_bounds__(kNW * 64, 2) void sa_bf16_stream_d128_kernel(FwdArgs a) {
     constexpr int S = kS;
     constexpr int ROWB = kROWB, STAGE = kSTAGE;
@@ -102,7 +102,9 @@ __global__ __launch_bounds__(kNW * 64, 2) void sa_bf16_stream_d128_kernel(FwdArg
     const int64_t krow = a.k_stride * 2, vrow = a.v_stride * 2;   // bytes between rows
 
     // prototype fragments, scale * log2(e) folded in (rounded to bf16 once),
-    // so that the score products are base-2 scores
+    // so that the score products are base-2 scores; with EXACT unscaled: the
+    // products are raw scores s (as is the running maximum M below), weights
+    // 2^(c (s - M)) and the stored maximum c M
     bf16x8 pf[NSB][KC];
     auto load_p = [&](int b) {
         const bf16* base = Pg + (int64_t)b * a.q_batch_stride + ((int64_t)head * a.m + pb * 32) * kDH;
@@ -111,6 +113,10 @@ __global__ __launch_bounds__(kNW * 64, 2) void sa_bf16_stream_d128_kernel(FwdArg
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 const bf16x8 v = *(const bf16x8*)(base + (int64_t)(16 * sb + l16) * kDH + 32 * kc + 8 * g);
+                if constexpr (EXACT) {
+                    pf[sb][kc] = v;
+                    continue;
+                }
                 bf16x8 q;
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
@@ -285,7 +291,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void sa_bf16_stream_d128_kernel(FwdArg
                 float p[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    p[i] = __builtin_amdgcn_exp2f(sc[h][sb][i]);
+                    p[i] = __builtin_amdgcn_exp2f(EXACT ? sc[h][sb][i] * a.c : sc[h][sb][i]);
                     if constexpr (MASKED) p[i] = ((vj >> (4 * h + i)) & 1) ? p[i] : 0.f;
                 }
                 q[sb][2 * h] = pack2(p[0], p[1]);
@@ -353,10 +359,12 @@ __global__ __launch_bounds__(kNW * 64, 2) void sa_bf16_stream_d128_kernel(FwdArg
                     const float Mnew = none ? tm : fmaxf(Mold, tm);
                     const bool found = Mnew != -INFINITY;   // the prototype has a valid row
                     const float Mset = found ? Mnew : 0.f;
-                    f[sb] = none ? 0.f : (Mset == Mold ? 1.f : __builtin_amdgcn_exp2f(Mold - Mset));
+                    f[sb] = none ? 0.f
+                                 : (Mset == Mold ? 1.f : __builtin_amdgcn_exp2f(EXACT ? (Mold - Mset) * a.c : Mold - Mset));
                     float p[8];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) p[j] = ((vj >> j) & 1) ? __builtin_amdgcn_exp2f(x[j] - Mset) : 0.f;
+                    for (int j = 0; j < 8; ++j)
+                        p[j] = ((vj >> j) & 1) ? __builtin_amdgcn_exp2f(EXACT ? (x[j] - Mset) * a.c : x[j] - Mset) : 0.f;
                     const bf16x2 e0 = pack2(p[0], p[1]), e1 = pack2(p[2], p[3]);
                     const bf16x2 e2 = pack2(p[4], p[5]), e3 = pack2(p[6], p[7]);
                     pk[sb] = cat8(e0, e1, e2, e3);
@@ -460,7 +468,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void sa_bf16_stream_d128_kernel(FwdArg
                 z += __shfl_xor(z, 16, 64);
                 z += __shfl_xor(z, 32, 64);
                 if (g == 0) {
-                    a.part.M[base] = z > 0.f ? -nM[sb][0] : -INFINITY;
+                    a.part.M[base] = z > 0.f ? (EXACT ? -nM[sb][0] * a.c : -nM[sb][0]) : -INFINITY;
                     a.part.Z[base] = z;
                 }
 #pragma unroll
@@ -491,8 +499,13 @@ bool stream_d128_config(int m, int H, StreamConfig* cfg) {
 hipError_t launch_stream_d128(const FwdArgs& a, const StreamConfig& cfg, hipStream_t s) {
     if (a.dh != kDH || a.norm != 0 || a.m % 256 != 0 || cfg.groups != a.H * (a.m / 256)) return hipErrorInvalidValue;
     dim3 grid(a.G, cfg.groups), block(kNW * 64);
-    if (a.mask) hipLaunchKernelGGL((sa_bf16_stream_d128_kernel<true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((sa_bf16_stream_d128_kernel<false>), grid, block, 0, s, a);
+    if (a.exact_scale) {
+        if (a.mask) hipLaunchKernelGGL((sa_bf16_stream_d128_kernel<true, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((sa_bf16_stream_d128_kernel<false, true>), grid, block, 0, s, a);
+    } else {
+        if (a.mask) hipLaunchKernelGGL((sa_bf16_stream_d128_kernel<true, false>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((sa_bf16_stream_d128_kernel<false, false>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -284,20 +284,22 @@ def test_peaked_and_shifted_scores(scale_p, offset):
     assert_lse(lse, lo, "bf16", f"peaked x{scale_p} offset {offset}")
 
 
-@pytest.mark.parametrize("ramp,masked", [(0.0, False), (1.0, False), (-1.0, False), (1.0, True)])
-def test_dh128_pipeline_segments_and_moving_maximum(ramp, masked):
+@pytest.mark.parametrize("ramp,masked,unit_scale", [(0.0, False, True), (1.0, False, True), (-1.0, False, True),
+                                                    (1.0, True, True), (1.0, False, False), (1.0, True, False)])
+def test_dh128_pipeline_segments_and_moving_maximum(ramp, masked, unit_scale):
     """The dh = 128 kernel forms a stage's weights while the next stage's
     score products run, shifting those products when the weights move the
     running maximum.  Segments of 1 .. 14 stages (every remainder of the
     six-slot ring, ragged tails) and a score ramp along the rows: channel 0 of
     every prototype is 4 and channel 0 of key row r is ramp * r / 4, so base-2
     scores move by about `ramp` per row (the maximum moves in almost every
-    stage when ramp > 0, never after the first when ramp < 0).  The scale is
+    stage when ramp > 0, never after the first when ramp < 0).  unit_scale:
     the float nearest 1 / log2(e), for which scale * log2(e) is exactly 1 in
-    float, so the prototypes enter the products unrounded and the scores of
-    several hundred stay exact enough for the lse bar."""
+    float, so the pre-scaled prototypes are exact; else the default
+    1 / sqrt(dh), where the requested lse makes the kernel scale unrounded
+    products.  Either way scores of several hundred meet the lse bar."""
     dh, m = 128, 256
-    unit = float(np.float32(1.0) / np.float32(np.log2(np.e)))
+    unit = float(np.float32(1.0) / np.float32(np.log2(np.e))) if unit_scale else 1.0 / np.sqrt(dh)
     lengths = [1, 32, 33, 64, 95, 160, 191, 192, 193, 224, 385, 448]
     w = W.random_case(131 + int(ramp * 10) + masked, B=len(lengths), H=1, m=m, dh=dh, lengths=lengths,
                       dtype="bf16", mask_p=0.2 if masked else 0.0)
@@ -308,7 +310,7 @@ def test_dh128_pipeline_segments_and_moving_maximum(ramp, masked):
         cu = w["cu_offsets"].tolist()
         for b in range(len(lengths)):
             r = torch.arange(cu[b + 1] - cu[b], dtype=torch.float32)
-            K[cu[b]:cu[b + 1], :, 0] = (ramp * r / 4.0)[:, None]
+            K[cu[b]:cu[b + 1], :, 0] = (ramp * r / 4.0 / (unit * np.log2(np.e)))[:, None]
     w = dict(w, P=P.to(torch.bfloat16), K=K.to(torch.bfloat16))
     assert sa.sa_forward_kernel_name(sa.make_problem(len(lengths), 1, m, dh, int(sum(lengths)))) == \
         "sa_bf16_stream_d128_kernel"
@@ -318,6 +320,35 @@ def test_dh128_pipeline_segments_and_moving_maximum(ramp, masked):
         assert np.all(np.isfinite(S))
         assert_parity(S, So, "bf16", f"dh=128 ramp {ramp} masked {masked} chunk {chunk}")
         assert_lse(lse, lo, "bf16", f"dh=128 ramp {ramp} masked {masked} chunk {chunk}")
+
+
+@pytest.mark.parametrize("H,m,dh", [(8, 128, 64), (8, 64, 32), (1, 256, 128)])
+def test_streaming_lse_with_large_scores(H, m, dh):
+    """Scores of several hundred on the streaming kernels' shapes at the
+    default scale: with the lse requested the kernels scale unrounded
+    products (a prototype rounded once to bf16 after scaling would shift its
+    lse by about 2^-9 of the scores), so lse meets its bar; S computed with
+    and without the lse agrees to the bf16 bar."""
+    lengths = [700, 33, 1300, 1]
+    w = W.random_case(141 + dh + m, B=len(lengths), H=H, m=m, dh=dh, lengths=lengths, dtype="bf16")
+    P = w["P"].float()
+    K = w["K"].float()
+    P[:, :, 0] = 4.0
+    cu = w["cu_offsets"].tolist()
+    for b in range(len(lengths)):
+        r = torch.arange(cu[b + 1] - cu[b], dtype=torch.float32)
+        K[cu[b]:cu[b + 1], :, 0] = (0.5 * r * np.sqrt(dh) / 4.0)[:, None]   # scores up to ~650
+    w = dict(w, P=P.to(torch.bfloat16), K=K.to(torch.bfloat16))
+    assert sa.sa_forward_kernel_name(sa.make_problem(len(lengths), H, m, dh, int(sum(lengths)))).startswith(
+        "sa_bf16_stream")
+    S, lse = run(w)
+    So, lo = _oracle(w)
+    assert_parity(S, So, "bf16", f"large scores H={H} m={m} dh={dh}")
+    assert_lse(lse, lo, "bf16", f"large scores H={H} m={m} dh={dh}")
+    d = to_dev(w, device())
+    S2 = sa.sa_forward(d["P"], d["K"], d["V"], cu_offsets=d["cu_offsets"])
+    torch.cuda.synchronize()
+    assert_parity(S2.double().cpu().numpy(), So, "bf16", f"large scores without lse H={H} m={m} dh={dh}")
 
 
 @pytest.mark.parametrize("H,m,dh", [(2, 32, 32), (8, 128, 64), (3, 48, 32), (1, 256, 128)])
