@@ -284,15 +284,24 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
         // scores, weights and aggregation of one tile for this wave's prototypes
         auto attend = [&](const bf16x8 (&ka)[2], const bf16x8 (&vt)[2], uint32_t valid) {
             const uint32_t vj = lane_slots(valid, g);
-#pragma unroll
-            for (int sb = 0; sb < NSB; ++sb) {
+            // base-2 scores minus the running maximum of block sb
+            auto scores = [&](int sb, f32x4& s0, f32x4& s1) {
                 const bf16x8 pf = pl[wave][sb][lane];
-                // base-2 scores minus the running maximum
                 float m1 = nM[sb];
                 asm volatile("" : "+v"(m1));   // rebuilt per use, not hoisted
                 const f32x4 c4 = {m1, m1, m1, m1};
-                const f32x4 s0 = mfma(ka[0], pf, c4);
-                const f32x4 s1 = mfma(ka[1], pf, c4);
+                s0 = mfma(ka[0], pf, c4);
+                s1 = mfma(ka[1], pf, c4);
+            };
+            // the products of block sb + 1 are issued before the weights of
+            // block sb, which then overlap them (a block's running maximum is
+            // its own, so the exact path of sb does not touch them)
+            f32x4 s0, s1;
+            scores(0, s0, s1);
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb) {
+                f32x4 s0n, s1n;
+                if (sb + 1 < NSB) scores(sb + 1, s0n, s1n);
                 float p[8];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -341,6 +350,10 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
                 Zs[sb] = fmaf(Zs[sb], f, zadd);
                 acc[sb][0] = mfma(vt[0], pk, acc[sb][0]);
                 acc[sb][1] = mfma(vt[1], pk, acc[sb][1]);
+                if (sb + 1 < NSB) {
+                    s0 = s0n;
+                    s1 = s1n;
+                }
             }
         };
 
