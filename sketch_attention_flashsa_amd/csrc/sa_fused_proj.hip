@@ -293,15 +293,21 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
                 s0 = mfma(ka[0], pf, c4);
                 s1 = mfma(ka[1], pf, c4);
             };
-            // the products of block sb + 1 are issued before the weights of
-            // block sb, which then overlap them (a block's running maximum is
-            // its own, so the exact path of sb does not touch them)
+            // the products of block sb + 1 and the aggregation of block sb - 1
+            // are issued before the weights of block sb, which then overlap
+            // them (a block's running maximum and sums are its own, so the
+            // exact path of sb touches neither)
             f32x4 s0, s1;
             scores(0, s0, s1);
+            bf16x8 pkp;   // the previous block's weights, aggregated one block late
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
                 f32x4 s0n, s1n;
                 if (sb + 1 < NSB) scores(sb + 1, s0n, s1n);
+                if (sb > 0) {
+                    acc[sb - 1][0] = mfma(vt[0], pkp, acc[sb - 1][0]);
+                    acc[sb - 1][1] = mfma(vt[1], pkp, acc[sb - 1][1]);
+                }
                 float p[8];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -348,13 +354,14 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
                     acc[sb][1] *= f;
                 }
                 Zs[sb] = fmaf(Zs[sb], f, zadd);
-                acc[sb][0] = mfma(vt[0], pk, acc[sb][0]);
-                acc[sb][1] = mfma(vt[1], pk, acc[sb][1]);
+                pkp = pk;
                 if (sb + 1 < NSB) {
                     s0 = s0n;
                     s1 = s1n;
                 }
             }
+            acc[NSB - 1][0] = mfma(vt[0], pkp, acc[NSB - 1][0]);
+            acc[NSB - 1][1] = mfma(vt[1], pkp, acc[NSB - 1][1]);
         };
 
 #pragma unroll
