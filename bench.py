@@ -538,7 +538,7 @@ def bench_production(args):
                    "dh": dh, "d_model": dm, "layout": "packed", "parallelism": "single GPU"},
         "roofline": {
             "bound": "mfma",
-            "kernel": "prototype fold + sa_bf16_stream_kernel (dh = 128) + merge",
+            "kernel": "prototype fold + sa_bf16_stream_d128_kernel + merge",
             "achieved": tflops,
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
