@@ -1,6 +1,6 @@
 """Build libsketchattn.so in-tree with hipcc for gfx950.
 
-    python -m sketch_attention_flashsa_amd.build [-j N]
+    python -m sketch_attention_flashsa_amd.build [-j N] [--diag]
 
 Every HIP source under csrc/ is compiled to an object in parallel, then the
 objects are linked into ``sketch_attention_flashsa_amd/libsketchattn.so``.
@@ -89,8 +89,30 @@ def build(jobs: int = 8, extra: list[str] | None = None, verbose: bool = False,
     return lib
 
 
+DIAG = os.path.join(PKG, "diag")
+
+
+def build_diag(verbose: bool = False) -> list[str]:
+    """Compile the stand-alone measurement programs under diag/ (each .hip
+    into an executable of the same name beside it); return their paths."""
+    outs = []
+    for src in sorted(glob.glob(os.path.join(DIAG, "*.hip"))):
+        exe = src[:-4]
+        cmd = [_hipcc(), *[f for f in FLAGS if f != "-fPIC"], src, "-o", exe]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        outs.append(exe)
+        if verbose:
+            print(f"built {exe}")
+    return outs
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("-j", type=int, default=8)
+    ap.add_argument("--diag", action="store_true", help="also build the measurement programs under diag/")
     args = ap.parse_args()
     build(jobs=args.j, verbose=True)
+    if args.diag:
+        build_diag(verbose=True)

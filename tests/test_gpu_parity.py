@@ -322,15 +322,16 @@ def test_dh128_pipeline_segments_and_moving_maximum(ramp, masked, unit_scale):
         assert_lse(lse, lo, "bf16", f"dh=128 ramp {ramp} masked {masked} chunk {chunk}")
 
 
-@pytest.mark.parametrize("H,m,dh", [(8, 128, 64), (8, 64, 32), (1, 256, 128)])
-def test_streaming_lse_with_large_scores(H, m, dh):
+@pytest.mark.parametrize("H,m,dh,mask_p", [(8, 128, 64, 0.0), (8, 64, 32, 0.0), (1, 256, 128, 0.0),
+                                            (8, 128, 64, 0.3), (1, 256, 128, 0.3)])
+def test_streaming_lse_with_large_scores(H, m, dh, mask_p):
     """Scores of several hundred on the streaming kernels' shapes at the
     default scale: with the lse requested the kernels scale unrounded
     products (a prototype rounded once to bf16 after scaling would shift its
     lse by about 2^-9 of the scores), so lse meets its bar; S computed with
     and without the lse agrees to the bf16 bar."""
     lengths = [700, 33, 1300, 1]
-    w = W.random_case(141 + dh + m, B=len(lengths), H=H, m=m, dh=dh, lengths=lengths, dtype="bf16")
+    w = W.random_case(141 + dh + m, B=len(lengths), H=H, m=m, dh=dh, lengths=lengths, dtype="bf16", mask_p=mask_p)
     P = w["P"].float()
     K = w["K"].float()
     P[:, :, 0] = 4.0
@@ -346,7 +347,8 @@ def test_streaming_lse_with_large_scores(H, m, dh):
     assert_parity(S, So, "bf16", f"large scores H={H} m={m} dh={dh}")
     assert_lse(lse, lo, "bf16", f"large scores H={H} m={m} dh={dh}")
     d = to_dev(w, device())
-    S2 = sa.sa_forward(d["P"], d["K"], d["V"], cu_offsets=d["cu_offsets"])
+    S2 = sa.sa_forward(d["P"], d["K"], d["V"], cu_offsets=d["cu_offsets"],
+                       mask=d.get("mask"))
     torch.cuda.synchronize()
     assert_parity(S2.double().cpu().numpy(), So, "bf16", f"large scores without lse H={H} m={m} dh={dh}")
 

@@ -2,8 +2,8 @@
 and plan over the library's own per-device workspace array instead of a
 caller workspace, so the outputs must be bitwise equal.  Two calls in a row,
 the second on a smaller input (the array keeps the first call's contents),
-on the streaming kernel (both axes), the register-staged kernel and the fp32
-kernel; and a problem beyond the array is rejected before anything runs."""
+on the streaming kernels (both axes, and the pipelined dh = 128 one), the
+register-staged kernel and the fp32 kernel; and a problem beyond the array is rejected before anything runs."""
 import ctypes
 
 import numpy as np
@@ -46,6 +46,7 @@ def _both(w, norm):
     ("bf16", 8, 128, 64, "history", "packed", [30011, 1, 0, 20000, 4097], [700, 33]),
     ("bf16", 8, 128, 64, "prototype", "packed", [9000, 0, 2500], [64, 1, 31]),
     ("bf16", 3, 48, 32, "history", "dense", [4000, 17, 2100], [40, 0]),
+    ("bf16", 1, 256, 128, "history", "packed", [5000, 1, 777], [40, 3]),
     ("f32", 2, 16, 32, "history", "packed", [3000, 1, 999], [5]),
 ])
 def test_noalloc_equals_sa_forward_two_calls(dtype, H, m, dh, norm, layout, big, small):
