@@ -168,7 +168,12 @@ int32_t sa_check_offsets_host(const int32_t* cu_offsets_host, int32_t B, int64_t
  *             log-sum-exp of the scaled scores over the user's valid rows
  *             (-inf for empty users).  PROTOTYPE: [total_rows, H], the
  *             log-sum-exp over the m prototypes of each row (-inf for rows
- *             that are masked or belong to no user).
+ *             that are masked or belong to no user).  Requesting it makes
+ *             the bf16 kernels apply the scale to unrounded score products
+ *             (without it they may fold the scale into the prototypes,
+ *             rounded once to bf16, which shifts a normaliser by about 2^-9
+ *             of the scores but cancels in S); S from the two agrees within
+ *             the bf16 tolerance, not bitwise.
  * workspace   device scratch of at least sa_forward_workspace_size(pb)
  *             bytes, 256-byte aligned; contents need no initialisation and
  *             are clobbered.  May be NULL when the query returns 0.
