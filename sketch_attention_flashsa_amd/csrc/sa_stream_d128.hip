@@ -16,8 +16,9 @@
 // aggregation products, so nothing overlaps.  Here each step of the stage
 // loop forms the weights of stage t while the score products of stage t + 1
 // run (they depend only on the prototypes and K), then aggregates stage t:
-//   step t: [barrier: stage t + 1 in LDS] issue stage t + kS - 1;
-//           V^T(t), K(t + 1) reads; weights(t) || scores(t + 1); aggregate(t).
+//   step t: weights(t) || scores(t + 1) (K fragments read in step t - 1),
+//           V^T(t) reads; [barrier: stage t + 2 in LDS, slot t free] issue
+//           stage t + kS into slot t, read K(t + 2); aggregate(t).
 // The scores of stage t + 1 are taken against the running maximum as it was
 // before stage t's weights; on the rare exact path, where stage t moves the
 // maximum from M to M', they are shifted by M - M' (fp32 adds) so that the
@@ -25,8 +26,9 @@
 //
 // Block = one row range x 256 prototypes of one head (8 waves, two per SIMD,
 // one block per CU: a wave needs up to 256 registers), m / 256 blocks per
-// head.  The ring holds kS stages of K and V (16 KB each); kS - 3 stages are
-// in flight while a step computes (two stages are read by it).
+// head.  The ring holds kS stages of K and V (16 KB each); a step reads two
+// of them, and up to kS - 2 are in flight.  Four slots measured fastest
+// (three to eight tried: deeper rings were 1-3 % slower).
 #include "sa_device.h"
 #include "sa_stream_d128.h"
 
@@ -36,7 +38,7 @@ using namespace dev;
 
 namespace {
 
-constexpr int kS = 6;                      // ring slots
+constexpr int kS = 4;                      // ring slots
 constexpr int kNW = 8;                     // waves per block
 constexpr int kDH = 128;
 constexpr int kCPR = kDH / 8;              // 16-byte chunks per row per tensor
@@ -440,14 +442,10 @@ __global__ __launch_bounds__(kNW * 64, 2) void sa_bf16_stream_d128_kernel(FwdArg
             kreads(1, kf);
         }
         int t = 0;
-        static_assert(S == 6, "the step loop is unrolled by the ring size");
+        // unrolled by the ring size, so that every slot offset is a literal
         for (; t + S < ntiles; t += S) {
-            step(t, 0, 2, Next{});
-            step(t + 1, 1, 3, Next{});
-            step(t + 2, 2, 4, Next{});
-            step(t + 3, 3, 5, Next{});
-            step(t + 4, 4, 0, Next{});
-            step(t + 5, 5, 1, Next{});
+#pragma unroll
+            for (int i = 0; i < S; ++i) step(t + i, i, (i + 2) % S, Next{});
         }
         // at most S - 1 more steps with a next stage, then the last stage
         for (; t + 1 < ntiles; ++t) {

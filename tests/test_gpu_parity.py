@@ -149,7 +149,7 @@ def test_mask_poisoned_rows_bit_exact(dtype):
     assert np.array_equal(S4, S5), "all-ones mask must equal no mask"
 
 
-@pytest.mark.parametrize("H,m,dh", [(8, 128, 64), (8, 64, 32)])
+@pytest.mark.parametrize("H,m,dh", [(8, 128, 64), (8, 64, 32), (1, 256, 128)])
 @pytest.mark.parametrize("norm", ["history", "prototype"])
 def test_streaming_kernel_masks_bit_exact(H, m, dh, norm):
     """The same properties on shapes the streaming kernel serves (its masked
@@ -159,7 +159,9 @@ def test_streaming_kernel_masks_bit_exact(H, m, dh, norm):
     lengths = [700, 1, 33, 1000, 64, 0, 95]
     w = W.random_case(120 + dh, B=len(lengths), H=H, m=m, dh=dh, lengths=lengths, dtype="bf16", mask_p=0.3)
     pb = sa.make_problem(w["B"], H, m, dh, w["K"].shape[0], dtype="bf16", norm=norm)
-    assert sa.sa_forward_kernel_name(pb) == ("sa_bf16_stream_kernel" if norm == "history" else "sa_proto_stream_kernel")
+    expect = {("history", False): "sa_bf16_stream_kernel", ("history", True): "sa_bf16_stream_d128_kernel",
+              ("prototype", False): "sa_proto_stream_kernel", ("prototype", True): "sa_bf16_stream_kernel"}
+    assert sa.sa_forward_kernel_name(pb) == expect[(norm, dh == 128)]
     S_ref, l_ref = run(w, norm=norm)
     So, lo = _oracle(w, norm=norm)
     assert_parity(S_ref, So, "bf16", f"streaming masked {norm} dh={dh}")
