@@ -329,17 +329,19 @@ __global__ __launch_bounds__(kNW * 64, 2) void sa_bf16_stream_d128_kernel(FwdArg
             // fast path: the running maximum stays, Z += the stage's sum
             bf16x8 pk[NSB];
             float zt[NSB], f[NSB];
-            bool fits = true;
+            // lanes whose sums fit (false for NaN and Inf too) and whose
+            // prototypes have met a valid row, as compare masks (ordered <=
+            // and >=) ANDed on the scalar unit: no lane boolean is formed
+            uint64_t fits = ~0ull;
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
                 pk[sb] = cat8(q[sb][0], q[sb][1], q[sb][2], q[sb][3]);
                 zt[sb] = dot2sum(q[sb][3], dot2sum(q[sb][2], dot2sum(q[sb][1], dot2sum(q[sb][0], 0.f))));
                 f[sb] = 1.f;
-                // false for NaN and Inf too, and before the first valid row
-                fits = fits && (zt[sb] <= kLazyBound) && (Zs[sb] >= 0.f);
+                fits &= __builtin_amdgcn_fcmpf(zt[sb], kLazyBound, 5) & __builtin_amdgcn_fcmpf(Zs[sb], 0.f, 3);
             }
             // rare exact path: validity, running-maximum update, rescale
-            if (__builtin_expect(!(__all(fits) && seg_full), 0)) {
+            if (__builtin_expect(!(fits == ~0ull && seg_full), 0)) {
                 // the stage's scores again (its K is still in the ring): the
                 // same products as before, so that the fast path need not keep
                 // them alive past its exps
