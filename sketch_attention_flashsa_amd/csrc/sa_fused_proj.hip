@@ -355,13 +355,13 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
                     const bf16x2 q0 = pack2(p[0], p[1]), q1 = pack2(p[2], p[3]);
                     const bf16x2 q2 = pack2(p[4], p[5]), q3 = pack2(p[6], p[7]);
                     bf16x8 pk = cat8(q0, q1, q2, q3);
-                    // fast path: the running maximum stays; Z += the tile's sum
-                    float zadd = dot2sum(q3, dot2sum(q2, dot2sum(q1, dot2sum(q0, 0.f))));
-                    float f = 1.f;
-                    // lanes whose sum fits (false for NaN and Inf too) and whose
-                    // prototype has met a valid row, as compare masks (ordered
-                    // <= and >=), so no lane boolean is formed
-                    const uint64_t fits = __builtin_amdgcn_fcmpf(zadd, kLazyBound, 5) &
+                    // fast path: the running maximum stays; Z += the tile's sum,
+                    // summed straight onto Z (the tile's own sum is znew - Z)
+                    float znew = dot2sum(q3, dot2sum(q2, dot2sum(q1, dot2sum(q0, Zs[sb]))));
+                    // lanes whose tile sum fits (false for NaN and Inf too) and
+                    // whose prototype has met a valid row, as compare masks
+                    // (ordered <= and >=), so no lane boolean is formed
+                    const uint64_t fits = __builtin_amdgcn_fcmpf(znew - Zs[sb], kLazyBound, 5) &
                                           __builtin_amdgcn_fcmpf(Zs[sb], 0.f, 3);
                     // rare exact path (then-only, so the common path keeps its
                     // values in place): validity, running-maximum update, rescale
@@ -382,19 +382,20 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
                         const float Mnew = none ? tm : fmaxf(Mold, tm);
                         const bool found = Mnew != -INFINITY;   // the prototype has a valid row
                         const float Mset = found ? Mnew : 0.f;
-                        f = none ? 0.f : (Mset == Mold ? 1.f : __builtin_amdgcn_exp2f(Mold - Mset));
+                        const float f = none ? 0.f : (Mset == Mold ? 1.f : __builtin_amdgcn_exp2f(Mold - Mset));
 #pragma unroll
                         for (int j = 0; j < 8; ++j) p[j] = ((vj >> j) & 1) ? __builtin_amdgcn_exp2f(x[j] - Mset) : 0.f;
                         const bf16x2 e0 = pack2(p[0], p[1]), e1 = pack2(p[2], p[3]);
                         const bf16x2 e2 = pack2(p[4], p[5]), e3 = pack2(p[6], p[7]);
                         pk = cat8(e0, e1, e2, e3);
-                        zadd = dot2sum(e3, dot2sum(e2, dot2sum(e1, dot2sum(e0, 0.f))));
+                        float zadd = dot2sum(e3, dot2sum(e2, dot2sum(e1, dot2sum(e0, 0.f))));
                         if (none && !found) zadd = -1.f;        // Zs = -1 * 0 - 1 keeps the sentinel
                         nM[sb] = -Mset;
                         acc[sb][0] *= f;
                         acc[sb][1] *= f;
+                        znew = fmaf(Zs[sb], f, zadd);
                     }
-                    Zs[sb] = fmaf(Zs[sb], f, zadd);
+                    Zs[sb] = znew;
                     pkp = pk;
                     if (sb + 1 < NSB) {
                         s0 = s0n;

@@ -328,17 +328,18 @@ __global__ __launch_bounds__(kNW * 64, 2) void sa_bf16_stream_d128_kernel(FwdArg
             }
             // fast path: the running maximum stays, Z += the stage's sum
             bf16x8 pk[NSB];
-            float zt[NSB], f[NSB];
-            // lanes whose sums fit (false for NaN and Inf too) and whose
+            // the stage's sums added straight onto Z (the stage's own sum is
+            // zn - Z)
+            float zn[NSB];
+            // lanes whose stage sums fit (false for NaN and Inf too) and whose
             // prototypes have met a valid row, as compare masks (ordered <=
             // and >=) ANDed on the scalar unit: no lane boolean is formed
             uint64_t fits = ~0ull;
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
                 pk[sb] = cat8(q[sb][0], q[sb][1], q[sb][2], q[sb][3]);
-                zt[sb] = dot2sum(q[sb][3], dot2sum(q[sb][2], dot2sum(q[sb][1], dot2sum(q[sb][0], 0.f))));
-                f[sb] = 1.f;
-                fits &= __builtin_amdgcn_fcmpf(zt[sb], kLazyBound, 5) & __builtin_amdgcn_fcmpf(Zs[sb], 0.f, 3);
+                zn[sb] = dot2sum(q[sb][3], dot2sum(q[sb][2], dot2sum(q[sb][1], dot2sum(q[sb][0], Zs[sb]))));
+                fits &= __builtin_amdgcn_fcmpf(zn[sb] - Zs[sb], kLazyBound, 5) & __builtin_amdgcn_fcmpf(Zs[sb], 0.f, 3);
             }
             // rare exact path: validity, running-maximum update, rescale
             if (__builtin_expect(!(fits == ~0ull && seg_full), 0)) {
@@ -363,8 +364,8 @@ __global__ __launch_bounds__(kNW * 64, 2) void sa_bf16_stream_d128_kernel(FwdArg
                     const float Mnew = none ? tm : fmaxf(Mold, tm);
                     const bool found = Mnew != -INFINITY;   // the prototype has a valid row
                     const float Mset = found ? Mnew : 0.f;
-                    f[sb] = none ? 0.f
-                                 : (Mset == Mold ? 1.f : __builtin_amdgcn_exp2f(EXACT ? (Mold - Mset) * a.c : Mold - Mset));
+                    const float f = none ? 0.f
+                                         : (Mset == Mold ? 1.f : __builtin_amdgcn_exp2f(EXACT ? (Mold - Mset) * a.c : Mold - Mset));
                     float p[8];
 #pragma unroll
                     for (int j = 0; j < 8; ++j)
@@ -372,8 +373,9 @@ __global__ __launch_bounds__(kNW * 64, 2) void sa_bf16_stream_d128_kernel(FwdArg
                     const bf16x2 e0 = pack2(p[0], p[1]), e1 = pack2(p[2], p[3]);
                     const bf16x2 e2 = pack2(p[4], p[5]), e3 = pack2(p[6], p[7]);
                     pk[sb] = cat8(e0, e1, e2, e3);
-                    zt[sb] = dot2sum(e3, dot2sum(e2, dot2sum(e1, dot2sum(e0, 0.f))));
-                    if (none && !found) zt[sb] = -1.f;      // Zs = -1 * 0 - 1 keeps the sentinel
+                    float zt = dot2sum(e3, dot2sum(e2, dot2sum(e1, dot2sum(e0, 0.f))));
+                    if (none && !found) zt = -1.f;          // Zs = -1 * 0 - 1 keeps the sentinel
+                    zn[sb] = fmaf(Zs[sb], f, zt);
                     nM[sb] = (f32x4){-Mset, -Mset, -Mset, -Mset};
                     if constexpr (NEXT) {
                         // the next stage's products were taken against Mold
@@ -382,11 +384,11 @@ __global__ __launch_bounds__(kNW * 64, 2) void sa_bf16_stream_d128_kernel(FwdArg
                         sn[1][sb] += sh;
                     }
 #pragma unroll
-                    for (int db = 0; db < DB; ++db) acc[sb][db] *= f[sb];
+                    for (int db = 0; db < DB; ++db) acc[sb][db] *= f;
                 }
             }
 #pragma unroll
-            for (int sb = 0; sb < NSB; ++sb) Zs[sb] = fmaf(Zs[sb], f[sb], zt[sb]);
+            for (int sb = 0; sb < NSB; ++sb) Zs[sb] = zn[sb];
             if constexpr (NEXT) {
                 // this wave's reads of slot t (V^T above, K again on the exact
                 // path) have completed; wait for its part of stage t + 2 (stages
