@@ -193,288 +193,289 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
     // the segment loop, compiled once per role so that the two roles' loop
     // state (accumulators, running maxima) never meets at a branch join
     auto segments = [&](auto role_c) {
-    constexpr int ROLE = decltype(role_c)::value;
-    int b = a.users.find(v_lo);
-    for (; b < a.users.B; ++b) {
-        const int64_t us = a.users.vstart(b), ue = a.users.vstart(b + 1);
-        if (us >= v_hi) break;
-        const int64_t s_lo = max(v_lo, us), s_hi = min(v_hi, ue);
-        if (s_hi <= s_lo) continue;
-        if (a.q_batch_stride != 0) load_p(b);
-        const int64_t gbase = a.users.row_base(b) + (s_lo - us);
-        const int64_t nrows = s_hi - s_lo;
-        const int ntiles = (int)((nrows + 31) / 32);
-        const int nrows32 = (int)nrows;
-        const unsigned char* xseg = Xg + gbase * ROWB;
+        constexpr int ROLE = decltype(role_c)::value;
+        int b = a.users.find(v_lo);
+        for (; b < a.users.B; ++b) {
+            const int64_t us = a.users.vstart(b), ue = a.users.vstart(b + 1);
+            if (us >= v_hi) break;
+            const int64_t s_lo = max(v_lo, us), s_hi = min(v_hi, ue);
+            if (s_hi <= s_lo) continue;
+            if (a.q_batch_stride != 0) load_p(b);
+            const int64_t gbase = a.users.row_base(b) + (s_lo - us);
+            const int64_t nrows = s_hi - s_lo;
+            const int ntiles = (int)((nrows + 31) / 32);
+            const int nrows32 = (int)nrows;
+            const unsigned char* xseg = Xg + gbase * ROWB;
 
-        // tile t: lane fetches row min(dma_row, last row of the segment) of
-        // the tile (rows past the end re-read the last row; they are invalid)
-        auto issue = [&](int t) {
-            const uint32_t slot_lds = ring_lds + (uint32_t)((t % S) * STAGE) + (uint32_t)(wave * D * 1024);
-            const int r0 = t * 32;
-            const unsigned char* tbase = xseg + (int64_t)r0 * ROWB;
-            const int last = nrows32 - 1 - r0;
+            // tile t: lane fetches row min(dma_row, last row of the segment) of
+            // the tile (rows past the end re-read the last row; they are invalid)
+            auto issue = [&](int t) {
+                const uint32_t slot_lds = ring_lds + (uint32_t)((t % S) * STAGE) + (uint32_t)(wave * D * 1024);
+                const int r0 = t * 32;
+                const unsigned char* tbase = xseg + (int64_t)r0 * ROWB;
+                const int last = nrows32 - 1 - r0;
 #pragma unroll
-            for (int d = 0; d < D; ++d) {
-                const uint32_t voff = (uint32_t)(min(dma_row[d], last) * ROWB + dma_off[d]);
-                dma16c(tbase, voff, __builtin_amdgcn_readfirstlane(slot_lds + d * 1024));
-            }
-            if constexpr (MDMA) {
-                // lane -> row (lane % 32) clamped to the segment: the aligned
-                // word around its mask byte (never leaves the byte's page)
-                const uintptr_t m0 = (uintptr_t)(a.mask + gbase + r0);
-                const int rr = min(lane & 31, last);
-                dma4c((const void*)(m0 & ~(uintptr_t)3), (uint32_t)((int)(m0 & 3) + rr) & ~3u,
-                      __builtin_amdgcn_readfirstlane(mk_lds + (uint32_t)(((t % S) * kFWaves + wave) * 256)));
-            }
-        };
-        auto tile_valid = [&](int t) -> uint32_t {
-            const int64_t r0 = (int64_t)t * 32;
-            const int rows_here = (int)min((int64_t)32, nrows - r0);
-            bool v = lane < rows_here;
-            if constexpr (MDMA) {
-                // the tile's mask words arrived with it (this wave's own copy)
-                const uint32_t m0 = (uint32_t)((uintptr_t)(a.mask + gbase + r0) & 3);
-                const int sh = 8 * (int)((m0 + (uint32_t)min(lane & 31, rows_here - 1)) & 3);
-                const uint32_t wd = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)(
-                    mk_lds + (uint32_t)(((t % S) * kFWaves + wave) * 256 + 4 * lane));
-                v = v && ((wd >> sh) & 0xffu) != 0;
-            } else if constexpr (MASKED) {
-                v = v && a.mask[gbase + r0 + min(lane, rows_here - 1)] != 0;
-            }
-            return (uint32_t)__ballot(v);
-        };
-
-        // the running maximum M of each of the lane's prototypes is kept
-        // negated and broadcast into the score products' accumulator input
-        // (one scalar per block: the four-wide tuples would not fit beside
-        // the weight fragments); until the prototype meets a valid row M = 0
-        // and Zs = -1, which sends every tile to the exact path that sets M
-        float nM[NSB];
-        float Zs[NSB];
-        f32x4 acc[NSB][2];
-#pragma unroll
-        for (int sb = 0; sb < NSB; ++sb) {
-            nM[sb] = 0.f;
-            Zs[sb] = -1.f;
-            acc[sb][0] = acc[sb][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        }
-
-        // one step t: the softmax of tile t - 1 (ATT; its K and V were
-        // published in step t - 1) and the projection of tile t (PROJ), the
-        // projection's products spread over the prototype blocks beside each
-        // block's weights: only a wave's own vector instructions overlap its
-        // matrix products.  Projection unit u = (chunk kc = u / 2, row block
-        // rb = u % 2): one X fragment, two products.
-        constexpr int UPB = 2 * KCX / NSB;   // projection units per prototype block
-        static_assert(UPB >= 1 && UPB * NSB == 2 * KCX, "projection units per block");
-        uint32_t valid_prev = 0;
-        bf16x8 pn[2];                         // prototype blocks 0 and 1, read at the end of the step before
-        pn[0] = pl[wave][0][lane];
-        pn[1] = pl[wave][NSB > 1 ? 1 : 0][lane];
-        auto xread = [&](int t, int u) {
-            const int kc = u >> 1, rb = u & 1;
-            const uint32_t slot = ring_lds + (uint32_t)((t % S) * STAGE);
-            return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(
-                slot + xoff[kc & 3] + (uint32_t)(rb * 16 * ROWB + 256 * (kc >> 2)));
-        };
-        auto step = [&](auto att_c, auto proj_c, int t) {
-            constexpr bool ATT = decltype(att_c)::value != 0;
-            constexpr bool PROJ = decltype(proj_c)::value != 0;
-            bf16x8 ka[2], vt[2];
-            if constexpr (ATT) {
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    ka[i] = xchg[(t - 1) & 1][hl][0][i][lane];
-                    vt[i] = xchg[(t - 1) & 1][hl][1][i][lane];
+                for (int d = 0; d < D; ++d) {
+                    const uint32_t voff = (uint32_t)(min(dma_row[d], last) * ROWB + dma_off[d]);
+                    dma16c(tbase, voff, __builtin_amdgcn_readfirstlane(slot_lds + d * 1024));
                 }
-            }
-            const uint32_t vj = lane_slots(valid_prev, g);
-            const uint32_t valid = PROJ ? tile_valid(t) : 0u;
-            // projection accumulators: role 0 K^T[db][rb], role 1 V[rb][db]
-            f32x4 r[2][2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) r[i][0] = r[i][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            auto punit = [&](int u, const bf16x8& xf) {
-                const int kc = u >> 1, rb = u & 1;
-#pragma unroll
-                for (int db = 0; db < 2; ++db) {
-                    if constexpr (ROLE == 0) r[db][rb] = mfma(wf[db][kc], xf, r[db][rb]);
-                    else r[rb][db] = mfma(xf, wf[db][kc], r[rb][db]);
+                if constexpr (MDMA) {
+                    // lane -> row (lane % 32) clamped to the segment: the aligned
+                    // word around its mask byte (never leaves the byte's page)
+                    const uintptr_t m0 = (uintptr_t)(a.mask + gbase + r0);
+                    const int rr = min(lane & 31, last);
+                    dma4c((const void*)(m0 & ~(uintptr_t)3), (uint32_t)((int)(m0 & 3) + rr) & ~3u,
+                          __builtin_amdgcn_readfirstlane(mk_lds + (uint32_t)(((t % S) * kFWaves + wave) * 256)));
                 }
             };
-            // the first block's X fragments; the others are read in their
-            // block (one block ahead would not fit the registers)
-            bf16x8 xq[UPB];
-            if constexpr (PROJ) {
-#pragma unroll
-                for (int i = 0; i < UPB; ++i) xq[i] = xread(t, i);
-            }
-            // prototype fragments: block sb's is read during block sb - 2
-            bf16x8 pf[NSB];
-            pf[0] = pn[0];
-            if constexpr (NSB > 1) pf[1] = pn[1];
-            // base-2 scores minus the running maximum of block sb
-            auto scores = [&](int sb, f32x4& s0, f32x4& s1) {
-                float m1 = nM[sb];
-                asm volatile("" : "+v"(m1));   // rebuilt per use, not hoisted
-                const f32x4 c4 = {m1, m1, m1, m1};
-                s0 = mfma(ka[0], pf[sb], c4);
-                s1 = mfma(ka[1], pf[sb], c4);
+            auto tile_valid = [&](int t) -> uint32_t {
+                const int64_t r0 = (int64_t)t * 32;
+                const int rows_here = (int)min((int64_t)32, nrows - r0);
+                bool v = lane < rows_here;
+                if constexpr (MDMA) {
+                    // the tile's mask words arrived with it (this wave's own copy)
+                    const uint32_t m0 = (uint32_t)((uintptr_t)(a.mask + gbase + r0) & 3);
+                    const int sh = 8 * (int)((m0 + (uint32_t)min(lane & 31, rows_here - 1)) & 3);
+                    const uint32_t wd = *(const __attribute__((address_space(3))) uint32_t*)(uintptr_t)(
+                        mk_lds + (uint32_t)(((t % S) * kFWaves + wave) * 256 + 4 * lane));
+                    v = v && ((wd >> sh) & 0xffu) != 0;
+                } else if constexpr (MASKED) {
+                    v = v && a.mask[gbase + r0 + min(lane, rows_here - 1)] != 0;
+                }
+                return (uint32_t)__ballot(v);
             };
-            f32x4 s0, s1;
-            if constexpr (ATT) scores(0, s0, s1);
-            bf16x8 pkp;   // the previous block's weights, aggregated one block late
+
+            // the running maximum M of each of the lane's prototypes is kept
+            // negated and broadcast into the score products' accumulator input
+            // (one scalar per block: the four-wide tuples would not fit beside
+            // the weight fragments); until the prototype meets a valid row M = 0
+            // and Zs = -1, which sends every tile to the exact path that sets M
+            float nM[NSB];
+            float Zs[NSB];
+            f32x4 acc[NSB][2];
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
-                // the products of block sb + 1, a share of the projection and
-                // the aggregation of block sb - 1 go before the weights of
-                // block sb, which then overlap them (a block's running maximum
-                // and sums are its own, so the exact path of sb touches none)
-                __builtin_amdgcn_sched_barrier(0);
-                f32x4 s0n, s1n;
+                nM[sb] = 0.f;
+                Zs[sb] = -1.f;
+                acc[sb][0] = acc[sb][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            }
+
+            // one step t: the softmax of tile t - 1 (ATT; its K and V were
+            // published in step t - 1) and the projection of tile t (PROJ), the
+            // projection's products spread over the prototype blocks beside each
+            // block's weights: only a wave's own vector instructions overlap its
+            // matrix products.  Projection unit u = (chunk kc = u / 2, row block
+            // rb = u % 2): one X fragment, two products.
+            constexpr int UPB = 2 * KCX / NSB;   // projection units per prototype block
+            static_assert(UPB >= 1 && UPB * NSB == 2 * KCX, "projection units per block");
+            uint32_t valid_prev = 0;
+            bf16x8 pn[2];                         // prototype blocks 0 and 1, read at the end of the step before
+            pn[0] = pl[wave][0][lane];
+            pn[1] = pl[wave][NSB > 1 ? 1 : 0][lane];
+            auto xread = [&](int t, int u) {
+                const int kc = u >> 1, rb = u & 1;
+                const uint32_t slot = ring_lds + (uint32_t)((t % S) * STAGE);
+                return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(
+                    slot + xoff[kc & 3] + (uint32_t)(rb * 16 * ROWB + 256 * (kc >> 2)));
+            };
+            auto step = [&](auto att_c, auto proj_c, int t) {
+                constexpr bool ATT = decltype(att_c)::value != 0;
+                constexpr bool PROJ = decltype(proj_c)::value != 0;
+                bf16x8 ka[2], vt[2];
                 if constexpr (ATT) {
-                    if (sb + 1 < NSB) scores(sb + 1, s0n, s1n);
-                    if (sb + 2 < NSB) pf[sb + 2] = pl[wave][sb + 2][lane];
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        ka[i] = xchg[(t - 1) & 1][hl][0][i][lane];
+                        vt[i] = xchg[(t - 1) & 1][hl][1][i][lane];
+                    }
                 }
+                const uint32_t vj = lane_slots(valid_prev, g);
+                const uint32_t valid = PROJ ? tile_valid(t) : 0u;
+                // projection accumulators: role 0 K^T[db][rb], role 1 V[rb][db]
+                f32x4 r[2][2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) r[i][0] = r[i][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                auto punit = [&](int u, const bf16x8& xf) {
+                    const int kc = u >> 1, rb = u & 1;
+#pragma unroll
+                    for (int db = 0; db < 2; ++db) {
+                        if constexpr (ROLE == 0) r[db][rb] = mfma(wf[db][kc], xf, r[db][rb]);
+                        else r[rb][db] = mfma(xf, wf[db][kc], r[rb][db]);
+                    }
+                };
+                // the first block's X fragments; the others are read in their
+                // block (one block ahead would not fit the registers)
+                bf16x8 xq[UPB];
                 if constexpr (PROJ) {
 #pragma unroll
-                    for (int i = 0; i < UPB; ++i) punit(sb * UPB + i, sb == 0 ? xq[i] : xread(t, sb * UPB + i));
+                    for (int i = 0; i < UPB; ++i) xq[i] = xread(t, i);
                 }
-                if constexpr (ATT) {
-                    if (sb > 0) {
-                        acc[sb - 1][0] = mfma(vt[0], pkp, acc[sb - 1][0]);
-                        acc[sb - 1][1] = mfma(vt[1], pkp, acc[sb - 1][1]);
-                    }
-                    float p[8];
+                // prototype fragments: block sb's is read during block sb - 2
+                bf16x8 pf[NSB];
+                pf[0] = pn[0];
+                if constexpr (NSB > 1) pf[1] = pn[1];
+                // base-2 scores minus the running maximum of block sb
+                auto scores = [&](int sb, f32x4& s0, f32x4& s1) {
+                    float m1 = nM[sb];
+                    asm volatile("" : "+v"(m1));   // rebuilt per use, not hoisted
+                    const f32x4 c4 = {m1, m1, m1, m1};
+                    s0 = mfma(ka[0], pf[sb], c4);
+                    s1 = mfma(ka[1], pf[sb], c4);
+                };
+                f32x4 s0, s1;
+                if constexpr (ATT) scores(0, s0, s1);
+                bf16x8 pkp;   // the previous block's weights, aggregated one block late
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        p[j] = __builtin_amdgcn_exp2f(s0[j]);
-                        p[4 + j] = __builtin_amdgcn_exp2f(s1[j]);
+                for (int sb = 0; sb < NSB; ++sb) {
+                    // the products of block sb + 1, a share of the projection and
+                    // the aggregation of block sb - 1 go before the weights of
+                    // block sb, which then overlap them (a block's running maximum
+                    // and sums are its own, so the exact path of sb touches none)
+                    __builtin_amdgcn_sched_barrier(0);
+                    f32x4 s0n, s1n;
+                    if constexpr (ATT) {
+                        if (sb + 1 < NSB) scores(sb + 1, s0n, s1n);
+                        if (sb + 2 < NSB) pf[sb + 2] = pl[wave][sb + 2][lane];
                     }
-                    const bf16x2 q0 = pack2(p[0], p[1]), q1 = pack2(p[2], p[3]);
-                    const bf16x2 q2 = pack2(p[4], p[5]), q3 = pack2(p[6], p[7]);
-                    bf16x8 pk = cat8(q0, q1, q2, q3);
-                    // fast path: the running maximum stays; Z += the tile's sum,
-                    // summed straight onto Z (the tile's own sum is znew - Z)
-                    float znew = dot2sum(q3, dot2sum(q2, dot2sum(q1, dot2sum(q0, Zs[sb]))));
-                    // lanes whose tile sum fits (false for NaN and Inf too) and
-                    // whose prototype has met a valid row, as compare masks
-                    // (ordered <= and >=), so no lane boolean is formed
-                    const uint64_t fits = __builtin_amdgcn_fcmpf(znew - Zs[sb], kLazyBound, 5) &
-                                          __builtin_amdgcn_fcmpf(Zs[sb], 0.f, 3);
-                    // rare exact path (then-only, so the common path keeps its
-                    // values in place): validity, running-maximum update, rescale
-                    if (__builtin_expect(!(fits == ~0ull && valid_prev == 0xffffffffu), 0)) {
-                        // scores relative to 0 again (the products held s - M)
-                        const float Mold = -nM[sb];
-                        const bool none = Zs[sb] < 0.f;         // no valid row met yet
-                        float x[8];
-                        float tm = -INFINITY;
+                    if constexpr (PROJ) {
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            const float sv = j < 4 ? s0[j] : s1[j - 4];
-                            x[j] = ((vj >> j) & 1) ? sv + Mold : -INFINITY;
-                            tm = fmaxf(tm, x[j]);
+                        for (int i = 0; i < UPB; ++i) punit(sb * UPB + i, sb == 0 ? xq[i] : xread(t, sb * UPB + i));
+                    }
+                    if constexpr (ATT) {
+                        if (sb > 0) {
+                            acc[sb - 1][0] = mfma(vt[0], pkp, acc[sb - 1][0]);
+                            acc[sb - 1][1] = mfma(vt[1], pkp, acc[sb - 1][1]);
                         }
-                        tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
-                        tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
-                        const float Mnew = none ? tm : fmaxf(Mold, tm);
-                        const bool found = Mnew != -INFINITY;   // the prototype has a valid row
-                        const float Mset = found ? Mnew : 0.f;
-                        const float f = none ? 0.f : (Mset == Mold ? 1.f : __builtin_amdgcn_exp2f(Mold - Mset));
+                        float p[8];
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) p[j] = ((vj >> j) & 1) ? __builtin_amdgcn_exp2f(x[j] - Mset) : 0.f;
-                        const bf16x2 e0 = pack2(p[0], p[1]), e1 = pack2(p[2], p[3]);
-                        const bf16x2 e2 = pack2(p[4], p[5]), e3 = pack2(p[6], p[7]);
-                        pk = cat8(e0, e1, e2, e3);
-                        float zadd = dot2sum(e3, dot2sum(e2, dot2sum(e1, dot2sum(e0, 0.f))));
-                        if (none && !found) zadd = -1.f;        // Zs = -1 * 0 - 1 keeps the sentinel
-                        nM[sb] = -Mset;
-                        acc[sb][0] *= f;
-                        acc[sb][1] *= f;
-                        znew = fmaf(Zs[sb], f, zadd);
-                    }
-                    Zs[sb] = znew;
-                    pkp = pk;
-                    if (sb + 1 < NSB) {
-                        s0 = s0n;
-                        s1 = s1n;
-                    }
-                }
-            }
-            if constexpr (ATT) {
-                acc[NSB - 1][0] = mfma(vt[0], pkp, acc[NSB - 1][0]);
-                acc[NSB - 1][1] = mfma(vt[1], pkp, acc[NSB - 1][1]);
-            }
-            if constexpr (PROJ) {
-                // role 0: q = rb, (K^T[0][rb], K^T[1][rb]); role 1: q = db,
-                // (V[0][db], V[1][db]): slot j <- dh or row tok_of(g, j)
-                bf16x8 own[2];
+                        for (int j = 0; j < 4; ++j) {
+                            p[j] = __builtin_amdgcn_exp2f(s0[j]);
+                            p[4 + j] = __builtin_amdgcn_exp2f(s1[j]);
+                        }
+                        const bf16x2 q0 = pack2(p[0], p[1]), q1 = pack2(p[2], p[3]);
+                        const bf16x2 q2 = pack2(p[4], p[5]), q3 = pack2(p[6], p[7]);
+                        bf16x8 pk = cat8(q0, q1, q2, q3);
+                        // fast path: the running maximum stays; Z += the tile's sum,
+                        // summed straight onto Z (the tile's own sum is znew - Z)
+                        float znew = dot2sum(q3, dot2sum(q2, dot2sum(q1, dot2sum(q0, Zs[sb]))));
+                        // lanes whose tile sum fits (false for NaN and Inf too) and
+                        // whose prototype has met a valid row, as compare masks
+                        // (ordered <= and >=), so no lane boolean is formed
+                        const uint64_t fits = __builtin_amdgcn_fcmpf(znew - Zs[sb], kLazyBound, 5) &
+                                              __builtin_amdgcn_fcmpf(Zs[sb], 0.f, 3);
+                        // rare exact path (then-only, so the common path keeps its
+                        // values in place): validity, running-maximum update, rescale
+                        if (__builtin_expect(!(fits == ~0ull && valid_prev == 0xffffffffu), 0)) {
+                            // scores relative to 0 again (the products held s - M)
+                            const float Mold = -nM[sb];
+                            const bool none = Zs[sb] < 0.f;         // no valid row met yet
+                            float x[8];
+                            float tm = -INFINITY;
 #pragma unroll
-                for (int q = 0; q < 2; ++q)
-                    own[q] = cat8(pack2(r[0][q][0], r[0][q][1]), pack2(r[0][q][2], r[0][q][3]),
-                                  pack2(r[1][q][0], r[1][q][1]), pack2(r[1][q][2], r[1][q][3]));
-                if constexpr (ROLE == 1) {
-                    if (valid != 0xffffffffu) {   // invalid rows' values zeroed
-                        const uint32_t vv = lane_slots(valid, g);
-#pragma unroll
-                        for (int q = 0; q < 2; ++q)
+                            for (int j = 0; j < 8; ++j) {
+                                const float sv = j < 4 ? s0[j] : s1[j - 4];
+                                x[j] = ((vj >> j) & 1) ? sv + Mold : -INFINITY;
+                                tm = fmaxf(tm, x[j]);
+                            }
+                            tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
+                            tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+                            const float Mnew = none ? tm : fmaxf(Mold, tm);
+                            const bool found = Mnew != -INFINITY;   // the prototype has a valid row
+                            const float Mset = found ? Mnew : 0.f;
+                            const float f = none ? 0.f : (Mset == Mold ? 1.f : __builtin_amdgcn_exp2f(Mold - Mset));
 #pragma unroll
                             for (int j = 0; j < 8; ++j)
-                                if (!((vv >> j) & 1)) own[q][j] = (bf16)0.0f;
+                                p[j] = ((vj >> j) & 1) ? __builtin_amdgcn_exp2f(x[j] - Mset) : 0.f;
+                            const bf16x2 e0 = pack2(p[0], p[1]), e1 = pack2(p[2], p[3]);
+                            const bf16x2 e2 = pack2(p[4], p[5]), e3 = pack2(p[6], p[7]);
+                            pk = cat8(e0, e1, e2, e3);
+                            float zadd = dot2sum(e3, dot2sum(e2, dot2sum(e1, dot2sum(e0, 0.f))));
+                            if (none && !found) zadd = -1.f;        // Zs = -1 * 0 - 1 keeps the sentinel
+                            nM[sb] = -Mset;
+                            acc[sb][0] *= f;
+                            acc[sb][1] *= f;
+                            znew = fmaf(Zs[sb], f, zadd);
+                        }
+                        Zs[sb] = znew;
+                        pkp = pk;
+                        if (sb + 1 < NSB) {
+                            s0 = s0n;
+                            s1 = s1n;
+                        }
                     }
                 }
-                xchg[t & 1][hl][ROLE][0][lane] = own[0];
-                xchg[t & 1][hl][ROLE][1][lane] = own[1];
-            }
-            // the next step's first two prototype blocks
-            pn[0] = pl[wave][0][lane];
-            if constexpr (NSB > 1) pn[1] = pl[wave][1][lane];
-            valid_prev = valid;
-        };
-
-#pragma unroll
-        for (int t = 0; t < AHEAD; ++t)
-            if (t < ntiles) issue(t);
-
-        auto run = [&](auto att_c, auto proj_c, int t) {
-            if (t < ntiles) wait_after<AHEAD - 1, VMS>(min(AHEAD - 1, ntiles - 1 - t));
-            block_barrier();
-            if (t + AHEAD < ntiles) issue(t + AHEAD);
-            if (active) step(att_c, proj_c, t);
-            // every LDS access of this step has completed before the next barrier
-            wait_lgkm0();
-        };
-        run(Int<0>{}, Int<1>{}, 0);
-        for (int t = 1; t < ntiles; ++t) run(Int<1>{}, Int<1>{}, t);
-        run(Int<1>{}, Int<0>{}, ntiles);
-
-        // ---- segment epilogue: partial statistics at slot w + b
-        if (active) {
-            const int64_t slot = (int64_t)w + b;
-#pragma unroll
-            for (int sb = 0; sb < NSB; ++sb) {
-                const int j = pbase + 16 * sb + l16;
-                const int64_t base = (slot * a.H + head) * a.m + j;
-                float z = fmaxf(Zs[sb], 0.f);     // the -1 of a prototype with no valid row
-                z += __shfl_xor(z, 16, 64);
-                z += __shfl_xor(z, 32, 64);
-                if (g == 0) {
-                    // no valid row in the segment: M = -inf, as the merge expects
-                    a.part.M[base] = z > 0.f ? -nM[sb] : -INFINITY;
-                    a.part.Z[base] = z;
+                if constexpr (ATT) {
+                    acc[NSB - 1][0] = mfma(vt[0], pkp, acc[NSB - 1][0]);
+                    acc[NSB - 1][1] = mfma(vt[1], pkp, acc[NSB - 1][1]);
                 }
+                if constexpr (PROJ) {
+                    // role 0: q = rb, (K^T[0][rb], K^T[1][rb]); role 1: q = db,
+                    // (V[0][db], V[1][db]): slot j <- dh or row tok_of(g, j)
+                    bf16x8 own[2];
 #pragma unroll
-                for (int db = 0; db < 2; ++db)
-                    __builtin_nontemporal_store(
-                        acc[sb][db], (f32x4*)lane_major_acc(a.part, slot, a.H, head, a.m, DH, pbase / 16 + sb, db, lane));
+                    for (int q = 0; q < 2; ++q)
+                        own[q] = cat8(pack2(r[0][q][0], r[0][q][1]), pack2(r[0][q][2], r[0][q][3]),
+                                      pack2(r[1][q][0], r[1][q][1]), pack2(r[1][q][2], r[1][q][3]));
+                    if constexpr (ROLE == 1) {
+                        if (valid != 0xffffffffu) {   // invalid rows' values zeroed
+                            const uint32_t vv = lane_slots(valid, g);
+#pragma unroll
+                            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                                for (int j = 0; j < 8; ++j)
+                                    if (!((vv >> j) & 1)) own[q][j] = (bf16)0.0f;
+                        }
+                    }
+                    xchg[t & 1][hl][ROLE][0][lane] = own[0];
+                    xchg[t & 1][hl][ROLE][1][lane] = own[1];
+                }
+                // the next step's first two prototype blocks
+                pn[0] = pl[wave][0][lane];
+                if constexpr (NSB > 1) pn[1] = pl[wave][1][lane];
+                valid_prev = valid;
+            };
+
+#pragma unroll
+            for (int t = 0; t < AHEAD; ++t)
+                if (t < ntiles) issue(t);
+
+            auto run = [&](auto att_c, auto proj_c, int t) {
+                if (t < ntiles) wait_after<AHEAD - 1, VMS>(min(AHEAD - 1, ntiles - 1 - t));
+                block_barrier();
+                if (t + AHEAD < ntiles) issue(t + AHEAD);
+                if (active) step(att_c, proj_c, t);
+                // every LDS access of this step has completed before the next barrier
+                wait_lgkm0();
+            };
+            run(Int<0>{}, Int<1>{}, 0);
+            for (int t = 1; t < ntiles; ++t) run(Int<1>{}, Int<1>{}, t);
+            run(Int<1>{}, Int<0>{}, ntiles);
+
+            // ---- segment epilogue: partial statistics at slot w + b
+            if (active) {
+                const int64_t slot = (int64_t)w + b;
+#pragma unroll
+                for (int sb = 0; sb < NSB; ++sb) {
+                    const int j = pbase + 16 * sb + l16;
+                    const int64_t base = (slot * a.H + head) * a.m + j;
+                    float z = fmaxf(Zs[sb], 0.f);     // the -1 of a prototype with no valid row
+                    z += __shfl_xor(z, 16, 64);
+                    z += __shfl_xor(z, 32, 64);
+                    if (g == 0) {
+                        // no valid row in the segment: M = -inf, as the merge expects
+                        a.part.M[base] = z > 0.f ? -nM[sb] : -INFINITY;
+                        a.part.Z[base] = z;
+                    }
+#pragma unroll
+                    for (int db = 0; db < 2; ++db)
+                        __builtin_nontemporal_store(acc[sb][db], (f32x4*)lane_major_acc(a.part, slot, a.H, head, a.m, DH,
+                                                                                        pbase / 16 + sb, db, lane));
+                }
             }
+            wait_vm<0>();
+            wait_lgkm0();
+            block_barrier();
         }
-        wait_vm<0>();
-        wait_lgkm0();
-        block_barrier();
-    }
     };
     if (role == 0) segments(Int<0>{});
     else segments(Int<1>{});
