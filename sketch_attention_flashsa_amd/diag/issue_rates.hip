@@ -2,7 +2,8 @@
 // scheduling choices: per SIMD, how many cycles an MFMA (16x16x32 bf16), a
 // v_exp_f32 and a v_fma_f32 take when issued back to back, and what a mix
 // costs when the MFMAs and the vector instructions come from one wave or from
-// different waves of the same SIMD; and the LDS read rate per CU for 16-byte
+// different waves of the same SIMD, and whether a wave's exps and its
+// independent FMAs overlap each other; and the LDS read rate per CU for 16-byte
 // row reads and 8-byte transposed reads.  One block per CU (256 blocks), w
 // waves per SIMD; a block's elapsed shader-clock cycles come from s_memtime
 // around the loop (between two barriers), its clock from s_memrealtime
@@ -10,7 +11,7 @@
 // each thread writes one value so that nothing is optimised away.
 //
 // Build and run: python -m sketch_attention_flashsa_amd.build --diag, then
-// sketch_attention_flashsa_amd/_build/issue_rates (prints one JSON line per
+// sketch_attention_flashsa_amd/diag/issue_rates (prints one JSON line per
 // case).
 #include <hip/hip_runtime.h>
 #include <stdio.h>
@@ -24,7 +25,10 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kIters = 2048;
 
-enum Mode { MFMA = 0, EXP, FMA, MFMA_EXP_SAME, MFMA_FMA_SAME, MFMA_EXP_SPLIT, MFMA_FMA_SPLIT, LDS_B128, LDS_TR_B64 };
+enum Mode {
+    MFMA = 0, EXP, FMA, MFMA_EXP_SAME, MFMA_FMA_SAME, MFMA_EXP_SPLIT, MFMA_FMA_SPLIT, LDS_B128, LDS_TR_B64,
+    EXP_FMA_SAME, MFMA_EXP_FMA_SAME
+};
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -50,8 +54,11 @@ __global__ void rate_kernel(float* out, long long* cyc, long long* rt, float see
     }
     f32x4 c[4];
     for (int i = 0; i < 4; ++i) c[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    float x[8];
-    for (int i = 0; i < 8; ++i) x[i] = seed * (lane + i);
+    float x[8], y[8];
+    for (int i = 0; i < 8; ++i) {
+        x[i] = seed * (lane + i);
+        y[i] = seed * (lane - i);
+    }
     u32x4 acc4 = {0, 0, 0, 0};
     unsigned s0 = 0, s1 = 0;
     if constexpr (MODE == LDS_B128 || MODE == LDS_TR_B64) {
@@ -100,6 +107,26 @@ __global__ void rate_kernel(float* out, long long* cyc, long long* rt, float see
             } else {
                 MFMA4(c)
             }
+        } else if constexpr (MODE == EXP_FMA_SAME) {
+            // eight exps and eight independent FMAs, alternating (the
+            // scheduling barriers keep that order)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                x[i] = __builtin_amdgcn_exp2f(x[i]);
+                y[i] = fmaf(y[i], 1.0001f, 0.5f);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else if constexpr (MODE == MFMA_EXP_FMA_SAME) {
+            // four MFMAs, each followed by two exps and two independent FMAs
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                c[i] = mfma(a, b, c[i]);
+                x[2 * i] = __builtin_amdgcn_exp2f(x[2 * i]);
+                y[2 * i] = fmaf(y[2 * i], 1.0001f, 0.5f);
+                x[2 * i + 1] = __builtin_amdgcn_exp2f(x[2 * i + 1]);
+                y[2 * i + 1] = fmaf(y[2 * i + 1], 1.0001f, 0.5f);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         } else if constexpr (MODE == LDS_B128) {
             // 8 reads of 64 lanes x 16 consecutive bytes (1 KB each)
             const int base = ((it + wave) & 7) * 512;
@@ -125,7 +152,7 @@ __global__ void rate_kernel(float* out, long long* cyc, long long* rt, float see
     __syncthreads();
     const long long c1 = clock64(), r1 = wall_clock64();
     float r = c[0][0] + c[1][1] + c[2][2] + c[3][3];
-    for (int i = 0; i < 8; ++i) r += x[i];
+    for (int i = 0; i < 8; ++i) r += x[i] + y[i];
     r += (float)(acc4[0] ^ acc4[1] ^ acc4[2] ^ acc4[3] ^ s0 ^ s1);
     out[blockIdx.x * blockDim.x + t] = r;
     if (t == 0) {
@@ -190,6 +217,8 @@ int main() {
         {"mfma x4 waves + fma x8 waves (split)", MFMA_FMA_SPLIT, 4, 0, 8, 0, true},
         {"ds_read_b128 x8", LDS_B128, 0, 0, 0, 8 * 1024.0, false},
         {"ds_read_b64_tr_b16 x16", LDS_TR_B64, 0, 0, 0, 16 * 512.0, false},
+        {"exp x8 + fma x8, one wave", EXP_FMA_SAME, 0, 8, 8, 0, false},
+        {"mfma x4 + exp x8 + fma x8, one wave", MFMA_EXP_FMA_SAME, 4, 8, 8, 0, false},
     };
     for (int wps : {1, 2, 4}) {
         for (const Case& cs : cases) {
@@ -203,6 +232,8 @@ int main() {
                 case MFMA_EXP_SPLIT: run<MFMA_EXP_SPLIT>(cs, wps); break;
                 case MFMA_FMA_SPLIT: run<MFMA_FMA_SPLIT>(cs, wps); break;
                 case LDS_B128: run<LDS_B128>(cs, wps); break;
+                case EXP_FMA_SAME: run<EXP_FMA_SAME>(cs, wps); break;
+                case MFMA_EXP_FMA_SAME: run<MFMA_EXP_FMA_SAME>(cs, wps); break;
                 default: run<LDS_TR_B64>(cs, wps); break;
             }
         }
