@@ -79,8 +79,15 @@ constexpr int kRowMinF32 = 128;
 // Share (percent) of the rows that the first half of the streaming kernel's
 // row ranges takes when two of its blocks share a CU (measured on MI355X).
 constexpr int kStreamSplit = 64;
-// Blocks per CU of the backward's dK/dV kernel (row ranges x heads).
+// Grid of the backward's dK/dV kernel, in blocks per CU (row ranges x heads;
+// two of its 4-wave blocks are resident per CU at dh = 64, so larger grids
+// run in rounds).  With fp32 gradients at dh = 64 one block per CU: on the
+// 100K workload the whole backward took 2.97-3.00 ms against 3.19-3.21 ms
+// with four, the dK/dV kernel 2.13 against 2.25 ms (its 16-byte stores then
+// come from fewer concurrent row streams); with bf16 gradients the sweeps
+// disagreed with the profiled run, so four stays.
 constexpr int kDkdvBlocksPerCu = 4;
+constexpr int kDkdvBlocksPerCuF32d64 = 1;
 
 // Everything the dispatcher derives from the problem.
 struct Plan {
@@ -892,8 +899,14 @@ sa_status make_bwd_plan(const sa_problem* pb_in, bool packed, BwdPlan* bp) {
         const int64_t G = (rows_upper + pb->chunk_rows - 1) / pb->chunk_rows;
         bp->G = bp->G1 = (int)(G > 0 ? G : 1);
     } else {
-        bp->G = cus * 2 / groups > 0 ? cus * 2 / groups : 1;
+        // dP pass: blocks of 8 waves; at dh = 64 the ring kernel holds ~150
+        // registers, so one block fits a CU (a grid of two per CU ran in two
+        // rounds: the backward 0.5-0.9 % slower, the dP merge 37 against 20 us
+        // for twice the partials); at dh = 32 (~110 registers) two fit
+        const int dp_bpc = pb->dh == 64 ? 1 : 2;
+        bp->G = cus * dp_bpc / groups > 0 ? cus * dp_bpc / groups : 1;
         int bpc = kDkdvBlocksPerCu;
+        if (pb->dh == 64 && !(pb_in->flags & SA_FLAG_BF16_GRADS)) bpc = kDkdvBlocksPerCuF32d64;
         if (g_tune.bwd_blocks_per_cu > 0) bpc = g_tune.bwd_blocks_per_cu;
         bp->G1 = cus * bpc / pb->H > 0 ? cus * bpc / pb->H : 1;
     }
