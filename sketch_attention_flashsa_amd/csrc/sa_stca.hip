@@ -9,24 +9,32 @@
 // (target, head), then the per-head products with W_V (sa_gemm.hip).
 //
 // Attention block = (user, head pair, 16 targets): 32 query columns, one
-// 16-column MFMA tile per head.  Four waves, one per SIMD; wave w owns
-// channels [w D/4, (w+1) D/4) of the D-wide rows:
-//   * prologue: u^T over the wave's channels (MFMA with W_K and q), staged
-//     through LDS into the score product's B operand, kept in registers;
-//   * loop over 32-row tiles of the rows the block's targets see: the wave's
-//     slice of every row streams through the wave's own two-stage LDS ring by
-//     direct-to-LDS loads (no other wave reads it, so the ring needs no
-//     barrier); partial scores over the wave's channels (MFMA) go to a
-//     double-buffered LDS exchange; after the tile's one block barrier every
-//     wave adds the other three partials to its own (in wave order) and runs
-//     the online softmax on the full scores.  The four waves' sums differ
-//     only in rounding, and each wave normalises its channels with its own
+// 16-column MFMA tile per head.  Eight waves, two per SIMD; wave (cs, hs)
+// owns channels [cs D/4, (cs+1) D/4) of the D-wide rows for head 2 hp + hs,
+// and the two waves of a channel slice (one SIMD) share its ring:
+//   * prologue: u^T over the slice's channels for the wave's head (MFMA with
+//     W_K and q), staged through LDS into the score product's B operand,
+//     kept in registers;
+//   * loop over 32-row tiles of the rows the block's targets see: the slice
+//     of every row streams through the slice's two-stage LDS ring by
+//     direct-to-LDS loads, half of each stage issued by each of its two
+//     waves; partial scores over the slice (MFMA) go to a double-buffered
+//     LDS exchange; the tile's one block barrier certifies the next stage
+//     (each wave has waited for its own half) and frees the slot the wave
+//     pair has read, which is then refilled; every wave adds the other three
+//     slices' partials of its head to its own (in slice order) and runs the
+//     online softmax on the full scores.  The four slices' sums differ only
+//     in rounding, and each wave normalises its channels with its own
 //     running sum, so every output slice is a weighted mean under one
-//     consistent set of weights.  alpha X over the wave's channels
+//     consistent set of weights.  alpha X over the slice's channels
 //     accumulates on MFMA from transposed LDS reads of the same ring stage.
 //     The loop is software-pipelined: tile t+1's scores are computed while
 //     tile t's weights are formed;
 //   * epilogue: alpha X normalised, in bf16, written row by row through LDS.
+// (Four waves each with both heads of a slice ran at one wave per SIMD: the
+// wave then held twice the accumulators and operands, ~450 VGPRs and AGPRs,
+// and its LDS reads, exchange, barrier and MFMAs could not overlap another
+// wave's.)
 // Ring rows are XOR-swizzled per 16-byte chunk so that the row reads of the
 // score product and the transposed reads of the aggregation are both free of
 // bank conflicts.  A sa_stca_prep_kernel launch first builds the block table
@@ -66,16 +74,18 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 v) { return __builtin_convertv
 }  // namespace
 
 template <int D, int DH>
-__global__ __launch_bounds__(256, 1) void sa_stca_kernel(StcaArgs a) {
-    constexpr int NW = kStcaWaves;
-    constexpr int DW = D / NW;             // channels per wave
+__global__ __launch_bounds__(2 * kStcaWaves * 64, 2) void sa_stca_kernel(StcaArgs a) {
+    constexpr int NW = kStcaWaves;         // channel slices
+    constexpr int DW = D / NW;             // channels per slice
     constexpr int KC = DW / 32;            // 32-channel k-steps of the score product
     constexpr int DB = DW / 16;            // 16-channel row blocks of the aggregate
-    constexpr int ROWB = DW * 2;           // bytes of a wave's slice of one row
+    constexpr int ROWB = DW * 2;           // bytes of a slice of one row
     constexpr int STAGE = 32 * ROWB;       // bytes of one 32-row ring stage
-    constexpr int OPS = STAGE / 1024;      // direct-to-LDS ops per stage
+    constexpr int OPS = STAGE / 1024;      // direct-to-LDS ops per stage (both waves of a slice)
+    constexpr int OPW = OPS / 2;           // of them per wave
     constexpr int EK = DH / 32;            // k-steps over dh
-    static_assert(DW == 256 && DH % 32 == 0 && OPS * 1024 == STAGE, "compiled for 256 channels per wave");
+    static_assert(DW == 256 && DH % 32 == 0 && OPS * 1024 == STAGE && OPW * 2 == OPS,
+                  "compiled for 256 channels per slice");
 
     __shared__ __attribute__((aligned(1024))) unsigned char ring[NW][2][STAGE];
     __shared__ __attribute__((aligned(1024))) f32x4 xchg[2][NW][4][64];
@@ -83,6 +93,9 @@ __global__ __launch_bounds__(256, 1) void sa_stca_kernel(StcaArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, l16 = lane & 15;
+    // wave (cs, hs): channel slice cs of head 2 hp + hs; the two waves of a
+    // slice sit on one SIMD and share its ring
+    const int cs = wave & (NW - 1), hs = wave / NW;
 
     // block -> (user, target chunk, head pair): XCD x (blockIdx % 8) takes the
     // x-th contiguous run of the table, so a user's blocks share one L2
@@ -100,6 +113,7 @@ __global__ __launch_bounds__(256, 1) void sa_stca_kernel(StcaArgs a) {
     const int row0 = __builtin_amdgcn_readfirstlane(ent2.x);   // absolute first row the block streams
     const int nrows = __builtin_amdgcn_readfirstlane(ent2.y);
     const int ntiles = (nrows + 31) / 32;
+    const int hh = 2 * hp + hs;            // this wave's head
 
     // this lane's target (column l16) and its window, relative to the
     // block's first row (needed only once the loop starts)
@@ -118,64 +132,60 @@ __global__ __launch_bounds__(256, 1) void sa_stca_kernel(StcaArgs a) {
     }
 
     const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void*)&ring[0][0][0];
-    const uint32_t my_ring = ring_lds + (uint32_t)(wave * 2 * STAGE);
+    const uint32_t my_ring = ring_lds + (uint32_t)(cs * 2 * STAGE);
     const uint32_t xch_lds = (uint32_t)(uintptr_t)(lds_void*)&xchg[0][0][0][0];
 
-
     // ---- prologue: u^T[d][t] = sum_e W_K[d][hh dh + e] q[t][hh dh + e] over
-    // the wave's channels d, both heads (q = x W_Q comes precomputed); staged
-    // through the wave's own ring (as [hsel][t][channel], rows swizzled by t)
-    // into the score B operand
-    bf16x8 uf[2][KC];
+    // the slice's channels d, this wave's head (q = x W_Q comes precomputed);
+    // staged through the slice's ring (as [hs][t][channel], rows swizzled by
+    // t; the two heads' waves write disjoint rows) into the score B operand
+    bf16x8 uf[KC];
     {
+        bf16x8 qb[EK];
 #pragma unroll
-        for (int hsel = 0; hsel < 2; ++hsel) {
-            const int hh = 2 * hp + hsel;
-            bf16x8 qb[EK];
-#pragma unroll
-            for (int ek = 0; ek < EK; ++ek) qb[ek] = *(const bf16x8*)(a.qm + (int64_t)tl * D + hh * DH + 32 * ek + 8 * g);
-            // W_K operands in batches of 32 loads (all of a head's at once for
-            // dh = 64), every load of a batch in flight together
-            constexpr int DTB = 32 / EK;
+        for (int ek = 0; ek < EK; ++ek) qb[ek] = *(const bf16x8*)(a.qm + (int64_t)tl * D + hh * DH + 32 * ek + 8 * g);
+        // W_K operands in batches of 16 loads, every load of a batch in
+        // flight together
+        constexpr int DTB = 16 / EK;
 #pragma unroll 1
-            for (int d0 = 0; d0 < DB; d0 += DTB) {
-                bf16x8 wf[DTB][EK];
+        for (int d0 = 0; d0 < DB; d0 += DTB) {
+            bf16x8 wf[DTB][EK];
 #pragma unroll
-                for (int u = 0; u < DTB; ++u) {
-                    const bf16* wk = a.wk + (int64_t)(wave * DW + 16 * (d0 + u) + l16) * D + hh * DH + 8 * g;
+            for (int u = 0; u < DTB; ++u) {
+                const bf16* wk = a.wk + (int64_t)(cs * DW + 16 * (d0 + u) + l16) * D + hh * DH + 8 * g;
 #pragma unroll
-                    for (int ek = 0; ek < EK; ++ek) wf[u][ek] = *(const bf16x8*)(wk + 32 * ek);
-                }
+                for (int ek = 0; ek < EK; ++ek) wf[u][ek] = *(const bf16x8*)(wk + 32 * ek);
+            }
 #pragma unroll
-                for (int u = 0; u < DTB; ++u) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int u = 0; u < DTB; ++u) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ek = 0; ek < EK; ++ek) acc = mfma(wf[u][ek], qb[ek], acc);
-                    const int dt = d0 + u, row = hsel * 16 + l16, ck = (2 * dt + (g >> 1)) ^ l16;
-                    lds_st_b4(my_ring + (uint32_t)(row * ROWB + ck * 16 + (g & 1) * 8), to_bf16x4(acc));
-                }
+                for (int ek = 0; ek < EK; ++ek) acc = mfma(wf[u][ek], qb[ek], acc);
+                const int dt = d0 + u, row = hs * 16 + l16, ck = (2 * dt + (g >> 1)) ^ l16;
+                lds_st_b4(my_ring + (uint32_t)(row * ROWB + ck * 16 + (g & 1) * 8), to_bf16x4(acc));
             }
         }
 #pragma unroll
-        for (int hsel = 0; hsel < 2; ++hsel)
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                const int row = hsel * 16 + l16, ck = (4 * kc + g) ^ l16;
-                uf[hsel][kc] = lds_ld8(my_ring + (uint32_t)(row * ROWB + ck * 16));
-            }
-        // the ring is about to be refilled
+        for (int kc = 0; kc < KC; ++kc) {
+            const int row = hs * 16 + l16, ck = (4 * kc + g) ^ l16;
+            uf[kc] = lds_ld8(my_ring + (uint32_t)(row * ROWB + ck * 16));
+        }
+        // the ring is about to be refilled: both waves of the slice are done
+        // with it
         wait_lgkm0();
+        block_barrier();
     }
 
-    // ---- streaming
+    // ---- streaming: the two waves of a slice each load half of a stage
     const int64_t xrow = a.x_stride * 2;
-    const unsigned char* Xg = (const unsigned char*)a.X + ((int64_t)row0 * a.x_stride + (int64_t)wave * DW) * 2;
+    const unsigned char* Xg = (const unsigned char*)a.X + ((int64_t)row0 * a.x_stride + (int64_t)cs * DW) * 2;
     auto issue = [&](int t) {
         const uint32_t dst = my_ring + (uint32_t)((t & 1) * STAGE);
         const unsigned char* src = Xg + (int64_t)t * 32 * xrow;
         const int last = nrows - 1 - t * 32;   // rows past the block's end re-read its last row
 #pragma unroll
-        for (int d = 0; d < OPS; ++d) {
+        for (int i = 0; i < OPW; ++i) {
+            const int d = 2 * i + hs;
             const int row = 2 * d + (lane >> 5);          // one op = two 512-byte rows
             const int ck = (lane & 31) ^ stca_swz(row);
             const int rr = min(row, last);
@@ -200,55 +210,52 @@ __global__ __launch_bounds__(256, 1) void sa_stca_kernel(StcaArgs a) {
         for (int m = 0; m < 8; ++m)
             tb8[m] = (uint32_t)(row * ROWB + 32 * (m ^ v) + 16 * ((q >> 1) ^ (g >> 1)) + 8 * (q & 1));
     }
-    uint32_t xo[3];    // exchange slots of the other three waves, in wave order
+    // exchange slot of (slice k, row half r, head hs): [k][2 r + hs]; the
+    // partials of the other three slices, in slice order
+    uint32_t xo[3];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) xo[k] = (uint32_t)((k + (k >= wave ? 1 : 0)) * 4 * 64 * 16 + lane * 16);
+    for (int k = 0; k < 3; ++k) xo[k] = (uint32_t)((k + (k >= cs ? 1 : 0)) * 4 * 64 * 16 + lane * 16);
 
-    // Softmax state per lane (head sb, target l16), in log2 units.  The fast
-    // loop keeps the maximum at M = 0: weights 2^(s c) are used as long as a
+    // Softmax state per lane (target l16), in log2 units.  The fast loop
+    // keeps the maximum at M = 0: weights 2^(s c) are used as long as a
     // lane's tile sum stays within [2^-32, 2^32] (scores of usual scale are far
     // inside), so the accumulator is only ever written by MFMAs.  A wave whose
     // tile falls outside that range (or holds NaN or Inf) finishes the block in
     // the exact loop: running maximum, rescaled accumulator.  Both loops meet
     // the block barrier once per tile at the same point, so waves may switch
     // independently.
-    float Mc[2] = {0.f, 0.f}, Zs[2] = {0.f, 0.f};
-    f32x4 acc[2][DB];
+    float Mc = 0.f, Zs = 0.f;
+    f32x4 acc[DB];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[sb][db] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < DB; ++db) acc[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
     const float c = a.c;
 
     // Software pipeline, per wave: the scores of tile t+1 are computed while
     // the weights of tile t are formed, and tile t+1's transposed operands
-    // are read after tile t's aggregation, so a ring slot is free two tiles
-    // before it is needed again and its load has a whole tile to land.
-    //   stage_scores(k): tile k landed (own loads), partial scores S(k) -> s
-    //   stage_tail(k):   X^T(k) -> lo/hi, S(k) -> exchange buffer k & 1, slot
-    //                    k & 1 refilled with tile k + 2, block barrier
+    // are read after tile t's aggregation.
+    //   stage_scores(k): partial scores S(k) over the slice -> s (tile k was
+    //                    certified by the barrier of stage_tail(k - 1))
+    //   stage_tail(k):   X^T(k) -> lo/hi, S(k) -> exchange buffer k & 1; this
+    //                    wave's part of tile k + 1 landed; block barrier (both
+    //                    waves of a slice are done with slot k & 1, and tile
+    //                    k + 1 is complete); slot k & 1 refilled with tile k + 2
     //   iteration t:     full scores of t from the exchange, stage_scores(t+1),
     //                    weights of t, aggregation of t, stage_tail(t+1)
     // The last iteration runs both stages on stale ring data (results unused),
     // so every wave meets ntiles + 1 barriers whichever loop it is in.
     i16x4 lo[DB], hi[DB];
-    f32x4 s[2][2], tot[2][2];
+    f32x4 s[2], tot[2];
     auto stage_scores = [&](int k) {
-        if (k + 1 < ntiles) wait_vm<OPS>();   // tile k + 1 may still be in flight
-        else wait_vm<0>();
         const uint32_t st = my_ring + (uint32_t)((k & 1) * STAGE);
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
             const uint32_t ad = st + xa[kc & 3] + 256 * (kc >> 2);
             const bf16x8 x0 = lds_ld8(ad);
             const bf16x8 x1 = lds_ld8(ad + 16 * ROWB);
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                const f32x4 z0 = kc == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : s[0][sb];
-                const f32x4 z1 = kc == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : s[1][sb];
-                s[0][sb] = mfma(x0, uf[sb][kc], z0);
-                s[1][sb] = mfma(x1, uf[sb][kc], z1);
-            }
+            const f32x4 z0 = kc == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : s[0];
+            const f32x4 z1 = kc == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : s[1];
+            s[0] = mfma(x0, uf[kc], z0);
+            s[1] = mfma(x1, uf[kc], z1);
         }
     };
     auto stage_tail = [&](int k) {
@@ -261,25 +268,27 @@ __global__ __launch_bounds__(256, 1) void sa_stca_kernel(StcaArgs a) {
         }
         const uint32_t xb = xch_lds + (uint32_t)((k & 1) * NW * 4 * 64 * 16);
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-            lds_st4(xb + (uint32_t)((wave * 4 + r4) * 64 * 16 + lane * 16), s[r4 >> 1][r4 & 1]);
-        // every read of slot k & 1 is done, and the partials are in place
+        for (int r = 0; r < 2; ++r)
+            lds_st4(xb + (uint32_t)((cs * 4 + 2 * r + hs) * 64 * 16 + lane * 16), s[r]);
+        // every read of slot k & 1 is done, the partials are in place, and
+        // this wave's part of tile k + 1 (the only load in flight) has landed
         wait_lgkm0();
-        if (k + 2 < ntiles) issue(k + 2);
+        wait_vm<0>();
         block_barrier();
+        if (k + 2 < ntiles) issue(k + 2);
     };
     auto read_exchange = [&](int t) {
         const uint32_t xb = xch_lds + (uint32_t)((t & 1) * NW * 4 * 64 * 16);
-        f32x4 l[3][4];
+        f32x4 l[3][2];
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
+        for (int r = 0; r < 2; ++r)
 #pragma unroll
-            for (int k = 0; k < 3; ++k) l[k][r4] = lds_ld4(xb + xo[k] + r4 * 64 * 16);
+            for (int k = 0; k < 3; ++k) l[k][r] = lds_ld4(xb + xo[k] + (2 * r + hs) * 64 * 16);
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) tot[r4 >> 1][r4 & 1] = ((tot[r4 >> 1][r4 & 1] + l[0][r4]) + l[1][r4]) + l[2][r4];
+        for (int r = 0; r < 2; ++r) tot[r] = ((tot[r] + l[0][r]) + l[1][r]) + l[2][r];
     };
-    // (alpha X)^T over the wave's channels += X^T p^T
-    auto aggregate = [&](const bf16x8 (&pk)[2]) {
+    // (alpha X)^T over the slice's channels += X^T p^T
+    auto aggregate = [&](const bf16x8& pk) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             union {
@@ -288,8 +297,7 @@ __global__ __launch_bounds__(256, 1) void sa_stca_kernel(StcaArgs a) {
             } vt;
             vt.h[0] = lo[db];
             vt.h[1] = hi[db];
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) acc[sb][db] = mfma(vt.v, pk[sb], acc[sb][db]);
+            acc[db] = mfma(vt.v, pk, acc[db]);
         }
     };
     // rows of tile t inside the lane's window: bit j <-> row tok_of(g, j)
@@ -306,115 +314,105 @@ __global__ __launch_bounds__(256, 1) void sa_stca_kernel(StcaArgs a) {
     if (ntiles > 0) {
         issue(0);
         if (ntiles > 1) issue(1);
+        // tile 0 complete for both waves of the slice (tile 1 may be in flight)
+        if (ntiles > 1) wait_vm<OPW>();
+        else wait_vm<0>();
+        block_barrier();
         stage_scores(0);
         stage_tail(0);
     }
     int t = 0;
     for (; t < ntiles; ++t) {
         // the wave's own partial of tile t is still in s: start the sum with it
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) tot[r4 >> 1][r4 & 1] = s[r4 >> 1][r4 & 1];
+        tot[0] = s[0];
+        tot[1] = s[1];
         read_exchange(t);
         // unconditional (the last tile's extra stage reads stale ring data
         // and is never used) so the MFMAs interleave with the weights below
         stage_scores(t + 1);
-        float p[2][8];
+        float p[8];
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) p[sb][j] = __builtin_amdgcn_exp2f(tot[j >> 2][sb][j & 3] * c);
+        for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(tot[j >> 2][j & 3] * c);
         const bool full = t * 32 >= qlo && t * 32 + 32 <= qhi;
         uint32_t vj = 0xffu;
         if (!__all(full)) {
             vj = valid_bits(t);
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) p[sb][j] = ((vj >> j) & 1) ? p[sb][j] : 0.f;
+            for (int j = 0; j < 8; ++j) p[j] = ((vj >> j) & 1) ? p[j] : 0.f;
         }
-        bf16x8 pk[2];
-        float zt[2];
-        bool fits = true;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            const bf16x2 q0 = pack2(p[sb][0], p[sb][1]), q1 = pack2(p[sb][2], p[sb][3]);
-            const bf16x2 q2 = pack2(p[sb][4], p[sb][5]), q3 = pack2(p[sb][6], p[sb][7]);
-            pk[sb] = cat8(q0, q1, q2, q3);
-            zt[sb] = dot2sum(q3, dot2sum(q2, dot2sum(q1, dot2sum(q0, 0.f))));
-            // false for NaN and Inf too
-            fits = fits && zt[sb] <= kStcaHiBound && (zt[sb] >= kStcaLoBound || vj == 0u);
-        }
+        const bf16x2 q0 = pack2(p[0], p[1]), q1 = pack2(p[2], p[3]);
+        const bf16x2 q2 = pack2(p[4], p[5]), q3 = pack2(p[6], p[7]);
+        const bf16x8 pk = cat8(q0, q1, q2, q3);
+        const float zt = dot2sum(q3, dot2sum(q2, dot2sum(q1, dot2sum(q0, 0.f))));
+        // false for NaN and Inf too
+        const bool fits = zt <= kStcaHiBound && (zt >= kStcaLoBound || vj == 0u);
         if (__builtin_expect(!__all(fits), 0)) break;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) Zs[sb] += zt[sb];
+        Zs += zt;
         aggregate(pk);
         stage_tail(t + 1);
     }
     // exact loop, entered after the scores of tile t + 1 (if any) are in s
     for (bool resume = true; t < ntiles; ++t, resume = false) {
         if (!resume) {
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) tot[r4 >> 1][r4 & 1] = s[r4 >> 1][r4 & 1];
+            tot[0] = s[0];
+            tot[1] = s[1];
             read_exchange(t);
             stage_scores(t + 1);
         }
         const uint32_t vj = valid_bits(t);
-        bf16x8 pk[2];
+        float x[8];
+        float tm = -INFINITY;
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            float x[8];
-            float tm = -INFINITY;
+        for (int j = 0; j < 8; ++j) {
+            x[j] = ((vj >> j) & 1) ? tot[j >> 2][j & 3] * c : -INFINITY;
+            tm = fmaxf(tm, x[j]);
+        }
+        tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
+        tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+        // with no weight accumulated yet the maximum may also move down
+        const float Mold = Mc;
+        const float Mnew = Zs > 0.f ? fmaxf(Mold, tm) : tm;
+        const float f = (Zs > 0.f && Mnew != Mold) ? __builtin_amdgcn_exp2f(Mold - Mnew) : 1.f;
+        float pe[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                x[j] = ((vj >> j) & 1) ? tot[j >> 2][sb][j & 3] * c : -INFINITY;
-                tm = fmaxf(tm, x[j]);
-            }
-            tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
-            tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
-            // with no weight accumulated yet the maximum may also move down
-            const float Mold = Mc[sb];
-            const float Mnew = Zs[sb] > 0.f ? fmaxf(Mold, tm) : tm;
-            const float f = (Zs[sb] > 0.f && Mnew != Mold) ? __builtin_amdgcn_exp2f(Mold - Mnew) : 1.f;
-            float pe[8];
+        for (int j = 0; j < 8; ++j) pe[j] = ((vj >> j) & 1) ? __builtin_amdgcn_exp2f(x[j] - Mnew) : 0.f;
+        const bf16x2 q0 = pack2(pe[0], pe[1]), q1 = pack2(pe[2], pe[3]);
+        const bf16x2 q2 = pack2(pe[4], pe[5]), q3 = pack2(pe[6], pe[7]);
+        const bf16x8 pk = cat8(q0, q1, q2, q3);
+        Zs = fmaf(Zs, f, dot2sum(q3, dot2sum(q2, dot2sum(q1, dot2sum(q0, 0.f)))));
+        if (tm != -INFINITY || Zs > 0.f) Mc = Mnew;
+        if (f != 1.f) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) pe[j] = ((vj >> j) & 1) ? __builtin_amdgcn_exp2f(x[j] - Mnew) : 0.f;
-            const bf16x2 q0 = pack2(pe[0], pe[1]), q1 = pack2(pe[2], pe[3]);
-            const bf16x2 q2 = pack2(pe[4], pe[5]), q3 = pack2(pe[6], pe[7]);
-            pk[sb] = cat8(q0, q1, q2, q3);
-            Zs[sb] = fmaf(Zs[sb], f, dot2sum(q3, dot2sum(q2, dot2sum(q1, dot2sum(q0, 0.f)))));
-            if (tm != -INFINITY || Zs[sb] > 0.f) Mc[sb] = Mnew;
-            if (f != 1.f) {
-#pragma unroll
-                for (int db = 0; db < DB; ++db) scale_in_place_acc(acc[sb][db], f);
-            }
+            for (int db = 0; db < DB; ++db) acc[db] *= f;
         }
         aggregate(pk);
         stage_tail(t + 1);
     }
     wait_lgkm0();
+    // both waves of the slice are done with its ring before it stages the output
+    block_barrier();
 
-    // ---- epilogue: y = acc / Z in bf16, staged through the wave's own ring
-    // as [head sb * 16 + target][channel] (rows swizzled by target) and
-    // written row by row: 512 contiguous bytes per row
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-        float z = Zs[sb];
+    // ---- epilogue: y = acc / Z in bf16, staged through the slice's ring as
+    // [head hs * 16 + target][channel] (rows swizzled by target; the two
+    // heads' waves write disjoint rows) and written row by row: 512
+    // contiguous bytes per row
+    {
+        float z = Zs;
         z += __shfl_xor(z, 16, 64);
         z += __shfl_xor(z, 32, 64);
         const float inv = z > 0.f ? 1.f / z : 0.f;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const int row = sb * 16 + l16, ck = (2 * db + (g >> 1)) ^ l16;
-            lds_st_b4(my_ring + (uint32_t)(row * ROWB + ck * 16 + (g & 1) * 8), to_bf16x4(acc[sb][db] * inv));
+            const int row = hs * 16 + l16, ck = (2 * db + (g >> 1)) ^ l16;
+            lds_st_b4(my_ring + (uint32_t)(row * ROWB + ck * 16 + (g & 1) * 8), to_bf16x4(acc[db] * inv));
         }
     }
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-        const int row = 2 * it + (lane >> 5), c = lane & 31, tt = row & 15;
+    for (int it = 0; it < 8; ++it) {
+        const int tt = 2 * it + (lane >> 5), row = hs * 16 + tt, c2 = lane & 31;
         const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(
-            my_ring + (uint32_t)(row * ROWB + ((c ^ tt) * 16)));
-        if (tt < nt)
-            *(u32x4*)(a.y + ((int64_t)(tb + tt) * a.h + 2 * hp + (row >> 4)) * D + wave * DW + 8 * c) = v;
+            my_ring + (uint32_t)(row * ROWB + ((c2 ^ tt) * 16)));
+        if (tt < nt) *(u32x4*)(a.y + ((int64_t)(tb + tt) * a.h + hh) * D + cs * DW + 8 * c2) = v;
     }
 }
 
@@ -487,8 +485,8 @@ hipError_t launch_stca(const StcaArgs& a, int dh, hipStream_t s) {
     hipLaunchKernelGGL(sa_stca_prep_kernel, dim3(1), dim3(1024), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (dh == 64) hipLaunchKernelGGL((sa_stca_kernel<1024, 64>), dim3(a.grid), dim3(256), 0, s, a);
-    if (dh == 128) hipLaunchKernelGGL((sa_stca_kernel<1024, 128>), dim3(a.grid), dim3(256), 0, s, a);
+    if (dh == 64) hipLaunchKernelGGL((sa_stca_kernel<1024, 64>), dim3(a.grid), dim3(2 * kStcaWaves * 64), 0, s, a);
+    if (dh == 128) hipLaunchKernelGGL((sa_stca_kernel<1024, 128>), dim3(a.grid), dim3(2 * kStcaWaves * 64), 0, s, a);
     return hipGetLastError();
 }
 
