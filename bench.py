@@ -658,6 +658,9 @@ def main():
     ap.add_argument("--grad-dtype", choices=("fp32", "bf16"), default="fp32",
                     help="workload 7: element type of dK and dV")
     ap.add_argument("--cpu-users", type=int, default=4, help="users in the CPU oracle sample")
+    ap.add_argument("--dense-lengths", action="store_true",
+                    help="dense workloads: pass the per-user lengths even when all equal the slot size "
+                         "(adds the kernel that places users on the virtual row axis)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ref-mib", type=int, default=2048,
                     help="workloads 1-4: before the warm-up, measure the device's read and copy rates over a "
@@ -711,7 +714,10 @@ def main():
         keep = np.random.default_rng(77).uniform(size=nrow) >= args.mask_p
         mask = torch.from_numpy(keep.astype(np.uint8)).to(dev)
     cu = w["cu_offsets"].to(dev) if w["layout"] == "packed" else None
-    lengths = w["lengths"].to(dev) if w["layout"] == "dense" else None
+    # dense layout: per-user lengths only when some user is shorter than the
+    # slot (with every length equal to L_max the slot is the whole history)
+    dense_short = w["layout"] == "dense" and int(w["lengths"].min()) < K.shape[1]
+    lengths = w["lengths"].to(dev) if dense_short or (w["layout"] == "dense" and args.dense_lengths) else None
     S = torch.empty((B, H, m, dh), dtype=torch.float32, device=dev)
     pb_kw = {"norm": args.norm}
     proto = args.norm == "prototype"
@@ -757,7 +763,8 @@ def main():
         "dtype": w["dtype"],
         "data": "synthetic (seeded normal draws shaped like the paper's histories)",
         "config": {"workload": spec.name, "B": B, "sum_L": tokens, "L_max": int(w["lengths"].max()), "H": H,
-                   "m": m, "dh": dh, "layout": w["layout"], "mask_p": args.mask_p, "flush_mib": args.flush_mib,
+                   "m": m, "dh": dh, "layout": w["layout"] + ("+lengths" if lengths is not None else ""),
+                   "mask_p": args.mask_p, "flush_mib": args.flush_mib,
                    "flush_kind": args.flush_kind if args.flush_mib else None,
                    "parallelism": "single GPU"},
         "hbm_frac_step": step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS,

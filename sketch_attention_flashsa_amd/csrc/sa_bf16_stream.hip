@@ -195,7 +195,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * blocks_per_cu(DH, NW, NH)) void s
                                             (colb & 15));
     }
 
-    int b = a.users.find(v_lo);
+    int b = a.users.find_wave(v_lo);
     for (; b < a.users.B; ++b) {
         const int64_t us = a.users.vstart(b), ue = a.users.vstart(b + 1);
         if (us >= v_hi) break;

@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
     // state (accumulators, running maxima) never meets at a branch join
     auto segments = [&](auto role_c) {
         constexpr int ROLE = decltype(role_c)::value;
-        int b = a.users.find(v_lo);
+        int b = a.users.find_wave(v_lo);
         for (; b < a.users.B; ++b) {
             const int64_t us = a.users.vstart(b), ue = a.users.vstart(b + 1);
             if (us >= v_hi) break;

@@ -59,6 +59,31 @@ struct Users {
         }
         return lo;
     }
+    // find() with its probes spread over the 64 lanes of a wave: one round of
+    // independent loads per factor of 64 in B (one round for B <= 64)
+    // instead of log2(B) dependent ones, which a kernel otherwise waits for
+    // before its first row load.  Lane k of a round probes lo + k (at most 64
+    // candidates left) or lo + floor(k (hi - lo) / 64); the largest probe
+    // with vstart <= v becomes lo and the next probe hi, so the invariant
+    // vstart(lo) <= v < vstart(hi) of find() holds and, for non-decreasing
+    // offsets, the result equals find()'s.  Every lane of the wave calls it
+    // with the same v.
+    __device__ __forceinline__ int find_wave(int64_t v) const {
+        const int lane = (int)__lane_id();
+        int lo = 0, hi = B;
+        while (hi - lo > 1) {
+            const int64_t span = hi - lo;
+            const int np = span < 64 ? (int)span : 64;            // probes this round
+            auto probe = [&](int k) { return span <= 64 ? lo + k : lo + (int)((span * k) >> 6); };
+            const bool le = lane < np && vstart(probe(lane)) <= v;
+            const uint64_t m = __ballot(le);
+            const int k = m ? 63 - __clzll((long long)m) : 0;
+            const int nlo = probe(k);
+            hi = k + 1 < np ? probe(k + 1) : hi;
+            lo = nlo;
+        }
+        return lo;
+    }
 };
 
 // Rules of the debug offsets check (SA_FLAG_CHECK_OFFSETS), evaluated for

@@ -221,7 +221,7 @@ __global__ __launch_bounds__(NW * 64, NW / 4 * proto_blocks_per_cu(DH, NW, NH)) 
     // (lanes g = 0 and 1 of the head's first wave: row 16 g + l16, = lane)
     const bool lse_writer = LSE && pbi == 0 && g < 2;
 
-    int b = a.users.find(v_lo);
+    int b = a.users.find_wave(v_lo);
     for (; b < a.users.B; ++b) {
         const int64_t us = a.users.vstart(b), ue = a.users.vstart(b + 1);
         if (us >= v_hi) break;

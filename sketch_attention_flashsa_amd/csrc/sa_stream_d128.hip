@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void sa_bf16_stream_d128_kernel(FwdArg
                                             (colb & 15));
     }
 
-    int b = a.users.find(v_lo);
+    int b = a.users.find_wave(v_lo);
     for (; b < a.users.B; ++b) {
         const int64_t us = a.users.vstart(b), ue = a.users.vstart(b + 1);
         if (us >= v_hi) break;
