@@ -57,6 +57,12 @@ namespace {
 
 constexpr int kFStages = 4;   // X ring slots: 3 tiles in flight, 1 computed
 constexpr int kFWaves = 8;    // waves per block: two per head
+// bounds of the running maximum's moves (base-2 exponents): a weight stays
+// below 2^kLazyLog2, so a lane's eight weights of a tile stay within
+// kLazyBound; the first summed mass of a prototype is at least 2^-kFloorLog2
+constexpr float kLazyLog2 = 13.0f;
+constexpr float kFloorLog2 = 60.0f;
+constexpr float kSumFloor = 8.673617379884035e-19f;   // 2^-60
 
 template <int V>
 using Int = std::integral_constant<int, V>;
@@ -248,17 +254,22 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
             // the running maximum M of each of the lane's prototypes is kept
             // negated and broadcast into the score products' accumulator input
             // (one scalar per block: the four-wide tuples would not fit beside
-            // the weight fragments); until the prototype meets a valid row M = 0
-            // and Zs = -1, which sends every tile to the exact path that sets M
+            // the weight fragments).  Every M starts at 0 and moves only when
+            // a tile's weights 2^(s - M) would leave the range the sums keep
+            // exact (see the exact path), so with scores of usual size it stays
+            // 0 for the whole segment; while all of the wave's maxima are 0
+            // (mz) the products take the constant 0 as accumulator input and
+            // no tuple is built.  Zs = 0 until the prototype meets a valid row.
             float nM[NSB];
             float Zs[NSB];
             f32x4 acc[NSB][2];
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
                 nM[sb] = 0.f;
-                Zs[sb] = -1.f;
+                Zs[sb] = 0.f;
                 acc[sb][0] = acc[sb][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
             }
+            bool mz = true;   // wave-uniform: every nM of this wave is 0
 
             // one step t: the softmax of tile t - 1 (ATT; its K and V were
             // published in step t - 1) and the projection of tile t (PROJ), the
@@ -278,9 +289,10 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
                 return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(
                     slot + xoff[kc & 3] + (uint32_t)(rb * 16 * ROWB + 256 * (kc >> 2)));
             };
-            auto step = [&](auto att_c, auto proj_c, int t) {
+            auto step = [&](auto att_c, auto proj_c, auto mz_c, int t) {
                 constexpr bool ATT = decltype(att_c)::value != 0;
                 constexpr bool PROJ = decltype(proj_c)::value != 0;
+                constexpr bool MZ = decltype(mz_c)::value != 0;   // all maxima 0: products from 0
                 bf16x8 ka[2], vt[2];
                 if constexpr (ATT) {
 #pragma unroll
@@ -316,6 +328,12 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
                 if constexpr (NSB > 1) pf[1] = pn[1];
                 // base-2 scores minus the running maximum of block sb
                 auto scores = [&](int sb, f32x4& s0, f32x4& s1) {
+                    if constexpr (MZ) {
+                        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+                        s0 = mfma(ka[0], pf[sb], z4);
+                        s1 = mfma(ka[1], pf[sb], z4);
+                        return;
+                    }
                     float m1 = nM[sb];
                     asm volatile("" : "+v"(m1));   // rebuilt per use, not hoisted
                     const f32x4 c4 = {m1, m1, m1, m1};
@@ -359,16 +377,16 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
                         // summed straight onto Z (the tile's own sum is znew - Z)
                         float znew = dot2sum(q3, dot2sum(q2, dot2sum(q1, dot2sum(q0, Zs[sb]))));
                         // lanes whose tile sum fits (false for NaN and Inf too) and
-                        // whose prototype has met a valid row, as compare masks
+                        // whose running sum is clear of underflow, as compare masks
                         // (ordered <= and >=), so no lane boolean is formed
                         const uint64_t fits = __builtin_amdgcn_fcmpf(znew - Zs[sb], kLazyBound, 5) &
-                                              __builtin_amdgcn_fcmpf(Zs[sb], 0.f, 3);
+                                              __builtin_amdgcn_fcmpf(znew, kSumFloor, 3);
                         // rare exact path (then-only, so the common path keeps its
                         // values in place): validity, running-maximum update, rescale
                         if (__builtin_expect(!(fits == ~0ull && valid_prev == 0xffffffffu), 0)) {
                             // scores relative to 0 again (the products held s - M)
                             const float Mold = -nM[sb];
-                            const bool none = Zs[sb] < 0.f;         // no valid row met yet
+                            const bool none = !(Zs[sb] > 0.f);      // no valid row met yet
                             float x[8];
                             float tm = -INFINITY;
 #pragma unroll
@@ -379,9 +397,17 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
                             }
                             tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
                             tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
-                            const float Mnew = none ? tm : fmaxf(Mold, tm);
-                            const bool found = Mnew != -INFINITY;   // the prototype has a valid row
-                            const float Mset = found ? Mnew : 0.f;
+                            // the maximum moves to the tile's only where it must: when a
+                            // weight 2^(s - M) of the tile could exceed 2^kLazyLog2 (eight
+                            // of them per lane stay within the fast path's bound), or,
+                            // before any mass is summed, when the largest would fall
+                            // below 2^-kFloorLog2 (with no valid row tm is -inf: M stays)
+                            const bool up = tm > Mold + kLazyLog2;
+                            const bool low = none && tm < Mold - kFloorLog2;
+                            const float Mset = (tm != -INFINITY && (up || low)) ? tm : Mold;
+                            if constexpr (MZ) {
+                                if (__ballot(Mset != 0.f) != 0) mz = false;
+                            }
                             const float f = none ? 0.f : (Mset == Mold ? 1.f : __builtin_amdgcn_exp2f(Mold - Mset));
 #pragma unroll
                             for (int j = 0; j < 8; ++j)
@@ -389,8 +415,7 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
                             const bf16x2 e0 = pack2(p[0], p[1]), e1 = pack2(p[2], p[3]);
                             const bf16x2 e2 = pack2(p[4], p[5]), e3 = pack2(p[6], p[7]);
                             pk = cat8(e0, e1, e2, e3);
-                            float zadd = dot2sum(e3, dot2sum(e2, dot2sum(e1, dot2sum(e0, 0.f))));
-                            if (none && !found) zadd = -1.f;        // Zs = -1 * 0 - 1 keeps the sentinel
+                            const float zadd = dot2sum(e3, dot2sum(e2, dot2sum(e1, dot2sum(e0, 0.f))));
                             nM[sb] = -Mset;
                             acc[sb][0] *= f;
                             acc[sb][1] *= f;
@@ -439,17 +464,22 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
             for (int t = 0; t < AHEAD; ++t)
                 if (t < ntiles) issue(t);
 
-            auto run = [&](auto att_c, auto proj_c, int t) {
+            auto run = [&](auto att_c, auto proj_c, auto mz_c, int t) {
                 if (t < ntiles) wait_after<AHEAD - 1, VMS>(min(AHEAD - 1, ntiles - 1 - t));
                 block_barrier();
                 if (t + AHEAD < ntiles) issue(t + AHEAD);
-                if (active) step(att_c, proj_c, t);
+                if (active) step(att_c, proj_c, mz_c, t);
                 // every LDS access of this step has completed before the next barrier
                 wait_lgkm0();
             };
-            run(Int<0>{}, Int<1>{}, 0);
-            for (int t = 1; t < ntiles; ++t) run(Int<1>{}, Int<1>{}, t);
-            run(Int<1>{}, Int<0>{}, ntiles);
+            // steps with every maximum at 0, then (once one has moved: a
+            // wave-uniform, one-way switch) the general steps
+            run(Int<0>{}, Int<1>{}, Int<1>{}, 0);
+            int t = 1;
+            for (; t < ntiles && mz; ++t) run(Int<1>{}, Int<1>{}, Int<1>{}, t);
+            for (; t < ntiles; ++t) run(Int<1>{}, Int<1>{}, Int<0>{}, t);
+            if (mz) run(Int<1>{}, Int<0>{}, Int<1>{}, ntiles);
+            else run(Int<1>{}, Int<0>{}, Int<0>{}, ntiles);
 
             // ---- segment epilogue: partial statistics at slot w + b
             if (active) {
@@ -458,7 +488,7 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
                 for (int sb = 0; sb < NSB; ++sb) {
                     const int j = pbase + 16 * sb + l16;
                     const int64_t base = (slot * a.H + head) * a.m + j;
-                    float z = fmaxf(Zs[sb], 0.f);     // the -1 of a prototype with no valid row
+                    float z = Zs[sb];                 // 0 for a prototype with no valid row
                     z += __shfl_xor(z, 16, 64);
                     z += __shfl_xor(z, 32, 64);
                     if (g == 0) {

@@ -55,6 +55,45 @@ def test_fused_v_equals_x():
     assert_lse(lse, lo, "bf16", "fused, V = X")
 
 
+@pytest.mark.parametrize("offset,ramp", [(100.0, 0.0), (-200.0, 0.0), (0.0, 0.05), (0.0, -0.05), (60.0, 0.02)])
+def test_fused_running_maximum_moves(offset, ramp):
+    """Scores far from 0, and scores that rise or fall along each user's rows.
+    The fused kernel keeps each running maximum at 0 while the weights 2^s stay
+    in range and moves it only where they would not, so these cases take the
+    moves up (offset +100, rising ramps), the move down before any mass is
+    summed (offset -200) and the lazy steps between.  Model channel 0 of X
+    carries the shift: column h dh of W_K reads that channel alone (weight 1),
+    channel 0 of every prototype is 4, so a row's base-2 scores move by
+    offset + ramp * (its index in the user).  The scale is the float nearest
+    1 / log2(e), for which the kernel's pre-scaled prototypes are exact, so
+    scores of several hundred keep the lse bar."""
+    d_model, H, m, dh = 128, 4, 64, 32
+    unit_scale = float(np.float32(1.0) / np.float32(np.log2(np.e)))
+    w = W.random_fused_case(211 + int(offset) + int(100 * ramp), B=3, H=H, m=m, dh=dh, d_model=d_model,
+                            lengths=[3000, 777, 65])
+    X, Wk, P = w["X"].float(), w["Wk"].float(), w["P"].float()
+    cu = w["cu_offsets"].tolist()
+    unit = 0.25                                       # X[:, 0] per base-2 unit of score
+    for b in range(3):
+        r = torch.arange(cu[b + 1] - cu[b], dtype=torch.float32)
+        X[cu[b]:cu[b + 1], 0] = (offset + ramp * r) * unit
+    Wk[0, :] = 0.0
+    for h in range(H):
+        Wk[:, h * dh] = 0.0
+        Wk[0, h * dh] = 1.0
+    # the other channels at the usual size of base-2 scores (the unit scale
+    # drops the 1 / sqrt(dh)), so the rounding of the projected keys stays as
+    # small against the lse bar as at the default scale
+    P[:, :, 1:] *= 1.0 / np.sqrt(dh)
+    P[:, :, 0] = 4.0
+    w = dict(w, X=X.to(torch.bfloat16), Wk=Wk.to(torch.bfloat16), P=P.to(torch.bfloat16))
+    S, lse = run_fused(w, scale=unit_scale)
+    So, lo = oracle.fused_forward(w["X"], w["Wk"], w["Wv"], w["P"], w["cu_offsets"], scale=unit_scale)
+    assert np.all(np.isfinite(S)) and np.all(np.isfinite(lse))
+    assert_parity(S, So, "bf16", f"fused, offset {offset}, ramp {ramp}")
+    assert_lse(lse, lo, "bf16", f"fused, offset {offset}, ramp {ramp}")
+
+
 @pytest.mark.parametrize("d_model,H,m", [(256, 8, 256), (256, 8, 128), (256, 8, 64), (128, 4, 256), (128, 4, 64),
                                          (256, 5, 128)])
 def test_fused_shapes_ragged(d_model, H, m):
