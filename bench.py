@@ -240,6 +240,85 @@ def _emit(out: dict) -> None:
     print(json.dumps(out))
 
 
+def _power_file():
+    """The board power reading of the one visible GPU (amdgpu hwmon
+    power1_input, microwatts) and its cap, or (None, None)."""
+    import glob
+    found = []
+    for d in sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*")):
+        try:
+            with open(os.path.join(d, "name")) as fh:
+                if fh.read().strip() != "amdgpu":
+                    continue
+            with open(os.path.join(d, "power1_input")) as fh:
+                int(fh.read())
+        except (OSError, ValueError):
+            continue
+        cap = None
+        try:
+            with open(os.path.join(d, "power1_cap")) as fh:
+                cap = int(fh.read()) / 1e6
+        except (OSError, ValueError):
+            pass
+        found.append((os.path.join(d, "power1_input"), cap))
+    return found[0] if len(found) == 1 else (None, None)
+
+
+def power_leg(step, seconds: float):
+    """Back-to-back steps for ``seconds`` while a thread reads the board's
+    power every 5 ms: the loaded power (against the board's cap) and the
+    kernel's event-timed duration under it.  None without a readable power
+    file (or with several GPUs' files, which would be ambiguous)."""
+    import threading
+    import torch
+    import sketch_attention_flashsa_amd as sa
+    path, cap = _power_file()
+    if path is None or seconds <= 0:
+        return None
+    hip = _Hip()
+    watts, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                with open(path) as fh:
+                    watts.append(int(fh.read()) / 1e6)
+            except (OSError, ValueError):
+                pass
+            time.sleep(0.005)
+
+    th = threading.Thread(target=sample, daemon=True)
+    kern = []
+    evs = [(hip.event(), hip.event()) for _ in range(8)]
+    n = 0
+    t0 = time.perf_counter()
+    th.start()
+    try:
+        while time.perf_counter() - t0 < seconds:
+            # launches in batches of 64 (events on 8 of them), so the queue
+            # stays short; the chip never idles between batches for long
+            for i in range(64):
+                if i % 8 == 0:
+                    a, b = evs[i // 8]
+                    sa.sa_set_timing_events(a, b)
+                step()
+            torch.cuda.synchronize()
+            kern.extend(hip.elapsed_ms(a, b) for a, b in evs)
+            n += 64
+    finally:
+        stop.set()
+        th.join()
+        for a, b in evs:
+            hip.destroy(a)
+            hip.destroy(b)
+    dt = time.perf_counter() - t0
+    # the first 0.5 s of samples cover the ramp to the loaded state
+    tail = [w for i, w in enumerate(watts) if i * 0.005 >= 0.5] or watts
+    return {"seconds": round(dt, 3), "steps": n, "board_power_w_avg": sum(tail) / len(tail) if tail else None,
+            "board_power_w_max": max(watts) if watts else None, "power_cap_w": cap, "power_samples": len(watts),
+            "kernel_ms_avg": sum(kern) / len(kern), "kernel_ms_p10_p50_p90": _percentiles(kern)}
+
+
 def _timed(step, steps: int, warmup: int, flush_mib: int = 0, flush_kind: str = "write"):
     """Run warmup + timed steps; returns (ms per step, the streaming kernel's
     HIP-event durations in ms).  ms per step is the wall clock over the timed
@@ -658,6 +737,9 @@ def main():
     ap.add_argument("--grad-dtype", choices=("fp32", "bf16"), default="fp32",
                     help="workload 7: element type of dK and dV")
     ap.add_argument("--cpu-users", type=int, default=4, help="users in the CPU oracle sample")
+    ap.add_argument("--power-s", type=float, default=2.0,
+                    help="workloads 1-4: after the timed steps, this many seconds of back-to-back steps with the "
+                         "board power read every 5 ms (0: skip); reported as sustained_power")
     ap.add_argument("--dense-lengths", action="store_true",
                     help="dense workloads: pass the per-user lengths even when all equal the slot size "
                          "(adds the kernel that places users on the virtual row axis)")
@@ -791,6 +873,11 @@ def main():
     if idle is not None:
         idle["frac"] = alg_bytes / (idle["kernel_ms_avg_timed_launches"] / 1e3) / 1e9 / HBM_PEAK_GBS
         out["from_idle"] = idle
+    if args.flush_mib == 0 and args.power_s > 0 and not two_pass:
+        pw = power_leg(step, args.power_s)
+        if pw is not None:
+            pw["frac"] = alg_bytes / (pw["kernel_ms_avg"] / 1e3) / 1e9 / HBM_PEAK_GBS
+            out["sustained_power"] = pw
     if args.flush_mib == 0 and args.cold_mib > 0 and not two_pass:
         # the same launches with a buffer overwritten before each one (after
         # the timed region above, which it does not affect): no input left in

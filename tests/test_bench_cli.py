@@ -41,3 +41,32 @@ def test_traffic_only_for_matching_sources(monkeypatch):
     assert b._traffic(rec["kernel"]) == rec["hbm_bytes_per_launch"]
     monkeypatch.setattr(b, "_kernel_hash", lambda k="": "0" * 16)
     assert b._traffic(rec["kernel"]) is None
+
+
+def test_power_file_picks_the_one_amdgpu_reading(tmp_path, monkeypatch):
+    """The sustained-power leg reads the amdgpu hwmon power1_input (and its
+    cap) of exactly one card; other hwmon devices, unreadable files and
+    several amdgpu cards give no reading."""
+    import glob as globmod
+    b = _load()
+
+    def card(n, name, power="269000000", cap="1400000000"):
+        d = tmp_path / f"card{n}" / "device" / "hwmon" / f"hwmon{n}"
+        d.mkdir(parents=True)
+        (d / "name").write_text(name + "\n")
+        if power is not None:
+            (d / "power1_input").write_text(power + "\n")
+        if cap is not None:
+            (d / "power1_cap").write_text(cap + "\n")
+        return str(d)
+
+    real_glob = globmod.glob
+    monkeypatch.setattr(globmod, "glob", lambda pat: real_glob(pat.replace("/sys/class/drm", str(tmp_path))))
+    assert b._power_file() == (None, None)
+    card(0, "k10temp")
+    card(1, "amdgpu", power=None)
+    assert b._power_file() == (None, None)
+    d = card(2, "amdgpu")
+    assert b._power_file() == (os.path.join(d, "power1_input"), 1400.0)
+    card(3, "amdgpu")
+    assert b._power_file() == (None, None)
