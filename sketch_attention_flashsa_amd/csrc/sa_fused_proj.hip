@@ -269,7 +269,10 @@ __global__ __launch_bounds__(kFWaves * 64, 1) void sa_fused_proj_kernel(FusedArg
                 Zs[sb] = 0.f;
                 acc[sb][0] = acc[sb][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
             }
-            bool mz = true;   // wave-uniform: every nM of this wave is 0
+            // wave-uniform: every nM of this wave is 0.  With a mask most tiles
+            // hold an excluded row and take the exact path anyway, so masked
+            // instances run the general loop alone (one loop: no spills)
+            bool mz = !MASKED;
 
             // one step t: the softmax of tile t - 1 (ATT; its K and V were
             // published in step t - 1) and the projection of tile t (PROJ), the
